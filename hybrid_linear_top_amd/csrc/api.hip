@@ -1,0 +1,318 @@
+// C ABI of the LISA layer: argument validation, workspace layout and the
+// launch sequence of each entry point.  Every check runs before the first
+// HIP call, so a rejected call enqueues nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "lisa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lisa_status fail(lisa_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+lisa_status ok() {
+    g_err[0] = 0;
+    return LISA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(int dtype) { return dtype == LISA_BF16 ? 2 : 4; }
+
+lisa_status check_dims(const lisa_dims *d, bool prefill) {
+    if (!d) return fail(LISA_ERR_INVALID_ARGUMENT, "dims is NULL");
+    if (d->dtype != LISA_F32 && d->dtype != LISA_BF16)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "dtype %d is neither LISA_F32 nor LISA_BF16", d->dtype);
+    if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Hq=%d, Hkv=%d)",
+                    d->num_q_heads, d->num_kv_heads);
+    if (d->num_q_heads % d->num_kv_heads != 0)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    d->num_q_heads, d->num_kv_heads);
+    if (d->num_q_heads / d->num_kv_heads > 16)
+        return fail(LISA_ERR_UNSUPPORTED, "more than 16 query heads per KV group (%d)",
+                    d->num_q_heads / d->num_kv_heads);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(LISA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", d->head_dim);
+    if (d->idx_dim != 32 && d->idx_dim != 64)
+        return fail(LISA_ERR_UNSUPPORTED, "idx_dim %d not in {32, 64}", d->idx_dim);
+    if (d->idx_heads < 1 || d->idx_heads > 8)
+        return fail(LISA_ERR_UNSUPPORTED, "idx_heads %d not in [1, 8]", d->idx_heads);
+    const int mmax = prefill ? 512 : 2048;
+    if (d->top_m < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "top_m %d must be >= 1", d->top_m);
+    if (d->top_m > mmax)
+        return fail(LISA_ERR_UNSUPPORTED, "top_m %d above the supported %d", d->top_m, mmax);
+    if (d->chunk != 0 && d->chunk != 64)
+        return fail(LISA_ERR_UNSUPPORTED, "chunk %d not in {0, 64}", d->chunk);
+    if (!std::isfinite(d->softmax_scale))
+        return fail(LISA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+    return LISA_OK;
+}
+
+float scale_log2(const lisa_dims *d) {
+    const double s = d->softmax_scale > 0.0f ? (double)d->softmax_scale : 1.0 / std::sqrt((double)d->head_dim);
+    return (float)(s * 1.4426950408889634);
+}
+
+// ---- prefill workspace ------------------------------------------------------
+struct PrefillWs {
+    size_t idx, dS, P, total;
+};
+PrefillWs prefill_ws(const lisa_dims *d, int B, int n) {
+    const size_t G = d->num_kv_heads, Hq = d->num_q_heads, D = d->head_dim;
+    const size_t nC = ((size_t)n + 63) / 64;
+    PrefillWs w;
+    size_t off = 0;
+    w.idx = off;
+    off += align_up((size_t)B * n * G * d->top_m * 4);
+    w.dS = off;
+    off += align_up((size_t)B * G * nC * D * D * 4);
+    w.P = off;
+    off += align_up((size_t)B * Hq * nC * D * D * elt_bytes(d->dtype));
+    w.total = off;
+    return w;
+}
+
+struct DecodeWs {
+    size_t scores, olin, idx, total;
+};
+DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
+    const size_t G = d->num_kv_heads, Hq = d->num_q_heads, D = d->head_dim;
+    DecodeWs w;
+    size_t off = 0;
+    w.scores = off;
+    off += align_up((size_t)B * G * (size_t)max_ctx * 4);
+    w.olin = off;
+    off += align_up((size_t)B * Hq * D * 4);
+    w.idx = off;
+    off += align_up((size_t)B * G * d->top_m * 4);
+    w.total = off;
+    return w;
+}
+
+#define LISA_NEED(p, name)                                                                  \
+    do {                                                                                    \
+        if (!(p)) return fail(LISA_ERR_INVALID_ARGUMENT, "%s is NULL", name);               \
+        if (!aligned16(p)) return fail(LISA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
+    } while (0)
+#define LISA_OPT(p, name)                                                                   \
+    do {                                                                                    \
+        if ((p) && !aligned16(p))                                                           \
+            return fail(LISA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);      \
+    } while (0)
+#define LISA_HIP(call, what)                                                                \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail(LISA_ERR_HIP, "%s: %s", what, hipGetErrorString(e_));               \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *lisa_last_error(void) { return g_err; }
+
+const char *lisa_build_info(void) {
+    return "lisa-mi355x 0.1 (gfx950)";
+}
+
+lisa_status lisa_prefill_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
+                                         size_t *bytes) {
+    lisa_status st = check_dims(dims, true);
+    if (st) return st;
+    if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
+    if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
+    *bytes = prefill_ws(dims, B, n).total;
+    return ok();
+}
+
+lisa_status lisa_decode_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t max_ctx,
+                                        size_t *bytes) {
+    lisa_status st = check_dims(dims, false);
+    if (st) return st;
+    if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (B < 0 || max_ctx < 1)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0 and max_ctx=%d >= 1", B, max_ctx);
+    *bytes = decode_ws(dims, B, max_ctx).total;
+    return ok();
+}
+
+lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void *q,
+                         const void *k, const void *v, const void *q_idx, const void *k_idx,
+                         const void *w_idx, const void *gate, const float *state_in, void *out,
+                         float *state_out, int32_t *topm_out, void *workspace,
+                         size_t workspace_bytes, lisa_stream_t stream) {
+    lisa_status st = check_dims(dims, true);
+    if (st) return st;
+    if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
+    if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
+    if (B == 0 || n == 0) return ok();
+    LISA_NEED(q, "q");
+    LISA_NEED(k, "k");
+    LISA_NEED(v, "v");
+    LISA_NEED(q_idx, "q_idx");
+    LISA_NEED(k_idx, "k_idx");
+    LISA_NEED(w_idx, "w_idx");
+    LISA_NEED(gate, "gate");
+    LISA_NEED(out, "out");
+    LISA_OPT(state_in, "state_in");
+    LISA_OPT(state_out, "state_out");
+    LISA_OPT(topm_out, "topm_out");
+    LISA_NEED(workspace, "workspace");
+    const PrefillWs w = prefill_ws(dims, B, n);
+    if (workspace_bytes < w.total)
+        return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const int G = dims->num_kv_heads, Hq = dims->num_q_heads, D = dims->head_dim;
+    int32_t *idx = topm_out ? topm_out : reinterpret_cast<int32_t *>(ws + w.idx);
+
+    lisa::LinearArgs la{};
+    la.q = q;
+    la.k = k;
+    la.v = v;
+    la.state_in = state_in;
+    la.state_out = state_out;
+    la.dS = reinterpret_cast<float *>(ws + w.dS);
+    la.P = ws + w.P;
+    la.out = out;
+    la.B = B;
+    la.n = n;
+    la.Hq = Hq;
+    la.G = G;
+    la.r = Hq / G;
+    la.nC = (n + 63) / 64;
+    la.per_head = state_in != nullptr;
+    LISA_HIP(lisa::launch_linear_prefill(la, dims->dtype, D, s), "linear-attention launch");
+
+    lisa::IndexerArgs ia{};
+    ia.q_idx = q_idx;
+    ia.k_idx = k_idx;
+    ia.w_idx = w_idx;
+    ia.idx = idx;
+    ia.B = B;
+    ia.n = n;
+    ia.G = G;
+    ia.HI = dims->idx_heads;
+    ia.M = dims->top_m;
+    LISA_HIP(lisa::launch_indexer_prefill(ia, dims->dtype, dims->idx_dim, s), "indexer launch");
+
+    lisa::SparseArgs sa{};
+    sa.q = q;
+    sa.k = k;
+    sa.v = v;
+    sa.cu = nullptr;
+    sa.idx = idx;
+    sa.lin = out;
+    sa.gate = gate;
+    sa.out = out;
+    sa.B = B;
+    sa.n = n;
+    sa.Hq = Hq;
+    sa.G = G;
+    sa.r = Hq / G;
+    sa.M = dims->top_m;
+    sa.max_ctx = n;
+    sa.scale_log2 = scale_log2(dims);
+    sa.units = B * n * G;
+    LISA_HIP(lisa::launch_sparse_gate(sa, dims->dtype, D, false, s), "sparse-attention launch");
+    return ok();
+}
+
+lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
+                             int32_t max_ctx, const void *q, const void *k_cache,
+                             const void *v_cache, const void *q_idx, const void *k_idx_cache,
+                             const void *w_idx, const void *gate, float *state, void *out,
+                             int32_t *topm_out, void *workspace, size_t workspace_bytes,
+                             lisa_stream_t stream) {
+    lisa_status st = check_dims(dims, false);
+    if (st) return st;
+    if (B < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
+    if (max_ctx < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "max_ctx=%d must be >= 1", max_ctx);
+    if (B == 0) return ok();
+    if (!cu_ctx) return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is NULL");
+    if (reinterpret_cast<uintptr_t>(cu_ctx) & 7u)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is not 8-byte aligned");
+    LISA_NEED(q, "q");
+    LISA_NEED(k_cache, "k_cache");
+    LISA_NEED(v_cache, "v_cache");
+    LISA_NEED(q_idx, "q_idx");
+    LISA_NEED(k_idx_cache, "k_idx_cache");
+    LISA_NEED(w_idx, "w_idx");
+    LISA_NEED(gate, "gate");
+    LISA_NEED(state, "state");
+    LISA_NEED(out, "out");
+    LISA_OPT(topm_out, "topm_out");
+    LISA_NEED(workspace, "workspace");
+    const DecodeWs w = decode_ws(dims, B, max_ctx);
+    if (workspace_bytes < w.total)
+        return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const int G = dims->num_kv_heads, Hq = dims->num_q_heads, D = dims->head_dim;
+    float *scores = reinterpret_cast<float *>(ws + w.scores);
+    float *olin = reinterpret_cast<float *>(ws + w.olin);
+    int32_t *idx = topm_out ? topm_out : reinterpret_cast<int32_t *>(ws + w.idx);
+
+    lisa::DecodeScoreArgs da{};
+    da.q = q;
+    da.k_cache = k_cache;
+    da.v_cache = v_cache;
+    da.q_idx = q_idx;
+    da.k_idx_cache = k_idx_cache;
+    da.w_idx = w_idx;
+    da.cu = cu_ctx;
+    da.state = state;
+    da.olin = olin;
+    da.scores = scores;
+    da.B = B;
+    da.Hq = Hq;
+    da.G = G;
+    da.HI = dims->idx_heads;
+    da.max_ctx = max_ctx;
+    da.tiles_per_seq = (max_ctx + lisa::kDecodeTile - 1) / lisa::kDecodeTile;
+    LISA_HIP(lisa::launch_decode_score_state(da, dims->dtype, D, dims->idx_dim, s),
+             "indexer-scan/state launch");
+    LISA_HIP(lisa::launch_decode_select(scores, cu_ctx, B, G, dims->top_m, max_ctx, idx, s),
+             "top-M select launch");
+
+    lisa::SparseArgs sa{};
+    sa.q = q;
+    sa.k = k_cache;
+    sa.v = v_cache;
+    sa.cu = cu_ctx;
+    sa.idx = idx;
+    sa.lin = olin;
+    sa.gate = gate;
+    sa.out = out;
+    sa.B = B;
+    sa.n = 1;
+    sa.Hq = Hq;
+    sa.G = G;
+    sa.r = Hq / G;
+    sa.M = dims->top_m;
+    sa.max_ctx = max_ctx;
+    sa.scale_log2 = scale_log2(dims);
+    sa.units = B * G;
+    LISA_HIP(lisa::launch_sparse_gate(sa, dims->dtype, D, true, s), "sparse-attention launch");
+    return ok();
+}
+
+}  // extern "C"

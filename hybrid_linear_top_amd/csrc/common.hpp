@@ -1,0 +1,157 @@
+// Device helpers shared by the LISA kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lisa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Element traits: storage type T is uint16_t (bf16 bit pattern) or float.
+template <typename T> struct Elt;
+template <> struct Elt<uint16_t> {
+    static constexpr int kBytes = 2;
+    __device__ static __forceinline__ float load(const uint16_t *p) { return bf16_bits_to_f32(*p); }
+    __device__ static __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+    __device__ static __forceinline__ uint16_t from_f32(float f) { return (uint16_t)f32_to_bf16_bits(f); }
+};
+template <> struct Elt<float> {
+    static constexpr int kBytes = 4;
+    __device__ static __forceinline__ float load(const float *p) { return *p; }
+    __device__ static __forceinline__ float to_f32(float x) { return x; }
+    __device__ static __forceinline__ float from_f32(float f) { return f; }
+};
+
+// A 16x16x32 MFMA operand fragment: 8 consecutive K-elements of one row (A)
+// or one column (B) per lane.  Lane l covers row/column l%16 and K-elements
+// 8*(l/16) .. 8*(l/16)+7.  bf16 uses one v_mfma_f32_16x16x32_bf16; fp32 uses
+// eight v_mfma_f32_16x16x4_f32, element e of every lane forming the e-th
+// K-slice.  Both produce the same accumulator layout: lane l holds
+// D[4*(l/16)+r][l%16], r = 0..3.
+template <typename T> struct Frag;
+template <> struct Frag<uint16_t> {
+    u32x4 v;
+    __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ void load(const uint16_t *p) { v = *reinterpret_cast<const u32x4 *>(p); }
+    // set from 8 fp32 values (rounded to bf16)
+    __device__ __forceinline__ void set(const float *x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+    }
+    __device__ __forceinline__ void set_bits(const uint16_t *x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (uint32_t)x[2 * i] | ((uint32_t)x[2 * i + 1] << 16);
+    }
+};
+template <> struct Frag<float> {
+    f32x4 lo, hi;
+    __device__ __forceinline__ void zero() { lo = f32x4{0, 0, 0, 0}; hi = lo; }
+    __device__ __forceinline__ void load(const float *p) {
+        lo = reinterpret_cast<const f32x4 *>(p)[0];
+        hi = reinterpret_cast<const f32x4 *>(p)[1];
+    }
+    __device__ __forceinline__ void set(const float *x) {
+        lo = f32x4{x[0], x[1], x[2], x[3]};
+        hi = f32x4{x[4], x[5], x[6], x[7]};
+    }
+    __device__ __forceinline__ void set_bits(const float *x) { set(x); }
+};
+
+__device__ __forceinline__ f32x4 mma16(const Frag<uint16_t> &a, const Frag<uint16_t> &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                   __builtin_bit_cast(bf16x8_t, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const Frag<float> &a, const Frag<float> &b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+    return c;
+}
+
+// Total order on fp32 scores as unsigned keys: larger key = larger score;
+// -0.0 and +0.0 map to the same key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (f == 0.0f) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip, each
+// with its own L2.  Map the hardware block id to a logical id such that each
+// XCD receives one contiguous range of logical ids (neighbouring logical
+// blocks then share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    constexpr int X = 8;
+    const int per = nblocks / X, rem = nblocks % X;
+    const int xcd = bid % X, j = bid / X;
+    return xcd * per + (xcd < rem ? xcd : rem) + j;
+}
+
+// Make this wave's LDS writes visible to its own lanes before they read.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_max_across16(float v) {  // over lanes l, l^16, l^32, l^48
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_across16(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT multiple of 64).
+// `tmp` must hold NT/64 + 1 words; returns the exclusive prefix and the
+// block total in *total.  Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = wave_inclusive_scan(v);
+    if (lane == 63) tmp[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0;
+        for (int w = 0; w < NT / 64; ++w) { uint32_t x = tmp[w]; tmp[w] = run; run += x; }
+        tmp[NT / 64] = run;
+    }
+    __syncthreads();
+    uint32_t res = tmp[wave] + inc - v;
+    *total = tmp[NT / 64];
+    __syncthreads();
+    return res;
+}
+
+}  // namespace lisa

@@ -1,0 +1,292 @@
+// Decode-step kernels of the LISA layer on gfx950.
+//
+// (1) decode_score_state: one launch with two kinds of work-groups.
+//   * score groups stream the packed indexer-key cache k_idx and write, for
+//     the new token t = L_b - 1 of every sequence, the Lightning Indexer score
+//     I(s) = sum_j w_j * max(0, q_idx_j . k_idx_s) of every visible token s
+//     (the indexer scans the full context with a ReLU'd dot product: arxivdaily
+//     page for arXiv 2607.19358, English abstract; gptget.net analysis,
+//     method-details section).  This stream is the largest HBM consumer of a
+//     decode step, so it is laid out for coalescing: each wave reads whole
+//     128/256-byte key rows, 16 bytes per lane, and reduces the per-lane
+//     partial dot products across the lanes of a row.
+//   * state groups do the linear-attention step of one query head:
+//     S_t = S_{t-1} + k_t v_t^T in place and o_lin = q_t^T S_t (identity
+//     feature map and state matrix S_t, O(1) per token: gptget.net,
+//     method-details section), one read-modify-write pass over the fp32 state.
+//   Both halves are HBM streams of similar size per group, so they share a
+//   grid and fill the chip together.
+// (2) decode_select: per (sequence, group) radix select of the top-M scores
+//   (M = 256 in the paper's runs: gptget.net, experiment-design section)
+//   with the lower index winning ties; the set is written in ascending order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lisa {
+
+namespace {
+
+// dot product of one 16-byte chunk of keys with the matching chunk of an
+// indexer query (kept packed in the storage format).
+__device__ __forceinline__ float chunk_dot(const u32x4 &k, const u32x4 &q, uint16_t) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[i]),
+                                              __builtin_bit_cast(bf16x2_t, k[i]), acc, false);
+    return acc;
+}
+__device__ __forceinline__ float chunk_dot(const u32x4 &k, const u32x4 &q, float) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), acc);
+    return acc;
+}
+
+template <typename T, int DI, int HIPAD>
+__device__ void score_group(const DecodeScoreArgs &a, int sb) {
+    constexpr int EPC = 16 / Elt<T>::kBytes;  // elements per 16-byte chunk
+    constexpr int CPR = DI / EPC;             // lanes per key row
+    constexpr int RPI = 64 / CPR;             // rows per wave iteration
+    constexpr int TPW = 64;                   // tokens per wave task
+    constexpr int NIT = TPW / RPI;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int b = sb / a.tiles_per_seq, tile = sb % a.tiles_per_seq;
+    const int64_t row0 = a.cu[b];
+    const int L = (int)min((int64_t)a.max_ctx, a.cu[b + 1] - row0);
+    const int tok0 = tile * kDecodeTile;
+    if (tok0 >= L) return;
+    const int tok_end = min(tok0 + kDecodeTile, L);
+    const int c = lane % CPR, rr = lane / CPR;
+    const int G = a.G;
+    const int ntask = G * (kDecodeTile / TPW);
+    const T *qI = reinterpret_cast<const T *>(a.q_idx);
+    const T *wI = reinterpret_cast<const T *>(a.w_idx);
+    const T *kI = reinterpret_cast<const T *>(a.k_idx_cache);
+    for (int task = wave; task < ntask; task += 4) {
+        const int g = task % G, sub = task / G;
+        const int tb = tok0 + sub * TPW;
+        if (tb >= tok_end) continue;
+        u32x4 qv[HIPAD];
+        float wv[HIPAD];
+#pragma unroll
+        for (int j = 0; j < HIPAD; ++j) {
+            if (j < a.HI) {
+                qv[j] = *reinterpret_cast<const u32x4 *>(qI + ((size_t)(b * G + g) * a.HI + j) * DI +
+                                                         c * EPC);
+                wv[j] = Elt<T>::to_f32(wI[(size_t)(b * G + g) * a.HI + j]);
+            } else {
+                qv[j] = u32x4{0u, 0u, 0u, 0u};
+                wv[j] = 0.0f;
+            }
+        }
+        u32x4 raw[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int tok = tb + it * RPI + rr;
+            if (tok < tok_end)
+                raw[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    kI + ((size_t)(row0 + tok) * G + g) * DI + c * EPC));
+            else
+                raw[it] = u32x4{0u, 0u, 0u, 0u};
+        }
+        float *out = a.scores + (size_t)(b * G + g) * a.max_ctx;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            float score = 0.0f;
+#pragma unroll
+            for (int j = 0; j < HIPAD; ++j) {
+                float p = chunk_dot(raw[it], qv[j], T{});
+#pragma unroll
+                for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o);
+                score = fmaf(wv[j], fmaxf(p, 0.0f), score);
+            }
+            const int tok = tb + it * RPI + rr;
+            if (c == 0 && tok < tok_end) out[tok] = score;
+        }
+    }
+}
+
+template <typename T, int D>
+__device__ void state_group(const DecodeScoreArgs &a, int u, float *smem) {
+    const int tid = threadIdx.x;
+    const int Hq = a.Hq, b = u / Hq, h = u % Hq;
+    const int g = (int)(((int64_t)h * a.G) / Hq);
+    const int64_t row0 = a.cu[b];
+    const int L = (int)min((int64_t)a.max_ctx, a.cu[b + 1] - row0);
+    float *olin = a.olin + ((size_t)b * Hq + h) * D;
+    if (L < 1) {
+        if (tid < D) olin[tid] = 0.0f;
+        return;
+    }
+    const int64_t trow = row0 + L - 1;
+    float *kk = smem, *vv = smem + D, *qq = smem + 2 * D, *red = smem + 3 * D;
+    const T *kc = reinterpret_cast<const T *>(a.k_cache);
+    const T *vc = reinterpret_cast<const T *>(a.v_cache);
+    const T *qp = reinterpret_cast<const T *>(a.q);
+    if (tid < D) {
+        kk[tid] = Elt<T>::to_f32(kc[((size_t)trow * a.G + g) * D + tid]);
+        vv[tid] = Elt<T>::to_f32(vc[((size_t)trow * a.G + g) * D + tid]);
+        qq[tid] = Elt<T>::to_f32(qp[((size_t)b * Hq + h) * D + tid]);
+    }
+    __syncthreads();
+    constexpr int NQ = D / 4, RG = 256 / NQ, RPT = D / RG;
+    const int jq = tid % NQ, rg = tid / NQ;
+    const f32x4 v4 = *reinterpret_cast<const f32x4 *>(vv + 4 * jq);
+    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + ((size_t)b * Hq + h) * D * D);
+    f32x4 sv[RPT];
+#pragma unroll
+    for (int s = 0; s < RPT; ++s) sv[s] = __builtin_nontemporal_load(&S[(rg + RG * s) * NQ + jq]);
+    f32x4 o = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < RPT; ++s) {
+        const int i = rg + RG * s;
+        const float ki = kk[i], qi = qq[i];
+        f32x4 x = sv[s];
+        x[0] = fmaf(ki, v4[0], x[0]);
+        x[1] = fmaf(ki, v4[1], x[1]);
+        x[2] = fmaf(ki, v4[2], x[2]);
+        x[3] = fmaf(ki, v4[3], x[3]);
+        __builtin_nontemporal_store(x, &S[i * NQ + jq]);
+        o[0] = fmaf(qi, x[0], o[0]);
+        o[1] = fmaf(qi, x[1], o[1]);
+        o[2] = fmaf(qi, x[2], o[2]);
+        o[3] = fmaf(qi, x[3], o[3]);
+    }
+    *reinterpret_cast<f32x4 *>(red + rg * D + 4 * jq) = o;
+    __syncthreads();
+    if (tid < D) {
+        float acc = 0.0f;
+        for (int r = 0; r < RG; ++r) acc += red[r * D + tid];
+        olin[tid] = acc;
+    }
+}
+
+template <typename T, int D, int DI, int HIPAD>
+__global__ __launch_bounds__(256) void decode_score_state_kernel(DecodeScoreArgs a, int n_state) {
+    __shared__ float smem[3 * 128 + 16 * 128];
+    if ((int)blockIdx.x < n_state)
+        state_group<T, D>(a, blockIdx.x, smem);
+    else
+        score_group<T, DI, HIPAD>(a, blockIdx.x - n_state);
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 512;
+
+template <int NT>
+__global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores, const int64_t *cu,
+                                                           int G, int M, int max_ctx,
+                                                           int32_t *idx) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t tmp[NT / 64 + 1];
+    __shared__ uint32_t found[2];
+    const int tid = threadIdx.x;
+    const int bg = blockIdx.x, b = bg / G;
+    const int L = (int)max((int64_t)0, min((int64_t)max_ctx, cu[b + 1] - cu[b]));
+    const float *sc = scores + (size_t)bg * max_ctx;
+    int32_t *out = idx + (size_t)bg * M;
+    if (L <= M) {
+        for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
+        return;
+    }
+    // Radix select of the M-th largest key, digits of 11, 11 and 10 bits.
+    uint32_t prefix = 0;
+    uint32_t need = (uint32_t)M;
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int p = 0; p < 3; ++p) {
+        const int sh = shifts[p], bits = widths[p], nb = 1 << bits;
+        for (int i = tid; i < nb; i += NT) hist[i] = 0;
+        __syncthreads();
+        for (int s = tid; s < L; s += NT) {
+            const uint32_t u = order_key(sc[s]);
+            if (p == 0 || (u >> (sh + bits)) == prefix) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        // thread tid owns bins in descending order: top bins first
+        const int bpt = nb / NT;
+        uint32_t local = 0;
+        for (int e = 0; e < bpt; ++e) local += hist[nb - 1 - (tid * bpt + e)];
+        uint32_t tot;
+        uint32_t before = block_exclusive_scan<NT>(local, tmp, &tot);
+        if (before < need && before + local >= need) {
+            uint32_t run = before;
+            for (int e = 0; e < bpt; ++e) {
+                const int bin = nb - 1 - (tid * bpt + e);
+                const uint32_t c = hist[bin];
+                if (run + c >= need) {
+                    found[0] = (uint32_t)bin;
+                    found[1] = need - run;
+                    break;
+                }
+                run += c;
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << bits) | found[0];
+        need = found[1];
+        __syncthreads();
+    }
+    const uint32_t theta = prefix;   // key of the M-th largest score
+    const uint32_t take_eq = need;   // how many keys equal to theta are taken
+    // Compaction in index order: each thread owns one contiguous span.
+    const int span = (L + NT - 1) / NT;
+    const int s0 = min(L, tid * span), s1 = min(L, s0 + span);
+    uint32_t ngt = 0, neq = 0;
+    for (int s = s0; s < s1; ++s) {
+        const uint32_t u = order_key(sc[s]);
+        ngt += u > theta;
+        neq += u == theta;
+    }
+    uint32_t tot;
+    uint32_t gt_before = block_exclusive_scan<NT>(ngt, tmp, &tot);
+    uint32_t eq_before = block_exclusive_scan<NT>(neq, tmp, &tot);
+    for (int s = s0; s < s1; ++s) {
+        const uint32_t u = order_key(sc[s]);
+        if (u > theta) {
+            const uint32_t pos = gt_before + min(eq_before, take_eq);
+            if (pos < (uint32_t)M) out[pos] = s;
+            ++gt_before;
+        } else if (u == theta) {
+            const uint32_t pos = gt_before + eq_before;
+            if (eq_before < take_eq && pos < (uint32_t)M) out[pos] = s;
+            ++eq_before;
+        }
+    }
+}
+
+template <typename T, int D, int DI, int HIPAD>
+hipError_t launch_ss(const DecodeScoreArgs &a, hipStream_t s) {
+    const int n_state = a.B * a.Hq;
+    const int n_score = a.B * a.tiles_per_seq;
+    hipLaunchKernelGGL((decode_score_state_kernel<T, D, DI, HIPAD>), dim3(n_state + n_score),
+                       dim3(256), 0, s, a, n_state);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_ss(const DecodeScoreArgs &a, int d, int dI, hipStream_t s) {
+    const bool h8 = a.HI > 4;
+#define LISA_SS(D_, DI_)                                                                 \
+    if (d == D_ && dI == DI_) return h8 ? launch_ss<T, D_, DI_, 8>(a, s) : launch_ss<T, D_, DI_, 4>(a, s);
+    LISA_SS(64, 32) LISA_SS(64, 64) LISA_SS(128, 32) LISA_SS(128, 64)
+#undef LISA_SS
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI,
+                                     hipStream_t s) {
+    return dtype == 1 ? dispatch_ss<uint16_t>(a, d, dI, s) : dispatch_ss<float>(a, d, dI, s);
+}
+
+hipError_t launch_decode_select(const float *scores, const int64_t *cu, int B, int G, int M,
+                                int max_ctx, int32_t *idx, hipStream_t s) {
+    hipLaunchKernelGGL((decode_select_kernel<kSelThreads>), dim3(B * G), dim3(kSelThreads), 0, s,
+                       scores, cu, G, M, max_ctx, idx);
+    return hipGetLastError();
+}
+
+}  // namespace lisa

@@ -1,0 +1,69 @@
+// Launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lisa {
+
+// ---- decode ---------------------------------------------------------------
+struct DecodeScoreArgs {
+    const void *q;            // [B,Hq,d]
+    const void *k_cache;      // [sumL,G,d]
+    const void *v_cache;      // [sumL,G,d]
+    const void *q_idx;        // [B,G,HI,dI]
+    const void *k_idx_cache;  // [sumL,G,dI]
+    const void *w_idx;        // [B,G,HI]
+    const int64_t *cu;        // [B+1] device
+    float *state;             // [B,Hq,d,d] in/out
+    float *olin;              // [B,Hq,d] workspace
+    float *scores;            // [B,G,max_ctx] workspace
+    int B, Hq, G, HI, max_ctx;
+    int tiles_per_seq;        // ceil(max_ctx / kDecodeTile)
+};
+constexpr int kDecodeTile = 256;  // tokens per score work-group
+
+hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI,
+                                     hipStream_t s);
+hipError_t launch_decode_select(const float *scores, const int64_t *cu, int B, int G, int M,
+                                int max_ctx, int32_t *idx, hipStream_t s);
+
+// ---- sparse attention + gate (prefill and decode) -------------------------
+struct SparseArgs {
+    const void *q;        // prefill [B,n,Hq,d]; decode [B,Hq,d]
+    const void *k;        // prefill [B,n,G,d];  decode cache [sumL,G,d]
+    const void *v;
+    const int64_t *cu;    // decode only
+    const int32_t *idx;   // [units, M]  (units = B*n*G or B*G)
+    const void *lin;      // o_lin: prefill = out buffer (dtype); decode = fp32 workspace
+    const void *gate;     // prefill [B,n,Hq]; decode [B,Hq]
+    void *out;            // prefill [B,n,Hq,d]; decode [B,Hq,d]
+    int B, n, Hq, G, r, M, max_ctx;
+    float scale_log2;     // softmax scale * log2(e)
+    int units;
+};
+hipError_t launch_sparse_gate(const SparseArgs &a, int dtype, int d, bool decode, hipStream_t s);
+
+// ---- prefill: chunked linear attention -----------------------------------
+struct LinearArgs {
+    const void *q, *k, *v;       // [B,n,Hq,d], [B,n,G,d]
+    const float *state_in;       // [B,Hq,d,d] or null
+    float *state_out;            // [B,Hq,d,d] or null
+    float *dS;                   // [B,G,nC,d,d] fp32: per-chunk K^T V, stored transposed [j][i]
+    void *P;                     // [B,Hp,nC,d,d] dtype: exclusive prefix states, transposed
+    void *out;                   // [B,n,Hq,d]: receives o_lin
+    int B, n, Hq, G, r, nC;
+    int per_head;                // 1 if state_in != null (prefix states per query head)
+};
+hipError_t launch_linear_prefill(const LinearArgs &a, int dtype, int d, hipStream_t s);
+
+// ---- prefill: indexer + streaming top-M ------------------------------------
+struct IndexerArgs {
+    const void *q_idx;   // [B,n,G,HI,dI]
+    const void *k_idx;   // [B,n,G,dI]
+    const void *w_idx;   // [B,n,G,HI]
+    int32_t *idx;        // [B,n,G,M]
+    int B, n, G, HI, M;
+};
+hipError_t launch_indexer_prefill(const IndexerArgs &a, int dtype, int dI, hipStream_t s);
+
+}  // namespace lisa

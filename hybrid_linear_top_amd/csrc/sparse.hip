@@ -1,0 +1,246 @@
+// Sparse softmax attention over the selected rows, fused with the gate.
+//
+// The Lightning Indexer's top-M tokens feed a sparse self-attention, and a
+// gate fuses its output with the linear branch (arxivdaily page for arXiv
+// 2607.19358, English abstract; gptget.net analysis, method-details section:
+// learned gate g).  For one query position and one KV group (a "unit") the
+// r query heads of the group share the selected K/V rows, so each gathered
+// row is read once and used by all r heads:
+//
+//   S^T[key][head] = K_sel Q^T     (MFMA, A = gathered K rows, B = Q^T)
+//   online softmax over keys per head (fp32, exp2 with the scale folded in)
+//   O^T[dim][head] += V_sel^T P^T  (MFMA, A = V rows staged in LDS, B = P^T
+//                                   taken straight from the S^T accumulators)
+//
+// The r heads are padded to the 16 columns of a 16x16x32 MFMA tile.  The M
+// selected slots are split over the 4 waves of the work-group (32 slots per
+// step); the waves' partial (max, sum, O) are merged in LDS, then the gate
+// gamma = sigmoid(z) mixes o_sparse with o_lin and the result is stored.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lisa {
+namespace {
+
+constexpr int kChunk = 32;  // selected slots per wave step
+
+template <typename T, int D>
+struct SparseSmem {
+    static constexpr int kVStride = D + 8 / Elt<T>::kBytes;  // row pad: 8 bytes
+    static constexpr int kVBytes = 4 * kChunk * kVStride * Elt<T>::kBytes;
+    static constexpr int kMergeBytes = 4 * (D * 16 + 32) * 4;
+    static constexpr int kBytes = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+};
+
+template <typename T, int D, bool DECODE>
+__global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
+    using S = SparseSmem<T, D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
+    constexpr int VS = S::kVStride;
+    constexpr int KC = D / 32;  // K-steps of 32 over the head dim
+    constexpr int MB = D / 16;  // 16-row blocks of O^T
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    // Logical unit: decode (b, g) -> b*G + g.  Prefill units are taken
+    // group-major, and the XCD remap hands each XCD a contiguous range, so an
+    // XCD's L2 only ever holds the K/V rows of one or two groups.
+    const int lu = xcd_remap(blockIdx.x, gridDim.x);
+    const int G = a.G, r = a.r, M = a.M;
+    const int u = DECODE ? lu : (lu % (a.B * a.n)) * G + lu / (a.B * a.n);
+
+    const T *qrows, *kbase, *vbase;
+    int smax;  // largest valid key position of the unit (defensive bound on gathered rows)
+    const void *linp;
+    const T *zp;
+    T *outp;
+    size_t lin_off;
+    {
+        if (DECODE) {
+            const int b = u / G, g = u % G;
+            const int64_t row0 = a.cu[b];
+            smax = (int)min((int64_t)a.max_ctx, a.cu[b + 1] - row0) - 1;
+            qrows = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.Hq + g * r) * D;
+            kbase = reinterpret_cast<const T *>(a.k) + ((size_t)row0 * G + g) * D;
+            vbase = reinterpret_cast<const T *>(a.v) + ((size_t)row0 * G + g) * D;
+            zp = reinterpret_cast<const T *>(a.gate) + (size_t)b * a.Hq + g * r;
+            lin_off = ((size_t)b * a.Hq + g * r) * D;
+            outp = reinterpret_cast<T *>(a.out) + lin_off;
+        } else {
+            const int g = u % G, bt = u / G, b = bt / a.n;
+            smax = bt % a.n;
+            qrows = reinterpret_cast<const T *>(a.q) + ((size_t)bt * a.Hq + g * r) * D;
+            kbase = reinterpret_cast<const T *>(a.k) + ((size_t)b * a.n * G + g) * D;
+            vbase = reinterpret_cast<const T *>(a.v) + ((size_t)b * a.n * G + g) * D;
+            zp = reinterpret_cast<const T *>(a.gate) + (size_t)bt * a.Hq + g * r;
+            lin_off = ((size_t)bt * a.Hq + g * r) * D;
+            outp = reinterpret_cast<T *>(a.out) + lin_off;
+        }
+        linp = a.lin;
+    }
+    const size_t rstride = (size_t)G * D;  // elements between consecutive token rows
+    const int32_t *idxp = a.idx + (size_t)u * M;
+
+    // Q^T fragments: column = head (zero beyond r), K = head dim.
+    Frag<T> qf[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        if (col < r) qf[kc].load(qrows + (size_t)col * D + kc * 32 + grp * 8);
+        else qf[kc].zero();
+    }
+
+    f32x4 o[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) o[mb] = f32x4{0, 0, 0, 0};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    T *vs = reinterpret_cast<T *>(smem) + (size_t)wave * kChunk * VS;
+    const int per_wave = ((M + 3) / 4 + kChunk - 1) / kChunk * kChunk;
+    const int s_begin = wave * per_wave, s_end = min(M, s_begin + per_wave);
+    for (int cs = s_begin; cs < s_end; cs += kChunk) {
+        if (idxp[cs] < 0) break;  // sets are ascending with -1 padding at the end
+        // --- logits S^T for two 16-slot key blocks --------------------------
+        f32x4 acc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int slot = cs + kb * 16 + col;
+            int s = slot < s_end ? idxp[slot] : -1;
+            if (s > smax) s = -1;
+            acc[kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                Frag<T> kf;
+                if (s >= 0) kf.load(kbase + (size_t)s * rstride + kc * 32 + grp * 8);
+                else kf.zero();
+                acc[kb] = mma16(kf, qf[kc], acc[kb]);
+            }
+        }
+        // rows of acc[kb] are slots cs + 16*kb + 4*grp + i
+        float x[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int slot = cs + kb * 16 + grp * 4 + i;
+                const bool ok = slot < s_end && idxp[slot] >= 0 && idxp[slot] <= smax;
+                const float v = ok ? acc[kb][i] * a.scale_log2 : -INFINITY;
+                x[kb * 4 + i] = v;
+                cmax = fmaxf(cmax, v);
+            }
+        }
+        cmax = wave_max_across16(cmax);
+        const float m_new = fmaxf(m_run, cmax);
+        float p[8];
+        float psum = 0.0f;
+        float alpha = 1.0f;
+        if (m_new == -INFINITY) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = 0.0f;
+        } else {
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+                psum += p[e];
+            }
+        }
+        psum = wave_sum_across16(psum);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+
+        // --- stage the 32 V rows in LDS (row-major, padded) -----------------
+        constexpr int CPRV = D * Elt<T>::kBytes / 8;  // 8-byte pieces per row
+        constexpr int PIECES = kChunk * CPRV;
+        for (int pc = lane; pc < PIECES; pc += 64) {
+            const int row = pc / CPRV, cc = pc % CPRV;
+            const int slot = cs + row;
+            int s = slot < s_end ? idxp[slot] : -1;
+            if (s > smax) s = -1;
+            u32x2 val = {0u, 0u};
+            if (s >= 0)
+                val = *reinterpret_cast<const u32x2 *>(
+                    reinterpret_cast<const unsigned char *>(vbase + (size_t)s * rstride) + cc * 8);
+            *reinterpret_cast<u32x2 *>(reinterpret_cast<unsigned char *>(vs + row * VS) + cc * 8) = val;
+        }
+        wave_lds_sync();
+        // --- O^T += V^T P^T --------------------------------------------------
+        Frag<T> pf;
+        pf.set(p);  // K-slot e <-> chunk slot (e<4 ? 4*grp+e : 16+4*grp+e-4)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int dim = mb * 16 + col;
+            T vv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int row = (e < 4) ? (grp * 4 + e) : (16 + grp * 4 + e - 4);
+                vv[e] = vs[row * VS + dim];
+            }
+            Frag<T> vf;
+            vf.set_bits(vv);
+            o[mb] = mma16(vf, pf, o[mb]);
+        }
+        wave_lds_sync();
+    }
+
+    // --- merge the 4 waves -------------------------------------------------
+    __syncthreads();
+    float *mrg = reinterpret_cast<float *>(smem);
+    float *wm = mrg + wave * (D * 16 + 32);  // [0..15] max, [16..31] sum, then O^T[D][16]
+    if (grp == 0) {
+        wm[col] = m_run;
+        wm[16 + col] = l_run;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wm[32 + (mb * 16 + grp * 4 + i) * 16 + col] = o[mb][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < r * D; e += 256) {
+        const int hh = e / D, dim = e % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mrg[w * (D * 16 + 32) + hh]);
+        float num = 0.0f, den = 0.0f;
+        if (mx != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float *ww = mrg + w * (D * 16 + 32);
+                const float sc = __builtin_amdgcn_exp2f(ww[hh] - mx);
+                den += ww[16 + hh] * sc;
+                num += ww[32 + dim * 16 + hh] * sc;
+            }
+        }
+        const float osp = den > 0.0f ? num / den : 0.0f;
+        const float z = Elt<T>::to_f32(zp[hh]);
+        const float gam = 1.0f / (1.0f + expf(-z));
+        float lin;
+        if (DECODE) lin = reinterpret_cast<const float *>(linp)[lin_off + e];
+        else lin = Elt<T>::to_f32(reinterpret_cast<const T *>(linp)[lin_off + e]);
+        outp[e] = Elt<T>::from_f32(gam * osp + (1.0f - gam) * lin);
+    }
+}
+
+template <typename T>
+hipError_t dispatch(const SparseArgs &a, int d, bool decode, hipStream_t s) {
+    if (a.units == 0) return hipSuccess;
+    dim3 grid(a.units), block(256);
+#define LISA_SP(D_)                                                                              \
+    if (d == D_) {                                                                               \
+        if (decode) hipLaunchKernelGGL((sparse_gate_kernel<T, D_, true>), grid, block, 0, s, a);  \
+        else hipLaunchKernelGGL((sparse_gate_kernel<T, D_, false>), grid, block, 0, s, a);        \
+        return hipGetLastError();                                                                \
+    }
+    LISA_SP(64) LISA_SP(128)
+#undef LISA_SP
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_sparse_gate(const SparseArgs &a, int dtype, int d, bool decode, hipStream_t s) {
+    return dtype == 1 ? dispatch<uint16_t>(a, d, decode, s) : dispatch<float>(a, d, decode, s);
+}
+
+}  // namespace lisa

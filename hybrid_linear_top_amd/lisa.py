@@ -1,0 +1,190 @@
+"""Python binding of liblisa.so (the gfx950 HIP library behind include/lisa.h).
+
+The functions named like the C ABI (``lisa_prefill``, ``lisa_decode_step``,
+...) only marshal arguments: every step of the layer runs in the library's
+kernels.  ``prefill`` / ``decode_step`` are conveniences that take torch
+device tensors and allocate outputs and the workspace with torch (memory
+plumbing only).  Importing this module fails if the library is not built:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblisa.so")
+
+LISA_OK = 0
+LISA_ERR_INVALID_ARGUMENT = 1
+LISA_ERR_UNSUPPORTED = 2
+LISA_ERR_WORKSPACE = 3
+LISA_ERR_HIP = 4
+LISA_F32 = 0
+LISA_BF16 = 1
+
+EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill", "lisa_decode_workspace_bytes",
+           "lisa_decode_step", "lisa_last_error", "lisa_build_info"]
+
+
+class LisaDims(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("idx_heads", ctypes.c_int32),
+                ("idx_dim", ctypes.c_int32), ("top_m", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class LisaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"LISA status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m hybrid_linear_top_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, i64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p
+    dp = ctypes.POINTER(LisaDims)
+    lib.lisa_prefill_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
+    lib.lisa_prefill_workspace_bytes.restype = ctypes.c_int
+    lib.lisa_prefill.argtypes = [dp, i32, i32] + [vp] * 7 + [vp, vp, vp, vp, vp, sz, vp]
+    lib.lisa_prefill.restype = ctypes.c_int
+    lib.lisa_decode_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
+    lib.lisa_decode_workspace_bytes.restype = ctypes.c_int
+    lib.lisa_decode_step.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp, sz, vp]
+    lib.lisa_decode_step.restype = ctypes.c_int
+    lib.lisa_last_error.argtypes = []
+    lib.lisa_last_error.restype = ctypes.c_char_p
+    lib.lisa_build_info.argtypes = []
+    lib.lisa_build_info.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != LISA_OK:
+        raise LisaError(status, _lib.lisa_last_error().decode())
+
+
+# ---- C-ABI-named wrappers (pointers are Python ints, 0 = NULL) -------------
+def lisa_last_error() -> str:
+    return _lib.lisa_last_error().decode()
+
+
+def lisa_build_info() -> str:
+    return _lib.lisa_build_info().decode()
+
+
+def lisa_prefill_workspace_bytes(dims: LisaDims, B: int, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.lisa_prefill_workspace_bytes(ctypes.byref(dims), B, n, ctypes.byref(out)))
+    return out.value
+
+
+def lisa_decode_workspace_bytes(dims: LisaDims, B: int, max_ctx: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.lisa_decode_workspace_bytes(ctypes.byref(dims), B, max_ctx, ctypes.byref(out)))
+    return out.value
+
+
+def lisa_prefill(dims, B, n, q, k, v, q_idx, k_idx, w_idx, gate, state_in, out, state_out,
+                 topm_out, workspace, workspace_bytes, stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_prefill(ctypes.byref(dims), B, n, q, k, v, q_idx, k_idx, w_idx, gate,
+                             state_in, out, state_out, topm_out, workspace, workspace_bytes, stream)
+
+
+def lisa_decode_step(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
+                     gate, state, out, topm_out, workspace, workspace_bytes, stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_decode_step(ctypes.byref(dims), B, cu_ctx, max_ctx, q, k_cache, v_cache,
+                                 q_idx, k_idx_cache, w_idx, gate, state, out, topm_out, workspace,
+                                 workspace_bytes, stream)
+
+
+# ---- torch conveniences ---------------------------------------------------
+def make_dims(Hq, Hkv, d, HI, dI, M, dtype, chunk=64, softmax_scale=0.0) -> LisaDims:
+    code = dtype if isinstance(dtype, int) else (LISA_BF16 if dtype == "bf16" else LISA_F32)
+    return LisaDims(Hq, Hkv, d, HI, dI, M, chunk, softmax_scale, code)
+
+
+def dims_from_config(cfg, softmax_scale=0.0) -> LisaDims:
+    return make_dims(cfg.Hq, cfg.Hkv, cfg.d, cfg.HI, cfg.dI, cfg.M, cfg.dtype, cfg.chunk,
+                     softmax_scale)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def prefill(dims: LisaDims, q, k, v, q_idx, k_idx, w_idx, gate, state_in=None, out=None,
+            state_out=None, topm_out=None, workspace=None, stream=None):
+    """q [B,n,Hq,d] etc. as torch device tensors.  Allocates missing outputs.
+    Returns (out, state_out, topm_out)."""
+    import torch
+    B, n = int(q.shape[0]), int(q.shape[1])
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None:
+        state_out = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
+                                dtype=torch.float32, device=dev)
+    if topm_out is None:
+        topm_out = torch.empty((B, n, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev)
+    wsb = lisa_prefill_workspace_bytes(dims, B, n)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(lisa_prefill(dims, B, n, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
+                        _ptr(w_idx), _ptr(gate), _ptr(state_in), _ptr(out), _ptr(state_out),
+                        _ptr(topm_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, state_out, topm_out
+
+
+def decode_step(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache, q_idx, k_idx_cache,
+                w_idx, gate, state, out=None, topm_out=None, workspace=None, stream=None):
+    """One decode step; `state` is updated in place.  Returns (out, topm_out)."""
+    import torch
+    B = int(q.shape[0])
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if topm_out is None:
+        topm_out = torch.empty((B, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev)
+    wsb = lisa_decode_workspace_bytes(dims, B, max_ctx)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(lisa_decode_step(dims, B, _ptr(cu_ctx), int(max_ctx), _ptr(q), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(q_idx), _ptr(k_idx_cache), _ptr(w_idx), _ptr(gate),
+                            _ptr(state), _ptr(out), _ptr(topm_out), _ptr(workspace),
+                            workspace.numel(), _stream(stream)))
+    return out, topm_out
+
+
+def to_device(arr, device="cuda"):
+    """numpy storage array (uint16 bf16 bits / float32 / int) -> torch tensor."""
+    import numpy as np
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def from_device(t):
+    """torch tensor -> numpy storage array (bf16 as uint16 bits)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

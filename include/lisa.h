@@ -1,0 +1,146 @@
+/*
+ * lisa.h -- C ABI of the MI355X (gfx950) LISA layer forward pass.
+ *
+ * LISA (Linear-Indexed Sparse Attention, arXiv 2607.19358) replaces a
+ * layer's self-attention by two branches that run in parallel and a gate
+ * that fuses them (arxivdaily page for 2607.19358, English abstract):
+ *   - a Lightning Indexer scores every visible token and keeps the top-M of
+ *     the full context for a sparse softmax self-attention; the indexer uses
+ *     query/key projections and a ReLU'd dot product (gptget.net analysis of
+ *     2607.19358, method-details section); M = 256 in the paper's runs (same
+ *     page, experiment-design section);
+ *   - a linear-attention branch with the identity feature map and a state
+ *     matrix S_t updated once per token (gptget.net, method-details);
+ *   - a learned gate mixes the two outputs (arxivdaily abstract: "fused via
+ *     a gating mechanism"; zhuanzhiai page: "learned gate").
+ * The library is the attention core after the projections: the caller owns
+ * the learned projections and passes their outputs.
+ *
+ * Definitions used (the pages give prose only; these are the readings):
+ *   groups    G = num_kv_heads; query head h belongs to group
+ *             g(h) = floor(h * G / num_q_heads) (contiguous blocks of r =
+ *             num_q_heads / G heads).  One indexer per group.
+ *   indexer   I[t,s] = sum_j w[t,g,j] * max(0, q_idx[t,g,j,:] . k_idx[s,g,:])
+ *             for candidates s = 0..t (the current token included); the key
+ *             k_idx is shared by the idx_heads indexer heads.
+ *   top-M     the min(M, t+1) candidates first in the order (higher I, then
+ *             lower s); -0.0 equals +0.0.  Written ascending, padded with -1.
+ *   sparse    o_sp[t,h] = sum_{s in set} softmax_s(scale * q[t,h].k[s,g]) v[s,g],
+ *             scale = softmax_scale > 0 ? softmax_scale : 1/sqrt(head_dim).
+ *   linear    S_t = S_{t-1} + k[t,g] v[t,g]^T (S_{-1} = state_in or 0; one
+ *             fp32 d x d state per query head, row index = key dim);
+ *             o_lin[t,h] = q[t,h]^T S_t  (no normaliser, no decay).
+ *   gate      gamma = 1 / (1 + exp(-gate[t,h])); out = gamma*o_sp + (1-gamma)*o_lin.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense, row-major, contiguous device buffers owned by
+ *     the caller, 16-byte aligned.  Activations (q, k, v, q_idx, k_idx,
+ *     w_idx, gate, out) use dims->dtype (LISA_BF16 = bf16 bit patterns, or
+ *     LISA_F32); states are always fp32; indices int32.
+ *   - Work is enqueued on `stream` and the call returns at once; there is no
+ *     device synchronisation inside.  Calls on different streams are
+ *     independent if their workspaces and outputs are distinct.
+ *   - Arguments are validated before anything is enqueued.  On error nothing
+ *     is enqueued and lisa_last_error() (thread-local) describes it.
+ *   - Non-finite inputs are undefined behaviour (no fault, unspecified
+ *     values).  The library allocates nothing; the workspace comes from the
+ *     caller and must be at least the size the *_workspace_bytes query gives.
+ *
+ * Supported shapes: head_dim in {64, 128}; idx_dim in {32, 64};
+ * 1 <= idx_heads <= 8; num_q_heads % num_kv_heads == 0 with r <= 16;
+ * chunk in {0, 64} (0 means 64); prefill: 1 <= top_m <= 512, n <= 32768;
+ * decode: 1 <= top_m <= 2048.
+ */
+#ifndef LISA_H
+#define LISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *lisa_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+    LISA_OK = 0,
+    LISA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad count */
+    LISA_ERR_UNSUPPORTED = 2,      /* a shape outside the supported set above */
+    LISA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    LISA_ERR_HIP = 4               /* a HIP launch failed; message has the HIP error */
+} lisa_status;
+
+enum { LISA_F32 = 0, LISA_BF16 = 1 };
+
+typedef struct {
+    int32_t num_q_heads;   /* Hq */
+    int32_t num_kv_heads;  /* Hkv = G, also the number of indexers */
+    int32_t head_dim;      /* d = d_k = d_v */
+    int32_t idx_heads;     /* H_I, indexer heads per group */
+    int32_t idx_dim;       /* d_I */
+    int32_t top_m;         /* M */
+    int32_t chunk;         /* linear-attention chunk length in prefill (0 or 64) */
+    float softmax_scale;   /* <= 0: 1/sqrt(head_dim) */
+    int32_t dtype;         /* LISA_F32 or LISA_BF16 */
+} lisa_dims;
+
+/* Workspace needed by lisa_prefill for batch B and length n. */
+lisa_status lisa_prefill_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
+                                         size_t *bytes);
+
+/*
+ * Whole-prompt forward pass of one LISA layer (all four parts above).
+ *   q      [B, n, Hq, d]          k, v  [B, n, Hkv, d]
+ *   q_idx  [B, n, G, H_I, d_I]    k_idx [B, n, G, d_I]    w_idx [B, n, G, H_I]
+ *   gate   [B, n, Hq]  (logits z; gamma = sigmoid(z))
+ *   state_in  [B, Hq, d, d] fp32 or NULL (zero initial state)
+ *   out    [B, n, Hq, d]  (written)
+ *   state_out [B, Hq, d, d] fp32 or NULL: S after the last token
+ *   topm_out  [B, n, G, M] int32 or NULL: the selected sets
+ * n == 0 or B == 0 is a valid no-op.
+ */
+lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void *q,
+                         const void *k, const void *v, const void *q_idx, const void *k_idx,
+                         const void *w_idx, const void *gate, const float *state_in, void *out,
+                         float *state_out, int32_t *topm_out, void *workspace,
+                         size_t workspace_bytes, lisa_stream_t stream);
+
+/* Workspace needed by lisa_decode_step for B sequences of at most max_ctx
+ * visible tokens each. */
+lisa_status lisa_decode_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t max_ctx,
+                                        size_t *bytes);
+
+/*
+ * One generated token per sequence against packed token-major caches.
+ *   cu_ctx  [B+1] int64, DEVICE memory: sequence b owns cache rows
+ *           [cu_ctx[b], cu_ctx[b+1]); L_b = cu_ctx[b+1]-cu_ctx[b] >= 1 visible
+ *           tokens.  The caller has already appended the new token's k, v and
+ *           k_idx as the last row, so the new token is position t = L_b - 1.
+ *   max_ctx host int32 >= every L_b (sizes the workspace; rows beyond it are
+ *           ignored, which gives unspecified results but never reads out of
+ *           bounds).
+ *   q [B, Hq, d]; k_cache, v_cache [sum L, Hkv, d]; q_idx [B, G, H_I, d_I];
+ *   k_idx_cache [sum L, G, d_I]; w_idx [B, G, H_I]; gate [B, Hq];
+ *   state [B, Hq, d, d] fp32, in/out: S_{t-1} on entry, S_t on return.
+ *   out [B, Hq, d]; topm_out [B, G, M] int32 or NULL.
+ * B == 0 is a valid no-op.
+ */
+lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
+                             int32_t max_ctx, const void *q, const void *k_cache,
+                             const void *v_cache, const void *q_idx, const void *k_idx_cache,
+                             const void *w_idx, const void *gate, float *state, void *out,
+                             int32_t *topm_out, void *workspace, size_t workspace_bytes,
+                             lisa_stream_t stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *lisa_last_error(void);
+
+/* Build description: target architecture and library version. */
+const char *lisa_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LISA_H */

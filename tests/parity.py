@@ -1,0 +1,162 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+and compare with the fp64 oracle.
+
+Parity rules (the bar the tests enforce):
+  * index sets: for every (query, group), |B| = m = min(M, t+1), B is an
+    ascending subset of [0, t] padded with -1, and every candidate in the
+    symmetric difference of B and the oracle's set A scores within
+    eps = 1e-5 * |s_m| of the m-th oracle score s_m (eps = 1e-5 * max I when
+    s_m == 0; exact match when every score is 0);
+  * outputs: normwise relative error ||x - ref||_F / ||ref||_F <= 1e-2 for bf16
+    and <= 1e-4 for fp32, checked separately for the sparse branch alone
+    (gate logit +inf), the linear branch alone (-inf), the gated output and
+    the final state.  The sparse reference is the oracle evaluated on the
+    GPU's own (validated) index sets.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from hybrid_linear_top_amd import inputs as gen
+from oracle import oracle as orc
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def normwise(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(x - ref)
+    return float(num / den) if den > 0 else float(num)
+
+
+def check_set(sel, scores, M, rel=1e-5):
+    """Band rule for one (query, group).  scores: fp64 oracle scores of the
+    candidates 0..T-1.  Returns the number of swapped candidates."""
+    T = len(scores)
+    m = min(M, T)
+    sel = np.asarray(sel)
+    assert len(sel) == M
+    assert np.all(sel[m:] == -1), "padding"
+    s = sel[:m]
+    assert np.all(s >= 0) and np.all(s < T), "range"
+    assert np.all(np.diff(s) > 0), "ascending and distinct"
+    ref = orc.topm(scores, M)[:m]
+    diff = set(ref.tolist()) ^ set(s.tolist())
+    if diff:
+        s_m = np.sort(scores)[::-1][m - 1]
+        eps = rel * abs(s_m) if s_m != 0 else rel * float(np.max(scores))
+        for c in diff:
+            assert abs(scores[c] - s_m) <= eps, (c, scores[c], s_m, eps)
+    return len(diff)
+
+
+def gate_fill(shape, dtype, value):
+    x = np.full(shape, value, dtype=np.float32)
+    return gen.round_bf16(x) if dtype == "bf16" else x
+
+
+def run_prefill(cfg, inp, gate=None, state_in=None, dims=None):
+    import torch
+    from hybrid_linear_top_amd import lisa
+    dims = dims or lisa.dims_from_config(cfg)
+    dv = lisa.to_device
+    tens = [dv(inp[k]) for k in ("q", "k", "v", "q_idx", "k_idx", "w_idx")]
+    g = dv(inp["gate"] if gate is None else gate)
+    s0 = None if state_in is None else dv(np.ascontiguousarray(state_in, dtype=np.float32))
+    out, st, idx = lisa.prefill(dims, *tens, g, state_in=s0)
+    torch.cuda.synchronize()
+    return (orc.widen(lisa.from_device(out), cfg.dtype), lisa.from_device(st).astype(np.float64),
+            lisa.from_device(idx))
+
+
+def run_decode(cfg, inp, gate=None, dims=None):
+    import torch
+    from hybrid_linear_top_amd import lisa
+    dims = dims or lisa.dims_from_config(cfg)
+    dv = lisa.to_device
+    state = dv(inp["state"])
+    out, idx = lisa.decode_step(dims, dv(inp["cu_ctx"]), inp["max_ctx"], dv(inp["q"]),
+                                dv(inp["k_cache"]), dv(inp["v_cache"]), dv(inp["q_idx"]),
+                                dv(inp["k_idx_cache"]), dv(inp["w_idx"]),
+                                dv(inp["gate"] if gate is None else gate), state)
+    torch.cuda.synchronize()
+    return (orc.widen(lisa.from_device(out), cfg.dtype), lisa.from_device(state).astype(np.float64),
+            lisa.from_device(idx))
+
+
+def prefill_parity(cfg, inp, rows=None, state_in=None, report=None):
+    """Full prefill parity (all four checks) on the listed rows (None = all)."""
+    dt = cfg.dtype
+    B, n = inp["B"], inp["n"]
+    tol = TOL[dt]
+    ref = orc.prefill(inp, cfg, rows=rows, state_in=state_in)
+    R = ref["rows"] if rows is not None else np.arange(n)
+    out, st, idx = run_prefill(cfg, inp, state_in=state_in)
+    osp, _, idx_p = run_prefill(cfg, inp, gate=gate_fill(inp["gate"].shape, dt, np.inf), state_in=state_in)
+    olin, _, _ = run_prefill(cfg, inp, gate=gate_fill(inp["gate"].shape, dt, -np.inf), state_in=state_in)
+    assert np.array_equal(idx, idx_p), "index sets differ between two runs"
+    qI, kI, w = (orc.widen(inp[x], dt) for x in ("q_idx", "k_idx", "w_idx"))
+    swaps = 0
+    for b in range(B):
+        for t in R:
+            for g in range(cfg.Hkv):
+                sc = orc.index_scores(qI[b, t, g], w[b, t, g], kI[b, :t + 1, g])
+                swaps += check_set(idx[b, t, g], sc, cfg.M)
+    # oracle sparse branch and gate on the GPU's sets
+    q = orc.widen(inp["q"], dt)
+    kr = orc.widen(inp["k"], dt).reshape(B * n, cfg.Hkv, cfg.d)
+    vr = orc.widen(inp["v"], dt).reshape(B * n, cfg.Hkv, cfg.d)
+    z = orc.widen(inp["gate"], dt)
+    U = B * len(R)
+    qs = q[:, R].reshape(U, cfg.Hq, cfg.d)
+    row0 = np.repeat(np.arange(B) * n, len(R))
+    sets = idx[:, R].reshape(U, cfg.Hkv, cfg.M)
+    out_g, osp_g = orc.sparse_given_sets(qs, kr, vr, row0, sets, z[:, R].reshape(U, cfg.Hq),
+                                         ref["olin"].reshape(U, cfg.Hq, cfg.d), cfg.Hq, cfg.Hkv,
+                                         cfg.d, cfg.M)
+    e_sp = normwise(osp[:, R].reshape(U, -1), osp_g.reshape(U, -1))
+    e_lin = normwise(olin[:, R], ref["olin"])
+    e_out = normwise(out[:, R].reshape(U, -1), out_g.reshape(U, -1))
+    e_out_own = normwise(out[:, R], ref["out"])
+    e_st = normwise(st, ref["state_out"])
+    res = dict(e_sparse=e_sp, e_linear=e_lin, e_out=e_out, e_out_vs_oracle_sets=e_out_own,
+               e_state=e_st, swaps=swaps)
+    if report is not None:
+        report.update(res)
+    assert e_sp <= tol, res
+    assert e_lin <= tol, res
+    assert e_out <= tol, res
+    assert e_st <= tol, res
+    return res
+
+
+def decode_parity(cfg, inp, report=None):
+    dt = cfg.dtype
+    tol = TOL[dt]
+    ref = orc.decode(inp, cfg)
+    out, st, idx = run_decode(cfg, inp)
+    osp, _, idx_p = run_decode(cfg, inp, gate=gate_fill(inp["gate"].shape, dt, np.inf))
+    olin, _, _ = run_decode(cfg, inp, gate=gate_fill(inp["gate"].shape, dt, -np.inf))
+    assert np.array_equal(idx, idx_p), "index sets differ between two runs"
+    cu = inp["cu_ctx"]
+    qI, kIc, w = (orc.widen(inp[x], dt) for x in ("q_idx", "k_idx_cache", "w_idx"))
+    swaps = 0
+    for b in range(inp["B"]):
+        for g in range(cfg.Hkv):
+            sc = orc.index_scores(qI[b, g], w[b, g], kIc[cu[b]:cu[b + 1], g])
+            swaps += check_set(idx[b, g], sc, cfg.M)
+    q = orc.widen(inp["q"], dt)
+    kc, vc = orc.widen(inp["k_cache"], dt), orc.widen(inp["v_cache"], dt)
+    z = orc.widen(inp["gate"], dt)
+    out_g, osp_g = orc.sparse_given_sets(q, kc, vc, cu[:-1], idx, z, ref["olin"], cfg.Hq, cfg.Hkv,
+                                         cfg.d, cfg.M)
+    res = dict(e_sparse=normwise(osp, osp_g), e_linear=normwise(olin, ref["olin"]),
+               e_out=normwise(out, out_g), e_out_vs_oracle_sets=normwise(out, ref["out"]),
+               e_state=normwise(st, ref["state_out"]), swaps=swaps)
+    if report is not None:
+        report.update(res)
+    for key in ("e_sparse", "e_linear", "e_out", "e_state"):
+        assert res[key] <= tol, res
+    return res

@@ -1,0 +1,135 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+symbol include/lisa.h declares, and rejects bad arguments with the
+documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_linear_top_amd import lisa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on error paths
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "lisa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(lisa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(lisa.LIB_PATH)
+    declared = _declared_symbols()
+    assert set(declared) == set(lisa.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_build_info_names_target():
+    assert "gfx950" in lisa.lisa_build_info()
+
+
+def _dims(**kw):
+    base = dict(Hq=12, Hkv=2, d=128, HI=4, dI=64, M=256, dtype="bf16")
+    base.update(kw)
+    return lisa.make_dims(base["Hq"], base["Hkv"], base["d"], base["HI"], base["dI"], base["M"],
+                          base["dtype"], chunk=base.get("chunk", 64))
+
+
+def _prefill(d, B=1, n=64, ws_bytes=1 << 40, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, q_idx=FAKE, k_idx=FAKE, w_idx=FAKE, gate=FAKE, state_in=0,
+             out=FAKE, state_out=0, topm_out=0, workspace=FAKE)
+    p.update(ptrs)
+    return lisa.lisa_prefill(d, B, n, p["q"], p["k"], p["v"], p["q_idx"], p["k_idx"], p["w_idx"],
+                             p["gate"], p["state_in"], p["out"], p["state_out"], p["topm_out"],
+                             p["workspace"], ws_bytes, 0)
+
+
+def _decode(d, B=2, max_ctx=100, ws_bytes=1 << 40, **ptrs):
+    p = dict(cu=FAKE, q=FAKE, kc=FAKE, vc=FAKE, q_idx=FAKE, kic=FAKE, w_idx=FAKE, gate=FAKE,
+             state=FAKE, out=FAKE, topm_out=0, workspace=FAKE)
+    p.update(ptrs)
+    return lisa.lisa_decode_step(d, B, p["cu"], max_ctx, p["q"], p["kc"], p["vc"], p["q_idx"],
+                                 p["kic"], p["w_idx"], p["gate"], p["state"], p["out"],
+                                 p["topm_out"], p["workspace"], ws_bytes, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), lisa.LISA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=12, Hkv=5), lisa.LISA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=0), lisa.LISA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=34, Hkv=2), lisa.LISA_ERR_UNSUPPORTED),
+    (dict(d=96), lisa.LISA_ERR_UNSUPPORTED),
+    (dict(dI=48), lisa.LISA_ERR_UNSUPPORTED),
+    (dict(HI=0), lisa.LISA_ERR_UNSUPPORTED),
+    (dict(HI=9), lisa.LISA_ERR_UNSUPPORTED),
+    (dict(M=0), lisa.LISA_ERR_INVALID_ARGUMENT),
+    (dict(M=513), lisa.LISA_ERR_UNSUPPORTED),
+    (dict(chunk=32), lisa.LISA_ERR_UNSUPPORTED),
+])
+def test_prefill_rejects_bad_dims(kw, status):
+    assert _prefill(_dims(**kw)) == status
+    assert lisa.lisa_last_error() != ""
+
+
+def test_decode_accepts_larger_topm_than_prefill():
+    d = _dims(M=2048)
+    assert lisa.lisa_decode_workspace_bytes(d, 4, 4096) > 0
+    assert _prefill(d) == lisa.LISA_ERR_UNSUPPORTED
+    assert _decode(_dims(M=2049)) == lisa.LISA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "q_idx", "k_idx", "w_idx", "gate", "out", "workspace"])
+def test_prefill_null_pointer(name):
+    assert _prefill(_dims(), **{name: 0}) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert name in lisa.lisa_last_error()
+
+
+@pytest.mark.parametrize("name", ["q", "gate", "out", "state_in", "topm_out"])
+def test_prefill_misaligned_pointer(name):
+    assert _prefill(_dims(), **{name: FAKE + 8}) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert "aligned" in lisa.lisa_last_error()
+
+
+def test_prefill_workspace_too_small():
+    d = _dims()
+    need = lisa.lisa_prefill_workspace_bytes(d, 1, 64)
+    assert _prefill(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
+    assert str(need) in lisa.lisa_last_error()
+
+
+def test_prefill_empty_is_noop():
+    d = _dims()
+    assert _prefill(d, B=0, q=0, k=0, workspace=0) == lisa.LISA_OK
+    assert _prefill(d, n=0, q=0, k=0, workspace=0) == lisa.LISA_OK
+    assert _prefill(d, n=-1) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _prefill(d, n=40000) == lisa.LISA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["cu", "q", "kc", "vc", "q_idx", "kic", "w_idx", "gate", "state",
+                                  "out", "workspace"])
+def test_decode_null_pointer(name):
+    assert _decode(_dims(), **{name: 0}) == lisa.LISA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_argument_errors():
+    d = _dims()
+    assert _decode(d, cu=FAKE + 4) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _decode(d, max_ctx=0) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _decode(d, B=-1) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _decode(d, B=0, q=0) == lisa.LISA_OK
+    need = lisa.lisa_decode_workspace_bytes(d, 2, 100)
+    assert _decode(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    d = _dims()
+    # decode: fp32 scores per (sequence, group, position) dominate
+    assert lisa.lisa_decode_workspace_bytes(d, 16, 16385) >= 16 * 2 * 16385 * 4
+    a = lisa.lisa_prefill_workspace_bytes(d, 1, 4096)
+    b = lisa.lisa_prefill_workspace_bytes(d, 1, 8192)
+    assert b > a > 4096 * 2 * 256 * 4
+    with pytest.raises(lisa.LisaError):
+        lisa.lisa_prefill_workspace_bytes(_dims(d=80), 1, 10)

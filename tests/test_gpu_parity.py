@@ -1,0 +1,196 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name, shape and seed before touching the GPU.  The
+rules are in tests/parity.py: index sets within the 1e-5 score band of the
+M-th score, normwise error <= 1e-2 (bf16) / 1e-4 (fp32) for the sparse
+branch, the linear branch, the gated output and the final state.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from hybrid_linear_top_amd import inputs as gen
+from hybrid_linear_top_amd.inputs import LayerConfig
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hybrid_linear_top_amd import lisa  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def _pcfg(n, Hq, Hkv, d, HI, dI, M, dtype="bf16", B=1, seed=1):
+    return LayerConfig(f"p_n{n}_h{Hq}x{Hkv}_d{d}_i{HI}x{dI}_m{M}_{dtype}", "prefill", dtype, B=B,
+                       n=n, Hq=Hq, Hkv=Hkv, d=d, HI=HI, dI=dI, M=M, seed=seed)
+
+
+PREFILL_SMALL = [
+    _pcfg(200, 4, 2, 64, 4, 32, 16),
+    _pcfg(333, 7, 1, 128, 3, 64, 64),
+    _pcfg(130, 6, 2, 128, 8, 64, 300),            # M > n: full causal attention
+    _pcfg(257, 4, 4, 64, 5, 32, 1, dtype="f32"),
+    _pcfg(1, 4, 2, 128, 4, 64, 256),
+    _pcfg(65, 12, 2, 128, 4, 64, 256, B=2, seed=3),
+    _pcfg(700, 8, 2, 128, 4, 64, 512, seed=4),    # largest prefill M (1024-entry buffers)
+    _pcfg(520, 4, 2, 64, 4, 64, 200, dtype="f32", seed=5),
+    _pcfg(900, 14, 2, 128, 2, 64, 96, seed=6),
+    _pcfg(1500, 12, 2, 128, 4, 64, 256, seed=7),  # several compactions per query
+]
+
+
+@pytest.mark.parametrize("cfg", PREFILL_SMALL, ids=lambda c: c.name)
+def test_prefill_small(cfg):
+    _say("prefill", cfg.name, "seed", cfg.seed)
+    inp = gen.make_prefill_inputs(cfg)
+    rep = {}
+    parity.prefill_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+def test_prefill_with_initial_state():
+    cfg = _pcfg(150, 6, 2, 128, 4, 64, 32, seed=11)
+    _say("prefill state_in", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    S0 = np.random.default_rng(2).standard_normal((1, cfg.Hq, cfg.d, cfg.d)).astype(np.float32)
+    rep = {}
+    parity.prefill_parity(cfg, inp, state_in=S0, report=rep)
+    _say("  ", rep)
+
+
+def test_prefill_config0_tiny_fp32():
+    cfg = gen.CONFIGS[0]
+    _say("prefill", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    rep = {}
+    parity.prefill_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+def test_prefill_config1_full():
+    cfg = gen.CONFIGS[1]
+    _say("prefill", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    rep = {}
+    parity.prefill_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+def test_prefill_config3_sampled_rows():
+    cfg = gen.CONFIGS[3]
+    _say("prefill", cfg.name, "(sampled rows, full state)")
+    inp = gen.make_prefill_inputs(cfg)
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 2, 63, 64, 65, 254, 255, 256, 257, 1000, 4095, 4096, 8191, 12345,
+                       16383] + rng.integers(0, cfg.n, size=40).tolist()))
+    rep = {}
+    parity.prefill_parity(cfg, inp, rows=rows, report=rep)
+    _say("  ", rep)
+
+
+def _dcfg(Hq, Hkv, d, HI, dI, M, lengths, dtype="bf16", seed=1):
+    return LayerConfig(f"d_h{Hq}x{Hkv}_d{d}_i{HI}x{dI}_m{M}_{dtype}_L{'-'.join(map(str, lengths))}",
+                       "decode", dtype, B=len(lengths), Hq=Hq, Hkv=Hkv, d=d, HI=HI, dI=dI, M=M,
+                       seed=seed), np.asarray(lengths)
+
+
+DECODE_SMALL = [
+    _dcfg(12, 2, 128, 4, 64, 256, [1, 2, 255, 256, 257, 1000]),
+    _dcfg(7, 7, 64, 3, 32, 16, [17, 300, 513, 64]),
+    _dcfg(28, 4, 128, 4, 64, 512, [4097, 700, 513, 20000], seed=2),
+    _dcfg(8, 2, 64, 8, 64, 100, [999, 1001, 5000], dtype="f32", seed=3),
+    _dcfg(16, 1, 128, 6, 64, 2048, [3000, 2048, 2049], seed=4),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SMALL, ids=lambda c: c[0].name)
+def test_decode_small(case):
+    cfg, lengths = case
+    _say("decode", cfg.name, "seed", cfg.seed)
+    inp = gen.make_decode_inputs(cfg, lengths=lengths)
+    rep = {}
+    parity.decode_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_decode_configs(cid):
+    cfg = gen.CONFIGS[cid]
+    _say("decode", cfg.name)
+    inp = gen.make_decode_inputs(cfg)
+    rep = {}
+    parity.decode_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+def test_ties_lowest_index_wins():
+    """w = 0 makes every score exactly 0: the sets must be the first m positions."""
+    cfg = _pcfg(400, 4, 2, 64, 4, 32, 100)
+    _say("prefill all-ties", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    inp["w_idx"] = np.zeros_like(inp["w_idx"])
+    _, _, idx = parity.run_prefill(cfg, inp)
+    for t in range(cfg.n):
+        m = min(cfg.M, t + 1)
+        exp = np.concatenate([np.arange(m), -np.ones(cfg.M - m)]).astype(np.int32)
+        assert np.array_equal(idx[0, t, 0], exp) and np.array_equal(idx[0, t, 1], exp), t
+    dcfg, L = _dcfg(4, 2, 64, 4, 32, 100, [50, 100, 101, 3000])
+    _say("decode all-ties", dcfg.name)
+    dinp = gen.make_decode_inputs(dcfg, lengths=L)
+    dinp["w_idx"] = np.zeros_like(dinp["w_idx"])
+    _, _, didx = parity.run_decode(dcfg, dinp)
+    for b, Lb in enumerate(L):
+        m = min(dcfg.M, Lb)
+        exp = np.concatenate([np.arange(m), -np.ones(dcfg.M - m)]).astype(np.int32)
+        assert np.array_equal(didx[b, 0], exp) and np.array_equal(didx[b, 1], exp), b
+
+
+def test_deterministic():
+    cfg = gen.CONFIGS[1]
+    _say("determinism", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    a = parity.run_prefill(cfg, inp)
+    b = parity.run_prefill(cfg, inp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    dcfg = gen.CONFIGS[2]
+    _say("determinism", dcfg.name)
+    dinp = gen.make_decode_inputs(dcfg, B=4)
+    a = parity.run_decode(dcfg, dinp)
+    b = parity.run_decode(dcfg, dinp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_prefill_then_decode_matches_longer_prefill():
+    """GPU prefill(n) + GPU decode of token n equals row n of GPU prefill(n+1)."""
+    cfg = _pcfg(600, 12, 2, 128, 4, 64, 256, seed=21)
+    _say("cross-path", cfg.name)
+    full = gen.make_prefill_inputs(cfg)
+    n = cfg.n - 1
+    short = {k: (v[:, :n] if isinstance(v, np.ndarray) else v) for k, v in full.items()}
+    short["n"] = n
+    _, st, _ = parity.run_prefill(cfg, short)
+    out_full, st_full, idx_full = parity.run_prefill(cfg, full)
+    dcfg = LayerConfig("cross", "decode", cfg.dtype, B=1, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d,
+                       HI=cfg.HI, dI=cfg.dI, M=cfg.M)
+    dec = {"q": full["q"][:, n], "k_cache": full["k"][0], "v_cache": full["v"][0],
+           "q_idx": full["q_idx"][:, n], "k_idx_cache": full["k_idx"][0],
+           "w_idx": full["w_idx"][:, n], "gate": full["gate"][:, n],
+           "state": st.astype(np.float32), "cu_ctx": np.array([0, cfg.n], dtype=np.int64),
+           "B": 1, "max_ctx": cfg.n}
+    out_d, st_d, idx_d = parity.run_decode(dcfg, dec)
+    assert np.array_equal(idx_d[0], idx_full[0, n])
+    assert parity.normwise(out_d[0], out_full[0, n]) <= 1e-2
+    assert parity.normwise(st_d, st_full) <= 1e-3
