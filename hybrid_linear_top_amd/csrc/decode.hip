@@ -26,22 +26,23 @@ namespace lisa {
 
 namespace {
 
-// dot product of one 16-byte chunk of keys with the matching chunk of an
-// indexer query (kept packed in the storage format).
-__device__ __forceinline__ float chunk_dot(const u32x4 &k, const u32x4 &q, uint16_t) {
-    float acc = 0.0f;
+// Widen one 16-byte chunk (8 bf16 or 4 fp32) to fp32.
+template <typename T> struct Chunk;
+template <> struct Chunk<uint16_t> {
+    __device__ static __forceinline__ void widen(const u32x4 &x, float *f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[i]),
-                                              __builtin_bit_cast(bf16x2_t, k[i]), acc, false);
-    return acc;
-}
-__device__ __forceinline__ float chunk_dot(const u32x4 &k, const u32x4 &q, float) {
-    float acc = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(x[i] << 16);
+            f[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct Chunk<float> {
+    __device__ static __forceinline__ void widen(const u32x4 &x, float *f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), acc);
-    return acc;
-}
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(x[i]);
+    }
+};
 
 template <typename T, int DI, int HIPAD>
 __device__ void score_group(const DecodeScoreArgs &a, int sb) {
@@ -67,18 +68,18 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb) {
         const int g = task % G, sub = task / G;
         const int tb = tok0 + sub * TPW;
         if (tb >= tok_end) continue;
-        u32x4 qv[HIPAD];
+        float qv[HIPAD][EPC];
         float wv[HIPAD];
 #pragma unroll
         for (int j = 0; j < HIPAD; ++j) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            wv[j] = 0.0f;
             if (j < a.HI) {
-                qv[j] = *reinterpret_cast<const u32x4 *>(qI + ((size_t)(b * G + g) * a.HI + j) * DI +
-                                                         c * EPC);
+                raw = *reinterpret_cast<const u32x4 *>(qI + ((size_t)(b * G + g) * a.HI + j) * DI +
+                                                       c * EPC);
                 wv[j] = Elt<T>::to_f32(wI[(size_t)(b * G + g) * a.HI + j]);
-            } else {
-                qv[j] = u32x4{0u, 0u, 0u, 0u};
-                wv[j] = 0.0f;
             }
+            Chunk<T>::widen(raw, qv[j]);
         }
         u32x4 raw[NIT];
 #pragma unroll
@@ -93,10 +94,14 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb) {
         float *out = a.scores + (size_t)(b * G + g) * a.max_ctx;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
+            float kf[EPC];
+            Chunk<T>::widen(raw[it], kf);
             float score = 0.0f;
 #pragma unroll
             for (int j = 0; j < HIPAD; ++j) {
-                float p = chunk_dot(raw[it], qv[j], T{});
+                float p = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) p = fmaf(qv[j][e], kf[e], p);
 #pragma unroll
                 for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o);
                 score = fmaf(wv[j], fmaxf(p, 0.0f), score);
