@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""LISA layer benchmark on one MI355X.
+
+Prints ONE JSON line.  The headline is the prefill of one Qwen2.5-7B-shaped
+LISA layer at 16K context (B=1, n=16384, 28 query / 4 KV heads, d=128,
+indexer 4 x 64, M=256, C=64): `value` = tokens/s = n / call time.  The
+decode step at 16K context (Qwen2.5-1.5B shapes, B=16, 16384 cached + 1 new
+token, M=256) is measured in the same run and reported under "decode".
+
+Inputs are seeded synthetic tensors (the generator in
+hybrid_linear_top_amd/inputs.py), resident in HBM before timing starts, and
+rotated over several copies so the 256 MB Infinity Cache cannot serve
+repeated reads.  Per-kernel durations come from HIP events the library
+records around each launch on the caller's stream (lisa_stage_timing), in a
+separate pass so the headline timing carries no event overhead.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K2]
+                  [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LISA layer tokens/s at 16K ctx (decode + prefill); % of HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (counts of the method itself, not of any implementation)
+def tri(n):
+    return n * (n + 1) // 2
+
+
+def pairs(n, M):
+    """sum_{t<n} min(M, t+1): selected (query, key) pairs per group."""
+    if n <= M:
+        return tri(n)
+    return tri(M) + (n - M) * M
+
+
+def prefill_flops(cfg, n, B=1):
+    G, Hq, d, C = cfg.Hkv, cfg.Hq, cfg.d, cfg.chunk
+    f = {
+        "indexer_topm": 2 * G * cfg.HI * cfg.dI * tri(n),
+        "sparse_gate_prefill": 4 * Hq * d * pairs(n, cfg.M),
+        "linear_chunk_state": G * 2 * n * d * d,
+        "linear_prefix_scan": 0,
+        "linear_chunk_output": Hq * (4 * n * C * d + 2 * n * d * d),
+    }
+    return {k: v * B for k, v in f.items()}
+
+
+def decode_bytes(cfg, lengths):
+    import numpy as np
+    L = np.asarray(lengths, dtype=np.int64)
+    B, G, Hq, d = len(L), cfg.Hkv, cfg.Hq, cfg.d
+    kI = int(L.sum()) * G * cfg.dI * 2
+    kv_rows = int(np.minimum(L, cfg.M).sum()) * G * 2 * d * 2
+    state = B * Hq * d * d * 4 * 2
+    small = B * (2 * Hq * d * 2 + G * cfg.HI * cfg.dI * 2 + G * cfg.HI * 2 + Hq * 2 + 2 * G * d * 2)
+    return {
+        "decode_score_state": kI + state + B * (Hq * d * 2 + G * cfg.HI * cfg.dI * 2
+                                                + G * cfg.HI * 2 + 2 * G * d * 2),
+        "decode_select": 0,
+        "sparse_gate_decode": kv_rows + B * (2 * Hq * d * 2 + Hq * 2),
+        "total": kI + kv_rows + state + small,
+        "kI": kI, "kv_rows": kv_rows, "state": state, "small": small,
+    }
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(ROOT, "hybrid_linear_top_amd", "csrc", nm), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key, src_files):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or when the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash(*src_files):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def timed_loop(fn, steps, warmup, copies):
+    import torch
+    for i in range(warmup):
+        fn(i % copies)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        fn(i % copies)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def stage_pass(fn, steps, copies):
+    import torch
+    from hybrid_linear_top_amd import lisa
+    lisa.lisa_stage_timing_read(reset=True)
+    lisa.lisa_stage_timing(True)
+    for i in range(steps):
+        fn(i % copies)
+    torch.cuda.synchronize()
+    lisa.lisa_stage_timing(False)
+    return {k: tot / max(cnt, 1) for k, (cnt, tot) in lisa.lisa_stage_timing_read(reset=True).items()}
+
+
+def roofline_entry(kernel, ms, work, bound, traffic=None):
+    if bound == "hbm":
+        achieved = work / (ms * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = work / (ms * 1e-3) / 1e12
+        peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel,
+            "avg_launch_ms": round(ms, 5), "algorithmic_per_launch": work}
+
+
+def cores_used():
+    n = os.environ.get("OMP_NUM_THREADS")
+    if n and n.isdigit():
+        return int(n)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(args):
+    import numpy as np
+    import torch
+    from hybrid_linear_top_amd import inputs as gen, lisa
+    cfg = gen.CONFIGS[3]
+    inp = gen.make_prefill_inputs(cfg)
+    dims = lisa.dims_from_config(cfg)
+    B, n = inp["B"], inp["n"]
+    copies = 2
+    keys = ("q", "k", "v", "q_idx", "k_idx", "w_idx", "gate")
+    sets = [{k: lisa.to_device(inp[k]) for k in keys} for _ in range(copies)]
+    outs = [torch.empty_like(s["q"]) for s in sets]
+    st = torch.empty((B, cfg.Hq, cfg.d, cfg.d), dtype=torch.float32, device="cuda")
+    idx = [torch.empty((B, n, cfg.Hkv, cfg.M), dtype=torch.int32, device="cuda") for _ in range(copies)]
+    ws = torch.empty(lisa.lisa_prefill_workspace_bytes(dims, B, n), dtype=torch.uint8, device="cuda")
+
+    def step(c):
+        s = sets[c]
+        lisa.prefill(dims, s["q"], s["k"], s["v"], s["q_idx"], s["k_idx"], s["w_idx"], s["gate"],
+                     out=outs[c], state_out=st, topm_out=idx[c], workspace=ws)
+
+    ms = timed_loop(step, args.steps, args.warmup, copies)
+    stages = stage_pass(step, max(3, min(args.steps, 10)), copies)
+    flops = prefill_flops(cfg, n, B)
+    total_flops = sum(flops.values())
+    stage_rows = {}
+    for k, v in stages.items():
+        f = flops.get(k, 0)
+        stage_rows[k] = {"ms": round(v, 5),
+                         "tflops": round(f / (v * 1e-3) / 1e12, 3) if f else None,
+                         "frac_mfma_peak": round(f / (v * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+                         if f else None}
+    dom = max(stages, key=stages.get)
+    src = {"indexer_topm": ["indexer.hip", "common.hpp"],
+           "sparse_gate_prefill": ["sparse.hip", "common.hpp"],
+           "linear_chunk_output": ["linear.hip", "common.hpp"],
+           "linear_chunk_state": ["linear.hip", "common.hpp"],
+           "linear_prefix_scan": ["linear.hip", "common.hpp"]}[dom]
+    roof = roofline_entry(dom, stages[dom], flops.get(dom, 0), "mfma",
+                          traffic_from_profiles(dom, src))
+    res = {
+        "workload": f"lisa_prefill qwen2.5-7b-shaped B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
+                    f"d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} C={cfg.chunk} bf16",
+        "tokens_per_s": B * n / (ms * 1e-3), "ms": ms, "roofline": roof, "stages": stage_rows,
+        "step_roofline": {"bound": "mfma", "algorithmic_flops": total_flops,
+                          "achieved_tflops": round(total_flops / (ms * 1e-3) / 1e12, 3),
+                          "frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cfg": cfg, "inp": inp,
+    }
+    del sets, outs, idx, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+    from hybrid_linear_top_amd import inputs as gen, lisa
+    cfg = gen.CONFIGS[2]
+    inp = gen.make_decode_inputs(cfg)
+    dims = lisa.dims_from_config(cfg)
+    B = inp["B"]
+    copies = 9  # 9 x ~96 MB of bytes read per step >= 3 x the 256 MB Infinity Cache
+    cu = lisa.to_device(inp["cu_ctx"])
+    shared = {k: lisa.to_device(inp[k]) for k in ("q", "q_idx", "w_idx", "gate")}
+    per = [{k: lisa.to_device(inp[k]) for k in ("k_cache", "v_cache", "k_idx_cache", "state")}
+           for _ in range(copies)]
+    out = torch.empty_like(shared["q"])
+    idx = torch.empty((B, cfg.Hkv, cfg.M), dtype=torch.int32, device="cuda")
+    ws = torch.empty(lisa.lisa_decode_workspace_bytes(dims, B, inp["max_ctx"]), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(c):
+        p = per[c]
+        lisa.decode_step(dims, cu, inp["max_ctx"], shared["q"], p["k_cache"], p["v_cache"],
+                         shared["q_idx"], p["k_idx_cache"], shared["w_idx"], shared["gate"],
+                         p["state"], out=out, topm_out=idx, workspace=ws)
+
+    ms = timed_loop(step, args.decode_steps, args.decode_warmup, copies)
+    stages = stage_pass(step, max(copies, min(args.decode_steps, 45)), copies)
+    by = decode_bytes(cfg, inp["lengths"])
+    stage_rows = {}
+    for k, v in stages.items():
+        b = by.get(k, 0)
+        stage_rows[k] = {"ms": round(v, 5),
+                         "gbs": round(b / (v * 1e-3) / 1e9, 1) if b else None,
+                         "frac_hbm_peak": round(b / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if b else None}
+    dom = max(stages, key=stages.get)
+    roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm",
+                          traffic_from_profiles(dom, ["decode.hip", "common.hpp"]))
+    res = {
+        "workload": f"lisa_decode_step qwen2.5-1.5b-shaped B={B} ctx=16384+1 Hq={cfg.Hq} "
+                    f"Hkv={cfg.Hkv} d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} bf16",
+        "tokens_per_s": B / (ms * 1e-3), "ms": ms, "roofline": roof, "stages": stage_rows,
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": by["total"],
+                          "achieved_gbs": round(by["total"] / (ms * 1e-3) / 1e9, 1),
+                          "frac": round(by["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "cfg": cfg, "inp": inp,
+    }
+    del per, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_prefill(res):
+    """The fp64 oracle's full prefill call on the same n=16384 inputs (all rows;
+    input widening excluded from the timed region)."""
+    from oracle import oracle as orc
+    cfg, inp = res["cfg"], res["inp"]
+    n = inp["n"]
+    secs = orc.prefill(inp, cfg)["seconds"]
+    return {"value": round(inp["B"] * n / secs, 3), "unit": "tokens/s", "cores": cores_used(),
+            "kind": "oracle",
+            "sample": f"one full fp64 oracle prefill call on the same B=1, n={n} inputs "
+                      f"({secs:.1f}s); not a sample: the whole call fits the CPU budget",
+            "seconds_measured": round(secs, 2)}
+
+
+def cpu_decode(res, reps=31):
+    from oracle import oracle as orc
+    cfg, inp = res["cfg"], res["inp"]
+    secs = sorted(orc.decode(inp, cfg)["seconds"] for _ in range(reps))
+    med = secs[len(secs) // 2]
+    return {"value": round(inp["B"] / med, 3), "unit": "tokens/s", "cores": cores_used(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle decode step on the full batch (B={inp['B']}, 16385 visible "
+                      f"tokens each), median of {reps} calls ({med:.3f}s per step)",
+            "seconds_measured": round(sum(secs), 2)}
+
+
+def copy_calibration(nbytes=1 << 30):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings (the copy reads and writes nbytes each)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return nbytes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the LISA layer here is a single-GPU kernel path "
+              "(no collectives are built); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    t_start = time.time()
+    if args.copy_calibration:
+        nb = copy_calibration()
+        print(json.dumps({"copy_calibration_bytes": nb}), flush=True)
+    pre = bench_prefill(args)
+    print(f"[bench] prefill {pre['ms']:.3f} ms/call, stages {pre['stages']}", file=sys.stderr, flush=True)
+    dec = bench_decode(args)
+    print(f"[bench] decode {dec['ms'] * 1e3:.1f} us/step, stages {dec['stages']}", file=sys.stderr, flush=True)
+    cpu_p = cpu_d = None
+    if not args.no_cpu_baseline:
+        cpu_p = cpu_prefill(pre)
+        print(f"[bench] cpu prefill baseline {cpu_p}", file=sys.stderr, flush=True)
+        cpu_d = cpu_decode(dec)
+        print(f"[bench] cpu decode baseline {cpu_d}", file=sys.stderr, flush=True)
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": pre["workload"], "global_batch": 1, "seq_len": 16384,
+                   "parallelism": "single-gpu"},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu_p,
+        "step_roofline": pre["step_roofline"],
+        "stages": pre["stages"],
+        "decode": {
+            "workload": dec["workload"], "value": round(dec["tokens_per_s"], 1), "unit": "tokens/s",
+            "steps": args.decode_steps, "warmup": args.decode_warmup,
+            "ms_per_step": round(dec["ms"], 5), "roofline": dec["roofline"],
+            "step_roofline": dec["step_roofline"], "stages": dec["stages"], "cpu_baseline": cpu_d,
+        },
+        "wall_s": round(time.time() - t_start, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

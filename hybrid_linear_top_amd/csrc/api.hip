@@ -6,6 +6,9 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "lisa.h"
 #include "kernels.hpp"
@@ -105,6 +108,49 @@ DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
     return w;
 }
 
+// ---- optional per-stage timing (benchmarking) -------------------------------
+enum Stage {
+    ST_LIN_STATE, ST_LIN_SCAN, ST_LIN_OUT, ST_INDEXER, ST_SPARSE_PREFILL,
+    ST_DEC_SCORE_STATE, ST_DEC_SELECT, ST_SPARSE_DECODE, ST_COUNT
+};
+const char *const kStageNames[ST_COUNT] = {
+    "linear_chunk_state", "linear_prefix_scan", "linear_chunk_output", "indexer_topm",
+    "sparse_gate_prefill", "decode_score_state", "decode_select", "sparse_gate_decode"};
+
+struct Timing {
+    std::mutex mu;
+    std::atomic<bool> enabled{false};
+    struct Rec { int stage; hipEvent_t a, b; };
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> pool;
+    double total_ms[ST_COUNT] = {};
+    int64_t launches[ST_COUNT] = {};
+    hipEvent_t get() {
+        if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+};
+Timing g_timing;
+
+// Launch through `fn`, bracketed by an event pair when timing is enabled.
+template <typename F>
+hipError_t timed(int stage, hipStream_t s, F fn) {
+    if (!g_timing.enabled) return fn();
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    hipEvent_t a = g_timing.get(), b = g_timing.get();
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, s);
+    if (e != hipSuccess) return e;
+    e = fn();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, s);
+    if (e != hipSuccess) return e;
+    g_timing.pending.push_back({stage, a, b});
+    return hipSuccess;
+}
+
 #define LISA_NEED(p, name)                                                                  \
     do {                                                                                    \
         if (!(p)) return fail(LISA_ERR_INVALID_ARGUMENT, "%s is NULL", name);               \
@@ -200,7 +246,12 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
     la.r = Hq / G;
     la.nC = (n + 63) / 64;
     la.per_head = state_in != nullptr;
-    LISA_HIP(lisa::launch_linear_prefill(la, dims->dtype, D, s), "linear-attention launch");
+    LISA_HIP(timed(ST_LIN_STATE, s, [&] { return lisa::launch_linear_chunk_state(la, dims->dtype, D, s); }),
+             "linear chunk-state launch");
+    LISA_HIP(timed(ST_LIN_SCAN, s, [&] { return lisa::launch_linear_prefix_scan(la, dims->dtype, D, s); }),
+             "linear prefix-scan launch");
+    LISA_HIP(timed(ST_LIN_OUT, s, [&] { return lisa::launch_linear_chunk_output(la, dims->dtype, D, s); }),
+             "linear chunk-output launch");
 
     lisa::IndexerArgs ia{};
     ia.q_idx = q_idx;
@@ -212,7 +263,8 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
     ia.G = G;
     ia.HI = dims->idx_heads;
     ia.M = dims->top_m;
-    LISA_HIP(lisa::launch_indexer_prefill(ia, dims->dtype, dims->idx_dim, s), "indexer launch");
+    LISA_HIP(timed(ST_INDEXER, s, [&] { return lisa::launch_indexer_prefill(ia, dims->dtype, dims->idx_dim, s); }),
+             "indexer launch");
 
     lisa::SparseArgs sa{};
     sa.q = q;
@@ -232,7 +284,8 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
     sa.max_ctx = n;
     sa.scale_log2 = scale_log2(dims);
     sa.units = B * n * G;
-    LISA_HIP(lisa::launch_sparse_gate(sa, dims->dtype, D, false, s), "sparse-attention launch");
+    LISA_HIP(timed(ST_SPARSE_PREFILL, s, [&] { return lisa::launch_sparse_gate(sa, dims->dtype, D, false, s); }),
+             "sparse-attention launch");
     return ok();
 }
 
@@ -288,9 +341,9 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
     da.HI = dims->idx_heads;
     da.max_ctx = max_ctx;
     da.tiles_per_seq = (max_ctx + lisa::kDecodeTile - 1) / lisa::kDecodeTile;
-    LISA_HIP(lisa::launch_decode_score_state(da, dims->dtype, D, dims->idx_dim, s),
+    LISA_HIP(timed(ST_DEC_SCORE_STATE, s, [&] { return lisa::launch_decode_score_state(da, dims->dtype, D, dims->idx_dim, s); }),
              "indexer-scan/state launch");
-    LISA_HIP(lisa::launch_decode_select(scores, cu_ctx, B, G, dims->top_m, max_ctx, idx, s),
+    LISA_HIP(timed(ST_DEC_SELECT, s, [&] { return lisa::launch_decode_select(scores, cu_ctx, B, G, dims->top_m, max_ctx, idx, s); }),
              "top-M select launch");
 
     lisa::SparseArgs sa{};
@@ -311,8 +364,42 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
     sa.max_ctx = max_ctx;
     sa.scale_log2 = scale_log2(dims);
     sa.units = B * G;
-    LISA_HIP(lisa::launch_sparse_gate(sa, dims->dtype, D, true, s), "sparse-attention launch");
+    LISA_HIP(timed(ST_SPARSE_DECODE, s, [&] { return lisa::launch_sparse_gate(sa, dims->dtype, D, true, s); }),
+             "sparse-attention launch");
+    return ok();
+}
+
+lisa_status lisa_stage_timing(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.enabled = enable != 0;
+    return ok();
+}
+
+lisa_status lisa_stage_timing_read(int32_t max_stages, const char **names, int64_t *launches,
+                                   double *total_ms, int32_t *n_stages, int32_t reset) {
+    if (max_stages < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "max_stages < 0");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    for (auto &r : g_timing.pending) {
+        float ms = 0.0f;
+        LISA_HIP(hipEventSynchronize(r.b), "event synchronize");
+        LISA_HIP(hipEventElapsedTime(&ms, r.a, r.b), "event elapsed time");
+        g_timing.total_ms[r.stage] += ms;
+        g_timing.launches[r.stage] += 1;
+        g_timing.pool.push_back(r.a);
+        g_timing.pool.push_back(r.b);
+    }
+    g_timing.pending.clear();
+    for (int i = 0; i < ST_COUNT && i < max_stages; ++i) {
+        if (names) names[i] = kStageNames[i];
+        if (launches) launches[i] = g_timing.launches[i];
+        if (total_ms) total_ms[i] = g_timing.total_ms[i];
+    }
+    if (n_stages) *n_stages = ST_COUNT;
+    if (reset) {
+        for (int i = 0; i < ST_COUNT; ++i) { g_timing.total_ms[i] = 0.0; g_timing.launches[i] = 0; }
+    }
     return ok();
 }
 
 }  // extern "C"
+

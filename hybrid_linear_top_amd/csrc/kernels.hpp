@@ -54,7 +54,9 @@ struct LinearArgs {
     int B, n, Hq, G, r, nC;
     int per_head;                // 1 if state_in != null (prefix states per query head)
 };
-hipError_t launch_linear_prefill(const LinearArgs &a, int dtype, int d, hipStream_t s);
+hipError_t launch_linear_chunk_state(const LinearArgs &a, int dtype, int d, hipStream_t s);
+hipError_t launch_linear_prefix_scan(const LinearArgs &a, int dtype, int d, hipStream_t s);
+hipError_t launch_linear_chunk_output(const LinearArgs &a, int dtype, int d, hipStream_t s);
 
 // ---- prefill: indexer + streaming top-M ------------------------------------
 struct IndexerArgs {

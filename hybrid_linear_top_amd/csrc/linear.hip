@@ -250,25 +250,38 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
 }
 
 template <typename T, int D>
-hipError_t run(const LinearArgs &a, hipStream_t s) {
-    const int nblk = a.B * a.G * a.nC;
-    hipLaunchKernelGGL((chunk_state_kernel<T, D>), dim3(nblk), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t run_state(const LinearArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((chunk_state_kernel<T, D>), dim3(a.B * a.G * a.nC), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+template <typename T, int D>
+hipError_t run_scan(const LinearArgs &a, hipStream_t s) {
     constexpr int BPG = (D * D / 4 + 255) / 256;
     hipLaunchKernelGGL((prefix_scan_kernel<T, D>), dim3(a.B * a.G * BPG), dim3(256), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_output_kernel<T, D>), dim3(nblk), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+template <typename T, int D>
+hipError_t run_output(const LinearArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((chunk_output_kernel<T, D>), dim3(a.B * a.G * a.nC), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_linear_prefill(const LinearArgs &a, int dtype, int d, hipStream_t s) {
-    if (a.B * a.nC == 0) return hipSuccess;
-    if (dtype == 1) return d == 128 ? run<uint16_t, 128>(a, s) : run<uint16_t, 64>(a, s);
-    return d == 128 ? run<float, 128>(a, s) : run<float, 64>(a, s);
+#define LISA_LIN_DISPATCH(fn)                                                            \
+    if (a.B * a.nC == 0) return hipSuccess;                                              \
+    if (dtype == 1) return d == 128 ? fn<uint16_t, 128>(a, s) : fn<uint16_t, 64>(a, s);  \
+    return d == 128 ? fn<float, 128>(a, s) : fn<float, 64>(a, s);
+
+hipError_t launch_linear_chunk_state(const LinearArgs &a, int dtype, int d, hipStream_t s) {
+    LISA_LIN_DISPATCH(run_state)
 }
+hipError_t launch_linear_prefix_scan(const LinearArgs &a, int dtype, int d, hipStream_t s) {
+    LISA_LIN_DISPATCH(run_scan)
+}
+hipError_t launch_linear_chunk_output(const LinearArgs &a, int dtype, int d, hipStream_t s) {
+    LISA_LIN_DISPATCH(run_output)
+}
+#undef LISA_LIN_DISPATCH
 
 }  // namespace lisa

@@ -24,7 +24,8 @@ LISA_F32 = 0
 LISA_BF16 = 1
 
 EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill", "lisa_decode_workspace_bytes",
-           "lisa_decode_step", "lisa_last_error", "lisa_build_info"]
+           "lisa_decode_step", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
+           "lisa_build_info"]
 
 
 class LisaDims(ctypes.Structure):
@@ -55,6 +56,13 @@ def _load(path: str = LIB_PATH):
     lib.lisa_decode_workspace_bytes.restype = ctypes.c_int
     lib.lisa_decode_step.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp, sz, vp]
     lib.lisa_decode_step.restype = ctypes.c_int
+    lib.lisa_stage_timing.argtypes = [i32]
+    lib.lisa_stage_timing.restype = ctypes.c_int
+    lib.lisa_stage_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p),
+                                           ctypes.POINTER(ctypes.c_int64),
+                                           ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int32), i32]
+    lib.lisa_stage_timing_read.restype = ctypes.c_int
     lib.lisa_last_error.argtypes = []
     lib.lisa_last_error.restype = ctypes.c_char_p
     lib.lisa_build_info.argtypes = []
@@ -104,6 +112,22 @@ def lisa_decode_step(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx
     return _lib.lisa_decode_step(ctypes.byref(dims), B, cu_ctx, max_ctx, q, k_cache, v_cache,
                                  q_idx, k_idx_cache, w_idx, gate, state, out, topm_out, workspace,
                                  workspace_bytes, stream)
+
+
+def lisa_stage_timing(enable: bool) -> None:
+    _check(_lib.lisa_stage_timing(1 if enable else 0))
+
+
+def lisa_stage_timing_read(reset: bool = True) -> dict:
+    """{stage name: (launches, total_ms)} for every stage with launches."""
+    N = 16
+    names = (ctypes.c_char_p * N)()
+    launches = (ctypes.c_int64 * N)()
+    total = (ctypes.c_double * N)()
+    n = ctypes.c_int32(0)
+    _check(_lib.lisa_stage_timing_read(N, names, launches, total, ctypes.byref(n), 1 if reset else 0))
+    return {names[i].decode(): (int(launches[i]), float(total[i])) for i in range(n.value)
+            if launches[i] > 0}
 
 
 # ---- torch conveniences ---------------------------------------------------

@@ -133,6 +133,26 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
                              int32_t *topm_out, void *workspace, size_t workspace_bytes,
                              lisa_stream_t stream);
 
+/*
+ * Per-kernel timing, for benchmarking only.  While enabled (process-wide),
+ * every kernel the entry points launch is bracketed by a pair of HIP events
+ * recorded on the caller's stream; this adds host work per launch, so whole-
+ * call timings should be taken with it disabled.  Stages, in order:
+ * linear_chunk_state, linear_prefix_scan, linear_chunk_output, indexer_topm,
+ * sparse_gate_prefill, decode_score_state, decode_select, sparse_gate_decode.
+ */
+lisa_status lisa_stage_timing(int32_t enable);
+
+/*
+ * Waits for the recorded events, adds their elapsed times to per-stage
+ * totals and copies out up to max_stages entries: static stage names (the
+ * library owns the strings), launch counts and total milliseconds since the
+ * last reset.  Any output pointer may be NULL.  *n_stages receives the number
+ * of stages.  reset != 0 clears the totals after copying.
+ */
+lisa_status lisa_stage_timing_read(int32_t max_stages, const char **names, int64_t *launches,
+                                   double *total_ms, int32_t *n_stages, int32_t reset);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char *lisa_last_error(void);
 

@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import time
 
 import numpy as np
 
@@ -115,12 +116,15 @@ def prefill(inp: dict, cfg, rows=None, M=None, scale=0.0, state_in=None, nthread
     olin = np.zeros((B, R, Hq, d))
     st = np.zeros((B, Hq, d, d))
     idx = np.zeros((B, R, G, M), dtype=np.int32)
+    t0 = time.perf_counter()
     lib.oracle_prefill(B, n, Hq, cfg.Hkv, d, cfg.HI, cfg.dI, M, float(scale),
                        _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(qI, _dp), _ptr(kI, _dp),
                        _ptr(w, _dp), _ptr(z, _dp), _ptr(S0, _dp),
                        _ptr(rows, _ip), R, _ptr(out, _dp), _ptr(st, _dp), _ptr(idx, _ip),
                        _ptr(osp, _dp), _ptr(olin, _dp), int(nthreads))
-    return {"out": out, "osp": osp, "olin": olin, "idx": idx, "state_out": st, "rows": rows}
+    secs = time.perf_counter() - t0
+    return {"out": out, "osp": osp, "olin": olin, "idx": idx, "state_out": st, "rows": rows,
+            "seconds": secs}
 
 
 def decode(inp: dict, cfg, M=None, scale=0.0, nthreads=0, lib=None, z_override=None):
@@ -140,11 +144,13 @@ def decode(inp: dict, cfg, M=None, scale=0.0, nthreads=0, lib=None, z_override=N
     olin = np.zeros((B, Hq, d))
     st = np.zeros((B, Hq, d, d))
     idx = np.zeros((B, G, M), dtype=np.int32)
+    t0 = time.perf_counter()
     lib.oracle_decode(B, _ptr(cu, _lp), Hq, cfg.Hkv, d, cfg.HI, cfg.dI, M, float(scale),
                       _ptr(q, _dp), _ptr(kc, _dp), _ptr(vc, _dp), _ptr(qI, _dp), _ptr(kIc, _dp),
                       _ptr(w, _dp), _ptr(z, _dp), _ptr(S, _dp), _ptr(out, _dp), _ptr(st, _dp),
                       _ptr(idx, _ip), _ptr(osp, _dp), _ptr(olin, _dp), int(nthreads))
-    return {"out": out, "osp": osp, "olin": olin, "idx": idx, "state_out": st}
+    secs = time.perf_counter() - t0
+    return {"out": out, "osp": osp, "olin": olin, "idx": idx, "state_out": st, "seconds": secs}
 
 
 def sparse_given_sets(q, k_rows, v_rows, row0, idx, z, olin, Hq, Hkv, d, M, scale=0.0,
