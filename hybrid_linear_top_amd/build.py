@@ -21,6 +21,10 @@ SOURCES = ["api.hip", "decode.hip", "sparse.hip", "linear.hip", "indexer.hip"]
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I", INCLUDE,
          # packed fp32 arithmetic is kept off on this part
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # scores and activations are finite by contract: no NaN canonicalisation
+         "-fno-honor-nans",
+         # keep MFMA accumulators in arch VGPRs (no AGPR round trips)
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function"]
 
 

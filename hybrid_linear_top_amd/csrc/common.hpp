@@ -111,25 +111,59 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float wave_max_across16(float v) {  // over lanes l, l^16, l^32, l^48
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+// ---- cross-lane helpers (DPP and gfx950 permlane swaps: VALU only, no LDS) --
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
-__device__ __forceinline__ float wave_sum_across16(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                                 __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+// The swaps return {v of this lane, v of lane^16 (or ^32)} in some order, so
+// a symmetric combine of the two halves gives the pairwise result.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// over lanes l, l^16, l^32, l^48 (the four lane groups of a 16x16 MFMA tile)
+__device__ __forceinline__ float wave_max_across16(float v) { return max_xor32(max_xor16(v)); }
+__device__ __forceinline__ float wave_sum_across16(float v) { return sum_xor32(sum_xor16(v)); }
+
+// over all 64 lanes
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+    return wave_max_across16(v);
+}
+__device__ __forceinline__ float wave_min(float v) { return -wave_max(-v); }
+
+// Inclusive prefix sum over the 64 lanes of a wave (row shifts, then row
+// broadcasts of lanes 15 and 31).
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
+    v += dpp_u32<0x111>(0u, v);  // row_shr:1
+    v += dpp_u32<0x112>(0u, v);  // row_shr:2
+    v += dpp_u32<0x114>(0u, v);  // row_shr:4
+    v += dpp_u32<0x118>(0u, v);  // row_shr:8
+    v += dpp_u32<0x142, 0xA>(0u, v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_u32<0x143, 0xC>(0u, v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 

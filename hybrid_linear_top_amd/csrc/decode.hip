@@ -44,6 +44,16 @@ template <> struct Chunk<float> {
     }
 };
 
+// Sum over aligned groups of N lanes (N = 4, 8 or 16), result in every lane.
+template <int N>
+__device__ __forceinline__ float row_sum(float p) {
+    p += dpp_f32<0xB1>(p);                      // lanes i^1
+    p += dpp_f32<0x4E>(p);                      // lanes i^2
+    if constexpr (N >= 8) p += dpp_f32<0x141>(p);   // other quad of the 8
+    if constexpr (N >= 16) p += dpp_f32<0x140>(p);  // other half of the row
+    return p;
+}
+
 template <typename T, int DI, int HIPAD>
 __device__ void score_group(const DecodeScoreArgs &a, int sb) {
     constexpr int EPC = 16 / Elt<T>::kBytes;  // elements per 16-byte chunk
@@ -102,8 +112,7 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb) {
                 float p = 0.0f;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) p = fmaf(qv[j][e], kf[e], p);
-#pragma unroll
-                for (int o = 1; o < CPR; o <<= 1) p += __shfl_xor(p, o);
+                p = row_sum<CPR>(p);
                 score = fmaf(wv[j], fmaxf(p, 0.0f), score);
             }
             const int tok = tb + it * RPI + rr;

@@ -7,23 +7,25 @@
 // of the full context (arxivdaily page, English abstract), the lower index
 // winning ties.  The n^2/2 scores never leave the chip:
 //
-//  * A work-group owns QB consecutive queries of one group; each wave owns 8.
-//    Key tiles of 64 keys are staged in LDS (double buffered, XOR-swizzled
-//    16-byte chunks) and scored with v_mfma_f32_16x16x32_bf16.  The A operand
-//    rows are (query, indexer head) pairs laid out so that the four
-//    accumulator rows a lane receives are the four heads of one query: the
-//    ReLU and the w-weighted head sum are lane-local.
+//  * A work-group is one wave that owns 8 consecutive queries of one group.
+//    It streams the group's keys (L2-resident: every XCD serves a single
+//    group) in tiles of 64, loading the MFMA B fragments straight from memory
+//    one tile ahead, and scores each tile with 16 v_mfma_f32_16x16x32_bf16
+//    issued back to back.  The A operand rows are (query, indexer head) pairs
+//    laid out so that the four accumulator rows a lane receives are the four
+//    heads of one query: the ReLU and the w-weighted head sum are lane-local.
 //  * Each query keeps a candidate buffer in LDS, always sorted by key index:
 //    candidates are appended in ascending key order (ballot + mbcnt give
-//    positions, no atomics) if their score beats the query's threshold tau.
-//  * When a buffer could overflow on the next tile, the wave selects the
-//    exact current top-M of it (radix select on order-preserving keys, ties
-//    to the lower index = earlier buffer position) and compacts it stably;
-//    tau becomes the M-th score.  Later keys have larger indices, so a later
-//    key must score strictly above tau to enter: equal scores lose, which is
-//    the lowest-index tie-break.
-//  * At the end the same select trims each buffer to min(M, t+1) entries,
-//    which are already in ascending index order, and writes them out.
+//    positions) when their score is strictly above the query's threshold tau.
+//  * When a buffer could overflow on the next tile it is trimmed: a one-pass
+//    256-bin histogram over the buffered scores finds the bin holding the
+//    M-th largest; the lower bins are dropped and tau becomes the largest
+//    dropped score, so at least M kept candidates beat everything rejected.
+//    When that frees too little (exact ties) the exact select below is used.
+//  * The exact select (radix select on order-preserving keys, ties to the
+//    lower index = earlier buffer position, stable compaction) trims each
+//    buffer to min(M, t+1) entries at the end; they are already in ascending
+//    index order and are written out.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,11 +34,6 @@ namespace {
 
 constexpr int kKT = 64;  // keys per tile
 constexpr int kQW = 8;   // queries per wave
-
-struct Cand {
-    float score;
-    int32_t s;
-};
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
     const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
@@ -47,27 +44,33 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Candidate buffers are two LDS arrays: fp32 scores and 16-bit key indices
+// (prefill n <= 32768).
+struct CandBuf {
+    float *sc;
+    uint16_t *key;
+};
+
 // Keep exactly the first m of the c buffered candidates in the order
 // (higher score, lower index); stable, so the buffer stays sorted by index.
 // Whole wave, uniform control flow.  Returns the order key of the m-th.
 template <int NE>
-__device__ uint32_t wave_select(Cand *buf, int c, int m, uint32_t *hist) {
+__device__ uint32_t wave_select(CandBuf buf, int c, int m, uint32_t *hist) {
     const int lane = threadIdx.x & 63;
     c = min(c, NE * 64);
     float sc[NE];
-    int32_t ss[NE];
+    uint32_t ss[NE];
     uint32_t u[NE];
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
         const int e = k * 64 + lane;
         if (e < c) {
-            const Cand x = buf[e];
-            sc[k] = x.score;
-            ss[k] = x.s;
-            u[k] = order_key(x.score);
+            sc[k] = buf.sc[e];
+            ss[k] = buf.key[e];
+            u[k] = order_key(sc[k]);
         } else {
             sc[k] = 0.0f;
-            ss[k] = 0;
+            ss[k] = 0u;
             u[k] = 0u;
         }
     }
@@ -121,42 +124,121 @@ __device__ uint32_t wave_select(Cand *buf, int c, int m, uint32_t *hist) {
         const uint64_t km = __ballot(keep);
         const uint32_t pos = base + mbcnt64(km);
         base += (uint32_t)__popcll(km);
-        if (keep && pos < (uint32_t)(NE * 64)) buf[pos] = Cand{sc[k], ss[k]};
+        if (keep && pos < (uint32_t)(NE * 64)) {
+            buf.sc[pos] = sc[k];
+            buf.key[pos] = (uint16_t)ss[k];
+        }
     }
     wave_lds_sync();
     return theta;
 }
 
-template <typename T, int DI, int HH, int W, int CAP>
+template <int NE>
+__device__ bool wave_trim(CandBuf buf, int &c_io, int M, int need_free, uint32_t *hist, float &tau) {
+    const int lane = threadIdx.x & 63;
+    const int c = min(c_io, NE * 64);
+    float sc[NE];
+    uint16_t ss[NE];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const int e = k * 64 + lane;
+        if (e < c) {
+            sc[k] = buf.sc[e];
+            ss[k] = buf.key[e];
+            mn = fminf(mn, sc[k]);
+            mx = fmaxf(mx, sc[k]);
+        } else {
+            sc[k] = 0.0f;
+            ss[k] = 0;
+        }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (!(mx > mn)) return false;
+    const float scale = 255.99f / (mx - mn);
+    *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+    wave_lds_sync();
+    int bin[NE];
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        bin[k] = -1;
+        if (k * 64 + lane < c) {
+            bin[k] = min(255, (int)((sc[k] - mn) * scale));
+            atomicAdd(&hist[bin[k]], 1u);
+        }
+    }
+    wave_lds_sync();
+    const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
+    const uint32_t lsum = h[0] + h[1] + h[2] + h[3];
+    const uint32_t incl = wave_inclusive_scan(lsum);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    uint32_t run = total - incl;
+    int fb = -1;
+    uint32_t kept = 0;
+#pragma unroll
+    for (int bb = 3; bb >= 0; --bb) {
+        const uint32_t hb = h[bb];
+        if (fb < 0 && run < (uint32_t)M && run + hb >= (uint32_t)M) {
+            fb = 4 * lane + bb;
+            kept = run + hb;
+        }
+        run += hb;
+    }
+    const uint64_t fm = __ballot(fb >= 0);
+    const int src = __ffsll((unsigned long long)fm) - 1;
+    fb = __builtin_amdgcn_readlane(fb, src);
+    kept = (uint32_t)__builtin_amdgcn_readlane((int)kept, src);
+    wave_lds_sync();
+    if (fb <= 0 || (int)kept > c - need_free) return false;
+    float dmax = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NE; ++k)
+        if (bin[k] >= 0 && bin[k] < fb) dmax = fmaxf(dmax, sc[k]);
+    dmax = wave_max(dmax);
+    uint32_t base = 0u;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const bool keep = bin[k] >= fb;
+        const uint64_t km = __ballot(keep);
+        const uint32_t pos = base + mbcnt64(km);
+        base += (uint32_t)__popcll(km);
+        if (keep && pos < (uint32_t)(NE * 64)) {
+            buf.sc[pos] = sc[k];
+            buf.key[pos] = ss[k];
+        }
+    }
+    wave_lds_sync();
+    c_io = (int)base;
+    tau = dmax;
+    return true;
+}
+
+template <typename T, int DI, int HH, int CAP>
 struct IdxCfg {
-    static constexpr int EB = Elt<T>::kBytes;
-    static constexpr int EPC = 16 / EB;     // elements per 16-byte chunk
-    static constexpr int CPRK = DI / EPC;   // chunks per key row
-    static constexpr int SWM = (CPRK < 8 ? CPRK : 8) - 1;
     static constexpr int KD = DI / 32;      // MFMA K-steps
-    static constexpr int QB = W * kQW;      // queries per work-group
+    static constexpr int RB = 2 * HH;       // 16-row A blocks: 2 query quads x head halves
     static constexpr int NE = CAP / 64;
-    static constexpr int TILE_ELEMS = kKT * DI;
 };
 
-template <typename T, int DI, int HH, int W, int CAP>
-__global__ __launch_bounds__(W * 64) void indexer_topm_kernel(IndexerArgs a) {
-    using C = IdxCfg<T, DI, HH, W, CAP>;
-    __shared__ __attribute__((aligned(16))) Cand cand[C::QB * CAP];
-    __shared__ __attribute__((aligned(16))) T ktile[2 * C::TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[W * 256];
+template <typename T, int DI, int HH, int CAP>
+__global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
+    using C = IdxCfg<T, DI, HH, CAP>;
+    __shared__ __attribute__((aligned(16))) float cand_sc[kQW * CAP];
+    __shared__ __attribute__((aligned(16))) uint16_t cand_key[kQW * CAP];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+    auto qbuf_of = [&](int q) { return CandBuf{cand_sc + q * CAP, cand_key + q * CAP}; };
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int col = lane & 15, grp = lane >> 4;
     const int G = a.G, n = a.n, HI = a.HI, M = a.M;
-    const int nqb = (n + C::QB - 1) / C::QB;
+    const int nqb = (n + kQW - 1) / kQW;
     // Block order: group fastest (with G | 8 every XCD sees a single group's
-    // keys), heaviest (latest) query blocks first.
+    // keys), latest (heaviest) query blocks first.
     const int L = blockIdx.x;
     const int g = L % G, rest = L / G, b = rest % a.B, qblk = nqb - 1 - rest / a.B;
-    const int q0 = qblk * C::QB;
-    const int qw0 = q0 + wave * kQW;
-    const int t_hi = min(n, q0 + C::QB) - 1;  // last query of the block
+    const int qw0 = qblk * kQW;
+    const int t_hi = min(n, qw0 + kQW) - 1;  // last query of this wave
     const int ntiles = t_hi / kKT + 1;
 
     const T *qI = reinterpret_cast<const T *>(a.q_idx);
@@ -194,106 +276,108 @@ __global__ __launch_bounds__(W * 64) void indexer_topm_kernel(IndexerArgs a) {
     }
     int cnt[2] = {0, 0};
     float tau[2] = {-INFINITY, -INFINITY};
-    Cand *mybuf[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) mybuf[qb] = cand + (size_t)(wave * kQW + qb * 4 + grp) * CAP;
-    uint32_t *whist = hist + wave * 256;
 
-    // ---- cooperative key-tile loads -------------------------------------------
-    constexpr int CH_PER_T = kKT * C::CPRK / (W * 64) > 0 ? kKT * C::CPRK / (W * 64) : 1;
-    auto load_tile = [&](int kt, u32x4 *regs) {
+    // B fragments of one key tile: key 16*cb + col, dims 32*kc + 8*grp .. +7
+    auto load_b = [&](int kt, Frag<T> (&bf)[4][C::KD]) {
 #pragma unroll
-        for (int i = 0; i < CH_PER_T; ++i) {
-            const int q = i * W * 64 + threadIdx.x;
-            const int row = q / C::CPRK, cc = q % C::CPRK;
-            const int s = kt * kKT + row;
-            if (q < kKT * C::CPRK && s < n)
-                regs[i] = *reinterpret_cast<const u32x4 *>(kI + (size_t)s * krs + cc * C::EPC);
-            else
-                regs[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_tile = [&](int buf, const u32x4 *regs) {
-        u32x4 *dst = reinterpret_cast<u32x4 *>(ktile + buf * C::TILE_ELEMS);
+        for (int cb = 0; cb < 4; ++cb) {
+            const int s = kt * kKT + cb * 16 + col;
 #pragma unroll
-        for (int i = 0; i < CH_PER_T; ++i) {
-            const int q = i * W * 64 + threadIdx.x;
-            if (q < kKT * C::CPRK) {
-                const int row = q / C::CPRK, cc = q % C::CPRK;
-                dst[row * C::CPRK + (cc ^ (row & C::SWM))] = regs[i];
+            for (int kc = 0; kc < C::KD; ++kc) {
+                if (s < n) bf[cb][kc].load(kI + (size_t)s * krs + kc * 32 + grp * 8);
+                else bf[cb][kc].zero();
             }
         }
     };
 
-    u32x4 pre[CH_PER_T];
-    load_tile(0, pre);
-    store_tile(0, pre);
-    __syncthreads();
-
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const bool more = kt + 1 < ntiles;
-        if (more) load_tile(kt + 1, pre);
+    auto tile_step = [&](int kt, const Frag<T> (&bcur)[4][C::KD]) {
         const int k0 = kt * kKT;
-        if (qw0 + kQW - 1 >= k0 && qw0 < n) {  // this wave has a query that sees the tile
-            const u32x4 *tb = reinterpret_cast<const u32x4 *>(ktile + (kt & 1) * C::TILE_ELEMS);
+        // all MFMAs of the tile first
+        f32x4 acc[2][HH][4];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int hh = 0; hh < HH; ++hh)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    f32x4 x = {0, 0, 0, 0};
+#pragma unroll
+                    for (int kc = 0; kc < C::KD; ++kc) x = mma16(af[qb][hh][kc], bcur[cb][kc], x);
+                    acc[qb][hh][cb] = x;
+                }
+        // scores and threshold tests
+        float score[2][4];
+        uint64_t mask[2][4];
+        uint64_t any = 0;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                const int krow = cb * 16 + col;
-                Frag<T> bf[C::KD];
+                float sc = 0.0f;
 #pragma unroll
-                for (int kc = 0; kc < C::KD; ++kc) {
-                    const int c0 = (kc * 32 + grp * 8) / C::EPC;
-                    if constexpr (C::EB == 2) {
-                        bf[kc].v = tb[krow * C::CPRK + (c0 ^ (krow & C::SWM))];
-                    } else {
-                        const u32x4 x0 = tb[krow * C::CPRK + (c0 ^ (krow & C::SWM))];
-                        const u32x4 x1 = tb[krow * C::CPRK + ((c0 + 1) ^ (krow & C::SWM))];
-                        reinterpret_cast<Frag<float> &>(bf[kc]).lo = __builtin_bit_cast(f32x4, x0);
-                        reinterpret_cast<Frag<float> &>(bf[kc]).hi = __builtin_bit_cast(f32x4, x1);
-                    }
-                }
-                const int s = k0 + krow;
+                for (int hh = 0; hh < HH; ++hh)
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    float score = 0.0f;
-#pragma unroll
-                    for (int hh = 0; hh < HH; ++hh) {
-                        f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-                        for (int kc = 0; kc < C::KD; ++kc) acc = mma16(af[qb][hh][kc], bf[kc], acc);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) score = fmaf(wv[qb][hh][i], fmaxf(acc[i], 0.0f), score);
-                    }
-                    const bool ok = (s <= tq[qb]) && (tq[qb] < n) && (score > tau[qb]);
-                    const uint64_t mask = __ballot(ok);
-                    if (mask) {
-                        const uint64_t gm = mask & (0xFFFFull << (16 * grp));
-                        const int pos = cnt[qb] + (int)mbcnt64(gm);
-                        if (ok && pos < CAP) mybuf[qb][pos] = Cand{score, s};
-                        cnt[qb] += __popcll(gm);
-                    }
-                }
+                    for (int i = 0; i < 4; ++i)
+                        sc = fmaf(wv[qb][hh][i], fmaxf(acc[qb][hh][cb][i], 0.0f), sc);
+                score[qb][cb] = sc;
+                const int s = k0 + cb * 16 + col;
+                mask[qb][cb] = __ballot(s <= tq[qb] && tq[qb] < n && sc > tau[qb]);
+                any |= mask[qb][cb];
             }
-            // trim any buffer that could overflow on the next tile
-            wave_lds_sync();
+        if (!any) return;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const uint64_t full = __ballot(cnt[qb] > CAP - kKT);
+        for (int qb = 0; qb < 2; ++qb) {
+            const CandBuf qbuf = qbuf_of(qb * 4 + grp);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const uint64_t m = mask[qb][cb];
+                if (!m) continue;
+                const uint64_t gm = m & (0xFFFFull << (16 * grp));
+                const int pos = cnt[qb] + (int)mbcnt64(gm);
+                if (((gm >> lane) & 1ull) && pos < CAP) {
+                    qbuf.sc[pos] = score[qb][cb];
+                    qbuf.key[pos] = (uint16_t)(k0 + cb * 16 + col);
+                }
+                cnt[qb] += __popcll(gm);
+            }
+        }
+        // trim any buffer that could overflow on the next tile
+        wave_lds_sync();
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const uint64_t full = __ballot(cnt[qb] > CAP - kKT);
+            if (!full) continue;
 #pragma unroll 1
-                for (int gg = 0; gg < 4; ++gg) {
-                    if (!((full >> (16 * gg)) & 1ull)) continue;
-                    Cand *qbuf = cand + (size_t)(wave * kQW + qb * 4 + gg) * CAP;
-                    const int c = __builtin_amdgcn_readlane(cnt[qb], 16 * gg);
-                    const uint32_t th = wave_select<C::NE>(qbuf, c, M, whist);
-                    if (grp == gg) {
-                        cnt[qb] = M;
-                        tau[qb] = key_to_float(th);
-                    }
+            for (int gg = 0; gg < 4; ++gg) {
+                if (!((full >> (16 * gg)) & 1ull)) continue;
+                const CandBuf qbuf = qbuf_of(qb * 4 + gg);
+                int c = __builtin_amdgcn_readlane(cnt[qb], 16 * gg);
+                float th = -INFINITY;
+                if (!wave_trim<C::NE>(qbuf, c, M, CAP / 4, hist, th)) {
+                    th = key_to_float(wave_select<C::NE>(qbuf, c, M, hist));
+                    c = M;
+                }
+                if (grp == gg) {
+                    cnt[qb] = c;
+                    tau[qb] = th;
                 }
             }
         }
-        if (more) store_tile((kt + 1) & 1, pre);
-        __syncthreads();
+    };
+
+    // three fragment buffers rotate: tiles kt+1 and kt+2 load while kt computes
+    Frag<T> b0[4][C::KD], b1[4][C::KD], b2[4][C::KD];
+    load_b(0, b0);
+    if (1 < ntiles) load_b(1, b1);
+    for (int kt = 0; kt < ntiles; kt += 3) {
+        if (kt + 2 < ntiles) load_b(kt + 2, b2);
+        tile_step(kt, b0);
+        if (kt + 1 >= ntiles) break;
+        if (kt + 3 < ntiles) load_b(kt + 3, b0);
+        tile_step(kt + 1, b1);
+        if (kt + 2 >= ntiles) break;
+        if (kt + 4 < ntiles) load_b(kt + 4, b1);
+        tile_step(kt + 2, b2);
     }
 
     // ---- final trim and ordered write-out ---------------------------------------
@@ -303,37 +387,29 @@ __global__ __launch_bounds__(W * 64) void indexer_topm_kernel(IndexerArgs a) {
         for (int gg = 0; gg < 4; ++gg) {
             const int t = qw0 + qb * 4 + gg;
             if (t >= n) continue;
-            Cand *qbuf = cand + (size_t)(wave * kQW + qb * 4 + gg) * CAP;
+            const CandBuf qbuf = qbuf_of(qb * 4 + gg);
             const int c = __builtin_amdgcn_readlane(cnt[qb], 16 * gg);
             const int m = min(M, t + 1);
-            if (c > m) wave_select<C::NE>(qbuf, c, m, whist);
+            if (c > m) wave_select<C::NE>(qbuf, c, m, hist);
             int32_t *dst = a.idx + (((size_t)b * n + t) * G + g) * M;
-            for (int i = lane; i < M; i += 64) dst[i] = i < m ? qbuf[i].s : -1;
+            for (int i = lane; i < M; i += 64) dst[i] = i < m ? (int32_t)qbuf.key[i] : -1;
         }
     }
 }
 
-template <typename T, int DI, int HH, int W, int CAP>
+template <typename T, int DI, int HH, int CAP>
 hipError_t launch(const IndexerArgs &a, hipStream_t s) {
-    using C = IdxCfg<T, DI, HH, W, CAP>;
-    const int nqb = (a.n + C::QB - 1) / C::QB;
-    hipLaunchKernelGGL((indexer_topm_kernel<T, DI, HH, W, CAP>), dim3(a.B * a.G * nqb), dim3(W * 64),
-                       0, s, a);
+    const int nqb = (a.n + kQW - 1) / kQW;
+    hipLaunchKernelGGL((indexer_topm_kernel<T, DI, HH, CAP>), dim3(a.B * a.G * nqb), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
 template <typename T, int DI, int HH>
 hipError_t by_m(const IndexerArgs &a, hipStream_t s) {
-    // candidate buffers: QB * CAP * 8 bytes; key tiles 2 * 64 * DI * sizeof(T)
-    constexpr bool big_tile = (2 * kKT * DI * Elt<T>::kBytes) > 16384;
-    if (a.M <= 128) return launch<T, DI, HH, 4, 256>(a, s);
-    if constexpr (big_tile) {
-        if (a.M <= 256) return launch<T, DI, HH, 2, 512>(a, s);
-        return launch<T, DI, HH, 1, 1024>(a, s);
-    } else {
-        if (a.M <= 256) return launch<T, DI, HH, 4, 512>(a, s);
-        return launch<T, DI, HH, 2, 1024>(a, s);
-    }
+    // per-wave LDS: 8 candidate buffers of CAP 8-byte entries
+    if (a.M <= 128) return launch<T, DI, HH, 256>(a, s);
+    if (a.M <= 256) return launch<T, DI, HH, 512>(a, s);
+    return launch<T, DI, HH, 1024>(a, s);
 }
 
 template <typename T>
