@@ -31,6 +31,7 @@ lisa_status ok() {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxDecodeCtx = 65536;  // the select kernel keeps up to 64 keys per thread
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -196,6 +197,8 @@ lisa_status lisa_decode_workspace_bytes(const lisa_dims *dims, int32_t B, int32_
     if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (B < 0 || max_ctx < 1)
         return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0 and max_ctx=%d >= 1", B, max_ctx);
+    if (max_ctx > kMaxDecodeCtx)
+        return fail(LISA_ERR_UNSUPPORTED, "max_ctx=%d above the supported %d", max_ctx, kMaxDecodeCtx);
     *bytes = decode_ws(dims, B, max_ctx).total;
     return ok();
 }
@@ -299,6 +302,8 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
     if (st) return st;
     if (B < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
     if (max_ctx < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "max_ctx=%d must be >= 1", max_ctx);
+    if (max_ctx > kMaxDecodeCtx)
+        return fail(LISA_ERR_UNSUPPORTED, "max_ctx=%d above the supported %d", max_ctx, kMaxDecodeCtx);
     if (B == 0) return ok();
     if (!cu_ctx) return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is NULL");
     if (reinterpret_cast<uintptr_t>(cu_ctx) & 7u)

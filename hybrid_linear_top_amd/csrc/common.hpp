@@ -104,6 +104,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return xcd * per + (xcd < rem ? xcd : rem) + j;
 }
 
+// Number of set bits of a 64-lane mask in the lanes below this one.
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Make this wave's LDS writes visible to its own lanes before they read.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -155,6 +160,23 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 __device__ __forceinline__ float wave_min(float v) { return -wave_max(-v); }
 
+__device__ __forceinline__ uint32_t max_u32_xor16(uint32_t v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+__device__ __forceinline__ uint32_t max_u32_xor32(uint32_t v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v, v));
+    v = max(v, dpp_u32<0x4E>(v, v));
+    v = max(v, dpp_u32<0x141>(v, v));
+    v = max(v, dpp_u32<0x140>(v, v));
+    return max_u32_xor32(max_u32_xor16(v));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
 // Inclusive prefix sum over the 64 lanes of a wave (row shifts, then row
 // broadcasts of lanes 15 and 31).
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
@@ -167,23 +189,25 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
     return v;
 }
 
-// Exclusive prefix sum over a block of NT threads (NT multiple of 64).
-// `tmp` must hold NT/64 + 1 words; returns the exclusive prefix and the
-// block total in *total.  Contains __syncthreads().
+// Exclusive prefix sum over a block of NT threads (NT multiple of 64, at
+// most 64 waves).  `tmp` must hold NT/64 + 1 words; returns the exclusive
+// prefix and the block total in *total.  Contains __syncthreads().
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t *total) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t inc = wave_inclusive_scan(v);
+    const uint32_t inc = wave_inclusive_scan(v);
     if (lane == 63) tmp[wave] = inc;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t run = 0;
-        for (int w = 0; w < NT / 64; ++w) { uint32_t x = tmp[w]; tmp[w] = run; run += x; }
-        tmp[NT / 64] = run;
+    if (wave == 0) {
+        const uint32_t x = lane < NW ? tmp[lane] : 0u;
+        const uint32_t xs = wave_inclusive_scan(x);
+        if (lane < NW) tmp[lane] = xs - x;
+        if (lane == NW - 1) tmp[NW] = xs;
     }
     __syncthreads();
-    uint32_t res = tmp[wave] + inc - v;
-    *total = tmp[NT / 64];
+    const uint32_t res = tmp[wave] + inc - v;
+    *total = tmp[NW];
     __syncthreads();
     return res;
 }

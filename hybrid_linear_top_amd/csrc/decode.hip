@@ -186,16 +186,28 @@ __global__ __launch_bounds__(256) void decode_score_state_kernel(DecodeScoreArgs
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kSelThreads = 512;
-
-template <int NT>
-__global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores, const int64_t *cu,
-                                                           int G, int M, int max_ctx,
-                                                           int32_t *idx) {
+// Top-M select of one (sequence, group): NT threads, thread t holding the
+// order keys of positions t, t+NT, ... in registers (EPT of them).
+//  1. min / max key of the sequence;
+//  2. up to three 2048-bin histogram passes over the live key range (bins are
+//     (key - lo) >> shift, so they spread over the actual scores rather than
+//     the fixed top bits, which keeps LDS atomics uncontended), each narrowing
+//     to the bin that holds the M-th largest key; a pass stops early when that
+//     bin is taken whole;
+//  3. ordered compaction: per (round k, wave w) ballots give counts of keys
+//     above the threshold and equal to it; one block scan over the (k, w)
+//     grid, which is index order, gives every selected key its position, the
+//     lowest indices taking the ties.
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
+                                                                    const int64_t *cu, int G, int M,
+                                                                    int max_ctx, int32_t *idx) {
+    constexpr int BPT = (2048 + NT - 1) / NT;  // histogram bins per thread
     __shared__ uint32_t hist[2048];
-    __shared__ uint32_t tmp[NT / 64 + 1];
-    __shared__ uint32_t found[2];
-    const int tid = threadIdx.x;
+    __shared__ uint32_t wtmp[(NT / 64) + 1];
+    __shared__ uint32_t bases[2][2 * NT + 1];
+    __shared__ uint32_t found[3];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bg = blockIdx.x, b = bg / G;
     const int L = (int)max((int64_t)0, min((int64_t)max_ctx, cu[b + 1] - cu[b]));
     const float *sc = scores + (size_t)bg * max_ctx;
@@ -204,68 +216,145 @@ __global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores, 
         for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
         return;
     }
-    // Radix select of the M-th largest key, digits of 11, 11 and 10 bits.
-    uint32_t prefix = 0;
+    uint32_t keyreg[EPT];
+    // ---- 1. key range ----
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int s = k * NT + tid;
+        keyreg[k] = s < L ? order_key(sc[s]) : 0u;
+        if (s < L) {
+            kmin = min(kmin, keyreg[k]);
+            kmax = max(kmax, keyreg[k]);
+        }
+    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) { hist[wave] = kmin; hist[(NT / 64) + wave] = kmax; }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t a = 0xFFFFFFFFu, c = 0u;
+        for (int w = 0; w < (NT / 64); ++w) { a = min(a, hist[w]); c = max(c, hist[(NT / 64) + w]); }
+        found[0] = a;
+        found[1] = c;
+    }
+    __syncthreads();
+    // live range [lo, lo + 2^width): every key still in play
+    uint32_t lo = found[0];
+    const uint32_t span = found[1] - lo;
+    int width = span == 0 ? 0 : 32 - __builtin_clz(span);  // bits needed for key - lo
     uint32_t need = (uint32_t)M;
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
-    for (int p = 0; p < 3; ++p) {
-        const int sh = shifts[p], bits = widths[p], nb = 1 << bits;
-        for (int i = tid; i < nb; i += NT) hist[i] = 0;
+    uint32_t T = lo;          // selection threshold: keys >= T are candidates
+    uint32_t take_eq = 0;     // keys == T taken (lowest indices first) when exact
+    bool exact = false;
+    __syncthreads();
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = width > 11 ? width - 11 : 0;
+        for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
         __syncthreads();
-        for (int s = tid; s < L; s += NT) {
-            const uint32_t u = order_key(sc[s]);
-            if (p == 0 || (u >> (sh + bits)) == prefix) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1u);
+        const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int s = k * NT + tid;
+            const uint32_t u = keyreg[k];
+            if (s < L && u >= lo && (uint64_t)u < hi_excl) atomicAdd(&hist[(u - lo) >> shift], 1u);
         }
         __syncthreads();
-        // thread tid owns bins in descending order: top bins first
-        const int bpt = nb / NT;
-        uint32_t local = 0;
-        for (int e = 0; e < bpt; ++e) local += hist[nb - 1 - (tid * bpt + e)];
+        // thread t owns bins 2047-BPT*t downwards; unused bins are empty
+        uint32_t hb[BPT], hsum = 0;
+#pragma unroll
+        for (int e = 0; e < BPT; ++e) {
+            const int bi = 2047 - BPT * tid - e;
+            hb[e] = bi >= 0 ? hist[bi] : 0u;
+            hsum += hb[e];
+        }
         uint32_t tot;
-        uint32_t before = block_exclusive_scan<NT>(local, tmp, &tot);
-        if (before < need && before + local >= need) {
+        const uint32_t before = block_exclusive_scan<NT>(hsum, wtmp, &tot);
+        if (before < need && before + hsum >= need) {
             uint32_t run = before;
-            for (int e = 0; e < bpt; ++e) {
-                const int bin = nb - 1 - (tid * bpt + e);
-                const uint32_t c = hist[bin];
-                if (run + c >= need) {
-                    found[0] = (uint32_t)bin;
+#pragma unroll
+            for (int e = 0; e < BPT; ++e) {
+                if (run + hb[e] >= need) {
+                    found[0] = 2047 - BPT * tid - e;
                     found[1] = need - run;
+                    found[2] = hb[e];
                     break;
                 }
-                run += c;
+                run += hb[e];
             }
         }
         __syncthreads();
-        prefix = (prefix << bits) | found[0];
-        need = found[1];
+        const uint32_t bin = found[0], rem = found[1], cnt_bin = found[2];
         __syncthreads();
+        lo = lo + (bin << shift);
+        if (rem == cnt_bin) {   // the whole bin is taken: keys >= lo are exactly the top M
+            T = lo;
+            take_eq = 0;
+            exact = false;
+            break;
+        }
+        need = rem;
+        width = shift;
+        if (shift == 0) {       // bin is a single key value: keys > lo, plus `rem` ties
+            T = lo;
+            take_eq = rem;
+            exact = true;
+            break;
+        }
     }
-    const uint32_t theta = prefix;   // key of the M-th largest score
-    const uint32_t take_eq = need;   // how many keys equal to theta are taken
-    // Compaction in index order: each thread owns one contiguous span.
-    const int span = (L + NT - 1) / NT;
-    const int s0 = min(L, tid * span), s1 = min(L, s0 + span);
-    uint32_t ngt = 0, neq = 0;
-    for (int s = s0; s < s1; ++s) {
-        const uint32_t u = order_key(sc[s]);
-        ngt += u > theta;
-        neq += u == theta;
+    // ---- 3. ordered compaction ----
+    // gt: key > T (exact) or key >= T (whole-bin cut); eq: key == T (exact only)
+    constexpr int nr = EPT;
+#pragma unroll
+    for (int k = 0; k < nr; ++k) {
+        const int s = k * NT + tid;
+        const uint32_t u = keyreg[k];
+        const bool valid = s < L;
+        const bool gt = valid && (exact ? u > T : u >= T);
+        const bool eq = valid && exact && u == T;
+        const uint64_t gm = __ballot(gt), em = __ballot(eq);
+        if (lane == 0) {
+            bases[0][k * (NT / 64) + wave] = (uint32_t)__popcll(gm);
+            bases[1][k * (NT / 64) + wave] = (uint32_t)__popcll(em);
+        }
     }
-    uint32_t tot;
-    uint32_t gt_before = block_exclusive_scan<NT>(ngt, tmp, &tot);
-    uint32_t eq_before = block_exclusive_scan<NT>(neq, tmp, &tot);
-    for (int s = s0; s < s1; ++s) {
-        const uint32_t u = order_key(sc[s]);
-        if (u > theta) {
-            const uint32_t pos = gt_before + min(eq_before, take_eq);
+    __syncthreads();
+    constexpr int cells = nr * (NT / 64);  // two per thread
+    static_assert(cells <= 2 * NT, "compaction cells");
+    {
+        uint32_t tot;
+        const int c0 = 2 * tid;
+        const uint32_t g0 = c0 < cells ? bases[0][c0] : 0u, g1 = c0 + 1 < cells ? bases[0][c0 + 1] : 0u;
+        const uint32_t e0 = c0 < cells ? bases[1][c0] : 0u, e1 = c0 + 1 < cells ? bases[1][c0 + 1] : 0u;
+        const uint32_t gpre = block_exclusive_scan<NT>(g0 + g1, wtmp, &tot);
+        const uint32_t epre = block_exclusive_scan<NT>(e0 + e1, wtmp, &tot);
+        if (c0 < cells) {
+            bases[0][c0] = gpre;
+            bases[1][c0] = epre;
+        }
+        if (c0 + 1 < cells) {
+            bases[0][c0 + 1] = gpre + g0;
+            bases[1][c0 + 1] = epre + e0;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < nr; ++k) {
+        const int s = k * NT + tid;
+        const uint32_t u = keyreg[k];
+        const bool valid = s < L;
+        const bool gt = valid && (exact ? u > T : u >= T);
+        const bool eq = valid && exact && u == T;
+        const uint64_t gm = __ballot(gt), em = __ballot(eq);
+        const int cell = k * (NT / 64) + wave;
+        const uint32_t gb = bases[0][cell] + mbcnt64(gm);
+        const uint32_t eb = bases[1][cell] + mbcnt64(em);
+        if (gt) {
+            const uint32_t pos = gb + min(eb, take_eq);
             if (pos < (uint32_t)M) out[pos] = s;
-            ++gt_before;
-        } else if (u == theta) {
-            const uint32_t pos = gt_before + eq_before;
-            if (eq_before < take_eq && pos < (uint32_t)M) out[pos] = s;
-            ++eq_before;
+        } else if (eq && eb < take_eq) {
+            const uint32_t pos = gb + eb;
+            if (pos < (uint32_t)M) out[pos] = s;
         }
     }
 }
@@ -298,9 +387,18 @@ hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d,
 
 hipError_t launch_decode_select(const float *scores, const int64_t *cu, int B, int G, int M,
                                 int max_ctx, int32_t *idx, hipStream_t s) {
-    hipLaunchKernelGGL((decode_select_kernel<kSelThreads>), dim3(B * G), dim3(kSelThreads), 0, s,
-                       scores, cu, G, M, max_ctx, idx);
-    return hipGetLastError();
+    const dim3 grid(B * G);
+#define LISA_SEL(NT_, E)                                                                          \
+    if (max_ctx <= (E) * (NT_)) {                                                                 \
+        hipLaunchKernelGGL((decode_select_kernel<NT_, E>), grid, dim3(NT_), 0, s, scores, cu, G, M, \
+                           max_ctx, idx);                                                         \
+        return hipGetLastError();                                                                 \
+    }
+    // keys per thread stay in registers: 1024 threads (128 VGPRs) for short
+    // contexts, 768 threads (170 VGPRs) for longer ones
+    LISA_SEL(1024, 8) LISA_SEL(1024, 17) LISA_SEL(768, 43) LISA_SEL(768, 86)
+#undef LISA_SEL
+    return hipErrorInvalidValue;  // longer contexts are rejected by the API layer
 }
 
 }  // namespace lisa

@@ -13,9 +13,12 @@
 //                                   taken straight from the S^T accumulators)
 //
 // The r heads are padded to the 16 columns of a 16x16x32 MFMA tile.  The M
-// selected slots are split over the 4 waves of the work-group (32 slots per
-// step); the waves' partial (max, sum, O) are merged in LDS, then the gate
+// selected slots are split over the NW waves of the work-group (32 slots per
+// step; prefill uses 4 waves per unit, decode up to 16 since it has few
+// units); the waves' partial (max, sum, O) are merged in LDS, then the gate
 // gamma = sigmoid(z) mixes o_sparse with o_lin and the result is stored.
+// Each step issues the gathered K fragment loads and the V row loads
+// together, so both gathers are in flight before the first MFMA.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,17 +27,22 @@ namespace {
 
 constexpr int kChunk = 32;  // selected slots per wave step
 
-template <typename T, int D>
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 f32x2_lo(f32x4 v) { return f32x2{v[0], v[1]}; }
+__device__ __forceinline__ f32x2 f32x2_hi(f32x4 v) { return f32x2{v[2], v[3]}; }
+
+template <typename T, int D, int NW>
 struct SparseSmem {
     static constexpr int kVStride = D + 8 / Elt<T>::kBytes;  // row pad: 8 bytes
-    static constexpr int kVBytes = 4 * kChunk * kVStride * Elt<T>::kBytes;
-    static constexpr int kMergeBytes = 4 * (D * 16 + 32) * 4;
+    static constexpr int kVBytes = NW * kChunk * kVStride * Elt<T>::kBytes;
+    static constexpr int kMergeStride = 32 + 16 * (D + 1);  // max[16] sum[16] O[head][D+1]
+    static constexpr int kMergeBytes = NW * kMergeStride * 4;
     static constexpr int kBytes = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
 };
 
-template <typename T, int D, bool DECODE>
-__global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
-    using S = SparseSmem<T, D>;
+template <typename T, int D, bool DECODE, int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
+    using S = SparseSmem<T, D, NW>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
     constexpr int VS = S::kVStride;
     constexpr int KC = D / 32;  // K-steps of 32 over the head dim
@@ -49,7 +57,8 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
     const int u = DECODE ? lu : (lu % (a.B * a.n)) * G + lu / (a.B * a.n);
 
     const T *qrows, *kbase, *vbase;
-    int smax;  // largest valid key position of the unit (defensive bound on gathered rows)
+    int smax;    // largest valid key position of the unit (defensive bound on gathered rows)
+    int nvalid;  // selected slots of the unit: min(M, visible tokens); the rest are -1
     const void *linp;
     const T *zp;
     T *outp;
@@ -59,6 +68,7 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
             const int b = u / G, g = u % G;
             const int64_t row0 = a.cu[b];
             smax = (int)min((int64_t)a.max_ctx, a.cu[b + 1] - row0) - 1;
+            nvalid = min(M, smax + 1);
             qrows = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.Hq + g * r) * D;
             kbase = reinterpret_cast<const T *>(a.k) + ((size_t)row0 * G + g) * D;
             vbase = reinterpret_cast<const T *>(a.v) + ((size_t)row0 * G + g) * D;
@@ -68,6 +78,7 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
         } else {
             const int g = u % G, bt = u / G, b = bt / a.n;
             smax = bt % a.n;
+            nvalid = min(M, smax + 1);
             qrows = reinterpret_cast<const T *>(a.q) + ((size_t)bt * a.Hq + g * r) * D;
             kbase = reinterpret_cast<const T *>(a.k) + ((size_t)b * a.n * G + g) * D;
             vbase = reinterpret_cast<const T *>(a.v) + ((size_t)b * a.n * G + g) * D;
@@ -94,35 +105,47 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     T *vs = reinterpret_cast<T *>(smem) + (size_t)wave * kChunk * VS;
-    const int per_wave = ((M + 3) / 4 + kChunk - 1) / kChunk * kChunk;
+    const int per_wave = ((M + NW - 1) / NW + kChunk - 1) / kChunk * kChunk;
     const int s_begin = wave * per_wave, s_end = min(M, s_begin + per_wave);
-    for (int cs = s_begin; cs < s_end; cs += kChunk) {
-        if (idxp[cs] < 0) break;  // sets are ascending with -1 padding at the end
+    const int s_stop = min(s_end, nvalid);
+    for (int cs = s_begin; cs < s_stop; cs += kChunk) {
+        // --- issue both gathers: lane (grp, col) fetches, for key block kb,
+        // 16-byte pieces kc*32 + grp*8 of the K row and of the V row of slot
+        // cs + 16*kb + col -- the K pieces are MFMA A fragments as loaded ----
+        Frag<T> kf[2][KC], vf8[2][KC];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int slot = cs + kb * 16 + col;
+            int s = slot < s_stop ? idxp[slot] : -1;
+            if (s > smax) s = -1;
+            const size_t roff = (size_t)(s < 0 ? 0 : s) * rstride;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                if (s >= 0) {
+                    kf[kb][kc].load(kbase + roff + kc * 32 + grp * 8);
+                    vf8[kb][kc].load(vbase + roff + kc * 32 + grp * 8);
+                } else {
+                    kf[kb][kc].zero();
+                    vf8[kb][kc].zero();
+                }
+            }
+        }
         // --- logits S^T for two 16-slot key blocks --------------------------
         f32x4 acc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int slot = cs + kb * 16 + col;
-            int s = slot < s_end ? idxp[slot] : -1;
-            if (s > smax) s = -1;
             acc[kb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                Frag<T> kf;
-                if (s >= 0) kf.load(kbase + (size_t)s * rstride + kc * 32 + grp * 8);
-                else kf.zero();
-                acc[kb] = mma16(kf, qf[kc], acc[kb]);
-            }
+            for (int kc = 0; kc < KC; ++kc) acc[kb] = mma16(kf[kb][kc], qf[kc], acc[kb]);
         }
-        // rows of acc[kb] are slots cs + 16*kb + 4*grp + i
+        // rows of acc[kb] are slots cs + 16*kb + 4*grp + i; slots >= s_stop are padding
         float x[8];
         float cmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int slot = cs + kb * 16 + grp * 4 + i;
-                const bool ok = slot < s_end && idxp[slot] >= 0 && idxp[slot] <= smax;
+                const bool ok = cs + kb * 16 + grp * 4 + i < s_stop;
                 const float v = ok ? acc[kb][i] * a.scale_log2 : -INFINITY;
                 x[kb * 4 + i] = v;
                 cmax = fmaxf(cmax, v);
@@ -150,19 +173,25 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
 
-        // --- stage the 32 V rows in LDS (row-major, padded) -----------------
-        constexpr int CPRV = D * Elt<T>::kBytes / 8;  // 8-byte pieces per row
-        constexpr int PIECES = kChunk * CPRV;
-        for (int pc = lane; pc < PIECES; pc += 64) {
-            const int row = pc / CPRV, cc = pc % CPRV;
-            const int slot = cs + row;
-            int s = slot < s_end ? idxp[slot] : -1;
-            if (s > smax) s = -1;
-            u32x2 val = {0u, 0u};
-            if (s >= 0)
-                val = *reinterpret_cast<const u32x2 *>(
-                    reinterpret_cast<const unsigned char *>(vbase + (size_t)s * rstride) + cc * 8);
-            *reinterpret_cast<u32x2 *>(reinterpret_cast<unsigned char *>(vs + row * VS) + cc * 8) = val;
+        // --- stage the 32 V rows in LDS (row-major, rows padded by 8 bytes) --
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            unsigned char *row = reinterpret_cast<unsigned char *>(vs + (kb * 16 + col) * VS);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                unsigned char *dst = row + (kc * 32 + grp * 8) * Elt<T>::kBytes;
+                if constexpr (Elt<T>::kBytes == 2) {
+                    const u32x4 raw = reinterpret_cast<const Frag<uint16_t> &>(vf8[kb][kc]).v;
+                    reinterpret_cast<u32x2 *>(dst)[0] = u32x2{raw[0], raw[1]};
+                    reinterpret_cast<u32x2 *>(dst)[1] = u32x2{raw[2], raw[3]};
+                } else {
+                    const Frag<float> &ff = reinterpret_cast<const Frag<float> &>(vf8[kb][kc]);
+                    reinterpret_cast<u32x2 *>(dst)[0] = __builtin_bit_cast(u32x2, f32x2_lo(ff.lo));
+                    reinterpret_cast<u32x2 *>(dst)[1] = __builtin_bit_cast(u32x2, f32x2_hi(ff.lo));
+                    reinterpret_cast<u32x2 *>(dst)[2] = __builtin_bit_cast(u32x2, f32x2_lo(ff.hi));
+                    reinterpret_cast<u32x2 *>(dst)[3] = __builtin_bit_cast(u32x2, f32x2_hi(ff.hi));
+                }
+            }
         }
         wave_lds_sync();
         // --- O^T += V^T P^T --------------------------------------------------
@@ -187,7 +216,8 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
     // --- merge the 4 waves -------------------------------------------------
     __syncthreads();
     float *mrg = reinterpret_cast<float *>(smem);
-    float *wm = mrg + wave * (D * 16 + 32);  // [0..15] max, [16..31] sum, then O^T[D][16]
+    constexpr int MS = S::kMergeStride;
+    float *wm = mrg + wave * MS;  // [0..15] max, [16..31] sum, then O[head][D+1]
     if (grp == 0) {
         wm[col] = m_run;
         wm[16 + col] = l_run;
@@ -195,21 +225,21 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wm[32 + (mb * 16 + grp * 4 + i) * 16 + col] = o[mb][i];
+        for (int i = 0; i < 4; ++i) wm[32 + col * (D + 1) + mb * 16 + grp * 4 + i] = o[mb][i];
     __syncthreads();
-    for (int e = threadIdx.x; e < r * D; e += 256) {
+    for (int e = threadIdx.x; e < r * D; e += NW * 64) {
         const int hh = e / D, dim = e % D;
         float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mrg[w * (D * 16 + 32) + hh]);
+        for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mrg[w * MS + hh]);
         float num = 0.0f, den = 0.0f;
         if (mx != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float *ww = mrg + w * (D * 16 + 32);
+            for (int w = 0; w < NW; ++w) {
+                const float *ww = mrg + w * MS;
                 const float sc = __builtin_amdgcn_exp2f(ww[hh] - mx);
                 den += ww[16 + hh] * sc;
-                num += ww[32 + dim * 16 + hh] * sc;
+                num += ww[32 + hh * (D + 1) + dim] * sc;
             }
         }
         const float osp = den > 0.0f ? num / den : 0.0f;
@@ -222,18 +252,28 @@ __global__ __launch_bounds__(256) void sparse_gate_kernel(SparseArgs a) {
     }
 }
 
+template <typename T, int D>
+hipError_t dispatch_d(const SparseArgs &a, bool decode, hipStream_t s) {
+    const dim3 grid(a.units);
+    if (!decode) {
+        hipLaunchKernelGGL((sparse_gate_kernel<T, D, false, 4>), grid, dim3(256), 0, s, a);
+    } else if (a.M <= 4 * kChunk) {
+        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 4>), grid, dim3(256), 0, s, a);
+    } else if (a.M <= 8 * kChunk) {
+        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
+    } else if constexpr (sizeof(T) == 4 && D == 128) {  // 16 waves of fp32 rows exceed the LDS
+        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 16>), grid, dim3(1024), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t dispatch(const SparseArgs &a, int d, bool decode, hipStream_t s) {
     if (a.units == 0) return hipSuccess;
-    dim3 grid(a.units), block(256);
-#define LISA_SP(D_)                                                                              \
-    if (d == D_) {                                                                               \
-        if (decode) hipLaunchKernelGGL((sparse_gate_kernel<T, D_, true>), grid, block, 0, s, a);  \
-        else hipLaunchKernelGGL((sparse_gate_kernel<T, D_, false>), grid, block, 0, s, a);        \
-        return hipGetLastError();                                                                \
-    }
-    LISA_SP(64) LISA_SP(128)
-#undef LISA_SP
+    if (d == 128) return dispatch_d<T, 128>(a, decode, s);
+    if (d == 64) return dispatch_d<T, 64>(a, decode, s);
     return hipErrorInvalidValue;
 }
 

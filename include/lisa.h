@@ -49,7 +49,7 @@
  * Supported shapes: head_dim in {64, 128}; idx_dim in {32, 64};
  * 1 <= idx_heads <= 8; num_q_heads % num_kv_heads == 0 with r <= 16;
  * chunk in {0, 64} (0 means 64); prefill: 1 <= top_m <= 512, n <= 32768;
- * decode: 1 <= top_m <= 2048.
+ * decode: 1 <= top_m <= 2048, max_ctx <= 65536.
  */
 #ifndef LISA_H
 #define LISA_H

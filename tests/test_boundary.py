@@ -118,6 +118,7 @@ def test_decode_argument_errors():
     d = _dims()
     assert _decode(d, cu=FAKE + 4) == lisa.LISA_ERR_INVALID_ARGUMENT
     assert _decode(d, max_ctx=0) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _decode(d, max_ctx=65537) == lisa.LISA_ERR_UNSUPPORTED
     assert _decode(d, B=-1) == lisa.LISA_ERR_INVALID_ARGUMENT
     assert _decode(d, B=0, q=0) == lisa.LISA_OK
     need = lisa.lisa_decode_workspace_bytes(d, 2, 100)

@@ -111,6 +111,7 @@ DECODE_SMALL = [
     _dcfg(28, 4, 128, 4, 64, 512, [4097, 700, 513, 20000], seed=2),
     _dcfg(8, 2, 64, 8, 64, 100, [999, 1001, 5000], dtype="f32", seed=3),
     _dcfg(16, 1, 128, 6, 64, 2048, [3000, 2048, 2049], seed=4),
+    _dcfg(4, 1, 64, 4, 32, 256, [40000, 3, 33100], seed=5),   # longest-context select variant
 ]
 
 
