@@ -104,6 +104,34 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return xcd * per + (xcd < rem ? xcd : rem) + j;
 }
 
+// Raw buffer access: a wave-uniform descriptor over [base, base + bytes).
+// Loads whose byte offset falls outside return zeros, so tails and invalid
+// rows need no branch; offsets are 32-bit VGPR values.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// The base and size must be wave-uniform; readfirstlane makes that explicit so
+// the descriptor lives in SGPRs (otherwise each load becomes a waterfall loop).
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000 /* gfx9-family raw buffer word 3 */);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0u, 0));
+}
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset beyond every descriptor used here
+
+// Fill a 16x16x32 fragment from a buffer: 8 consecutive elements at byte offset voff.
+__device__ __forceinline__ void frag_buf_load(Frag<uint16_t> &f, rsrc_t r, uint32_t voff) {
+    f.v = buf_load16(r, voff);
+}
+__device__ __forceinline__ void frag_buf_load(Frag<float> &f, rsrc_t r, uint32_t voff) {
+    f.lo = __builtin_bit_cast(f32x4, buf_load16(r, voff));
+    f.hi = __builtin_bit_cast(f32x4, buf_load16(r, voff + 16u));
+}
+
 // Number of set bits of a 64-lane mask in the lanes below this one.
 __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

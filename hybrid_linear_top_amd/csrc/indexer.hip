@@ -26,6 +26,8 @@
 //    lower index = earlier buffer position, stable compaction) trims each
 //    buffer to min(M, t+1) entries at the end; they are already in ascending
 //    index order and are written out.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,7 +35,9 @@ namespace lisa {
 namespace {
 
 constexpr int kKT = 64;  // keys per tile
-constexpr int kQW = 8;   // queries per wave
+#ifndef LISA_IDX_QB
+#define LISA_IDX_QB 2  // query quads per wave (4 queries each)
+#endif
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
     const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
@@ -211,16 +215,17 @@ __device__ bool wave_trim(CandBuf buf, int &c_io, int M, int need_free, uint32_t
     return true;
 }
 
-template <typename T, int DI, int HH, int CAP>
+template <typename T, int DI, int HH, int CAP, int QB>
 struct IdxCfg {
     static constexpr int KD = DI / 32;      // MFMA K-steps
-    static constexpr int RB = 2 * HH;       // 16-row A blocks: 2 query quads x head halves
+    static constexpr int QW = 4 * QB;       // queries per wave: QB quads of 4
     static constexpr int NE = CAP / 64;
 };
 
-template <typename T, int DI, int HH, int CAP>
+template <typename T, int DI, int HH, int CAP, int QB>
 __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
-    using C = IdxCfg<T, DI, HH, CAP>;
+    using C = IdxCfg<T, DI, HH, CAP, QB>;
+    constexpr int kQW = C::QW;
     __shared__ __attribute__((aligned(16))) float cand_sc[kQW * CAP];
     __shared__ __attribute__((aligned(16))) uint16_t cand_key[kQW * CAP];
     __shared__ __attribute__((aligned(16))) uint32_t hist[256];
@@ -244,11 +249,11 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     const size_t krs = (size_t)G * DI;  // key row stride
 
     // ---- per-lane constants: A fragments, head weights, query rows -----------
-    Frag<T> af[2][HH][C::KD];
-    float wv[2][HH][4];
-    int tq[2];
+    Frag<T> af[QB][HH][C::KD];
+    float wv[QB][HH][4];
+    int tq[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         tq[qb] = qw0 + qb * 4 + grp;  // the query whose four heads this lane accumulates
         const int tA = qw0 + qb * 4 + col / 4;  // the query of this lane's A row
 #pragma unroll
@@ -271,28 +276,43 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
             }
         }
     }
-    int cnt[2] = {0, 0};
-    float tau[2] = {-INFINITY, -INFINITY};
+    int cnt[QB];
+    float tau[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        cnt[qb] = 0;
+        tau[qb] = tq[qb] < n ? -INFINITY : INFINITY;  // queries past n accept nothing
+    }
 
-    // B fragments of one key tile: key 16*cb + col, dims 32*kc + 8*grp .. +7
+    // B fragments of one key tile: key 16*cb + col, dims 32*kc + 8*grp .. +7,
+    // through a per-tile buffer descriptor (keys >= n read as zeros)
+    constexpr uint32_t EB = Elt<T>::kBytes;
+    const uint32_t key_bytes = (uint32_t)n * (uint32_t)krs * EB;
+    uint32_t voff[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) voff[cb] = ((uint32_t)(cb * 16 + col) * (uint32_t)krs + grp * 8) * EB;
     auto load_b = [&](int kt, Frag<T> (&bf)[4][C::KD]) {
+        const uint32_t tile_off = (uint32_t)kt * kKT * (uint32_t)krs * EB;
+        const rsrc_t r = make_rsrc(reinterpret_cast<const unsigned char *>(kI) + tile_off,
+                                   key_bytes > tile_off ? key_bytes - tile_off : 0u);
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const int s = kt * kKT + cb * 16 + col;
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int kc = 0; kc < C::KD; ++kc) {
-                if (s < n) bf[cb][kc].load(kI + (size_t)s * krs + kc * 32 + grp * 8);
-                else bf[cb][kc].zero();
-            }
-        }
+            for (int kc = 0; kc < C::KD; ++kc) frag_buf_load(bf[cb][kc], r, voff[cb] + kc * 32 * EB);
     };
 
-    auto tile_step = [&](int kt, const Frag<T> (&bcur)[4][C::KD]) {
+    // bits of this lane's query key mask that precede its own key 16*cb + col
+    uint64_t below[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) below[cb] = (1ull << (16 * cb + col)) - 1ull;
+
+    auto tile_step = [&](int kt, const Frag<T> (&bcur)[4][C::KD], auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;  // tile reaches past the first query
         const int k0 = kt * kKT;
         // all MFMAs of the tile first
-        f32x4 acc[2][HH][4];
+        f32x4 acc[QB][HH][4];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int hh = 0; hh < HH; ++hh)
 #pragma unroll
@@ -303,11 +323,12 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                     acc[qb][hh][cb] = x;
                 }
         // scores and threshold tests
-        float score[2][4];
-        uint64_t mask[2][4];
+        float score[QB][4];
+        bool ok[QB][4];
+        uint64_t mask[QB][4];
         uint64_t any = 0;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
                 float sc = 0.0f;
@@ -317,33 +338,44 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                     for (int i = 0; i < 4; ++i)
                         sc = fmaf(wv[qb][hh][i], fmaxf(acc[qb][hh][cb][i], 0.0f), sc);
                 score[qb][cb] = sc;
-                const int s = k0 + cb * 16 + col;
-                mask[qb][cb] = __ballot(s <= tq[qb] && tq[qb] < n && sc > tau[qb]);
+                if constexpr (DIAG) ok[qb][cb] = (k0 + cb * 16 + col <= tq[qb]) && sc > tau[qb];
+                else ok[qb][cb] = sc > tau[qb];
+                mask[qb][cb] = __ballot(ok[qb][cb]);
                 any |= mask[qb][cb];
             }
         if (!any) return;
+        // Append in ascending key order.  Per query the four 16-bit ballot
+        // fields form a 64-bit key mask (bit 16*cb + col); a candidate's
+        // position is the number of accepted keys of its query below it.
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
+            if (!(mask[qb][0] | mask[qb][1] | mask[qb][2] | mask[qb][3])) continue;
+            uint64_t K[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint64_t k = 0;
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) k |= ((mask[qb][cb] >> (16 * g)) & 0xFFFFull) << (16 * cb);
+                K[g] = k;
+            }
+            const uint64_t Kl = grp == 0 ? K[0] : grp == 1 ? K[1] : grp == 2 ? K[2] : K[3];
             const CandBuf qbuf = qbuf_of(qb * 4 + grp);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                const uint64_t m = mask[qb][cb];
-                if (!m) continue;
-                const uint64_t gm = m & (0xFFFFull << (16 * grp));
-                const int pos = cnt[qb] + (int)mbcnt64(gm);
-                if (((gm >> lane) & 1ull) && pos < CAP) {
+                if (ok[qb][cb]) {
+                    const int pos = cnt[qb] + __popcll(Kl & below[cb]);
                     qbuf.sc[pos] = score[qb][cb];
                     qbuf.key[pos] = (uint16_t)(k0 + cb * 16 + col);
                 }
-                cnt[qb] += __popcll(gm);
             }
+            cnt[qb] += __popcll(Kl);
         }
         // trim any buffer that could overflow on the next tile
-        wave_lds_sync();
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             const uint64_t full = __ballot(cnt[qb] > CAP - kKT);
             if (!full) continue;
+            wave_lds_sync();
 #pragma unroll 1
             for (int gg = 0; gg < 4; ++gg) {
                 if (!((full >> (16 * gg)) & 1ull)) continue;
@@ -366,20 +398,26 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     Frag<T> b0[4][C::KD], b1[4][C::KD], b2[4][C::KD];
     load_b(0, b0);
     if (1 < ntiles) load_b(1, b1);
+    // tiles below kd hold only keys < qw0 <= every query of the wave
+    const int kd = qw0 / kKT;
+    auto step = [&](int kt, const Frag<T> (&bc)[4][C::KD]) {
+        if (kt >= kd) tile_step(kt, bc, std::true_type{});
+        else tile_step(kt, bc, std::false_type{});
+    };
     for (int kt = 0; kt < ntiles; kt += 3) {
         if (kt + 2 < ntiles) load_b(kt + 2, b2);
-        tile_step(kt, b0);
+        step(kt, b0);
         if (kt + 1 >= ntiles) break;
         if (kt + 3 < ntiles) load_b(kt + 3, b0);
-        tile_step(kt + 1, b1);
+        step(kt + 1, b1);
         if (kt + 2 >= ntiles) break;
         if (kt + 4 < ntiles) load_b(kt + 4, b1);
-        tile_step(kt + 2, b2);
+        step(kt + 2, b2);
     }
 
     // ---- final trim and ordered write-out ---------------------------------------
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll 1
         for (int gg = 0; gg < 4; ++gg) {
             const int t = qw0 + qb * 4 + gg;
@@ -396,8 +434,10 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 
 template <typename T, int DI, int HH, int CAP>
 hipError_t launch(const IndexerArgs &a, hipStream_t s) {
-    const int nqb = (a.n + kQW - 1) / kQW;
-    hipLaunchKernelGGL((indexer_topm_kernel<T, DI, HH, CAP>), dim3(a.B * a.G * nqb), dim3(64), 0, s, a);
+    constexpr int QB = LISA_IDX_QB;
+    constexpr int QW = 4 * QB;
+    const int nqb = (a.n + QW - 1) / QW;
+    hipLaunchKernelGGL((indexer_topm_kernel<T, DI, HH, CAP, QB>), dim3(a.B * a.G * nqb), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -108,6 +108,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
     const int per_wave = ((M + NW - 1) / NW + kChunk - 1) / kChunk * kChunk;
     const int s_begin = wave * per_wave, s_end = min(M, s_begin + per_wave);
     const int s_stop = min(s_end, nvalid);
+    // buffer descriptors over the unit's visible K and V rows: slots that are
+    // padding or out of range read as zeros without a branch
+    constexpr uint32_t EB = Elt<T>::kBytes;
+    const uint32_t row_bytes = (uint32_t)rstride * EB;
+    const uint32_t vis_bytes = (uint32_t)(smax + 1) * row_bytes;
+    const rsrc_t krs = make_rsrc(kbase, vis_bytes), vrs = make_rsrc(vbase, vis_bytes);
     for (int cs = s_begin; cs < s_stop; cs += kChunk) {
         // --- issue both gathers: lane (grp, col) fetches, for key block kb,
         // 16-byte pieces kc*32 + grp*8 of the K row and of the V row of slot
@@ -116,18 +122,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int slot = cs + kb * 16 + col;
-            int s = slot < s_stop ? idxp[slot] : -1;
-            if (s > smax) s = -1;
-            const size_t roff = (size_t)(s < 0 ? 0 : s) * rstride;
+            const int s = slot < s_stop ? idxp[slot] : -1;
+            const uint32_t roff = (s >= 0 && s <= smax) ? (uint32_t)s * row_bytes + grp * 8 * EB
+                                                        : kOffNone;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                if (s >= 0) {
-                    kf[kb][kc].load(kbase + roff + kc * 32 + grp * 8);
-                    vf8[kb][kc].load(vbase + roff + kc * 32 + grp * 8);
-                } else {
-                    kf[kb][kc].zero();
-                    vf8[kb][kc].zero();
-                }
+                frag_buf_load(kf[kb][kc], krs, roff + kc * 32 * EB);
+                frag_buf_load(vf8[kb][kc], vrs, roff + kc * 32 * EB);
             }
         }
         // --- logits S^T for two 16-slot key blocks --------------------------
