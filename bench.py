@@ -78,6 +78,20 @@ def decode_bytes(cfg, lengths):
     }
 
 
+# stage name (as lisa_stage_timing reports it) -> (rocprofv3 kernel-name
+# pattern, the sources that kernel is built from)
+STAGE_KERNELS = {
+    "indexer_topm": (r"indexer_topm_kernel<", ["indexer.hip", "common.hpp", "kernels.hpp"]),
+    "sparse_gate_prefill": (r"sparse_gate_kernel<[^>]*, false,", ["sparse.hip", "common.hpp", "kernels.hpp"]),
+    "sparse_gate_decode": (r"sparse_gate_kernel<[^>]*, true,", ["sparse.hip", "common.hpp", "kernels.hpp"]),
+    "linear_chunk_state": (r"chunk_state_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
+    "linear_prefix_scan": (r"prefix_scan_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
+    "linear_chunk_output": (r"chunk_output_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
+    "decode_score_state": (r"decode_score_state_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
+    "decode_select": (r"decode_select_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
+}
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for nm in names:
@@ -86,18 +100,67 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key, src_files):
+def traffic_from_profiles(stage):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when absent or when the kernel source changed since it was taken."""
+    None when absent or when the kernel's sources changed since it was taken."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get(kernel_key)
-    if not ent or ent.get("source_hash") != source_hash(*src_files):
+    ent = data.get("kernels", {}).get(stage)
+    if not ent or ent.get("source_hash") != source_hash(*STAGE_KERNELS[stage][1]):
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def traffic_summary(fetch_db, write_db, out_json, out_md, command):
+    """Turn two rocprofv3 --pmc databases (FETCH_SIZE and WRITE_SIZE, KiB per
+    dispatch) into HBM bytes per launch.  Each counter is scaled by what it
+    reads for the 1 GiB device copy that --copy-calibration runs first (the
+    copy reads and writes 2^30 bytes)."""
+    import re
+    import sqlite3
+
+    def per_kernel(db, counter):
+        cur = sqlite3.connect(db).cursor()
+        rows = list(cur.execute("select kernel_name, value from counters_collection "
+                                "where counter_name = ?", (counter,)))
+        cal = [v for nm, v in rows if "copyBuffer" in nm and v > 1e5]
+        if not cal:
+            raise SystemExit(f"{db}: no calibration copy found (run bench.py --copy-calibration)")
+        factor = (1 << 30) / (sum(cal) / len(cal) * 1024.0)
+        out = {}
+        for stage, (pat, _) in STAGE_KERNELS.items():
+            vals = [v for nm, v in rows if re.search(pat, nm)]
+            if vals:
+                out[stage] = (sum(vals) / len(vals) * 1024.0 * factor, len(vals))
+        return out, factor
+
+    fetch, ff = per_kernel(fetch_db, "FETCH_SIZE")
+    write, wf = per_kernel(write_db, "WRITE_SIZE")
+    kernels = {}
+    for stage in STAGE_KERNELS:
+        if stage in fetch and stage in write:
+            kernels[stage] = {"fetch_bytes": round(fetch[stage][0]), "write_bytes": round(write[stage][0]),
+                              "hbm_bytes_per_launch": round(fetch[stage][0] + write[stage][0]),
+                              "dispatches": fetch[stage][1],
+                              "source_hash": source_hash(*STAGE_KERNELS[stage][1])}
+    data = {"command": command, "fetch_scale": round(ff, 4), "write_scale": round(wf, 4),
+            "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(data, f, indent=1)
+    with open(out_md, "w") as f:
+        f.write("# HBM traffic per launch: 16K prefill and 16K decode step\n\n")
+        f.write("rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in a pass of its own:\n\n")
+        f.write("```\n" + command + "\n```\n\n")
+        f.write(f"Scale factors from the 1 GiB device copy: FETCH_SIZE x {ff:.3f}, "
+                f"WRITE_SIZE x {wf:.3f}.\n\n")
+        f.write("| stage | dispatches | fetch MB | write MB | HBM MB per launch |\n|---|---|---|---|---|\n")
+        for stage, e in kernels.items():
+            f.write(f"| {stage} | {e['dispatches']} | {e['fetch_bytes'] / 1e6:.2f} | "
+                    f"{e['write_bytes'] / 1e6:.2f} | {e['hbm_bytes_per_launch'] / 1e6:.2f} |\n")
+    return data
 
 
 # ---------------------------------------------------------------------------
@@ -183,13 +246,7 @@ def bench_prefill(args):
                          "frac_mfma_peak": round(f / (v * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
                          if f else None}
     dom = max(stages, key=stages.get)
-    src = {"indexer_topm": ["indexer.hip", "common.hpp"],
-           "sparse_gate_prefill": ["sparse.hip", "common.hpp"],
-           "linear_chunk_output": ["linear.hip", "common.hpp"],
-           "linear_chunk_state": ["linear.hip", "common.hpp"],
-           "linear_prefix_scan": ["linear.hip", "common.hpp"]}[dom]
-    roof = roofline_entry(dom, stages[dom], flops.get(dom, 0), "mfma",
-                          traffic_from_profiles(dom, src))
+    roof = roofline_entry(dom, stages[dom], flops.get(dom, 0), "mfma", traffic_from_profiles(dom))
     res = {
         "workload": f"lisa_prefill qwen2.5-7b-shaped B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                     f"d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} C={cfg.chunk} bf16",
@@ -237,9 +294,10 @@ def bench_decode(args):
         stage_rows[k] = {"ms": round(v, 5),
                          "gbs": round(b / (v * 1e-3) / 1e9, 1) if b else None,
                          "frac_hbm_peak": round(b / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if b else None}
-    dom = max(stages, key=stages.get)
-    roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm",
-                          traffic_from_profiles(dom, ["decode.hip", "common.hpp"]))
+    # the dominant kernel among those that move the step's algorithmic bytes
+    # (the select pass works on the scores already in the workspace)
+    dom = max((k for k in stages if by.get(k)), key=stages.get)
+    roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm", traffic_from_profiles(dom))
     res = {
         "workload": f"lisa_decode_step qwen2.5-1.5b-shaped B={B} ctx=16384+1 Hq={cfg.Hq} "
                     f"Hkv={cfg.Hkv} d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} bf16",
@@ -301,7 +359,20 @@ def main():
     ap.add_argument("--decode-warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && for c in FETCH_SIZE WRITE_SIZE; do "
+               "timeout -s KILL 180 rocprofv3 --pmc $c -d $REPO/gpurun_out/pmc_$c -o run -- "
+               "python3 $REPO/bench.py --steps 2 --warmup 1 --decode-steps 9 --decode-warmup 1 "
+               "--no-cpu-baseline --copy-calibration; done; cd $REPO && python3 bench.py "
+               "--traffic-summary gpurun_out/pmc_FETCH_SIZE/run_results.db "
+               "gpurun_out/pmc_WRITE_SIZE/run_results.db")
+        data = traffic_summary(*args.traffic_summary, os.path.join(PROFILES, "traffic.json"),
+                               os.path.join(PROFILES, "hbm_traffic_prefill16k_decode16k.md"), cmd)
+        print(json.dumps(data, indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the LISA layer here is a single-GPU kernel path "
               "(no collectives are built); run with --gpus 1.", file=sys.stderr)

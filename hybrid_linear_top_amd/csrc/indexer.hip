@@ -416,6 +416,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     }
 
     // ---- final trim and ordered write-out ---------------------------------------
+    wave_lds_sync();  // the last tiles' appends are read by other lanes below
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll 1
