@@ -253,11 +253,235 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
     }
 }
 
+// ---- prefill, bf16: one wave per unit ------------------------------------
+//
+// Prefill has B*n*G units, far more than the chip has waves, so a unit gets
+// a single wave that walks its M slots in steps of 32 with no cross-wave
+// merge.
+//
+// Gathers are row-coalesced: D*2/16 consecutive lanes fetch one whole K (or
+// V) row, so every group of four lanes reads one contiguous 64-byte piece.
+// (Loading rows straight into MFMA fragment order instead puts four
+// different rows under every four lanes, which the address path handles at
+// well under half the rate.)  The rows are staged in LDS and read back in
+// fragment order: K with plain 16-byte reads, V through the gfx950
+// transposing read ds_read_b64_tr_b16.  In each 16-lane block that read
+// gives lane l element l%4 of the 4-element row piece addressed by lane
+// 4e + l/4, e = 0..3; with lane j addressing slot row (base + j/4), dims
+// 16*mb + 4*(j%4), lane l receives V[base + e][16*mb + l%16] -- four
+// K-elements of the A operand of O^T += V^T P^T, in the slot order P^T has
+// in the S^T accumulators.  K and V of a step share one LDS region (K is
+// read into registers before V overwrites it), and the next step's gathers
+// are issued as soon as both have been copied out of their registers.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char *lds_byte_ptr) {
+    lds_bf16x4 *p = (lds_bf16x4 *)(__attribute__((address_space(3))) unsigned char *)(
+        (__attribute__((address_space(3))) void *)lds_byte_ptr);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
+}
+
+template <int D>
+struct WaveSmem {
+    static constexpr int kLPR = D * 2 / 16;      // lanes per gathered row
+    static constexpr int kRPI = 64 / kLPR;       // rows per load instruction
+    static constexpr int kNI = kChunk / kRPI;    // load instructions per 32 rows (per tensor)
+    // row strides: 16-byte pad makes the 16-row fragment reads of K
+    // conflict-free, 32-byte pad the 4-row transposing reads of V
+    static constexpr int kKRow = D * 2 + 16;
+    static constexpr int kVRow = D * 2 + 32;
+    static constexpr int kBytes = kChunk * kVRow;
+};
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
+void sparse_prefill_wave_kernel(SparseArgs a) {
+    using S = WaveSmem<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[S::kBytes];
+    constexpr int KRB = S::kKRow, VRB = S::kVRow, NI = S::kNI, LPR = S::kLPR;
+    constexpr int KC = D / 32;
+    constexpr int MB = D / 16;
+    const int lane = threadIdx.x;
+    const int col = lane & 15, grp = lane >> 4;
+    // group-major logical units, each XCD taking a contiguous range
+    const int lu = xcd_remap(blockIdx.x, gridDim.x);
+    const int G = a.G, r = a.r, M = a.M;
+    const int u = (lu % (a.B * a.n)) * G + lu / (a.B * a.n);
+    const int g = u % G, bt = u / G, b = bt / a.n;
+    const int smax = bt % a.n;                // the query position: keys 0..t are visible
+    const int nvalid = min(M, smax + 1);
+    const uint16_t *qrows = reinterpret_cast<const uint16_t *>(a.q) + ((size_t)bt * a.Hq + g * r) * D;
+    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k) + ((size_t)b * a.n * G + g) * D;
+    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v) + ((size_t)b * a.n * G + g) * D;
+    const uint32_t row_bytes = (uint32_t)G * D * 2;
+    const uint32_t vis_bytes = (uint32_t)(smax + 1) * row_bytes;
+    const rsrc_t krs = make_rsrc(kbase, vis_bytes), vrs = make_rsrc(vbase, vis_bytes);
+    const rsrc_t irs = make_rsrc(a.idx + (size_t)u * M, (uint32_t)M * 4u);
+
+    Frag<uint16_t> qf[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        if (col < r) qf[kc].load(qrows + (size_t)col * D + kc * 32 + grp * 8);
+        else qf[kc].zero();
+    }
+
+    // this lane fetches piece (lane % LPR) of the step's LDS rows
+    // rho = (lane / LPR) * NI + i, i = 0..NI-1 (slot 32*j + rho)
+    const int rsub = lane / LPR, piece = lane % LPR;
+    const int rho0 = rsub * NI;
+    const int nsteps = (nvalid + kChunk - 1) / kChunk;
+    struct Idx { u32x4 v[NI / 4]; };
+    const bool idx16 = (M & 3) == 0;  // index rows 16-byte aligned: vector loads
+    auto load_idx = [&](int j) {
+        Idx x;
+        const uint32_t o = (uint32_t)(j * kChunk + rho0) * 4u;
+        if (idx16) {
+#pragma unroll
+            for (int h = 0; h < NI / 4; ++h) x.v[h] = buf_load16(irs, o + 16u * h);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                x.v[i / 4][i % 4] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(irs, o + 4u * i, 0u, 0);
+        }
+        return x;
+    };
+    u32x4 kp[NI], vp[NI];
+    auto gather = [&](int j, const Idx &x) {
+        uint32_t off[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s = (int)x.v[i / 4][i % 4];
+            const bool ok = j * kChunk + rho0 + i < nvalid && s >= 0 && s <= smax;
+            off[i] = ok ? (uint32_t)s * row_bytes + piece * 16 : kOffNone;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) kp[i] = buf_load16(krs, off[i]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) vp[i] = buf_load16(vrs, off[i]);
+    };
+    // gathers run one step ahead of the compute and index loads two steps
+    // ahead; an index becomes an offset only when its gather is issued, so
+    // waiting for it never waits for a gather still in flight
+    gather(0, load_idx(0));
+    Idx inext = load_idx(1);  // reads past the row return zeros, masked by slot < nvalid
+
+    f32x4 o[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) o[mb] = f32x4{0, 0, 0, 0};
+    float m_run = -INFINITY, l_part = 0.0f;  // l_part: this lane's share of the row sum
+
+    const uint32_t kw_base = (uint32_t)rho0 * KRB + piece * 16;   // K row writes
+    const uint32_t vw_base = (uint32_t)rho0 * VRB + piece * 16;   // V row writes
+    const uint32_t kr_base = (uint32_t)col * KRB + grp * 16;      // K fragment reads
+    const uint32_t vr_base = (uint32_t)(grp * 4 + (col >> 2)) * VRB + (col & 3) * 8;  // V^T reads
+
+    for (int j = 0; j < nsteps; ++j) {
+        // K rows through LDS into fragment order, then V rows into the same
+        // region (a wave's LDS accesses complete in issue order)
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4 *>(lds + kw_base + i * KRB) = kp[i];
+        wave_lds_sync();
+        Frag<uint16_t> kf[2][KC];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                kf[kb][kc].v = *reinterpret_cast<const u32x4 *>(lds + kr_base + kb * 16 * KRB + kc * 64);
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4 *>(lds + vw_base + i * VRB) = vp[i];
+        if (j + 1 < nsteps) {
+            gather(j + 1, inext);
+            inext = load_idx(j + 2);
+        }
+        // logits S^T for the two 16-slot blocks
+        f32x4 acc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            acc[kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) acc[kb] = mma16(kf[kb][kc], qf[kc], acc[kb]);
+        }
+        // online softmax over the 32 slots, per head (column)
+        float x[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = j * kChunk + kb * 16 + grp * 4 + i < nvalid;
+                const float v = ok ? acc[kb][i] * a.scale_log2 : -INFINITY;
+                x[kb * 4 + i] = v;
+                cmax = fmaxf(cmax, v);
+            }
+        cmax = wave_max_across16(cmax);
+        const float m_new = fmaxf(m_run, cmax);  // finite from the first step on (slot 0 is valid)
+        if (__ballot(m_new > m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_part *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+            m_run = m_new;
+        }
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
+            l_part += p[e];
+        }
+        Frag<uint16_t> pf;
+        pf.set(p);  // K-element e <-> slot (e < 4 ? 4*grp + e : 16 + 4*grp + e - 4)
+        wave_lds_sync();
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const u32x2 lo = lds_read_tr16(lds + vr_base + mb * 32);
+            const u32x2 hi = lds_read_tr16(lds + vr_base + 16 * VRB + mb * 32);
+            Frag<uint16_t> vt;
+            vt.v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            o[mb] = mma16(vt, pf, o[mb]);
+        }
+    }
+
+    // gate epilogue: lane (col = head, grp) holds dims 16*mb + 4*grp + i
+    const float l = wave_sum_across16(l_part);
+    if (col < r) {
+        const size_t base = ((size_t)bt * a.Hq + g * r + col) * D;
+        const float z = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.gate)[(size_t)bt * a.Hq + g * r + col]);
+        const float gam = 1.0f / (1.0f + expf(-z));
+        const float inv = l > 0.0f ? gam / l : 0.0f;
+        const uint16_t *lin = reinterpret_cast<const uint16_t *>(a.lin) + base;
+        uint16_t *outp = reinterpret_cast<uint16_t *>(a.out) + base;
+        // o_lin lives in the output buffer: read all of it before any store
+        u32x2 lvs[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) lvs[mb] = *reinterpret_cast<const u32x2 *>(lin + mb * 16 + grp * 4);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int d0 = mb * 16 + grp * 4;
+            const u32x2 lv = lvs[mb];
+            float res[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t bits = (lv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                res[i] = o[mb][i] * inv + (1.0f - gam) * bf16_bits_to_f32(bits);
+            }
+            *reinterpret_cast<u32x2 *>(outp + d0) =
+                u32x2{f32_to_bf16_bits(res[0]) | (f32_to_bf16_bits(res[1]) << 16),
+                      f32_to_bf16_bits(res[2]) | (f32_to_bf16_bits(res[3]) << 16)};
+        }
+    }
+}
+
 template <typename T, int D>
 hipError_t dispatch_d(const SparseArgs &a, bool decode, hipStream_t s) {
     const dim3 grid(a.units);
     if (!decode) {
-        hipLaunchKernelGGL((sparse_gate_kernel<T, D, false, 4>), grid, dim3(256), 0, s, a);
+        if constexpr (sizeof(T) == 2)
+            hipLaunchKernelGGL((sparse_prefill_wave_kernel<D>), grid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL((sparse_gate_kernel<T, D, false, 4>), grid, dim3(256), 0, s, a);
     } else if (a.M <= 4 * kChunk) {
         hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 4>), grid, dim3(256), 0, s, a);
     } else if (a.M <= 8 * kChunk) {

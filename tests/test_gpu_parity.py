@@ -47,6 +47,8 @@ PREFILL_SMALL = [
     _pcfg(520, 4, 2, 64, 4, 64, 200, dtype="f32", seed=5),
     _pcfg(900, 14, 2, 128, 2, 64, 96, seed=6),
     _pcfg(1500, 12, 2, 128, 4, 64, 256, seed=7),  # several compactions per query
+    _pcfg(300, 8, 2, 128, 4, 64, 130, seed=8),    # index rows not 16-byte aligned (M % 4 = 2)
+    _pcfg(180, 6, 3, 64, 4, 32, 37, seed=9),      # d = 64 with odd M
 ]
 
 
