@@ -205,13 +205,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
 
-// Inclusive prefix sum over the 64 lanes of a wave (row shifts, then row
-// broadcasts of lanes 15 and 31).
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+// Inclusive prefix sum within each 16-lane row (row shifts; lanes shifted in
+// from outside the row contribute 0).
+__device__ __forceinline__ uint32_t row_inclusive_scan(uint32_t v) {
     v += dpp_u32<0x111>(0u, v);  // row_shr:1
     v += dpp_u32<0x112>(0u, v);  // row_shr:2
     v += dpp_u32<0x114>(0u, v);  // row_shr:4
     v += dpp_u32<0x118>(0u, v);  // row_shr:8
+    return v;
+}
+// Lane 15 of each 16-lane row, broadcast to the whole row (row_newbcast:15).
+__device__ __forceinline__ uint32_t row_broadcast15(uint32_t v) { return dpp_u32<0x15F>(0u, v); }
+
+// Inclusive prefix sum over the 64 lanes of a wave (row shifts, then row
+// broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    v = row_inclusive_scan(v);
     v += dpp_u32<0x142, 0xA>(0u, v);  // row_bcast:15 into rows 1 and 3
     v += dpp_u32<0x143, 0xC>(0u, v);  // row_bcast:31 into rows 2 and 3
     return v;

@@ -14,9 +14,13 @@
 //    issued back to back.  The A operand rows are (query, indexer head) pairs
 //    laid out so that the four accumulator rows a lane receives are the four
 //    heads of one query: the ReLU and the w-weighted head sum are lane-local.
-//  * Each query keeps a candidate buffer in LDS, always sorted by key index:
-//    candidates are appended in ascending key order (ballot + mbcnt give
-//    positions) when their score is strictly above the query's threshold tau.
+//  * Column n of key block cb holds key k0 + 4n + cb, so each lane scores
+//    four consecutive keys of its query.  Each query keeps a candidate buffer
+//    in LDS, always sorted by key index: a lane's accepted keys go to
+//    consecutive positions after an exclusive scan of the per-lane counts
+//    over the query's 16-lane row (DPP row shifts, row_newbcast for the row
+//    total).  A candidate is accepted when its score is strictly above the
+//    query's threshold tau.
 //  * When a buffer could overflow on the next tile it is trimmed: a one-pass
 //    256-bin histogram over the buffered scores finds the bin holding the
 //    M-th largest; the lower bins are dropped and tau becomes the largest
@@ -284,13 +288,13 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         tau[qb] = tq[qb] < n ? -INFINITY : INFINITY;  // queries past n accept nothing
     }
 
-    // B fragments of one key tile: key 16*cb + col, dims 32*kc + 8*grp .. +7,
+    // B fragments of one key tile: key 4*col + cb, dims 32*kc + 8*grp .. +7,
     // through a per-tile buffer descriptor (keys >= n read as zeros)
     constexpr uint32_t EB = Elt<T>::kBytes;
     const uint32_t key_bytes = (uint32_t)n * (uint32_t)krs * EB;
     uint32_t voff[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) voff[cb] = ((uint32_t)(cb * 16 + col) * (uint32_t)krs + grp * 8) * EB;
+    for (int cb = 0; cb < 4; ++cb) voff[cb] = ((uint32_t)(4 * col + cb) * (uint32_t)krs + grp * 8) * EB;
     auto load_b = [&](int kt, Frag<T> (&bf)[4][C::KD]) {
         const uint32_t tile_off = (uint32_t)kt * kKT * (uint32_t)krs * EB;
         const rsrc_t r = make_rsrc(reinterpret_cast<const unsigned char *>(kI) + tile_off,
@@ -301,10 +305,6 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
             for (int kc = 0; kc < C::KD; ++kc) frag_buf_load(bf[cb][kc], r, voff[cb] + kc * 32 * EB);
     };
 
-    // bits of this lane's query key mask that precede its own key 16*cb + col
-    uint64_t below[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) below[cb] = (1ull << (16 * cb + col)) - 1ull;
 
     auto tile_step = [&](int kt, const Frag<T> (&bcur)[4][C::KD], auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;  // tile reaches past the first query
@@ -338,37 +338,33 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                     for (int i = 0; i < 4; ++i)
                         sc = fmaf(wv[qb][hh][i], fmaxf(acc[qb][hh][cb][i], 0.0f), sc);
                 score[qb][cb] = sc;
-                if constexpr (DIAG) ok[qb][cb] = (k0 + cb * 16 + col <= tq[qb]) && sc > tau[qb];
+                if constexpr (DIAG) ok[qb][cb] = (k0 + 4 * col + cb <= tq[qb]) && sc > tau[qb];
                 else ok[qb][cb] = sc > tau[qb];
                 mask[qb][cb] = __ballot(ok[qb][cb]);
                 any |= mask[qb][cb];
             }
         if (!any) return;
-        // Append in ascending key order.  Per query the four 16-bit ballot
-        // fields form a 64-bit key mask (bit 16*cb + col); a candidate's
-        // position is the number of accepted keys of its query below it.
+        // Append in ascending key order: a query's accepted keys are ordered by
+        // (col, cb), so a lane's first position is the query's count plus the
+        // exclusive scan of the per-lane counts over its 16-lane row.
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             if (!(mask[qb][0] | mask[qb][1] | mask[qb][2] | mask[qb][3])) continue;
-            uint64_t K[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint64_t k = 0;
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) k |= ((mask[qb][cb] >> (16 * g)) & 0xFFFFull) << (16 * cb);
-                K[g] = k;
-            }
-            const uint64_t Kl = grp == 0 ? K[0] : grp == 1 ? K[1] : grp == 2 ? K[2] : K[3];
+            const uint32_t c4 = (uint32_t)ok[qb][0] + (uint32_t)ok[qb][1] + (uint32_t)ok[qb][2] +
+                                (uint32_t)ok[qb][3];
+            const uint32_t incl = row_inclusive_scan(c4);
+            const uint32_t tot = row_broadcast15(incl);
+            int pos = cnt[qb] + (int)(incl - c4);
             const CandBuf qbuf = qbuf_of(qb * 4 + grp);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
                 if (ok[qb][cb]) {
-                    const int pos = cnt[qb] + __popcll(Kl & below[cb]);
                     qbuf.sc[pos] = score[qb][cb];
-                    qbuf.key[pos] = (uint16_t)(k0 + cb * 16 + col);
+                    qbuf.key[pos] = (uint16_t)(k0 + 4 * col + cb);
                 }
+                pos += ok[qb][cb] ? 1 : 0;
             }
-            cnt[qb] += __popcll(Kl);
+            cnt[qb] += (int)tot;
         }
         // trim any buffer that could overflow on the next tile
 #pragma unroll
