@@ -188,6 +188,16 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 __device__ __forceinline__ float wave_min(float v) { return -wave_max(-v); }
 
+// over the 16 lanes of each row (result in every lane of the row)
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+    return v;
+}
+__device__ __forceinline__ float row_min(float v) { return -row_max(-v); }
+
 __device__ __forceinline__ uint32_t max_u32_xor16(uint32_t v) {
     const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
     return max((uint32_t)p[0], (uint32_t)p[1]);

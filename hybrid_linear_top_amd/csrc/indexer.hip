@@ -306,9 +306,8 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     };
 
 
-    auto tile_step = [&](int kt, const Frag<T> (&bcur)[4][C::KD], auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;  // tile reaches past the first query
-        const int k0 = kt * kKT;
+    // scores of one tile: score[qb][cb] for key k0 + 4*col + cb of query tq[qb]
+    auto tile_scores = [&](const Frag<T> (&bcur)[4][C::KD], float (&score)[QB][4]) {
         // all MFMAs of the tile first
         f32x4 acc[QB][HH][4];
 #pragma unroll
@@ -322,11 +321,6 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                     for (int kc = 0; kc < C::KD; ++kc) x = mma16(af[qb][hh][kc], bcur[cb][kc], x);
                     acc[qb][hh][cb] = x;
                 }
-        // scores and threshold tests
-        float score[QB][4];
-        bool ok[QB][4];
-        uint64_t mask[QB][4];
-        uint64_t any = 0;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -338,6 +332,23 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                     for (int i = 0; i < 4; ++i)
                         sc = fmaf(wv[qb][hh][i], fmaxf(acc[qb][hh][cb][i], 0.0f), sc);
                 score[qb][cb] = sc;
+            }
+    };
+
+    auto tile_step = [&](int kt, const Frag<T> (&bcur)[4][C::KD], auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;  // tile reaches past the first query
+        const int k0 = kt * kKT;
+        float score[QB][4];
+        tile_scores(bcur, score);
+        // threshold tests
+        bool ok[QB][4];
+        uint64_t mask[QB][4];
+        uint64_t any = 0;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const float sc = score[qb][cb];
                 if constexpr (DIAG) ok[qb][cb] = (k0 + 4 * col + cb <= tq[qb]) && sc > tau[qb];
                 else ok[qb][cb] = sc > tau[qb];
                 mask[qb][cb] = __ballot(ok[qb][cb]);
@@ -390,25 +401,117 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         }
     };
 
-    // three fragment buffers rotate: tiles kt+1 and kt+2 load while kt computes
     Frag<T> b0[4][C::KD], b1[4][C::KD], b2[4][C::KD];
-    load_b(0, b0);
-    if (1 < ntiles) load_b(1, b1);
     // tiles below kd hold only keys < qw0 <= every query of the wave
     const int kd = qw0 / kKT;
+
+    // ---- starting threshold from a key sample ---------------------------------
+    // With tau starting at -inf a late query appends about M*ln(t/M) keys and
+    // trims its buffer several times.  Instead, ns tiles spread over the keys
+    // below qw0 are scored first; each lane keeps its four best sample scores
+    // per query, and tau starts at (about) the R-th largest of a query's 64
+    // kept values, R chosen so that about kSlack*M of the query's t+1 keys are
+    // expected above it.  This is only a starting point: the scan below
+    // accepts what beats it, and a query left with fewer than min(M, t+1)
+    // candidates (tau was too high) is scanned again from tau = -inf, so the
+    // result is exact whatever the sample says.
+    constexpr float kSlack = 1.5f;
+    constexpr int kRank = 32;
+    int ns = 0;
+    if (qw0 >= 4 * M) {
+        ns = (int)ceilf((float)kRank * (float)(qw0 + 1) / (kSlack * (float)M * (float)kKT));
+        ns = min(ns, kd / 2);
+    }
+    if (ns > 0) {
+        float top[QB][4];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) top[qb][i] = -INFINITY;
+        auto sample_tile = [&](const Frag<T> (&bc)[4][C::KD]) {
+            float score[QB][4];
+            tile_scores(bc, score);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    float x = score[qb][cb];  // insert into the descending top-4
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        const float hi = fmaxf(top[qb][i], x);
+                        x = fminf(top[qb][i], x);
+                        top[qb][i] = hi;
+                    }
+                    top[qb][3] = fmaxf(top[qb][3], x);
+                }
+        };
+        auto ks = [&](int i) { return ((2 * i + 1) * kd) / (2 * ns); };
+        load_b(ks(0), b0);
+        for (int i = 0; i < ns; i += 2) {
+            if (i + 1 < ns) load_b(ks(i + 1), b1);
+            sample_tile(b0);
+            if (i + 1 >= ns) break;
+            if (i + 2 < ns) load_b(ks(i + 2), b0);
+            sample_tile(b1);
+        }
+        const float S = (float)(ns * kKT);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float R = fminf(48.0f, fmaxf(1.0f, rintf(kSlack * (float)M * S / (float)(tq[qb] + 1))));
+            auto count_ge = [&](float x) {
+                const uint32_t c = (uint32_t)(top[qb][0] >= x) + (uint32_t)(top[qb][1] >= x) +
+                                   (uint32_t)(top[qb][2] >= x) + (uint32_t)(top[qb][3] >= x);
+                return (float)row_broadcast15(row_inclusive_scan(c));
+            };
+            float lo = row_min(top[qb][3]), hi = row_max(top[qb][0]);
+            if (count_ge(hi) >= R) lo = hi;
+#pragma unroll 1
+            for (int it = 0; it < 12; ++it) {
+                const float mid = 0.5f * (lo + hi);
+                const bool up = count_ge(mid) >= R;
+                lo = up ? mid : lo;
+                hi = up ? hi : mid;
+            }
+            if (tq[qb] < n) tau[qb] = lo;
+        }
+    }
+
+    // ---- scan: every tile, three fragment buffers rotating (tiles kt+1 and
+    // kt+2 load while kt computes); a second pass redoes exactly the queries
+    // whose sampled threshold turned out too high ------------------------------
     auto step = [&](int kt, const Frag<T> (&bc)[4][C::KD]) {
         if (kt >= kd) tile_step(kt, bc, std::true_type{});
         else tile_step(kt, bc, std::false_type{});
     };
-    for (int kt = 0; kt < ntiles; kt += 3) {
-        if (kt + 2 < ntiles) load_b(kt + 2, b2);
-        step(kt, b0);
-        if (kt + 1 >= ntiles) break;
-        if (kt + 3 < ntiles) load_b(kt + 3, b0);
-        step(kt + 1, b1);
-        if (kt + 2 >= ntiles) break;
-        if (kt + 4 < ntiles) load_b(kt + 4, b1);
-        step(kt + 2, b2);
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        load_b(0, b0);
+        if (1 < ntiles) load_b(1, b1);
+        for (int kt = 0; kt < ntiles; kt += 3) {
+            if (kt + 2 < ntiles) load_b(kt + 2, b2);
+            step(kt, b0);
+            if (kt + 1 >= ntiles) break;
+            if (kt + 3 < ntiles) load_b(kt + 3, b0);
+            step(kt + 1, b1);
+            if (kt + 2 >= ntiles) break;
+            if (kt + 4 < ntiles) load_b(kt + 4, b1);
+            step(kt + 2, b2);
+        }
+        if (ns == 0) break;  // started from -inf: already exact
+        uint64_t redo = 0;
+        bool fail[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            fail[qb] = tq[qb] < n && cnt[qb] < min(M, tq[qb] + 1);
+            redo |= __ballot(fail[qb]);
+        }
+        if (!redo || pass == 1) break;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            // kept queries take nothing more (their counts stay below a trim)
+            tau[qb] = fail[qb] ? -INFINITY : INFINITY;
+            cnt[qb] = fail[qb] ? 0 : cnt[qb];
+        }
     }
 
     // ---- final trim and ordered write-out ---------------------------------------

@@ -148,6 +148,16 @@ def test_ties_lowest_index_wins():
         m = min(cfg.M, t + 1)
         exp = np.concatenate([np.arange(m), -np.ones(cfg.M - m)]).astype(np.int32)
         assert np.array_equal(idx[0, t, 0], exp) and np.array_equal(idx[0, t, 1], exp), t
+    # long enough for the sampled starting threshold (which admits nothing here)
+    cfg = _pcfg(2000, 4, 2, 64, 4, 32, 64, seed=2)
+    _say("prefill all-ties, sampled threshold", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    inp["w_idx"] = np.zeros_like(inp["w_idx"])
+    _, _, idx = parity.run_prefill(cfg, inp)
+    for t in range(cfg.n):
+        m = min(cfg.M, t + 1)
+        exp = np.concatenate([np.arange(m), -np.ones(cfg.M - m)]).astype(np.int32)
+        assert np.array_equal(idx[0, t, 0], exp) and np.array_equal(idx[0, t, 1], exp), t
     dcfg, L = _dcfg(4, 2, 64, 4, 32, 100, [50, 100, 101, 3000])
     _say("decode all-ties", dcfg.name)
     dinp = gen.make_decode_inputs(dcfg, lengths=L)
@@ -157,6 +167,20 @@ def test_ties_lowest_index_wins():
         m = min(dcfg.M, Lb)
         exp = np.concatenate([np.arange(m), -np.ones(dcfg.M - m)]).astype(np.int32)
         assert np.array_equal(didx[b, 0], exp) and np.array_equal(didx[b, 1], exp), b
+
+
+def test_prefill_sampled_threshold_rescan():
+    """Every third query has all-zero weights, so it scores every key 0 and a
+    sampled starting threshold admits nothing: those queries are rescanned
+    exactly (first m positions) while the other queries of the same waves keep
+    their candidates."""
+    cfg = _pcfg(2100, 4, 2, 64, 4, 32, 64, seed=12)
+    _say("prefill mixed rescan", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    inp["w_idx"][:, ::3] = 0
+    rep = {}
+    parity.prefill_parity(cfg, inp, report=rep)
+    _say("  ", rep)
 
 
 def test_deterministic():
