@@ -219,6 +219,24 @@ __device__ bool wave_trim(CandBuf buf, int &c_io, int M, int need_free, uint32_t
     return true;
 }
 
+// Trim one query's buffer of c candidates to about M (one histogram pass, or
+// the exact select when that frees too little).  Kept out of line: trims are
+// rare and the tile loop stays small enough for the instruction cache.
+struct TrimResult {
+    int c;
+    float tau;
+};
+template <int NE>
+__device__ __attribute__((noinline)) TrimResult trim_buffer(CandBuf buf, int c, int M, int need_free,
+                                                            uint32_t *hist) {
+    float th = -INFINITY;
+    if (!wave_trim<NE>(buf, c, M, need_free, hist, th)) {
+        th = key_to_float(wave_select<NE>(buf, c, M, hist));
+        c = M;
+    }
+    return TrimResult{c, th};
+}
+
 template <typename T, int DI, int HH, int CAP, int QB>
 struct IdxCfg {
     static constexpr int KD = DI / 32;      // MFMA K-steps
@@ -386,16 +404,12 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 #pragma unroll 1
             for (int gg = 0; gg < 4; ++gg) {
                 if (!((full >> (16 * gg)) & 1ull)) continue;
-                const CandBuf qbuf = qbuf_of(qb * 4 + gg);
-                int c = __builtin_amdgcn_readlane(cnt[qb], 16 * gg);
-                float th = -INFINITY;
-                if (!wave_trim<C::NE>(qbuf, c, M, CAP / 4, hist, th)) {
-                    th = key_to_float(wave_select<C::NE>(qbuf, c, M, hist));
-                    c = M;
-                }
+                const TrimResult tr = trim_buffer<C::NE>(qbuf_of(qb * 4 + gg),
+                                                         __builtin_amdgcn_readlane(cnt[qb], 16 * gg), M,
+                                                         CAP / 4, hist);
                 if (grp == gg) {
-                    cnt[qb] = c;
-                    tau[qb] = th;
+                    cnt[qb] = tr.c;
+                    tau[qb] = tr.tau;
                 }
             }
         }
@@ -404,6 +418,12 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     Frag<T> b0[4][C::KD], b1[4][C::KD], b2[4][C::KD];
     // tiles below kd hold only keys < qw0 <= every query of the wave
     const int kd = qw0 / kKT;
+    // Prefetches are never skipped: a tile past the end is fetched through an
+    // empty descriptor (all zeros, no memory access).  A skipped load on one
+    // path would make the wait counts of the merged paths wait for the
+    // prefetched tiles as well.
+    const int knull = (n + kKT - 1) / kKT;
+    auto tile_or_null = [&](int kt, int lim) { return kt < lim ? kt : knull; };
 
     // ---- starting threshold from a key sample ---------------------------------
     // With tau starting at -inf a late query appends about M*ln(t/M) keys and
@@ -448,10 +468,10 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         auto ks = [&](int i) { return ((2 * i + 1) * kd) / (2 * ns); };
         load_b(ks(0), b0);
         for (int i = 0; i < ns; i += 2) {
-            if (i + 1 < ns) load_b(ks(i + 1), b1);
+            load_b(i + 1 < ns ? ks(i + 1) : knull, b1);
             sample_tile(b0);
             if (i + 1 >= ns) break;
-            if (i + 2 < ns) load_b(ks(i + 2), b0);
+            load_b(i + 2 < ns ? ks(i + 2) : knull, b0);
             sample_tile(b1);
         }
         const float S = (float)(ns * kKT);
@@ -486,15 +506,15 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
         load_b(0, b0);
-        if (1 < ntiles) load_b(1, b1);
+        load_b(tile_or_null(1, ntiles), b1);
         for (int kt = 0; kt < ntiles; kt += 3) {
-            if (kt + 2 < ntiles) load_b(kt + 2, b2);
+            load_b(tile_or_null(kt + 2, ntiles), b2);
             step(kt, b0);
             if (kt + 1 >= ntiles) break;
-            if (kt + 3 < ntiles) load_b(kt + 3, b0);
+            load_b(tile_or_null(kt + 3, ntiles), b0);
             step(kt + 1, b1);
             if (kt + 2 >= ntiles) break;
-            if (kt + 4 < ntiles) load_b(kt + 4, b1);
+            load_b(tile_or_null(kt + 4, ntiles), b1);
             step(kt + 2, b2);
         }
         if (ns == 0) break;  // started from -inf: already exact
