@@ -251,6 +251,10 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     __shared__ __attribute__((aligned(16))) float cand_sc[kQW * CAP];
     __shared__ __attribute__((aligned(16))) uint16_t cand_key[kQW * CAP];
     __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+    // per-lane sink for the writes of rejected keys: appends are straight-line
+    // code, so the two query quads' scans and writes interleave
+    __shared__ __attribute__((aligned(16))) float sink_sc[64];
+    __shared__ __attribute__((aligned(16))) uint16_t sink_key[64];
     auto qbuf_of = [&](int q) { return CandBuf{cand_sc + q * CAP, cand_key + q * CAP}; };
 
     const int lane = threadIdx.x & 63;
@@ -360,7 +364,6 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         tile_scores(bcur, score);
         // threshold tests
         bool ok[QB][4];
-        uint64_t mask[QB][4];
         uint64_t any = 0;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -369,8 +372,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                 const float sc = score[qb][cb];
                 if constexpr (DIAG) ok[qb][cb] = (k0 + 4 * col + cb <= tq[qb]) && sc > tau[qb];
                 else ok[qb][cb] = sc > tau[qb];
-                mask[qb][cb] = __ballot(ok[qb][cb]);
-                any |= mask[qb][cb];
+                any |= __ballot(ok[qb][cb]);
             }
         if (!any) return;
         // Append in ascending key order: a query's accepted keys are ordered by
@@ -378,7 +380,6 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         // exclusive scan of the per-lane counts over its 16-lane row.
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            if (!(mask[qb][0] | mask[qb][1] | mask[qb][2] | mask[qb][3])) continue;
             const uint32_t c4 = (uint32_t)ok[qb][0] + (uint32_t)ok[qb][1] + (uint32_t)ok[qb][2] +
                                 (uint32_t)ok[qb][3];
             const uint32_t incl = row_inclusive_scan(c4);
@@ -387,10 +388,10 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
             const CandBuf qbuf = qbuf_of(qb * 4 + grp);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                if (ok[qb][cb]) {
-                    qbuf.sc[pos] = score[qb][cb];
-                    qbuf.key[pos] = (uint16_t)(k0 + 4 * col + cb);
-                }
+                float *psc = ok[qb][cb] ? qbuf.sc + pos : sink_sc + lane;
+                uint16_t *pkey = ok[qb][cb] ? qbuf.key + pos : sink_key + lane;
+                *psc = score[qb][cb];
+                *pkey = (uint16_t)(k0 + 4 * col + cb);
                 pos += ok[qb][cb] ? 1 : 0;
             }
             cnt[qb] += (int)tot;
