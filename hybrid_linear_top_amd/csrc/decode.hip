@@ -78,19 +78,6 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb) {
         const int g = task % G, sub = task / G;
         const int tb = tok0 + sub * TPW;
         if (tb >= tok_end) continue;
-        float qv[HIPAD][EPC];
-        float wv[HIPAD];
-#pragma unroll
-        for (int j = 0; j < HIPAD; ++j) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            wv[j] = 0.0f;
-            if (j < a.HI) {
-                raw = *reinterpret_cast<const u32x4 *>(qI + ((size_t)(b * G + g) * a.HI + j) * DI +
-                                                       c * EPC);
-                wv[j] = Elt<T>::to_f32(wI[(size_t)(b * G + g) * a.HI + j]);
-            }
-            Chunk<T>::widen(raw, qv[j]);
-        }
         u32x4 raw[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -100,6 +87,23 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb) {
                     kI + ((size_t)(row0 + tok) * G + g) * DI + c * EPC));
             else
                 raw[it] = u32x4{0u, 0u, 0u, 0u};
+        }
+        // query rows and head weights: unconditional loads (heads past HI
+        // re-read the last head and get weight 0) so they fly together
+        float qv[HIPAD][EPC];
+        float wv[HIPAD];
+        u32x4 qraw[HIPAD];
+        T wraw[HIPAD];
+#pragma unroll
+        for (int j = 0; j < HIPAD; ++j) {
+            const int jj = min(j, a.HI - 1);
+            qraw[j] = *reinterpret_cast<const u32x4 *>(qI + ((size_t)(b * G + g) * a.HI + jj) * DI + c * EPC);
+            wraw[j] = wI[(size_t)(b * G + g) * a.HI + jj];
+        }
+#pragma unroll
+        for (int j = 0; j < HIPAD; ++j) {
+            wv[j] = j < a.HI ? Elt<T>::to_f32(wraw[j]) : 0.0f;
+            Chunk<T>::widen(qraw[j], qv[j]);
         }
         float *out = a.scores + (size_t)(b * G + g) * a.max_ctx;
 #pragma unroll
@@ -216,13 +220,17 @@ __global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
         for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
         return;
     }
+    // ---- 1. key range (unconditional loads: positions >= L read zeros) ----
+    const rsrc_t srs = make_rsrc(sc, (uint32_t)L * 4u);
     uint32_t keyreg[EPT];
-    // ---- 1. key range ----
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+        keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(k * NT + tid) * 4u, 0u, 0);
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
         const int s = k * NT + tid;
-        keyreg[k] = s < L ? order_key(sc[s]) : 0u;
+        keyreg[k] = order_key(__uint_as_float(keyreg[k]));
         if (s < L) {
             kmin = min(kmin, keyreg[k]);
             kmax = max(kmax, keyreg[k]);
@@ -359,6 +367,219 @@ __global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Top-M select of one (sequence, group) with few block barriers: NT threads,
+// thread t holding the order keys of positions t, t+NT, ... in registers.
+//  1. key range by wave reductions (one barrier);
+//  2. 2048-bin histogram passes over the live range as above, but the bin
+//     holding the M-th largest key is found by wave 0 alone (32 bins a lane,
+//     one wave scan) -- three barriers a pass; passes stop as soon as that
+//     bin is taken whole or holds at most 64 keys;
+//  3. those boundary keys (key, position) are appended to LDS and wave 0
+//     ranks them exactly (higher key, then lower position) and marks the
+//     `need` best in an LDS bitmap of positions, while every thread marks its
+//     keys above the boundary bin; when the boundary bin is a single key value
+//     (ties, any number of them) its keys go to a second bitmap instead and
+//     the lowest `need` positions of it are taken;
+//  4. wave 0 walks the bitmaps in position order (contiguous words per lane,
+//     one wave scan of their counts) and writes the set ascending.
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, const int64_t *cu,
+                                                         int G, int M, int max_ctx, int32_t *idx) {
+    constexpr int NW = NT / 64;
+    constexpr int NWORD = (NT * EPT + 31) / 32;  // bitmap words
+    constexpr int WPL = (NWORD + 63) / 64;       // bitmap words per lane of wave 0
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ uint32_t bitmap[NWORD];   // selected outright
+    __shared__ uint32_t eqmap[NWORD];    // boundary keys that are all equal (ties)
+    __shared__ uint32_t red[2 * NW];
+    __shared__ uint32_t cand_key[64], cand_pos[64];
+    __shared__ uint32_t found[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bg = blockIdx.x, b = bg / G;
+    const int L = (int)max((int64_t)0, min((int64_t)max_ctx, cu[b + 1] - cu[b]));
+    const float *sc = scores + (size_t)bg * max_ctx;
+    int32_t *out = idx + (size_t)bg * M;
+    if (L <= M) {
+        for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
+        return;
+    }
+    // all loads unconditional (positions >= L read zeros through the
+    // descriptor) so they are in flight together
+    const rsrc_t srs = make_rsrc(sc, (uint32_t)L * 4u);
+    uint32_t keyreg[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+        keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(k * NT + tid) * 4u, 0u, 0);
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int s = k * NT + tid;
+        keyreg[k] = order_key(__uint_as_float(keyreg[k]));
+        if (s < L) {
+            kmin = min(kmin, keyreg[k]);
+            kmax = max(kmax, keyreg[k]);
+        }
+    }
+    for (int w = tid; w < NWORD; w += NT) {
+        bitmap[w] = 0u;
+        eqmap[w] = 0u;
+    }
+    if (tid == 0) found[3] = 0u;  // boundary candidates appended
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+        red[wave] = kmin;
+        red[NW + wave] = kmax;
+    }
+    __syncthreads();
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        lo = min(lo, red[w]);
+        hi = max(hi, red[NW + w]);
+    }
+    const uint32_t span = hi - lo;
+    int width = span == 0 ? 0 : 32 - __builtin_clz(span);  // bits of key - lo
+    uint32_t need = (uint32_t)M;
+    uint64_t bin_hi;     // keys >= bin_hi are selected outright
+    uint32_t bin_lo;     // keys in [bin_lo, bin_hi) are the boundary candidates
+    uint32_t cnt_b = 0;  // how many there are
+    bool tied = false;   // boundary bin is one key value
+    for (;;) {
+        const int shift = width > 11 ? width - 11 : 0;
+        for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+        __syncthreads();
+        const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int s = k * NT + tid;
+            const uint32_t u = keyreg[k];
+            if (s < L && u >= lo && (uint64_t)u < hi_excl) atomicAdd(&hist[(u - lo) >> shift], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l owns bins 2016 - 32*l .. 2047 - 32*l, walked downwards
+            const uint32_t *hl = hist + 2016 - 32 * lane;
+            uint32_t hsum = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(hl)[q];
+                hsum += v[0] + v[1] + v[2] + v[3];
+            }
+            const uint32_t before = wave_inclusive_scan(hsum) - hsum;
+            if (before < need && before + hsum >= need) {
+                uint32_t run = before, frem = 0, fcnt = 0;
+                int fe = 0;
+#pragma unroll
+                for (int q = 7; q >= 0; --q) {
+                    const u32x4 v = reinterpret_cast<const u32x4 *>(hl)[q];
+#pragma unroll
+                    for (int e = 3; e >= 0; --e) {
+                        const bool hit = run < need && run + v[e] >= need;
+                        fe = hit ? 4 * q + e : fe;
+                        frem = hit ? need - run : frem;
+                        fcnt = hit ? v[e] : fcnt;
+                        run += v[e];
+                    }
+                }
+                found[0] = 2016 - 32 * lane + fe;
+                found[1] = frem;
+                found[2] = fcnt;
+            }
+        }
+        __syncthreads();
+        const uint32_t bin = found[0], rem = found[1], cnt_bin = found[2];
+        const uint32_t blo = lo + (bin << shift);
+        if (rem == cnt_bin) {  // the whole bin is taken: keys >= blo are exactly the top M
+            bin_hi = blo;
+            bin_lo = blo;
+            cnt_b = 0;
+            break;
+        }
+        if (cnt_bin <= 64 || shift == 0) {
+            bin_lo = blo;
+            bin_hi = (uint64_t)blo + ((uint64_t)1 << shift);
+            cnt_b = cnt_bin;
+            need = rem;
+            tied = shift == 0;
+            break;
+        }
+        lo = blo;
+        width = shift;
+        need = rem;
+        __syncthreads();  // found[] is rewritten by the next pass
+    }
+    // ---- mark the keys above the boundary bin; collect the boundary keys ----
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int s = k * NT + tid;
+        const uint32_t u = keyreg[k];
+        if (s < L && (uint64_t)u >= bin_hi) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
+        if (cnt_b > 0 && s < L && u >= bin_lo && (uint64_t)u < bin_hi) {
+            if (tied) {
+                atomicOr(&eqmap[s >> 5], 1u << (s & 31));
+            } else {
+                const uint32_t slot = atomicAdd(&found[3], 1u);
+                if (slot < 64u) {
+                    cand_key[slot] = u;
+                    cand_pos[slot] = (uint32_t)s;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    if (cnt_b > 0 && !tied) {
+        // exact rank among the boundary keys: higher key first, lower position on ties
+        const uint32_t C = min(cnt_b, 64u);
+        const bool mine = (uint32_t)lane < C;
+        const uint32_t ku = mine ? cand_key[lane] : 0u, pu = mine ? cand_pos[lane] : 0xFFFFFFFFu;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < C; ++j) {
+            const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ku, (int)j);
+            const uint32_t pj = (uint32_t)__builtin_amdgcn_readlane((int)pu, (int)j);
+            rank += (kj > ku || (kj == ku && pj < pu)) ? 1u : 0u;
+        }
+        if (mine && rank < need) atomicOr(&bitmap[pu >> 5], 1u << (pu & 31));
+        wave_lds_sync();
+    }
+    // ---- ordered write-out: lane l walks bitmap words [WPL*l, WPL*l + WPL);
+    // a position's slot is (selected before it) + min(tied before it, need) ----
+    uint32_t gcnt = 0, ecnt = 0;
+#pragma unroll
+    for (int e = 0; e < WPL; ++e) {
+        const int w = WPL * lane + e;
+        gcnt += w < NWORD ? (uint32_t)__builtin_popcount(bitmap[w]) : 0u;
+        ecnt += w < NWORD ? (uint32_t)__builtin_popcount(eqmap[w]) : 0u;
+    }
+    uint32_t gpos = wave_inclusive_scan(gcnt) - gcnt;
+    uint32_t epos = wave_inclusive_scan(ecnt) - ecnt;
+    const uint32_t take = tied ? need : 0u;
+#pragma unroll
+    for (int e = 0; e < WPL; ++e) {
+        const int w = WPL * lane + e;
+        const uint32_t gw = w < NWORD ? bitmap[w] : 0u, ew = w < NWORD ? eqmap[w] : 0u;
+        uint32_t bits = gw | ew;
+        while (bits) {
+            const int bit = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int s = 32 * w + bit;
+            if ((gw >> bit) & 1u) {
+                const uint32_t pos = gpos + min(epos, take);
+                if (pos < (uint32_t)M) out[pos] = s;
+                ++gpos;
+            } else {
+                if (epos < take) {
+                    const uint32_t pos = gpos + epos;
+                    if (pos < (uint32_t)M) out[pos] = s;
+                }
+                ++epos;
+            }
+        }
+    }
+}
+
 template <typename T, int D, int DI, int HIPAD>
 hipError_t launch_ss(const DecodeScoreArgs &a, hipStream_t s) {
     const int n_state = a.B * a.Hq;
@@ -394,10 +615,17 @@ hipError_t launch_decode_select(const float *scores, const int64_t *cu, int B, i
                            max_ctx, idx);                                                         \
         return hipGetLastError();                                                                 \
     }
+#define LISA_TOPM(NT_, E)                                                                         \
+    if (max_ctx <= (E) * (NT_)) {                                                                 \
+        hipLaunchKernelGGL((decode_topm_kernel<NT_, E>), grid, dim3(NT_), 0, s, scores, cu, G, M,   \
+                           max_ctx, idx);                                                         \
+        return hipGetLastError();                                                                 \
+    }
     // keys per thread stay in registers: 1024 threads (128 VGPRs) for short
     // contexts, 768 threads (170 VGPRs) for longer ones
-    LISA_SEL(1024, 8) LISA_SEL(1024, 17) LISA_SEL(768, 43) LISA_SEL(768, 86)
+    LISA_TOPM(1024, 8) LISA_TOPM(1024, 17) LISA_SEL(768, 43) LISA_SEL(768, 86)
 #undef LISA_SEL
+#undef LISA_TOPM
     return hipErrorInvalidValue;  // longer contexts are rejected by the API layer
 }
 
