@@ -368,13 +368,62 @@ __global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
 }
 
 // ---------------------------------------------------------------------------
+// One wave: the m-th largest of c 32-bit keys kr[e] (element e*64 + lane) by
+// four 8-bit radix passes over a 256-bin LDS histogram.  theta is that key;
+// take_eq is how many keys equal to theta belong to the top m (the earliest
+// elements, as ties go to the lower position).
+template <int NE>
+__device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32_t *hist,
+                             uint32_t &theta, uint32_t &take_eq) {
+    const int lane = threadIdx.x & 63;
+    uint32_t prefix = 0u, need = m;
+#pragma unroll 1
+    for (int p = 0; p < 4; ++p) {
+        const int sh = 24 - 8 * p;
+        *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const bool live = k * 64 + lane < c && (p == 0 || (kr[k] >> (sh + 8)) == prefix);
+            if (live) atomicAdd(&hist[(kr[k] >> sh) & 255u], 1u);
+        }
+        wave_lds_sync();
+        const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
+        const uint32_t lsum = h[0] + h[1] + h[2] + h[3];
+        const uint32_t incl = wave_inclusive_scan(lsum);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        uint32_t run = total - incl;  // keys in the bins of higher lanes
+        int fb = -1;
+        uint32_t fneed = 0;
+#pragma unroll
+        for (int bb = 3; bb >= 0; --bb) {
+            if (fb < 0 && run < need && run + h[bb] >= need) {
+                fb = 4 * lane + bb;
+                fneed = need - run;
+            }
+            run += h[bb];
+        }
+        const int src = __ffsll((unsigned long long)__ballot(fb >= 0)) - 1;
+        fb = __builtin_amdgcn_readlane(fb, src);
+        fneed = (uint32_t)__builtin_amdgcn_readlane((int)fneed, src);
+        prefix = (prefix << 8) | (uint32_t)fb;
+        need = fneed;
+        wave_lds_sync();
+    }
+    theta = prefix;
+    take_eq = need;
+}
+
+// ---------------------------------------------------------------------------
 // Top-M select of one (sequence, group) with few block barriers: NT threads,
-// thread t holding the order keys of positions t, t+NT, ... in registers.
+// the keys in registers, wave w owning the contiguous positions
+// w*EPT*64 .. (w+1)*EPT*64 - 1.
+//  0. long sequences (L >= 8M) try a shortcut first (described at the code);
 //  1. key range by wave reductions (one barrier);
-//  2. 2048-bin histogram passes over the live range as above, but the bin
-//     holding the M-th largest key is found by wave 0 alone (32 bins a lane,
-//     one wave scan) -- three barriers a pass; passes stop as soon as that
-//     bin is taken whole or holds at most 64 keys;
+//  2. 2048-bin histogram passes over the live key range (bins are
+//     (key - lo) >> shift), the bin holding the M-th largest key found by
+//     wave 0 alone (32 bins a lane, one wave scan) -- three barriers a pass;
+//     passes stop as soon as that bin is taken whole or holds at most 64 keys;
 //  3. those boundary keys (key, position) are appended to LDS and wave 0
 //     ranks them exactly (higher key, then lower position) and marks the
 //     `need` best in an LDS bitmap of positions, while every thread marks its
@@ -404,23 +453,118 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, co
         for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
         return;
     }
-    // all loads unconditional (positions >= L read zeros through the
-    // descriptor) so they are in flight together
+    // wave w holds positions w*EPT*64 + k*64 + lane: each wave owns one
+    // contiguous range, so (wave, round, lane) order is position order.  All
+    // loads are unconditional (positions >= L read zeros through the
+    // descriptor) so they are in flight together.
+    const int wbase = wave * (EPT * 64);
+    auto pos_of = [&](int k) { return wbase + k * 64 + lane; };
     const rsrc_t srs = make_rsrc(sc, (uint32_t)L * 4u);
     uint32_t keyreg[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k)
-        keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(k * NT + tid) * 4u, 0u, 0);
+        keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)pos_of(k) * 4u, 0u, 0);
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        const int s = k * NT + tid;
+        const int s = pos_of(k);
         keyreg[k] = order_key(__uint_as_float(keyreg[k]));
         if (s < L) {
             kmin = min(kmin, keyreg[k]);
             kmax = max(kmax, keyreg[k]);
         }
     }
+
+    // ---- shortcut: per-wave thresholds, candidates packed for one wave ----
+    // Each wave picks a threshold T_w from its own keys (the R-th largest of
+    // its lanes' two largest, R a few standard deviations above the wave's
+    // expected share of the top M) and keeps its keys >= T_w.  If the kept
+    // keys number between M and 1024 they are packed in position order, and
+    // one wave finds their M-th largest theta.  When no T_w exceeds theta,
+    // every key >= theta was kept, so the top M (ties to the lower position)
+    // are exactly the kept ones that rank in the first M; otherwise, or when
+    // the count is out of range, the exact passes below run.
+    constexpr int CAP = 1024;
+    __shared__ uint32_t wcnt[NW], wthr[NW], verdict;
+    __shared__ uint32_t fkey[CAP], fpos[CAP];
+    if (L >= 8 * M) {
+        const int nv = min(max(L - wbase, 0), EPT * 64);  // this wave's valid keys
+        uint32_t a1 = 0u, a2 = 0u;                       // this lane's two largest
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const uint32_t u = pos_of(k) < L ? keyreg[k] : 0u;
+            a2 = max(a2, min(a1, u));
+            a1 = max(a1, u);
+        }
+        const float mu = (float)M * (float)nv / (float)L;
+        const uint32_t R = (uint32_t)fminf(128.0f, ceilf(mu + 4.0f * sqrtf(mu) + 4.0f));
+        uint32_t T = 0u;  // largest T with at least R of the 128 values >= T
+#pragma unroll 1
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            const uint32_t c = (uint32_t)__popcll(__ballot(a1 >= cand)) + (uint32_t)__popcll(__ballot(a2 >= cand));
+            T = c >= R ? cand : T;
+        }
+        uint32_t cw = 0;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) cw += (uint32_t)__popcll(__ballot(pos_of(k) < L && keyreg[k] >= T));
+        if (lane == 0) {
+            wcnt[wave] = cw;
+            wthr[wave] = nv > 0 ? T : 0u;
+        }
+        __syncthreads();
+        uint32_t C = 0, pre = 0, Tmax = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            pre += w < wave ? wcnt[w] : 0u;
+            C += wcnt[w];
+            Tmax = max(Tmax, wthr[w]);
+        }
+        if (C >= (uint32_t)M && C <= (uint32_t)CAP) {
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int s = pos_of(k);
+                const bool sel = s < L && keyreg[k] >= T;
+                const uint64_t bm = __ballot(sel);
+                if (sel) {
+                    fkey[pre + mbcnt64(bm)] = keyreg[k];
+                    fpos[pre + mbcnt64(bm)] = (uint32_t)s;
+                }
+                pre += (uint32_t)__popcll(bm);
+            }
+            __syncthreads();
+            if (wave == 0) {
+                constexpr int NE = CAP / 64;
+                uint32_t kr[NE];
+#pragma unroll
+                for (int e = 0; e < NE; ++e) kr[e] = e * 64 + lane < (int)C ? fkey[e * 64 + lane] : 0u;
+                uint32_t theta, take_eq;
+                wave_kth_u32<NE>(kr, (int)C, (uint32_t)M, hist, theta, take_eq);
+                const bool ok = Tmax <= theta;
+                if (ok) {
+                    uint32_t base = 0, eq_seen = 0;
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) {
+                        const bool valid = e * 64 + lane < (int)C;
+                        const bool gt = valid && kr[e] > theta;
+                        const bool eq = valid && kr[e] == theta;
+                        const uint64_t em = __ballot(eq);
+                        const uint32_t er = eq_seen + mbcnt64(em);
+                        eq_seen += (uint32_t)__popcll(em);
+                        const bool keep = gt || (eq && er < take_eq);
+                        const uint64_t km = __ballot(keep);
+                        const uint32_t pos = base + mbcnt64(km);
+                        base += (uint32_t)__popcll(km);
+                        if (keep && pos < (uint32_t)M) out[pos] = (int32_t)fpos[e * 64 + lane];
+                    }
+                }
+                if (lane == 0) verdict = ok ? 1u : 0u;
+            }
+            __syncthreads();
+            if (verdict) return;
+        }
+    }
+
     for (int w = tid; w < NWORD; w += NT) {
         bitmap[w] = 0u;
         eqmap[w] = 0u;
@@ -453,7 +597,7 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, co
         const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
-            const int s = k * NT + tid;
+            const int s = pos_of(k);
             const uint32_t u = keyreg[k];
             if (s < L && u >= lo && (uint64_t)u < hi_excl) atomicAdd(&hist[(u - lo) >> shift], 1u);
         }
@@ -513,7 +657,7 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, co
     // ---- mark the keys above the boundary bin; collect the boundary keys ----
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        const int s = k * NT + tid;
+        const int s = pos_of(k);
         const uint32_t u = keyreg[k];
         if (s < L && (uint64_t)u >= bin_hi) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
         if (cnt_b > 0 && s < L && u >= bin_lo && (uint64_t)u < bin_hi) {
