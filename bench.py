@@ -82,13 +82,14 @@ def decode_bytes(cfg, lengths):
 # pattern, the sources that kernel is built from)
 STAGE_KERNELS = {
     "indexer_topm": (r"indexer_topm_kernel<", ["indexer.hip", "common.hpp", "kernels.hpp"]),
-    "sparse_gate_prefill": (r"sparse_gate_kernel<[^>]*, false,", ["sparse.hip", "common.hpp", "kernels.hpp"]),
+    "sparse_gate_prefill": (r"sparse_prefill_wave_kernel<|sparse_gate_kernel<[^>]*, false,",
+                            ["sparse.hip", "common.hpp", "kernels.hpp"]),
     "sparse_gate_decode": (r"sparse_gate_kernel<[^>]*, true,", ["sparse.hip", "common.hpp", "kernels.hpp"]),
     "linear_chunk_state": (r"chunk_state_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
     "linear_prefix_scan": (r"prefix_scan_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
     "linear_chunk_output": (r"chunk_output_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
     "decode_score_state": (r"decode_score_state_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
-    "decode_select": (r"decode_select_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
+    "decode_select": (r"decode_topm_kernel<|decode_select_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
 }
 
 
