@@ -59,6 +59,11 @@ struct CandBuf {
 // Keep exactly the first m of the c buffered candidates in the order
 // (higher score, lower index); stable, so the buffer stays sorted by index.
 // Whole wave, uniform control flow.  Returns the order key of the m-th.
+// The threshold is found by 256-bin histogram passes over the live range of
+// order keys, [min, max] first (buffered candidates sit in a narrow band, so
+// fixed 8-bit digits of the key would waste passes on common high bits); a
+// pass stops as soon as the bin holding the m-th key is taken whole, or holds
+// a single key value (ties: the earliest buffer positions win).
 template <int NE>
 __device__ uint32_t wave_select(CandBuf buf, int c, int m, uint32_t *hist) {
     const int lane = threadIdx.x & 63;
@@ -66,6 +71,7 @@ __device__ uint32_t wave_select(CandBuf buf, int c, int m, uint32_t *hist) {
     float sc[NE];
     uint32_t ss[NE];
     uint32_t u[NE];
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
         const int e = k * 64 + lane;
@@ -73,59 +79,82 @@ __device__ uint32_t wave_select(CandBuf buf, int c, int m, uint32_t *hist) {
             sc[k] = buf.sc[e];
             ss[k] = buf.key[e];
             u[k] = order_key(sc[k]);
+            kmin = min(kmin, u[k]);
+            kmax = max(kmax, u[k]);
         } else {
             sc[k] = 0.0f;
             ss[k] = 0u;
             u[k] = 0u;
         }
     }
-    uint32_t prefix = 0u, need = (uint32_t)m;
+    uint32_t lo = wave_min_u32(kmin);
+    const uint32_t span = wave_max_u32(kmax) - lo;
+    int width = span == 0 ? 0 : 32 - __builtin_clz(span);  // bits of key - lo
+    uint32_t need = (uint32_t)m;
+    uint32_t theta;      // keys > theta are kept, and keys == theta up to take_eq,
+    uint32_t take_eq;    // or (whole_bin) every key >= theta
+    bool whole_bin;
 #pragma unroll 1
-    for (int p = 0; p < 4; ++p) {
-        const int sh = 24 - 8 * p;
+    for (;;) {
+        const int shift = width > 8 ? width - 8 : 0;
         *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
+        const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
 #pragma unroll
         for (int k = 0; k < NE; ++k) {
-            const bool match = (k * 64 + lane < c) && (p == 0 || (u[k] >> (sh + 8)) == prefix);
-            if (match) atomicAdd(&hist[(u[k] >> sh) & 255u], 1u);
+            if (k * 64 + lane < c && u[k] >= lo && (uint64_t)u[k] < hi_excl)
+                atomicAdd(&hist[(u[k] - lo) >> shift], 1u);
         }
         wave_lds_sync();
         const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
         const uint32_t lsum = h[0] + h[1] + h[2] + h[3];
         const uint32_t incl = wave_inclusive_scan(lsum);
         const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-        uint32_t run = total - incl;  // candidates in bins above this lane's four
+        uint32_t run = total - incl;  // keys in the bins of higher lanes
         int fb = -1;
-        uint32_t fneed = 0;
+        uint32_t fneed = 0, fcnt = 0;
 #pragma unroll
         for (int bb = 3; bb >= 0; --bb) {
-            const uint32_t hb = h[bb];
-            if (fb < 0 && run < need && run + hb >= need) {
+            if (fb < 0 && run < need && run + h[bb] >= need) {
                 fb = 4 * lane + bb;
                 fneed = need - run;
+                fcnt = h[bb];
             }
-            run += hb;
+            run += h[bb];
         }
-        const uint64_t fm = __ballot(fb >= 0);
-        const int src = __ffsll((unsigned long long)fm) - 1;
+        const int src = __ffsll((unsigned long long)__ballot(fb >= 0)) - 1;
         fb = __builtin_amdgcn_readlane(fb, src);
         fneed = (uint32_t)__builtin_amdgcn_readlane((int)fneed, src);
-        prefix = (prefix << 8) | (uint32_t)fb;
-        need = fneed;
+        fcnt = (uint32_t)__builtin_amdgcn_readlane((int)fcnt, src);
         wave_lds_sync();
+        const uint32_t blo = lo + ((uint32_t)fb << shift);
+        if (fneed == fcnt) {  // the whole bin is kept: keys >= blo are exactly the first m
+            theta = blo;
+            take_eq = 0u;
+            whole_bin = true;
+            break;
+        }
+        if (shift == 0) {  // one key value: the earliest fneed of them
+            theta = blo;
+            take_eq = fneed;
+            whole_bin = false;
+            break;
+        }
+        lo = blo;
+        width = shift;
+        need = fneed;
     }
-    const uint32_t theta = prefix, take_eq = need;
-    uint32_t base = 0u, eq_seen = 0u;
+    uint32_t base = 0u, eq_seen = 0u, kth = 0xFFFFFFFFu;
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
         const bool valid = k * 64 + lane < c;
-        const bool gt = valid && u[k] > theta;
-        const bool eq = valid && u[k] == theta;
+        const bool gt = valid && (whole_bin ? u[k] >= theta : u[k] > theta);
+        const bool eq = valid && !whole_bin && u[k] == theta;
         const uint64_t em = __ballot(eq);
         const uint32_t er = eq_seen + mbcnt64(em);
         eq_seen += (uint32_t)__popcll(em);
         const bool keep = gt || (eq && er < take_eq);
+        if (keep) kth = min(kth, u[k]);
         const uint64_t km = __ballot(keep);
         const uint32_t pos = base + mbcnt64(km);
         base += (uint32_t)__popcll(km);
@@ -135,7 +164,7 @@ __device__ uint32_t wave_select(CandBuf buf, int c, int m, uint32_t *hist) {
         }
     }
     wave_lds_sync();
-    return theta;
+    return wave_min_u32(kth);
 }
 
 template <int NE>
