@@ -208,10 +208,23 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
                          const void *w_idx, const void *gate, const float *state_in, void *out,
                          float *state_out, int32_t *topm_out, void *workspace,
                          size_t workspace_bytes, lisa_stream_t stream) {
+    return lisa_prefill_continue(dims, B, 0, n, q, k, v, q_idx, k_idx, w_idx, gate, state_in, out,
+                                 state_out, topm_out, workspace, workspace_bytes, stream);
+}
+
+lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past, int32_t n,
+                                  const void *q, const void *k, const void *v, const void *q_idx,
+                                  const void *k_idx, const void *w_idx, const void *gate,
+                                  const float *state_in, void *out, float *state_out,
+                                  int32_t *topm_out, void *workspace, size_t workspace_bytes,
+                                  lisa_stream_t stream) {
     lisa_status st = check_dims(dims, true);
     if (st) return st;
-    if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
-    if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
+    if (B < 0 || n < 0 || past < 0)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, past=%d, n=%d must be >= 0", B, past, n);
+    if ((int64_t)past + n > 32768)
+        return fail(LISA_ERR_UNSUPPORTED, "past + n = %lld above the supported 32768",
+                    (long long)past + n);
     if (B == 0 || n == 0) return ok();
     LISA_NEED(q, "q");
     LISA_NEED(k, "k");
@@ -248,6 +261,8 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
     la.G = G;
     la.r = Hq / G;
     la.nC = (n + 63) / 64;
+    la.kv_rows = past + n;
+    la.kv_off = past;
     la.per_head = state_in != nullptr;
     LISA_HIP(timed(ST_LIN_STATE, s, [&] { return lisa::launch_linear_chunk_state(la, dims->dtype, D, s); }),
              "linear chunk-state launch");
@@ -266,6 +281,7 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
     ia.G = G;
     ia.HI = dims->idx_heads;
     ia.M = dims->top_m;
+    ia.past = past;
     LISA_HIP(timed(ST_INDEXER, s, [&] { return lisa::launch_indexer_prefill(ia, dims->dtype, dims->idx_dim, s); }),
              "indexer launch");
 
@@ -284,7 +300,8 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
     sa.G = G;
     sa.r = Hq / G;
     sa.M = dims->top_m;
-    sa.max_ctx = n;
+    sa.max_ctx = past + n;
+    sa.past = past;
     sa.scale_log2 = scale_log2(dims);
     sa.units = B * n * G;
     LISA_HIP(timed(ST_SPARSE_PREFILL, s, [&] { return lisa::launch_sparse_gate(sa, dims->dtype, D, false, s); }),

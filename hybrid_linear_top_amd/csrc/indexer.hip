@@ -288,18 +288,20 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, grp = lane >> 4;
-    const int G = a.G, n = a.n, HI = a.HI, M = a.M;
-    const int nqb = (n + kQW - 1) / kQW;
+    // queries are the rows 0..nq-1 of q_idx / w_idx / idx; query row t sits at
+    // position p0 + t, and the keys are positions 0..nk-1 (nk = p0 + nq)
+    const int G = a.G, nq = a.n, p0 = a.past, nk = a.past + a.n, HI = a.HI, M = a.M;
+    const int nqb = (nq + kQW - 1) / kQW;
     // Block order: group fastest (with G | 8 every XCD sees a single group's
     // keys), latest (heaviest) query blocks first.
     const int L = blockIdx.x;
     const int g = L % G, rest = L / G, b = rest % a.B, qblk = nqb - 1 - rest / a.B;
-    const int qw0 = qblk * kQW;
-    const int t_hi = min(n, qw0 + kQW) - 1;  // last query of this wave
+    const int qw0 = p0 + qblk * kQW;          // position of the wave's first query
+    const int t_hi = min(nk, qw0 + kQW) - 1;  // position of its last query
     const int ntiles = t_hi / kKT + 1;
 
     const T *qI = reinterpret_cast<const T *>(a.q_idx);
-    const T *kI = reinterpret_cast<const T *>(a.k_idx) + ((size_t)b * n * G + g) * DI;
+    const T *kI = reinterpret_cast<const T *>(a.k_idx) + ((size_t)b * nk * G + g) * DI;
     const T *wI = reinterpret_cast<const T *>(a.w_idx);
     const size_t krs = (size_t)G * DI;  // key row stride
 
@@ -309,15 +311,15 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     int tq[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        tq[qb] = qw0 + qb * 4 + grp;  // the query whose four heads this lane accumulates
-        const int tA = qw0 + qb * 4 + col / 4;  // the query of this lane's A row
+        tq[qb] = qw0 + qb * 4 + grp;  // position of the query whose four heads this lane accumulates
+        const int tA = qw0 - p0 + qb * 4 + col / 4;  // row of the query of this lane's A row
 #pragma unroll
         for (int hh = 0; hh < HH; ++hh) {
             const int headA = hh * 4 + (col & 3);
 #pragma unroll
             for (int kc = 0; kc < C::KD; ++kc) {
-                if (tA < n && headA < HI)
-                    af[qb][hh][kc].load(qI + ((((size_t)b * n + tA) * G + g) * HI + headA) * DI +
+                if (tA < nq && headA < HI)
+                    af[qb][hh][kc].load(qI + ((((size_t)b * nq + tA) * G + g) * HI + headA) * DI +
                                         kc * 32 + grp * 8);
                 else
                     af[qb][hh][kc].zero();
@@ -325,8 +327,8 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int head = hh * 4 + i;
-                wv[qb][hh][i] = (tq[qb] < n && head < HI)
-                                    ? Elt<T>::to_f32(wI[(((size_t)b * n + tq[qb]) * G + g) * HI + head])
+                wv[qb][hh][i] = (tq[qb] < nk && head < HI)
+                                    ? Elt<T>::to_f32(wI[(((size_t)b * nq + tq[qb] - p0) * G + g) * HI + head])
                                     : 0.0f;
             }
         }
@@ -336,13 +338,13 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         cnt[qb] = 0;
-        tau[qb] = tq[qb] < n ? -INFINITY : INFINITY;  // queries past n accept nothing
+        tau[qb] = tq[qb] < nk ? -INFINITY : INFINITY;  // padding queries accept nothing
     }
 
     // B fragments of one key tile: key 4*col + cb, dims 32*kc + 8*grp .. +7,
-    // through a per-tile buffer descriptor (keys >= n read as zeros)
+    // through a per-tile buffer descriptor (keys >= nk read as zeros)
     constexpr uint32_t EB = Elt<T>::kBytes;
-    const uint32_t key_bytes = (uint32_t)n * (uint32_t)krs * EB;
+    const uint32_t key_bytes = (uint32_t)nk * (uint32_t)krs * EB;
     uint32_t voff[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) voff[cb] = ((uint32_t)(4 * col + cb) * (uint32_t)krs + grp * 8) * EB;
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     // empty descriptor (all zeros, no memory access).  A skipped load on one
     // path would make the wait counts of the merged paths wait for the
     // prefetched tiles as well.
-    const int knull = (n + kKT - 1) / kKT;
+    const int knull = (nk + kKT - 1) / kKT;
     auto tile_or_null = [&](int kt, int lim) { return kt < lim ? kt : knull; };
 
     // ---- starting threshold from a key sample ---------------------------------
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                 lo = up ? mid : lo;
                 hi = up ? hi : mid;
             }
-            if (tq[qb] < n) tau[qb] = lo;
+            if (tq[qb] < nk) tau[qb] = lo;
         }
     }
 
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         bool fail[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            fail[qb] = tq[qb] < n && cnt[qb] < min(M, tq[qb] + 1);
+            fail[qb] = tq[qb] < nk && cnt[qb] < min(M, tq[qb] + 1);
             redo |= __ballot(fail[qb]);
         }
         if (!redo || pass == 1) break;
@@ -571,12 +573,12 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 #pragma unroll 1
         for (int gg = 0; gg < 4; ++gg) {
             const int t = qw0 + qb * 4 + gg;
-            if (t >= n) continue;
+            if (t >= nk) continue;
             const CandBuf qbuf = qbuf_of(qb * 4 + gg);
             const int c = __builtin_amdgcn_readlane(cnt[qb], 16 * gg);
             const int m = min(M, t + 1);
             if (c > m) wave_select<C::NE>(qbuf, c, m, hist);
-            int32_t *dst = a.idx + (((size_t)b * n + t) * G + g) * M;
+            int32_t *dst = a.idx + (((size_t)b * nq + t - p0) * G + g) * M;
             for (int i = lane; i < M; i += 64) dst[i] = i < m ? (int32_t)qbuf.key[i] : -1;
         }
     }

@@ -30,7 +30,7 @@ hipError_t launch_decode_select(const float *scores, const int64_t *cu, int B, i
 // ---- sparse attention + gate (prefill and decode) -------------------------
 struct SparseArgs {
     const void *q;        // prefill [B,n,Hq,d]; decode [B,Hq,d]
-    const void *k;        // prefill [B,n,G,d];  decode cache [sumL,G,d]
+    const void *k;        // prefill [B,past+n,G,d];  decode cache [sumL,G,d]
     const void *v;
     const int64_t *cu;    // decode only
     const int32_t *idx;   // [units, M]  (units = B*n*G or B*G)
@@ -38,6 +38,7 @@ struct SparseArgs {
     const void *gate;     // prefill [B,n,Hq]; decode [B,Hq]
     void *out;            // prefill [B,n,Hq,d]; decode [B,Hq,d]
     int B, n, Hq, G, r, M, max_ctx;
+    int past;             // prefill: query t (0-based among the n) sits at position past + t
     float scale_log2;     // softmax scale * log2(e)
     int units;
 };
@@ -45,13 +46,14 @@ hipError_t launch_sparse_gate(const SparseArgs &a, int dtype, int d, bool decode
 
 // ---- prefill: chunked linear attention -----------------------------------
 struct LinearArgs {
-    const void *q, *k, *v;       // [B,n,Hq,d], [B,n,G,d]
+    const void *q, *k, *v;       // [B,n,Hq,d]; k, v [B,kv_rows,G,d], rows kv_off.. are the n tokens
     const float *state_in;       // [B,Hq,d,d] or null
     float *state_out;            // [B,Hq,d,d] or null
     float *dS;                   // [B,G,nC,d,d] fp32: per-chunk K^T V, stored transposed [j][i]
     void *P;                     // [B,Hp,nC,d,d] dtype: exclusive prefix states, transposed
     void *out;                   // [B,n,Hq,d]: receives o_lin
     int B, n, Hq, G, r, nC;
+    int kv_rows, kv_off;
     int per_head;                // 1 if state_in != null (prefix states per query head)
 };
 hipError_t launch_linear_chunk_state(const LinearArgs &a, int dtype, int d, hipStream_t s);
@@ -61,10 +63,11 @@ hipError_t launch_linear_chunk_output(const LinearArgs &a, int dtype, int d, hip
 // ---- prefill: indexer + streaming top-M ------------------------------------
 struct IndexerArgs {
     const void *q_idx;   // [B,n,G,HI,dI]
-    const void *k_idx;   // [B,n,G,dI]
+    const void *k_idx;   // [B,past+n,G,dI]
     const void *w_idx;   // [B,n,G,HI]
-    int32_t *idx;        // [B,n,G,M]
+    int32_t *idx;        // [B,n,G,M]: key positions in 0..past+t
     int B, n, G, HI, M;
+    int past;            // query t (0-based among the n) sits at position past + t
 };
 hipError_t launch_indexer_prefill(const IndexerArgs &a, int dtype, int dI, hipStream_t s);
 

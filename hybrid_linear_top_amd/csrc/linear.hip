@@ -72,8 +72,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(LinearArgs a) {
     const int blk = blockIdx.x, c = blk % a.nC, bg = blk / a.nC, g = bg % a.G, b = bg / a.G;
     const int t0 = c * kC, valid = min(kC, a.n - t0);
     const size_t rstride = (size_t)a.G * D;
-    const T *kp = reinterpret_cast<const T *>(a.k) + (((size_t)b * a.n + t0) * a.G + g) * D;
-    const T *vp = reinterpret_cast<const T *>(a.v) + (((size_t)b * a.n + t0) * a.G + g) * D;
+    const T *kp = reinterpret_cast<const T *>(a.k) + (((size_t)b * a.kv_rows + a.kv_off + t0) * a.G + g) * D;
+    const T *vp = reinterpret_cast<const T *>(a.v) + (((size_t)b * a.kv_rows + a.kv_off + t0) * a.G + g) * D;
     stage_transposed<T, D>(kt, TS, kp, rstride, valid);
     stage_transposed<T, D>(vt, TS, vp, rstride, valid);
     __syncthreads();
@@ -163,8 +163,8 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
     const int blk = blockIdx.x, c = blk % a.nC, bg = blk / a.nC, g = bg % a.G, b = bg / a.G;
     const int t0 = c * kC, valid = min(kC, a.n - t0);
     const size_t rstride = (size_t)a.G * D;
-    const T *kp = reinterpret_cast<const T *>(a.k) + (((size_t)b * a.n + t0) * a.G + g) * D;
-    const T *vp = reinterpret_cast<const T *>(a.v) + (((size_t)b * a.n + t0) * a.G + g) * D;
+    const T *kp = reinterpret_cast<const T *>(a.k) + (((size_t)b * a.kv_rows + a.kv_off + t0) * a.G + g) * D;
+    const T *vp = reinterpret_cast<const T *>(a.v) + (((size_t)b * a.kv_rows + a.kv_off + t0) * a.G + g) * D;
     const T *P = reinterpret_cast<const T *>(a.P);
     stage_rows<T, D>(ks_, KS, kp, rstride, kC, valid);
     stage_transposed<T, D>(vt_, VTS, vp, rstride, valid);

@@ -77,11 +77,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
             outp = reinterpret_cast<T *>(a.out) + lin_off;
         } else {
             const int g = u % G, bt = u / G, b = bt / a.n;
-            smax = bt % a.n;
+            smax = a.past + bt % a.n;  // the query's position: keys 0..smax are visible
             nvalid = min(M, smax + 1);
             qrows = reinterpret_cast<const T *>(a.q) + ((size_t)bt * a.Hq + g * r) * D;
-            kbase = reinterpret_cast<const T *>(a.k) + ((size_t)b * a.n * G + g) * D;
-            vbase = reinterpret_cast<const T *>(a.v) + ((size_t)b * a.n * G + g) * D;
+            kbase = reinterpret_cast<const T *>(a.k) + ((size_t)b * (a.past + a.n) * G + g) * D;
+            vbase = reinterpret_cast<const T *>(a.v) + ((size_t)b * (a.past + a.n) * G + g) * D;
             zp = reinterpret_cast<const T *>(a.gate) + (size_t)bt * a.Hq + g * r;
             lin_off = ((size_t)bt * a.Hq + g * r) * D;
             outp = reinterpret_cast<T *>(a.out) + lin_off;
@@ -309,11 +309,11 @@ void sparse_prefill_wave_kernel(SparseArgs a) {
     const int G = a.G, r = a.r, M = a.M;
     const int u = (lu % (a.B * a.n)) * G + lu / (a.B * a.n);
     const int g = u % G, bt = u / G, b = bt / a.n;
-    const int smax = bt % a.n;                // the query position: keys 0..t are visible
+    const int smax = a.past + bt % a.n;       // the query's position: keys 0..smax are visible
     const int nvalid = min(M, smax + 1);
     const uint16_t *qrows = reinterpret_cast<const uint16_t *>(a.q) + ((size_t)bt * a.Hq + g * r) * D;
-    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k) + ((size_t)b * a.n * G + g) * D;
-    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v) + ((size_t)b * a.n * G + g) * D;
+    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k) + ((size_t)b * (a.past + a.n) * G + g) * D;
+    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v) + ((size_t)b * (a.past + a.n) * G + g) * D;
     const uint32_t row_bytes = (uint32_t)G * D * 2;
     const uint32_t vis_bytes = (uint32_t)(smax + 1) * row_bytes;
     const rsrc_t krs = make_rsrc(kbase, vis_bytes), vrs = make_rsrc(vbase, vis_bytes);

@@ -23,7 +23,8 @@ LISA_ERR_HIP = 4
 LISA_F32 = 0
 LISA_BF16 = 1
 
-EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill", "lisa_decode_workspace_bytes",
+EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill", "lisa_prefill_continue",
+           "lisa_decode_workspace_bytes",
            "lisa_decode_step", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
            "lisa_build_info"]
 
@@ -52,6 +53,8 @@ def _load(path: str = LIB_PATH):
     lib.lisa_prefill_workspace_bytes.restype = ctypes.c_int
     lib.lisa_prefill.argtypes = [dp, i32, i32] + [vp] * 7 + [vp, vp, vp, vp, vp, sz, vp]
     lib.lisa_prefill.restype = ctypes.c_int
+    lib.lisa_prefill_continue.argtypes = [dp, i32, i32, i32] + [vp] * 7 + [vp, vp, vp, vp, vp, sz, vp]
+    lib.lisa_prefill_continue.restype = ctypes.c_int
     lib.lisa_decode_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
     lib.lisa_decode_workspace_bytes.restype = ctypes.c_int
     lib.lisa_decode_step.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp, sz, vp]
@@ -104,6 +107,15 @@ def lisa_prefill(dims, B, n, q, k, v, q_idx, k_idx, w_idx, gate, state_in, out, 
     """Raw call; returns the status code (0 = LISA_OK)."""
     return _lib.lisa_prefill(ctypes.byref(dims), B, n, q, k, v, q_idx, k_idx, w_idx, gate,
                              state_in, out, state_out, topm_out, workspace, workspace_bytes, stream)
+
+
+def lisa_prefill_continue(dims, B, past, n, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx, gate,
+                          state_in, out, state_out, topm_out, workspace, workspace_bytes,
+                          stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_prefill_continue(ctypes.byref(dims), B, past, n, q, k_cache, v_cache, q_idx,
+                                      k_idx_cache, w_idx, gate, state_in, out, state_out, topm_out,
+                                      workspace, workspace_bytes, stream)
 
 
 def lisa_decode_step(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
@@ -172,6 +184,32 @@ def prefill(dims: LisaDims, q, k, v, q_idx, k_idx, w_idx, gate, state_in=None, o
     _check(lisa_prefill(dims, B, n, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
                         _ptr(w_idx), _ptr(gate), _ptr(state_in), _ptr(out), _ptr(state_out),
                         _ptr(topm_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, state_out, topm_out
+
+
+def prefill_continue(dims: LisaDims, past: int, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
+                     gate, state_in=None, out=None, state_out=None, topm_out=None,
+                     workspace=None, stream=None):
+    """n new tokens against caches of past + n rows (torch device tensors;
+    q [B,n,Hq,d], k_cache [B,past+n,Hkv,d], ...).  Allocates missing outputs.
+    Returns (out, state_out, topm_out)."""
+    import torch
+    B, n = int(q.shape[0]), int(q.shape[1])
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None:
+        state_out = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
+                                dtype=torch.float32, device=dev)
+    if topm_out is None:
+        topm_out = torch.empty((B, n, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev)
+    wsb = lisa_prefill_workspace_bytes(dims, B, n)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(lisa_prefill_continue(dims, B, past, n, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(q_idx), _ptr(k_idx_cache), _ptr(w_idx), _ptr(gate),
+                                 _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(topm_out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, state_out, topm_out
 
 

@@ -11,8 +11,8 @@
  *     page, experiment-design section);
  *   - a linear-attention branch with the identity feature map and a state
  *     matrix S_t updated once per token (gptget.net, method-details);
- *   - a learned gate mixes the two outputs (arxivdaily abstract: "fused via
- *     a gating mechanism"; zhuanzhiai page: "learned gate").
+ *   - a gate mixes the two outputs (arxivdaily abstract; the zhuanzhiai page,
+ *     abstract, says the gate is learned).
  * The library is the attention core after the projections: the caller owns
  * the learned projections and passes their outputs.
  *
@@ -105,6 +105,34 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
                          const void *w_idx, const void *gate, const float *state_in, void *out,
                          float *state_out, int32_t *topm_out, void *workspace,
                          size_t workspace_bytes, lisa_stream_t stream);
+
+/*
+ * Continued prefill: n more prompt tokens of each sequence against the cache
+ * of its first `past` tokens -- the step between a prompt that was already
+ * processed and token-by-token generation.  Per position the result is the
+ * layer defined above: query row t (0-based) is position past + t, its
+ * candidates are positions 0..past+t, and the linear branch continues from
+ * S_{past-1}.  So `out` equals rows past..past+n-1 of one lisa_prefill over
+ * all past + n tokens.
+ *   q      [B, n, Hq, d]   q_idx [B, n, G, H_I, d_I]   w_idx [B, n, G, H_I]
+ *   gate   [B, n, Hq]
+ *   k_cache, v_cache [B, past + n, Hkv, d]; k_idx_cache [B, past + n, G, d_I]:
+ *          every position, the n new tokens included (rows past..).
+ *   state_in  [B, Hq, d, d] fp32 or NULL: S after the first `past` tokens
+ *          (NULL = zero, e.g. past == 0).
+ *   out    [B, n, Hq, d]; state_out [B, Hq, d, d] fp32 or NULL: S after the
+ *          last token; topm_out [B, n, G, M] int32 or NULL: positions in
+ *          0..past+t, ascending, -1 padded.
+ * The workspace is lisa_prefill_workspace_bytes(dims, B, n) (n new tokens).
+ * past + n <= 32768; n == 0 or B == 0 is a valid no-op; past == 0 is
+ * lisa_prefill.
+ */
+lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past, int32_t n,
+                                  const void *q, const void *k_cache, const void *v_cache,
+                                  const void *q_idx, const void *k_idx_cache, const void *w_idx,
+                                  const void *gate, const float *state_in, void *out,
+                                  float *state_out, int32_t *topm_out, void *workspace,
+                                  size_t workspace_bytes, lisa_stream_t stream);
 
 /* Workspace needed by lisa_decode_step for B sequences of at most max_ctx
  * visible tokens each. */

@@ -71,6 +71,29 @@ def run_prefill(cfg, inp, gate=None, state_in=None, dims=None):
             lisa.from_device(idx))
 
 
+def run_prefill_continue(cfg, inp, past, gate=None, state_in=None, dims=None):
+    """GPU prefill of the first `past` tokens (for its final state), then the
+    continued prefill of the rest against the full caches.  Returns the
+    continued call's (out, state_out, idx) for rows past..n-1."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    dims = dims or lisa.dims_from_config(cfg)
+    dv = lisa.to_device
+    gate = inp["gate"] if gate is None else gate
+    s0 = None if state_in is None else dv(np.ascontiguousarray(state_in, dtype=np.float32))
+    if past > 0:
+        head = [dv(np.ascontiguousarray(inp[k][:, :past])) for k in ("q", "k", "v", "q_idx", "k_idx", "w_idx")]
+        _, s0, _ = lisa.prefill(dims, *head, dv(np.ascontiguousarray(gate[:, :past])), state_in=s0)
+    tail = {k: dv(np.ascontiguousarray(inp[k][:, past:])) for k in ("q", "q_idx", "w_idx")}
+    caches = {k: dv(inp[k]) for k in ("k", "v", "k_idx")}
+    out, st, idx = lisa.prefill_continue(dims, past, tail["q"], caches["k"], caches["v"], tail["q_idx"],
+                                         caches["k_idx"], tail["w_idx"],
+                                         dv(np.ascontiguousarray(gate[:, past:])), state_in=s0)
+    torch.cuda.synchronize()
+    return (orc.widen(lisa.from_device(out), cfg.dtype), lisa.from_device(st).astype(np.float64),
+            lisa.from_device(idx))
+
+
 def run_decode(cfg, inp, gate=None, dims=None):
     import torch
     from hybrid_linear_top_amd import lisa
@@ -86,16 +109,31 @@ def run_decode(cfg, inp, gate=None, dims=None):
             lisa.from_device(idx))
 
 
-def prefill_parity(cfg, inp, rows=None, state_in=None, report=None):
-    """Full prefill parity (all four checks) on the listed rows (None = all)."""
+def prefill_parity(cfg, inp, rows=None, state_in=None, report=None, past=0):
+    """Full prefill parity (all four checks) on the listed rows (None = all).
+    With past > 0 the GPU side is a prefill of the first `past` tokens followed
+    by the continued prefill of the rest; the oracle is one prefill over all n
+    tokens, and the rows checked are past..n-1 (or the listed ones)."""
     dt = cfg.dtype
     B, n = inp["B"], inp["n"]
     tol = TOL[dt]
+    if rows is None and past > 0:
+        rows = list(range(past, n))
     ref = orc.prefill(inp, cfg, rows=rows, state_in=state_in)
     R = ref["rows"] if rows is not None else np.arange(n)
-    out, st, idx = run_prefill(cfg, inp, state_in=state_in)
-    osp, _, idx_p = run_prefill(cfg, inp, gate=gate_fill(inp["gate"].shape, dt, np.inf), state_in=state_in)
-    olin, _, _ = run_prefill(cfg, inp, gate=gate_fill(inp["gate"].shape, dt, -np.inf), state_in=state_in)
+    assert np.all(R >= past)
+
+    def gpu(gate=None):
+        if past == 0:
+            o, st_, ix = run_prefill(cfg, inp, gate=gate, state_in=state_in)
+            return o, st_, ix
+        o, st_, ix = run_prefill_continue(cfg, inp, past, gate=gate, state_in=state_in)
+        pad = lambda x: np.concatenate([np.zeros((B, past) + x.shape[2:], x.dtype), x], axis=1)
+        return pad(o), st_, pad(ix)
+
+    out, st, idx = gpu()
+    osp, _, idx_p = gpu(gate=gate_fill(inp["gate"].shape, dt, np.inf))
+    olin, _, _ = gpu(gate=gate_fill(inp["gate"].shape, dt, -np.inf))
     assert np.array_equal(idx, idx_p), "index sets differ between two runs"
     qI, kI, w = (orc.widen(inp[x], dt) for x in ("q_idx", "k_idx", "w_idx"))
     swaps = 0

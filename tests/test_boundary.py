@@ -134,3 +134,29 @@ def test_workspace_sizes():
     assert b > a > 4096 * 2 * 256 * 4
     with pytest.raises(lisa.LisaError):
         lisa.lisa_prefill_workspace_bytes(_dims(d=80), 1, 10)
+
+
+def _cont(d, B=1, past=10, n=64, ws_bytes=1 << 40, **ptrs):
+    p = dict(q=FAKE, kc=FAKE, vc=FAKE, q_idx=FAKE, kic=FAKE, w_idx=FAKE, gate=FAKE, state_in=0,
+             out=FAKE, state_out=0, topm_out=0, workspace=FAKE)
+    p.update(ptrs)
+    return lisa.lisa_prefill_continue(d, B, past, n, p["q"], p["kc"], p["vc"], p["q_idx"], p["kic"],
+                                      p["w_idx"], p["gate"], p["state_in"], p["out"], p["state_out"],
+                                      p["topm_out"], p["workspace"], ws_bytes, 0)
+
+
+@pytest.mark.parametrize("name", ["q", "kc", "vc", "q_idx", "kic", "w_idx", "gate", "out", "workspace"])
+def test_prefill_continue_null_pointer(name):
+    assert _cont(_dims(), **{name: 0}) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert name.replace("kc", "k").replace("vc", "v").replace("kic", "k_idx") in lisa.lisa_last_error()
+
+
+def test_prefill_continue_limits():
+    d = _dims()
+    assert _cont(d, past=-1) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _cont(d, past=32768 - 63, n=64) == lisa.LISA_ERR_UNSUPPORTED
+    assert _cont(d, n=0, q=0, workspace=0) == lisa.LISA_OK
+    assert _cont(d, B=0, q=0, workspace=0) == lisa.LISA_OK
+    need = lisa.lisa_prefill_workspace_bytes(d, 1, 64)
+    assert _cont(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
+    assert _cont(_dims(M=513)) == lisa.LISA_ERR_UNSUPPORTED

@@ -183,6 +183,41 @@ def test_prefill_sampled_threshold_rescan():
     _say("  ", rep)
 
 
+CONTINUE_CASES = [
+    (_pcfg(700, 12, 2, 128, 4, 64, 256, seed=31), 300),     # past not a multiple of 64
+    (_pcfg(400, 4, 2, 64, 4, 32, 64, B=2, seed=32), 384),   # 16 new tokens, chunk-aligned past
+    (_pcfg(1300, 8, 2, 128, 4, 64, 128, seed=33), 1299),    # one new token (a decode step by prefill)
+    (_pcfg(2500, 12, 2, 128, 4, 64, 256, seed=34), 1100),   # sampled threshold active
+    (_pcfg(520, 4, 2, 64, 4, 64, 100, dtype="f32", seed=35), 129),
+]
+
+
+@pytest.mark.parametrize("case", CONTINUE_CASES, ids=lambda c: f"{c[0].name}_past{c[1]}")
+def test_prefill_continue(case):
+    cfg, past = case
+    _say("prefill continue", cfg.name, "past", past, "seed", cfg.seed)
+    inp = gen.make_prefill_inputs(cfg)
+    rep = {}
+    parity.prefill_parity(cfg, inp, past=past, report=rep)
+    _say("  ", rep)
+
+
+def test_prefill_continue_with_state_and_past0():
+    """An initial state is carried through both calls, and past = 0 gives
+    exactly lisa_prefill's result."""
+    cfg = _pcfg(330, 6, 2, 128, 4, 64, 64, seed=36)
+    _say("prefill continue, state_in", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    S0 = np.random.default_rng(5).standard_normal((1, cfg.Hq, cfg.d, cfg.d)).astype(np.float32)
+    rep = {}
+    parity.prefill_parity(cfg, inp, past=200, state_in=S0, report=rep)
+    _say("  ", rep)
+    a = parity.run_prefill(cfg, inp, state_in=S0)
+    b = parity.run_prefill_continue(cfg, inp, 0, state_in=S0)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 def test_deterministic():
     cfg = gen.CONFIGS[1]
     _say("determinism", cfg.name)
