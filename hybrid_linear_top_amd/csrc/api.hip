@@ -38,7 +38,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int elt_bytes(int dtype) { return dtype == LISA_BF16 ? 2 : 4; }
 
-lisa_status check_dims(const lisa_dims *d, bool prefill) {
+// window: the sliding-window variant, which has no indexer (its fields are
+// not checked) and no top-M buffers (window up to 2048 in prefill too)
+lisa_status check_dims(const lisa_dims *d, bool prefill, bool window = false) {
     if (!d) return fail(LISA_ERR_INVALID_ARGUMENT, "dims is NULL");
     if (d->dtype != LISA_F32 && d->dtype != LISA_BF16)
         return fail(LISA_ERR_INVALID_ARGUMENT, "dtype %d is neither LISA_F32 nor LISA_BF16", d->dtype);
@@ -53,11 +55,11 @@ lisa_status check_dims(const lisa_dims *d, bool prefill) {
                     d->num_q_heads / d->num_kv_heads);
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(LISA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", d->head_dim);
-    if (d->idx_dim != 32 && d->idx_dim != 64)
+    if (!window && d->idx_dim != 32 && d->idx_dim != 64)
         return fail(LISA_ERR_UNSUPPORTED, "idx_dim %d not in {32, 64}", d->idx_dim);
-    if (d->idx_heads < 1 || d->idx_heads > 8)
+    if (!window && (d->idx_heads < 1 || d->idx_heads > 8))
         return fail(LISA_ERR_UNSUPPORTED, "idx_heads %d not in [1, 8]", d->idx_heads);
-    const int mmax = prefill ? 512 : 2048;
+    const int mmax = prefill && !window ? 512 : 2048;
     if (d->top_m < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "top_m %d must be >= 1", d->top_m);
     if (d->top_m > mmax)
         return fail(LISA_ERR_UNSUPPORTED, "top_m %d above the supported %d", d->top_m, mmax);
@@ -181,7 +183,8 @@ const char *lisa_build_info(void) {
 
 lisa_status lisa_prefill_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
                                          size_t *bytes) {
-    lisa_status st = check_dims(dims, true);
+    // sized for both prefill variants: the window one allows top_m up to 2048
+    lisa_status st = check_dims(dims, true, true);
     if (st) return st;
     if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
@@ -212,13 +215,19 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
                                  state_out, topm_out, workspace, workspace_bytes, stream);
 }
 
-lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past, int32_t n,
-                                  const void *q, const void *k, const void *v, const void *q_idx,
-                                  const void *k_idx, const void *w_idx, const void *gate,
-                                  const float *state_in, void *out, float *state_out,
-                                  int32_t *topm_out, void *workspace, size_t workspace_bytes,
-                                  lisa_stream_t stream) {
-    lisa_status st = check_dims(dims, true);
+}  // extern "C"
+
+namespace {
+
+// The prefill path: window = false runs the indexer and top-M; window = true
+// is the sliding-window variant (set of position t = max(0, t-M+1)..t), where
+// q_idx, k_idx, w_idx and topm_out are unused.
+lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t n, const void *q,
+                         const void *k, const void *v, const void *q_idx, const void *k_idx,
+                         const void *w_idx, const void *gate, const float *state_in, void *out,
+                         float *state_out, int32_t *topm_out, void *workspace,
+                         size_t workspace_bytes, lisa_stream_t stream, bool window) {
+    lisa_status st = check_dims(dims, true, window);
     if (st) return st;
     if (B < 0 || n < 0 || past < 0)
         return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, past=%d, n=%d must be >= 0", B, past, n);
@@ -229,9 +238,11 @@ lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past
     LISA_NEED(q, "q");
     LISA_NEED(k, "k");
     LISA_NEED(v, "v");
-    LISA_NEED(q_idx, "q_idx");
-    LISA_NEED(k_idx, "k_idx");
-    LISA_NEED(w_idx, "w_idx");
+    if (!window) {
+        LISA_NEED(q_idx, "q_idx");
+        LISA_NEED(k_idx, "k_idx");
+        LISA_NEED(w_idx, "w_idx");
+    }
     LISA_NEED(gate, "gate");
     LISA_NEED(out, "out");
     LISA_OPT(state_in, "state_in");
@@ -282,15 +293,17 @@ lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past
     ia.HI = dims->idx_heads;
     ia.M = dims->top_m;
     ia.past = past;
-    LISA_HIP(timed(ST_INDEXER, s, [&] { return lisa::launch_indexer_prefill(ia, dims->dtype, dims->idx_dim, s); }),
-             "indexer launch");
+    if (!window)
+        LISA_HIP(timed(ST_INDEXER, s, [&] { return lisa::launch_indexer_prefill(ia, dims->dtype, dims->idx_dim, s); }),
+                 "indexer launch");
 
     lisa::SparseArgs sa{};
     sa.q = q;
     sa.k = k;
     sa.v = v;
     sa.cu = nullptr;
-    sa.idx = idx;
+    sa.idx = window ? nullptr : idx;
+    sa.window = window ? 1 : 0;
     sa.lin = out;
     sa.gate = gate;
     sa.out = out;
@@ -309,13 +322,13 @@ lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past
     return ok();
 }
 
-lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
-                             int32_t max_ctx, const void *q, const void *k_cache,
-                             const void *v_cache, const void *q_idx, const void *k_idx_cache,
-                             const void *w_idx, const void *gate, float *state, void *out,
-                             int32_t *topm_out, void *workspace, size_t workspace_bytes,
-                             lisa_stream_t stream) {
-    lisa_status st = check_dims(dims, false);
+// The decode path; window as in prefill_impl.
+lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx, int32_t max_ctx,
+                        const void *q, const void *k_cache, const void *v_cache, const void *q_idx,
+                        const void *k_idx_cache, const void *w_idx, const void *gate, float *state,
+                        void *out, int32_t *topm_out, void *workspace, size_t workspace_bytes,
+                        lisa_stream_t stream, bool window) {
+    lisa_status st = check_dims(dims, false, window);
     if (st) return st;
     if (B < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
     if (max_ctx < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "max_ctx=%d must be >= 1", max_ctx);
@@ -328,9 +341,11 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
     LISA_NEED(q, "q");
     LISA_NEED(k_cache, "k_cache");
     LISA_NEED(v_cache, "v_cache");
-    LISA_NEED(q_idx, "q_idx");
-    LISA_NEED(k_idx_cache, "k_idx_cache");
-    LISA_NEED(w_idx, "w_idx");
+    if (!window) {
+        LISA_NEED(q_idx, "q_idx");
+        LISA_NEED(k_idx_cache, "k_idx_cache");
+        LISA_NEED(w_idx, "w_idx");
+    }
     LISA_NEED(gate, "gate");
     LISA_NEED(state, "state");
     LISA_NEED(out, "out");
@@ -362,18 +377,22 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
     da.G = G;
     da.HI = dims->idx_heads;
     da.max_ctx = max_ctx;
-    da.tiles_per_seq = (max_ctx + lisa::kDecodeTile - 1) / lisa::kDecodeTile;
-    LISA_HIP(timed(ST_DEC_SCORE_STATE, s, [&] { return lisa::launch_decode_score_state(da, dims->dtype, D, dims->idx_dim, s); }),
+    // the window variant launches the state groups only (no indexer scan)
+    da.tiles_per_seq = window ? 0 : (max_ctx + lisa::kDecodeTile - 1) / lisa::kDecodeTile;
+    const int dI = window ? 64 : dims->idx_dim;  // any supported width: no score groups run
+    LISA_HIP(timed(ST_DEC_SCORE_STATE, s, [&] { return lisa::launch_decode_score_state(da, dims->dtype, D, dI, s); }),
              "indexer-scan/state launch");
-    LISA_HIP(timed(ST_DEC_SELECT, s, [&] { return lisa::launch_decode_select(scores, cu_ctx, B, G, dims->top_m, max_ctx, idx, s); }),
-             "top-M select launch");
+    if (!window)
+        LISA_HIP(timed(ST_DEC_SELECT, s, [&] { return lisa::launch_decode_select(scores, cu_ctx, B, G, dims->top_m, max_ctx, idx, s); }),
+                 "top-M select launch");
 
     lisa::SparseArgs sa{};
     sa.q = q;
     sa.k = k_cache;
     sa.v = v_cache;
     sa.cu = cu_ctx;
-    sa.idx = idx;
+    sa.idx = window ? nullptr : idx;
+    sa.window = window ? 1 : 0;
     sa.lin = olin;
     sa.gate = gate;
     sa.out = out;
@@ -389,6 +408,48 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
     LISA_HIP(timed(ST_SPARSE_DECODE, s, [&] { return lisa::launch_sparse_gate(sa, dims->dtype, D, true, s); }),
              "sparse-attention launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past, int32_t n,
+                                  const void *q, const void *k, const void *v, const void *q_idx,
+                                  const void *k_idx, const void *w_idx, const void *gate,
+                                  const float *state_in, void *out, float *state_out,
+                                  int32_t *topm_out, void *workspace, size_t workspace_bytes,
+                                  lisa_stream_t stream) {
+    return prefill_impl(dims, B, past, n, q, k, v, q_idx, k_idx, w_idx, gate, state_in, out,
+                        state_out, topm_out, workspace, workspace_bytes, stream, false);
+}
+
+lisa_status lisa_prefill_window(const lisa_dims *dims, int32_t B, int32_t past, int32_t n,
+                                const void *q, const void *k_cache, const void *v_cache,
+                                const void *gate, const float *state_in, void *out,
+                                float *state_out, void *workspace, size_t workspace_bytes,
+                                lisa_stream_t stream) {
+    return prefill_impl(dims, B, past, n, q, k_cache, v_cache, nullptr, nullptr, nullptr, gate,
+                        state_in, out, state_out, nullptr, workspace, workspace_bytes, stream, true);
+}
+
+lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
+                             int32_t max_ctx, const void *q, const void *k_cache,
+                             const void *v_cache, const void *q_idx, const void *k_idx_cache,
+                             const void *w_idx, const void *gate, float *state, void *out,
+                             int32_t *topm_out, void *workspace, size_t workspace_bytes,
+                             lisa_stream_t stream) {
+    return decode_impl(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
+                       gate, state, out, topm_out, workspace, workspace_bytes, stream, false);
+}
+
+lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
+                                    int32_t max_ctx, const void *q, const void *k_cache,
+                                    const void *v_cache, const void *gate, float *state, void *out,
+                                    void *workspace, size_t workspace_bytes,
+                                    lisa_stream_t stream) {
+    return decode_impl(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, nullptr, nullptr, nullptr,
+                       gate, state, out, nullptr, workspace, workspace_bytes, stream, true);
 }
 
 lisa_status lisa_stage_timing(int32_t enable) {

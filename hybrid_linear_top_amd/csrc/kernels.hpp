@@ -39,6 +39,7 @@ struct SparseArgs {
     void *out;            // prefill [B,n,Hq,d]; decode [B,Hq,d]
     int B, n, Hq, G, r, M, max_ctx;
     int past;             // prefill: query t (0-based among the n) sits at position past + t
+    int window;           // 1: the set of a query at position t is max(0, t-M+1)..t (idx unused)
     float scale_log2;     // softmax scale * log2(e)
     int units;
 };

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int slot = cs + kb * 16 + col;
-            const int s = slot < s_stop ? idxp[slot] : -1;
+            const int s = slot >= s_stop ? -1 : a.window ? max(0, smax - M + 1) + slot : idxp[slot];
             const uint32_t roff = (s >= 0 && s <= smax) ? (uint32_t)s * row_bytes + grp * 8 * EB
                                                         : kOffNone;
 #pragma unroll
@@ -333,10 +333,14 @@ void sparse_prefill_wave_kernel(SparseArgs a) {
     const int nsteps = (nvalid + kChunk - 1) / kChunk;
     struct Idx { u32x4 v[NI / 4]; };
     const bool idx16 = (M & 3) == 0;  // index rows 16-byte aligned: vector loads
+    const int wbase = max(0, smax - M + 1);  // window mode: slot i is position wbase + i
     auto load_idx = [&](int j) {
         Idx x;
         const uint32_t o = (uint32_t)(j * kChunk + rho0) * 4u;
-        if (idx16) {
+        if (a.window) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) x.v[i / 4][i % 4] = (uint32_t)(wbase + j * kChunk + rho0 + i);
+        } else if (idx16) {
 #pragma unroll
             for (int h = 0; h < NI / 4; ++h) x.v[h] = buf_load16(irs, o + 16u * h);
         } else {

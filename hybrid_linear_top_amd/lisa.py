@@ -24,7 +24,7 @@ LISA_F32 = 0
 LISA_BF16 = 1
 
 EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill", "lisa_prefill_continue",
-           "lisa_decode_workspace_bytes",
+           "lisa_prefill_window", "lisa_decode_step_window", "lisa_decode_workspace_bytes",
            "lisa_decode_step", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
            "lisa_build_info"]
 
@@ -55,6 +55,10 @@ def _load(path: str = LIB_PATH):
     lib.lisa_prefill.restype = ctypes.c_int
     lib.lisa_prefill_continue.argtypes = [dp, i32, i32, i32] + [vp] * 7 + [vp, vp, vp, vp, vp, sz, vp]
     lib.lisa_prefill_continue.restype = ctypes.c_int
+    lib.lisa_prefill_window.argtypes = [dp, i32, i32, i32] + [vp] * 4 + [vp, vp, vp, vp, sz, vp]
+    lib.lisa_prefill_window.restype = ctypes.c_int
+    lib.lisa_decode_step_window.argtypes = [dp, i32, i64p, i32] + [vp] * 4 + [vp, vp, vp, sz, vp]
+    lib.lisa_decode_step_window.restype = ctypes.c_int
     lib.lisa_decode_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
     lib.lisa_decode_workspace_bytes.restype = ctypes.c_int
     lib.lisa_decode_step.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp, sz, vp]
@@ -116,6 +120,20 @@ def lisa_prefill_continue(dims, B, past, n, q, k_cache, v_cache, q_idx, k_idx_ca
     return _lib.lisa_prefill_continue(ctypes.byref(dims), B, past, n, q, k_cache, v_cache, q_idx,
                                       k_idx_cache, w_idx, gate, state_in, out, state_out, topm_out,
                                       workspace, workspace_bytes, stream)
+
+
+def lisa_prefill_window(dims, B, past, n, q, k_cache, v_cache, gate, state_in, out, state_out,
+                        workspace, workspace_bytes, stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_prefill_window(ctypes.byref(dims), B, past, n, q, k_cache, v_cache, gate,
+                                    state_in, out, state_out, workspace, workspace_bytes, stream)
+
+
+def lisa_decode_step_window(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, gate, state, out,
+                            workspace, workspace_bytes, stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_decode_step_window(ctypes.byref(dims), B, cu_ctx, max_ctx, q, k_cache, v_cache,
+                                        gate, state, out, workspace, workspace_bytes, stream)
 
 
 def lisa_decode_step(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
@@ -211,6 +229,43 @@ def prefill_continue(dims: LisaDims, past: int, q, k_cache, v_cache, q_idx, k_id
                                  _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(topm_out),
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, state_out, topm_out
+
+
+def prefill_window(dims: LisaDims, past: int, q, k_cache, v_cache, gate, state_in=None, out=None,
+                   state_out=None, workspace=None, stream=None):
+    """Sliding-window prefill of n new tokens against caches of past + n rows.
+    Returns (out, state_out)."""
+    import torch
+    B, n = int(q.shape[0]), int(q.shape[1])
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None:
+        state_out = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
+                                dtype=torch.float32, device=dev)
+    wsb = lisa_prefill_workspace_bytes(dims, B, n)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(lisa_prefill_window(dims, B, past, n, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(gate),
+                               _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace),
+                               workspace.numel(), _stream(stream)))
+    return out, state_out
+
+
+def decode_step_window(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache, gate, state,
+                       out=None, workspace=None, stream=None):
+    """Sliding-window decode step; `state` is updated in place.  Returns out."""
+    import torch
+    B = int(q.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    wsb = lisa_decode_workspace_bytes(dims, B, max_ctx)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _check(lisa_decode_step_window(dims, B, _ptr(cu_ctx), max_ctx, _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(gate), _ptr(state), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
 
 
 def decode_step(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache, q_idx, k_idx_cache,

@@ -85,7 +85,8 @@ typedef struct {
     int32_t dtype;         /* LISA_F32 or LISA_BF16 */
 } lisa_dims;
 
-/* Workspace needed by lisa_prefill for batch B and length n. */
+/* Workspace needed by lisa_prefill for batch B and length n (any top_m up to
+ * 2048, so the query also serves lisa_prefill_window). */
 lisa_status lisa_prefill_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
                                          size_t *bytes);
 
@@ -134,6 +135,22 @@ lisa_status lisa_prefill_continue(const lisa_dims *dims, int32_t B, int32_t past
                                   float *state_out, int32_t *topm_out, void *workspace,
                                   size_t workspace_bytes, lisa_stream_t stream);
 
+/*
+ * Sliding-window variant (the model before the indexer is introduced: in
+ * the first training stage the linear branch is paired with a static
+ * sliding-window attention, which the indexer later replaces -- arxivdaily
+ * page for 2607.19358, English abstract).  Readings: the window is the same
+ * budget M = dims->top_m (1..2048 here), the set of position t is
+ * max(0, t-M+1)..t, and the gate and linear branch are as above.  Arguments
+ * as lisa_prefill_continue without the indexer inputs and topm_out (the
+ * indexer fields of dims are ignored); same workspace query.
+ */
+lisa_status lisa_prefill_window(const lisa_dims *dims, int32_t B, int32_t past, int32_t n,
+                                const void *q, const void *k_cache, const void *v_cache,
+                                const void *gate, const float *state_in, void *out,
+                                float *state_out, void *workspace, size_t workspace_bytes,
+                                lisa_stream_t stream);
+
 /* Workspace needed by lisa_decode_step for B sequences of at most max_ctx
  * visible tokens each. */
 lisa_status lisa_decode_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t max_ctx,
@@ -160,6 +177,17 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
                              const void *w_idx, const void *gate, float *state, void *out,
                              int32_t *topm_out, void *workspace, size_t workspace_bytes,
                              lisa_stream_t stream);
+
+/*
+ * One generated token per sequence with the sliding-window set
+ * max(0, t-M+1)..t (see lisa_prefill_window); arguments as lisa_decode_step
+ * without the indexer inputs and topm_out; same workspace query.
+ */
+lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
+                                    int32_t max_ctx, const void *q, const void *k_cache,
+                                    const void *v_cache, const void *gate, float *state, void *out,
+                                    void *workspace, size_t workspace_bytes,
+                                    lisa_stream_t stream);
 
 /*
  * Per-kernel timing, for benchmarking only.  While enabled (process-wide),

@@ -287,7 +287,44 @@ def pin_decode_ragged_groups(lib):
         assert np.array_equal(rb["out"][0], r["out"][b])
 
 
+def window_sets(positions, M, G):
+    """Sliding-window sets: position t takes max(0, t-M+1)..t, ascending, -1 padded."""
+    sets = -np.ones((len(positions), G, M), dtype=np.int32)
+    for u, t in enumerate(positions):
+        m = min(M, t + 1)
+        sets[u, :, :m] = np.arange(t - m + 1, t + 1)
+    return sets
+
+
+def pin_window_banded(lib):
+    """The oracle's sparse branch on sliding-window sets equals dense attention
+    under a banded causal mask (torch SDPA with an explicit mask); with a
+    window at least n long it is plain causal attention."""
+    import torch
+    cfg = _cfg(n=29, Hq=4, Hkv=2, d=16, HI=2, dI=8, M=6)
+    inp = make_prefill_inputs(cfg)
+    q, k, v = (orc.widen(inp[x], "f32") for x in ("q", "k", "v"))
+    n, Hq, Hkv, d = cfg.n, cfg.Hq, cfg.Hkv, cfg.d
+    scale = 1.0 / math.sqrt(d)
+    zinf = np.full((n, Hq), np.inf)
+    for W in (6, 1, 40):
+        sets = window_sets(range(n), W, Hkv)
+        _, osp = orc.sparse_given_sets(q[0], k[0], v[0], np.zeros(n, dtype=np.int64), sets, zinf,
+                                       np.zeros((n, Hq, d)), Hq, Hkv, d, W, lib=lib)
+        t = np.arange(n)
+        band = (t[None, :] <= t[:, None]) & (t[None, :] > t[:, None] - W)   # [query, key]
+        r = Hq // Hkv
+        qt = torch.from_numpy(q[0]).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k[0]).permute(1, 0, 2).repeat_interleave(r, 0)[None]
+        vt = torch.from_numpy(v[0]).permute(1, 0, 2).repeat_interleave(r, 0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=torch.from_numpy(band), scale=scale)[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(osp, ref, rtol=1e-11, atol=1e-12)
+        if W >= n:
+            np.testing.assert_allclose(osp, _sdpa_causal(q, k, v, scale)[0], rtol=1e-11, atol=1e-12)
+
+
 ALL_PINS = [pin_golden_prefill, pin_golden_softmax, pin_golden_decode, pin_topm_bruteforce,
             pin_scores_reductions, pin_sparse_full_causal, pin_sparse_m1, pin_sparse_zero_query,
             pin_linear_closed_form, pin_gate_limits, pin_selection_properties, pin_rows_subset,
-            pin_decode_matches_prefill, pin_decode_ragged_groups]
+            pin_decode_matches_prefill, pin_decode_ragged_groups, pin_window_banded]

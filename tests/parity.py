@@ -198,3 +198,95 @@ def decode_parity(cfg, inp, report=None):
     for key in ("e_sparse", "e_linear", "e_out", "e_state"):
         assert res[key] <= tol, res
     return res
+
+
+# ---- sliding-window variant ------------------------------------------------
+def window_prefill_parity(cfg, inp, past=0, state_in=None, report=None):
+    """GPU lisa_prefill_window (after a prefill of the first `past` tokens for
+    the state) against the oracle: the sparse branch on the window sets
+    max(0, t-M+1)..t, the linear branch and state of one oracle prefill."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    from tests.oracle_pins import window_sets
+    dt = cfg.dtype
+    B, n = inp["B"], inp["n"]
+    tol = TOL[dt]
+    rows = list(range(past, n))
+    ref = orc.prefill(inp, cfg, rows=rows, state_in=state_in)
+    dims = lisa.dims_from_config(cfg)
+    dv = lisa.to_device
+
+    def gpu(gate):
+        s0 = None if state_in is None else dv(np.ascontiguousarray(state_in, dtype=np.float32))
+        if past > 0:
+            head = [dv(np.ascontiguousarray(inp[k][:, :past])) for k in ("q", "k", "v")]
+            _, s0 = lisa.prefill_window(dims, 0, head[0], head[1], head[2],
+                                        dv(np.ascontiguousarray(gate[:, :past])), state_in=s0)
+        o, st_ = lisa.prefill_window(dims, past, dv(np.ascontiguousarray(inp["q"][:, past:])),
+                                     dv(inp["k"]), dv(inp["v"]), dv(np.ascontiguousarray(gate[:, past:])),
+                                     state_in=s0)
+        torch.cuda.synchronize()
+        return orc.widen(lisa.from_device(o), dt), lisa.from_device(st_).astype(np.float64)
+
+    out, st = gpu(inp["gate"])
+    osp, _ = gpu(gate_fill(inp["gate"].shape, dt, np.inf))
+    olin, _ = gpu(gate_fill(inp["gate"].shape, dt, -np.inf))
+    q = orc.widen(inp["q"], dt)
+    kr = orc.widen(inp["k"], dt).reshape(B * n, cfg.Hkv, cfg.d)
+    vr = orc.widen(inp["v"], dt).reshape(B * n, cfg.Hkv, cfg.d)
+    z = orc.widen(inp["gate"], dt)
+    R = np.asarray(rows)
+    U = B * len(R)
+    sets = np.concatenate([window_sets(R, cfg.M, cfg.Hkv) for _ in range(B)])
+    row0 = np.repeat(np.arange(B) * n, len(R))
+    out_g, osp_g = orc.sparse_given_sets(q[:, R].reshape(U, cfg.Hq, cfg.d), kr, vr, row0, sets,
+                                         z[:, R].reshape(U, cfg.Hq), ref["olin"].reshape(U, cfg.Hq, cfg.d),
+                                         cfg.Hq, cfg.Hkv, cfg.d, cfg.M)
+    res = dict(e_sparse=normwise(osp.reshape(U, -1), osp_g.reshape(U, -1)),
+               e_linear=normwise(olin, ref["olin"]), e_out=normwise(out.reshape(U, -1), out_g.reshape(U, -1)),
+               e_state=normwise(st, ref["state_out"]))
+    if report is not None:
+        report.update(res)
+    for key in res:
+        assert res[key] <= tol, res
+    return res
+
+
+def window_decode_parity(cfg, inp, report=None):
+    """GPU lisa_decode_step_window against the oracle: sparse branch on the
+    window set of the new token, the oracle decode's linear branch and state."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    from tests.oracle_pins import window_sets
+    dt = cfg.dtype
+    tol = TOL[dt]
+    ref = orc.decode(inp, cfg)
+    dims = lisa.dims_from_config(cfg)
+    dv = lisa.to_device
+
+    def gpu(gate):
+        state = dv(inp["state"])
+        o = lisa.decode_step_window(dims, dv(inp["cu_ctx"]), inp["max_ctx"], dv(inp["q"]),
+                                    dv(inp["k_cache"]), dv(inp["v_cache"]), dv(gate), state)
+        torch.cuda.synchronize()
+        return orc.widen(lisa.from_device(o), dt), lisa.from_device(state).astype(np.float64)
+
+    out, st = gpu(inp["gate"])
+    osp, _ = gpu(gate_fill(inp["gate"].shape, dt, np.inf))
+    olin, _ = gpu(gate_fill(inp["gate"].shape, dt, -np.inf))
+    cu = inp["cu_ctx"]
+    L = np.diff(cu)
+    # positions are local to each sequence; rows of the packed cache are cu[b] + s
+    sets = window_sets(L - 1, cfg.M, cfg.Hkv)
+    q = orc.widen(inp["q"], dt)
+    kc, vc = orc.widen(inp["k_cache"], dt), orc.widen(inp["v_cache"], dt)
+    z = orc.widen(inp["gate"], dt)
+    out_g, osp_g = orc.sparse_given_sets(q, kc, vc, cu[:-1], sets, z, ref["olin"], cfg.Hq, cfg.Hkv,
+                                         cfg.d, cfg.M)
+    res = dict(e_sparse=normwise(osp, osp_g), e_linear=normwise(olin, ref["olin"]),
+               e_out=normwise(out, out_g), e_state=normwise(st, ref["state_out"]))
+    if report is not None:
+        report.update(res)
+    for key in res:
+        assert res[key] <= tol, res
+    return res

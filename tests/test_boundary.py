@@ -27,6 +27,26 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def _declared_param_counts():
+    with open(os.path.join(ROOT, "include", "lisa.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(lisa_[a-z_]+)\s*\(([^;{]*?)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header():
+    """Every ctypes prototype has as many arguments as the C declaration."""
+    counts = _declared_param_counts()
+    lib = lisa._lib
+    for name in lisa.EXPORTS:
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None, name
+        assert len(fn.argtypes) == counts[name], (name, len(fn.argtypes), counts[name])
+
+
 def test_build_info_names_target():
     assert "gfx950" in lisa.lisa_build_info()
 
@@ -160,3 +180,36 @@ def test_prefill_continue_limits():
     need = lisa.lisa_prefill_workspace_bytes(d, 1, 64)
     assert _cont(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
     assert _cont(_dims(M=513)) == lisa.LISA_ERR_UNSUPPORTED
+
+
+def _win(d, B=1, past=0, n=64, ws_bytes=1 << 40, **ptrs):
+    p = dict(q=FAKE, kc=FAKE, vc=FAKE, gate=FAKE, state_in=0, out=FAKE, state_out=0, workspace=FAKE)
+    p.update(ptrs)
+    return lisa.lisa_prefill_window(d, B, past, n, p["q"], p["kc"], p["vc"], p["gate"], p["state_in"],
+                                    p["out"], p["state_out"], p["workspace"], ws_bytes, 0)
+
+
+def _dwin(d, B=2, max_ctx=100, ws_bytes=1 << 40, **ptrs):
+    p = dict(cu=FAKE, q=FAKE, kc=FAKE, vc=FAKE, gate=FAKE, state=FAKE, out=FAKE, workspace=FAKE)
+    p.update(ptrs)
+    return lisa.lisa_decode_step_window(d, B, p["cu"], max_ctx, p["q"], p["kc"], p["vc"], p["gate"],
+                                        p["state"], p["out"], p["workspace"], ws_bytes, 0)
+
+
+@pytest.mark.parametrize("name", ["q", "kc", "vc", "gate", "out", "workspace"])
+def test_window_null_pointers(name):
+    assert _win(_dims(), **{name: 0}) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _dwin(_dims(), **{name: 0}) == lisa.LISA_ERR_INVALID_ARGUMENT
+
+
+def test_window_limits():
+    # the indexer fields are not used (and not checked); the window may be up to 2048
+    assert _win(_dims(HI=0, dI=48, M=2049)) == lisa.LISA_ERR_UNSUPPORTED
+    assert _win(_dims(M=0)) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _dwin(_dims(M=2049)) == lisa.LISA_ERR_UNSUPPORTED
+    assert _dwin(_dims(), max_ctx=65537) == lisa.LISA_ERR_UNSUPPORTED
+    assert _win(_dims(), n=0, q=0, workspace=0) == lisa.LISA_OK
+    assert _dwin(_dims(), B=0, q=0) == lisa.LISA_OK
+    d = _dims(M=1000)
+    need = lisa.lisa_prefill_workspace_bytes(d, 1, 64)
+    assert _win(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE

@@ -218,6 +218,42 @@ def test_prefill_continue_with_state_and_past0():
         assert np.array_equal(x, y)
 
 
+WINDOW_PREFILL = [
+    (_pcfg(300, 8, 2, 128, 1, 32, 64, seed=41), 0),
+    (_pcfg(150, 4, 2, 64, 1, 32, 300, seed=42), 0),               # window > n: full causal
+    (_pcfg(900, 12, 2, 128, 1, 32, 256, B=2, seed=43), 500),      # continued, B = 2
+    (_pcfg(400, 6, 3, 128, 1, 32, 1000, seed=44), 100),           # window above the indexer's 512
+    (_pcfg(260, 4, 2, 64, 1, 32, 50, dtype="f32", seed=45), 70),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_PREFILL, ids=lambda c: f"{c[0].name}_past{c[1]}")
+def test_prefill_window(case):
+    cfg, past = case
+    _say("prefill window", cfg.name, "past", past, "seed", cfg.seed)
+    inp = gen.make_prefill_inputs(cfg)
+    rep = {}
+    parity.window_prefill_parity(cfg, inp, past=past, report=rep)
+    _say("  ", rep)
+
+
+WINDOW_DECODE = [
+    _dcfg(12, 2, 128, 1, 32, 256, [1, 100, 256, 257, 3000]),
+    _dcfg(8, 4, 64, 1, 32, 1500, [1499, 1500, 1501, 40]),
+    _dcfg(8, 2, 128, 1, 32, 64, [65, 900], dtype="f32", seed=2),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_DECODE, ids=lambda c: c[0].name)
+def test_decode_window(case):
+    cfg, lengths = case
+    _say("decode window", cfg.name, "seed", cfg.seed)
+    inp = gen.make_decode_inputs(cfg, lengths=lengths)
+    rep = {}
+    parity.window_decode_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
 def test_deterministic():
     cfg = gen.CONFIGS[1]
     _say("determinism", cfg.name)
