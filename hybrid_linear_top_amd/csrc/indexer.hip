@@ -280,10 +280,11 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     __shared__ __attribute__((aligned(16))) float cand_sc[kQW * CAP];
     __shared__ __attribute__((aligned(16))) uint16_t cand_key[kQW * CAP];
     __shared__ __attribute__((aligned(16))) uint32_t hist[256];
-    // per-lane sink for the writes of rejected keys: appends are straight-line
-    // code, so the two query quads' scans and writes interleave
-    __shared__ __attribute__((aligned(16))) float sink_sc[64];
-    __shared__ __attribute__((aligned(16))) uint16_t sink_key[64];
+    // per-lane sink for the writes of rejected keys (appends are straight-line
+    // code, so the two query quads' scans and writes interleave).  It lives in
+    // the histogram, which every trim and select clears before use.
+    float *const sink_sc = reinterpret_cast<float *>(hist);
+    uint16_t *const sink_key = reinterpret_cast<uint16_t *>(hist + 64);
     auto qbuf_of = [&](int q) { return CandBuf{cand_sc + q * CAP, cand_key + q * CAP}; };
 
     const int lane = threadIdx.x & 63;
@@ -597,7 +598,7 @@ template <typename T, int DI, int HH>
 hipError_t by_m(const IndexerArgs &a, hipStream_t s) {
     // per-wave LDS: 8 candidate buffers of CAP 8-byte entries
     if (a.M <= 128) return launch<T, DI, HH, 256>(a, s);
-    if (a.M <= 256) return launch<T, DI, HH, 512>(a, s);
+    if (a.M <= 256) return launch<T, DI, HH, 448>(a, s);
     return launch<T, DI, HH, 1024>(a, s);
 }
 
