@@ -322,12 +322,15 @@ lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t
     return ok();
 }
 
-// The decode path; window as in prefill_impl.
+// The decode path; window as in prefill_impl.  map.table == nullptr: packed
+// caches described by cu_ctx; otherwise paged caches (pool_rows rows).
 lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx, int32_t max_ctx,
                         const void *q, const void *k_cache, const void *v_cache, const void *q_idx,
                         const void *k_idx_cache, const void *w_idx, const void *gate, float *state,
                         void *out, int32_t *topm_out, void *workspace, size_t workspace_bytes,
-                        lisa_stream_t stream, bool window) {
+                        lisa_stream_t stream, bool window, lisa::CacheMap map = lisa::CacheMap{},
+                        int64_t pool_rows = 0) {
+    const bool paged = map.table != nullptr;
     lisa_status st = check_dims(dims, false, window);
     if (st) return st;
     if (B < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
@@ -335,9 +338,12 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     if (max_ctx > kMaxDecodeCtx)
         return fail(LISA_ERR_UNSUPPORTED, "max_ctx=%d above the supported %d", max_ctx, kMaxDecodeCtx);
     if (B == 0) return ok();
-    if (!cu_ctx) return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is NULL");
-    if (reinterpret_cast<uintptr_t>(cu_ctx) & 7u)
-        return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is not 8-byte aligned");
+    if (!paged) {
+        if (!cu_ctx) return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is NULL");
+        if (reinterpret_cast<uintptr_t>(cu_ctx) & 7u)
+            return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is not 8-byte aligned");
+        map.cu = cu_ctx;
+    }
     LISA_NEED(q, "q");
     LISA_NEED(k_cache, "k_cache");
     LISA_NEED(v_cache, "v_cache");
@@ -369,6 +375,7 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     da.k_idx_cache = k_idx_cache;
     da.w_idx = w_idx;
     da.cu = cu_ctx;
+    da.map = map;
     da.state = state;
     da.olin = olin;
     da.scores = scores;
@@ -383,7 +390,7 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     LISA_HIP(timed(ST_DEC_SCORE_STATE, s, [&] { return lisa::launch_decode_score_state(da, dims->dtype, D, dI, s); }),
              "indexer-scan/state launch");
     if (!window)
-        LISA_HIP(timed(ST_DEC_SELECT, s, [&] { return lisa::launch_decode_select(scores, cu_ctx, B, G, dims->top_m, max_ctx, idx, s); }),
+        LISA_HIP(timed(ST_DEC_SELECT, s, [&] { return lisa::launch_decode_select(scores, map, B, G, dims->top_m, max_ctx, idx, s); }),
                  "top-M select launch");
 
     lisa::SparseArgs sa{};
@@ -391,6 +398,8 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     sa.k = k_cache;
     sa.v = v_cache;
     sa.cu = cu_ctx;
+    sa.map = map;
+    sa.pool_rows = pool_rows;
     sa.idx = window ? nullptr : idx;
     sa.window = window ? 1 : 0;
     sa.lin = olin;
@@ -441,6 +450,41 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
                              lisa_stream_t stream) {
     return decode_impl(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
                        gate, state, out, topm_out, workspace, workspace_bytes, stream, false);
+}
+
+lisa_status lisa_decode_step_paged(const lisa_dims *dims, int32_t B, const int32_t *lengths,
+                                   const int32_t *block_table, int32_t block_size,
+                                   int32_t max_blocks, int32_t num_pages, int32_t max_ctx,
+                                   const void *q, const void *k_pages, const void *v_pages,
+                                   const void *q_idx, const void *k_idx_pages, const void *w_idx,
+                                   const void *gate, float *state, void *out, int32_t *topm_out,
+                                   void *workspace, size_t workspace_bytes, lisa_stream_t stream) {
+    lisa_status st = check_dims(dims, false);
+    if (st) return st;
+    if (B < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
+    if (B == 0) return ok();
+    if (!lengths || !block_table) return fail(LISA_ERR_INVALID_ARGUMENT, "lengths or block_table is NULL");
+    if ((reinterpret_cast<uintptr_t>(lengths) | reinterpret_cast<uintptr_t>(block_table)) & 3u)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "lengths or block_table is not 4-byte aligned");
+    if (block_size < 1 || block_size > 4096 || (block_size & (block_size - 1)))
+        return fail(LISA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [1, 4096]", block_size);
+    if (max_ctx < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "max_ctx=%d must be >= 1", max_ctx);
+    if ((int64_t)max_blocks * block_size < max_ctx)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "max_blocks %d x block_size %d < max_ctx %d", max_blocks,
+                    block_size, max_ctx);
+    if (num_pages < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "num_pages=%d must be >= 1", num_pages);
+    const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim * (dims->dtype == LISA_BF16 ? 2 : 4);
+    if ((int64_t)num_pages * block_size * row_bytes >= ((int64_t)1 << 31))
+        return fail(LISA_ERR_UNSUPPORTED, "K/V page pool of %lld bytes: at most 2 GiB is supported",
+                    (long long)num_pages * block_size * row_bytes);
+    lisa::CacheMap map{};
+    map.table = block_table;
+    map.lengths = lengths;
+    map.max_blocks = max_blocks;
+    map.log2_block = __builtin_ctz((unsigned)block_size);
+    return decode_impl(dims, B, nullptr, max_ctx, q, k_pages, v_pages, q_idx, k_idx_pages, w_idx, gate,
+                       state, out, topm_out, workspace, workspace_bytes, stream, false, map,
+                       (int64_t)num_pages * block_size);
 }
 
 lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,

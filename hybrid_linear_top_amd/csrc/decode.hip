@@ -63,8 +63,9 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb) {
     constexpr int NIT = TPW / RPI;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = sb / a.tiles_per_seq, tile = sb % a.tiles_per_seq;
-    const int64_t row0 = a.cu[b];
-    const int L = (int)min((int64_t)a.max_ctx, a.cu[b + 1] - row0);
+    const int64_t row0 = a.map.table ? 0 : a.cu[b];
+    const int32_t *ptab = a.map.table ? a.map.table + (size_t)b * a.map.max_blocks : nullptr;
+    const int L = cache_len(a.map, b, a.max_ctx);
     const int tok0 = tile * kDecodeTile;
     if (tok0 >= L) return;
     const int tok_end = min(tok0 + kDecodeTile, L);
@@ -84,7 +85,7 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb) {
             const int tok = tb + it * RPI + rr;
             if (tok < tok_end)
                 raw[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                    kI + ((size_t)(row0 + tok) * G + g) * DI + c * EPC));
+                    kI + ((size_t)cache_row(a.map, row0, ptab, tok) * G + g) * DI + c * EPC));
             else
                 raw[it] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -130,14 +131,15 @@ __device__ void state_group(const DecodeScoreArgs &a, int u, float *smem) {
     const int tid = threadIdx.x;
     const int Hq = a.Hq, b = u / Hq, h = u % Hq;
     const int g = (int)(((int64_t)h * a.G) / Hq);
-    const int64_t row0 = a.cu[b];
-    const int L = (int)min((int64_t)a.max_ctx, a.cu[b + 1] - row0);
+    const int64_t row0 = a.map.table ? 0 : a.cu[b];
+    const int32_t *ptab = a.map.table ? a.map.table + (size_t)b * a.map.max_blocks : nullptr;
+    const int L = cache_len(a.map, b, a.max_ctx);
     float *olin = a.olin + ((size_t)b * Hq + h) * D;
     if (L < 1) {
         if (tid < D) olin[tid] = 0.0f;
         return;
     }
-    const int64_t trow = row0 + L - 1;
+    const int64_t trow = cache_row(a.map, row0, ptab, L - 1);
     float *kk = smem, *vv = smem + D, *qq = smem + 2 * D, *red = smem + 3 * D;
     const T *kc = reinterpret_cast<const T *>(a.k_cache);
     const T *vc = reinterpret_cast<const T *>(a.v_cache);
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void decode_score_state_kernel(DecodeScoreArgs
 //     lowest indices taking the ties.
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
-                                                                    const int64_t *cu, int G, int M,
+                                                                    CacheMap map, int G, int M,
                                                                     int max_ctx, int32_t *idx) {
     constexpr int BPT = (2048 + NT - 1) / NT;  // histogram bins per thread
     __shared__ uint32_t hist[2048];
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
     __shared__ uint32_t found[3];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bg = blockIdx.x, b = bg / G;
-    const int L = (int)max((int64_t)0, min((int64_t)max_ctx, cu[b + 1] - cu[b]));
+    const int L = cache_len(map, b, max_ctx);
     const float *sc = scores + (size_t)bg * max_ctx;
     int32_t *out = idx + (size_t)bg * M;
     if (L <= M) {
@@ -433,7 +435,7 @@ __device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32
 //  4. wave 0 walks the bitmaps in position order (contiguous words per lane,
 //     one wave scan of their counts) and writes the set ascending.
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, const int64_t *cu,
+__global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, CacheMap map,
                                                          int G, int M, int max_ctx, int32_t *idx) {
     constexpr int NW = NT / 64;
     constexpr int NWORD = (NT * EPT + 31) / 32;  // bitmap words
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, co
     __shared__ uint32_t found[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bg = blockIdx.x, b = bg / G;
-    const int L = (int)max((int64_t)0, min((int64_t)max_ctx, cu[b + 1] - cu[b]));
+    const int L = cache_len(map, b, max_ctx);
     const float *sc = scores + (size_t)bg * max_ctx;
     int32_t *out = idx + (size_t)bg * M;
     if (L <= M) {
@@ -750,7 +752,7 @@ hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d,
     return dtype == 1 ? dispatch_ss<uint16_t>(a, d, dI, s) : dispatch_ss<float>(a, d, dI, s);
 }
 
-hipError_t launch_decode_select(const float *scores, const int64_t *cu, int B, int G, int M,
+hipError_t launch_decode_select(const float *scores, const CacheMap &cu, int B, int G, int M,
                                 int max_ctx, int32_t *idx, hipStream_t s) {
     const dim3 grid(B * G);
 #define LISA_SEL(NT_, E)                                                                          \

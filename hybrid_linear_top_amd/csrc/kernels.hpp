@@ -6,6 +6,27 @@
 namespace lisa {
 
 // ---- decode ---------------------------------------------------------------
+// Where position s of sequence b lives in a decode cache.  Packed caches
+// (table == nullptr): row cu[b] + s, with L_b = cu[b+1] - cu[b].  Paged
+// caches: row table[b][s >> log2_block] * block + (s & (block - 1)) of the
+// page pool, with L_b = lengths[b].
+struct CacheMap {
+    const int64_t *cu;
+    const int32_t *table;    // [B, max_blocks] page ids, or nullptr
+    const int32_t *lengths;  // [B] (paged only)
+    int log2_block, max_blocks;
+};
+__device__ __forceinline__ int cache_len(const CacheMap &m, int b, int max_ctx) {
+    const int64_t L = m.table ? (int64_t)m.lengths[b] : m.cu[b + 1] - m.cu[b];
+    return (int)(L < 0 ? 0 : (L > max_ctx ? max_ctx : L));
+}
+// row of position s given the sequence's first packed row (row0, packed) or
+// its page-table row (tb, paged)
+__device__ __forceinline__ int64_t cache_row(const CacheMap &m, int64_t row0, const int32_t *tb, int s) {
+    if (!m.table) return row0 + s;
+    return ((int64_t)tb[s >> m.log2_block] << m.log2_block) + (s & ((1 << m.log2_block) - 1));
+}
+
 struct DecodeScoreArgs {
     const void *q;            // [B,Hq,d]
     const void *k_cache;      // [sumL,G,d]
@@ -14,6 +35,7 @@ struct DecodeScoreArgs {
     const void *k_idx_cache;  // [sumL,G,dI]
     const void *w_idx;        // [B,G,HI]
     const int64_t *cu;        // [B+1] device
+    CacheMap map;
     float *state;             // [B,Hq,d,d] in/out
     float *olin;              // [B,Hq,d] workspace
     float *scores;            // [B,G,max_ctx] workspace
@@ -24,7 +46,7 @@ constexpr int kDecodeTile = 256;  // tokens per score work-group
 
 hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI,
                                      hipStream_t s);
-hipError_t launch_decode_select(const float *scores, const int64_t *cu, int B, int G, int M,
+hipError_t launch_decode_select(const float *scores, const CacheMap &map, int B, int G, int M,
                                 int max_ctx, int32_t *idx, hipStream_t s);
 
 // ---- sparse attention + gate (prefill and decode) -------------------------
@@ -33,6 +55,8 @@ struct SparseArgs {
     const void *k;        // prefill [B,past+n,G,d];  decode cache [sumL,G,d]
     const void *v;
     const int64_t *cu;    // decode only
+    CacheMap map;         // decode only
+    int64_t pool_rows;    // paged decode: rows in the page pool (bounds the gathers)
     const int32_t *idx;   // [units, M]  (units = B*n*G or B*G)
     const void *lin;      // o_lin: prefill = out buffer (dtype); decode = fp32 workspace
     const void *gate;     // prefill [B,n,Hq]; decode [B,Hq]

@@ -63,11 +63,14 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
     const T *zp;
     T *outp;
     size_t lin_off;
+    const int32_t *tb = nullptr;  // paged decode: this sequence's page-table row
     {
         if (DECODE) {
             const int b = u / G, g = u % G;
-            const int64_t row0 = a.cu[b];
-            smax = (int)min((int64_t)a.max_ctx, a.cu[b + 1] - row0) - 1;
+            // paged caches: rows are relative to the pool, packed: to the sequence
+            const int64_t row0 = a.map.table ? 0 : a.cu[b];
+            if (a.map.table) tb = a.map.table + (size_t)b * a.map.max_blocks;
+            smax = cache_len(a.map, b, a.max_ctx) - 1;
             nvalid = min(M, smax + 1);
             qrows = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.Hq + g * r) * D;
             kbase = reinterpret_cast<const T *>(a.k) + ((size_t)row0 * G + g) * D;
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
     // padding or out of range read as zeros without a branch
     constexpr uint32_t EB = Elt<T>::kBytes;
     const uint32_t row_bytes = (uint32_t)rstride * EB;
-    const uint32_t vis_bytes = (uint32_t)(smax + 1) * row_bytes;
+    const uint32_t vis_bytes = DECODE && a.map.table ? (uint32_t)a.pool_rows * row_bytes
+                                                     : (uint32_t)(smax + 1) * row_bytes;
     const rsrc_t krs = make_rsrc(kbase, vis_bytes), vrs = make_rsrc(vbase, vis_bytes);
     for (int cs = s_begin; cs < s_stop; cs += kChunk) {
         // --- issue both gathers: lane (grp, col) fetches, for key block kb,
@@ -123,8 +127,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
         for (int kb = 0; kb < 2; ++kb) {
             const int slot = cs + kb * 16 + col;
             const int s = slot >= s_stop ? -1 : a.window ? max(0, smax - M + 1) + slot : idxp[slot];
-            const uint32_t roff = (s >= 0 && s <= smax) ? (uint32_t)s * row_bytes + grp * 8 * EB
-                                                        : kOffNone;
+            const uint32_t rrow = DECODE && tb ? (uint32_t)cache_row(a.map, 0, tb, min(max(s, 0), max(smax, 0))) : (uint32_t)s;
+            const uint32_t roff = (s >= 0 && s <= smax) ? rrow * row_bytes + grp * 8 * EB : kOffNone;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 frag_buf_load(kf[kb][kc], krs, roff + kc * 32 * EB);

@@ -24,7 +24,8 @@ LISA_F32 = 0
 LISA_BF16 = 1
 
 EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill", "lisa_prefill_continue",
-           "lisa_prefill_window", "lisa_decode_step_window", "lisa_decode_workspace_bytes",
+           "lisa_prefill_window", "lisa_decode_step_window", "lisa_decode_step_paged",
+           "lisa_decode_workspace_bytes",
            "lisa_decode_step", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
            "lisa_build_info"]
 
@@ -59,6 +60,9 @@ def _load(path: str = LIB_PATH):
     lib.lisa_prefill_window.restype = ctypes.c_int
     lib.lisa_decode_step_window.argtypes = [dp, i32, i64p, i32] + [vp] * 4 + [vp, vp, vp, sz, vp]
     lib.lisa_decode_step_window.restype = ctypes.c_int
+    lib.lisa_decode_step_paged.argtypes = [dp, i32, vp, vp, i32, i32, i32, i32] + [vp] * 7 + \
+        [vp, vp, vp, vp, sz, vp]
+    lib.lisa_decode_step_paged.restype = ctypes.c_int
     lib.lisa_decode_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
     lib.lisa_decode_workspace_bytes.restype = ctypes.c_int
     lib.lisa_decode_step.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp, sz, vp]
@@ -134,6 +138,16 @@ def lisa_decode_step_window(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, gate,
     """Raw call; returns the status code (0 = LISA_OK)."""
     return _lib.lisa_decode_step_window(ctypes.byref(dims), B, cu_ctx, max_ctx, q, k_cache, v_cache,
                                         gate, state, out, workspace, workspace_bytes, stream)
+
+
+def lisa_decode_step_paged(dims, B, lengths, block_table, block_size, max_blocks, num_pages, max_ctx,
+                           q, k_pages, v_pages, q_idx, k_idx_pages, w_idx, gate, state, out,
+                           topm_out, workspace, workspace_bytes, stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_decode_step_paged(ctypes.byref(dims), B, lengths, block_table, block_size,
+                                       max_blocks, num_pages, max_ctx, q, k_pages, v_pages, q_idx,
+                                       k_idx_pages, w_idx, gate, state, out, topm_out, workspace,
+                                       workspace_bytes, stream)
 
 
 def lisa_decode_step(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
@@ -266,6 +280,31 @@ def decode_step_window(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache
                                    _ptr(v_cache), _ptr(gate), _ptr(state), _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def decode_step_paged(dims: LisaDims, lengths, block_table, block_size: int, max_ctx: int, q, k_pages,
+                      v_pages, q_idx, k_idx_pages, w_idx, gate, state, out=None, topm_out=None,
+                      workspace=None, stream=None):
+    """Decode step on page pools (torch device tensors; lengths [B] int32,
+    block_table [B, max_blocks] int32, pools [num_pages*block_size, ...]).
+    `state` is updated in place.  Returns (out, topm_out)."""
+    import torch
+    B = int(q.shape[0])
+    max_blocks = int(block_table.shape[1])
+    num_pages = int(k_pages.shape[0]) // block_size
+    if out is None:
+        out = torch.empty_like(q)
+    if topm_out is None:
+        topm_out = torch.empty((B, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=q.device)
+    wsb = lisa_decode_workspace_bytes(dims, B, max_ctx)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _check(lisa_decode_step_paged(dims, B, _ptr(lengths), _ptr(block_table), block_size, max_blocks,
+                                  num_pages, max_ctx, _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                  _ptr(q_idx), _ptr(k_idx_pages), _ptr(w_idx), _ptr(gate),
+                                  _ptr(state), _ptr(out), _ptr(topm_out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
+    return out, topm_out
 
 
 def decode_step(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache, q_idx, k_idx_cache,

@@ -179,6 +179,30 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
                              lisa_stream_t stream);
 
 /*
+ * lisa_decode_step on paged (block-table) caches, the layout serving systems
+ * keep KV caches in (the pages say nothing about cache layouts; the result
+ * is the same decode step).  The three caches are page pools of
+ * num_pages * block_size rows: k_pages, v_pages [rows, Hkv, d];
+ * k_idx_pages [rows, G, d_I].  Position s of sequence b is row
+ *   block_table[b * max_blocks + s / block_size] * block_size + s % block_size.
+ *   lengths      [B] int32, DEVICE: L_b >= 1 visible tokens, the new token's
+ *                k, v, k_idx already written at position L_b - 1.
+ *   block_table  [B, max_blocks] int32, DEVICE: page ids in [0, num_pages)
+ *                for every block holding a position below L_b (others are
+ *                not read); ids out of range are undefined behaviour.
+ *   block_size   a power of two in [1, 4096]; max_blocks * block_size >= max_ctx.
+ *   The K/V pool of one cache is at most 2 GiB.
+ * Other arguments and the workspace query as lisa_decode_step.
+ */
+lisa_status lisa_decode_step_paged(const lisa_dims *dims, int32_t B, const int32_t *lengths,
+                                   const int32_t *block_table, int32_t block_size,
+                                   int32_t max_blocks, int32_t num_pages, int32_t max_ctx,
+                                   const void *q, const void *k_pages, const void *v_pages,
+                                   const void *q_idx, const void *k_idx_pages, const void *w_idx,
+                                   const void *gate, float *state, void *out, int32_t *topm_out,
+                                   void *workspace, size_t workspace_bytes, lisa_stream_t stream);
+
+/*
  * One generated token per sequence with the sliding-window set
  * max(0, t-M+1)..t (see lisa_prefill_window); arguments as lisa_decode_step
  * without the indexer inputs and topm_out; same workspace query.

@@ -109,6 +109,68 @@ def run_decode(cfg, inp, gate=None, dims=None):
             lisa.from_device(idx))
 
 
+def to_pages(inp, block_size, seed=0, spare=2, fill=64.0):
+    """Scatter packed decode caches into page pools whose pages are shuffled.
+    Table entries past a sequence's last block, and `spare` extra pages, point
+    at pages holding `fill` everywhere: a kernel that reads a row it should
+    not would pick up those values (and, in the indexer, score them highest)
+    instead of faulting."""
+    rng = np.random.default_rng(seed)
+    cu = np.asarray(inp["cu_ctx"], dtype=np.int64)
+    B, max_ctx = inp["B"], inp["max_ctx"]
+    L = np.diff(cu)
+    nblk = (L + block_size - 1) // block_size
+    max_blocks = max(int(nblk.max()), -(-max_ctx // block_size))
+    num_pages = int(nblk.sum()) + spare
+    order = rng.permutation(num_pages)
+    junk = int(order[-1])
+    table = np.full((B, max_blocks), junk, dtype=np.int32)
+    pools = {}
+    for name in ("k_cache", "v_cache", "k_idx_cache"):
+        src = inp[name]
+        pool = np.full((num_pages * block_size,) + src.shape[1:], fill, dtype=src.dtype)
+        pools[name] = pool
+    nxt = 0
+    for b in range(B):
+        for j in range(int(nblk[b])):
+            page = int(order[nxt])
+            nxt += 1
+            table[b, j] = page
+            lo = j * block_size
+            hi = min(int(L[b]), lo + block_size)
+            for name, pool in pools.items():
+                pool[page * block_size:page * block_size + hi - lo] = inp[name][cu[b] + lo:cu[b] + hi]
+    return dict(lengths=L.astype(np.int32), table=table, num_pages=num_pages, **pools)
+
+
+def run_decode_paged(cfg, inp, paged, block_size, dims=None):
+    import torch
+    from hybrid_linear_top_amd import lisa
+    dims = dims or lisa.dims_from_config(cfg)
+    dv = lisa.to_device
+    state = dv(inp["state"])
+    out, idx = lisa.decode_step_paged(dims, dv(paged["lengths"]), dv(paged["table"]), block_size,
+                                      inp["max_ctx"], dv(inp["q"]), dv(paged["k_cache"]),
+                                      dv(paged["v_cache"]), dv(inp["q_idx"]),
+                                      dv(paged["k_idx_cache"]), dv(inp["w_idx"]), dv(inp["gate"]),
+                                      state)
+    torch.cuda.synchronize()
+    return (orc.widen(lisa.from_device(out), cfg.dtype), lisa.from_device(state).astype(np.float64),
+            lisa.from_device(idx))
+
+
+def paged_decode_parity(cfg, inp, block_size, seed=0, report=None):
+    """The packed step against the oracle, then the paged step on the same
+    cache contents: same output, state and index sets, bit for bit (the two
+    differ only in where a row is fetched from)."""
+    decode_parity(cfg, inp, report=report)
+    ref = run_decode(cfg, inp)
+    paged = to_pages(inp, block_size, seed=seed)
+    got = run_decode_paged(cfg, inp, paged, block_size)
+    for name, x, y in zip(("out", "state", "idx"), got, ref):
+        assert np.array_equal(x, y), f"paged {name} differs from packed"
+
+
 def prefill_parity(cfg, inp, rows=None, state_in=None, report=None, past=0):
     """Full prefill parity (all four checks) on the listed rows (None = all).
     With past > 0 the GPU side is a prefill of the first `past` tokens followed

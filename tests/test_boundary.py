@@ -213,3 +213,38 @@ def test_window_limits():
     d = _dims(M=1000)
     need = lisa.lisa_prefill_workspace_bytes(d, 1, 64)
     assert _win(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
+
+
+def _paged(d, B=2, max_ctx=100, bs=16, max_blocks=8, num_pages=16, ws_bytes=1 << 40, **ptrs):
+    p = dict(lengths=FAKE, table=FAKE, q=FAKE, kp=FAKE, vp=FAKE, q_idx=FAKE, kip=FAKE, w_idx=FAKE,
+             gate=FAKE, state=FAKE, out=FAKE, topm_out=0, workspace=FAKE)
+    p.update(ptrs)
+    return lisa.lisa_decode_step_paged(d, B, p["lengths"], p["table"], bs, max_blocks, num_pages,
+                                       max_ctx, p["q"], p["kp"], p["vp"], p["q_idx"], p["kip"],
+                                       p["w_idx"], p["gate"], p["state"], p["out"], p["topm_out"],
+                                       p["workspace"], ws_bytes, 0)
+
+
+@pytest.mark.parametrize("name", ["lengths", "table", "q", "kp", "vp", "q_idx", "kip", "w_idx",
+                                  "gate", "state", "out", "workspace"])
+def test_paged_null_pointer(name):
+    assert _paged(_dims(), **{name: 0}) == lisa.LISA_ERR_INVALID_ARGUMENT
+
+
+def test_paged_limits():
+    d = _dims()
+    assert _paged(d, lengths=FAKE + 2) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _paged(d, table=FAKE + 1) == lisa.LISA_ERR_INVALID_ARGUMENT
+    for bs in (0, 3, 24, 8192):
+        assert _paged(d, bs=bs) == lisa.LISA_ERR_UNSUPPORTED
+    assert _paged(d, max_blocks=6) == lisa.LISA_ERR_INVALID_ARGUMENT      # 6 * 16 < 100
+    assert _paged(d, num_pages=0) == lisa.LISA_ERR_INVALID_ARGUMENT
+    # 2 GiB pool: 1024 pages of 4096 rows of 2 heads x 128 bf16
+    assert _paged(d, bs=4096, max_blocks=1, num_pages=1024) == lisa.LISA_ERR_UNSUPPORTED
+    assert _paged(d, max_ctx=0) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _paged(d, max_ctx=65537, max_blocks=4097) == lisa.LISA_ERR_UNSUPPORTED
+    assert _paged(_dims(M=2049)) == lisa.LISA_ERR_UNSUPPORTED
+    assert _paged(d, B=-1) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _paged(d, B=0, q=0) == lisa.LISA_OK
+    need = lisa.lisa_decode_workspace_bytes(d, 2, 100)
+    assert _paged(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE

@@ -254,6 +254,25 @@ def test_decode_window(case):
     _say("  ", rep)
 
 
+PAGED_DECODE = [
+    (_dcfg(12, 2, 128, 4, 64, 256, [1, 2, 255, 256, 257, 1000]), 16),
+    (_dcfg(28, 4, 128, 4, 64, 512, [4097, 700, 513, 20000], seed=2), 64),
+    (_dcfg(8, 2, 64, 8, 64, 100, [999, 1001, 5000], dtype="f32", seed=3), 1),
+    (_dcfg(4, 1, 64, 4, 32, 256, [40000, 3, 33100], seed=5), 256),  # longest-context select
+    (_dcfg(7, 7, 64, 3, 32, 16, [17, 300, 513, 64], seed=6), 4096),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_DECODE, ids=lambda c: f"{c[0][0].name}_bs{c[1]}")
+def test_decode_paged(case):
+    (cfg, lengths), bs = case
+    _say("decode paged", cfg.name, "block", bs, "seed", cfg.seed)
+    inp = gen.make_decode_inputs(cfg, lengths=lengths)
+    rep = {}
+    parity.paged_decode_parity(cfg, inp, bs, seed=cfg.seed, report=rep)
+    _say("  ", rep)
+
+
 def test_deterministic():
     cfg = gen.CONFIGS[1]
     _say("determinism", cfg.name)
