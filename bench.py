@@ -82,6 +82,7 @@ def decode_bytes(cfg, lengths):
 # pattern, the sources that kernel is built from)
 STAGE_KERNELS = {
     "indexer_topm": (r"indexer_topm_kernel<", ["indexer.hip", "common.hpp", "kernels.hpp"]),
+    "indexer_pack": (r"pack_keys_kernel<", ["indexer.hip", "common.hpp", "kernels.hpp"]),
     "sparse_gate_prefill": (r"sparse_prefill_wave_kernel<|sparse_gate_kernel<[^>]*, false,",
                             ["sparse.hip", "common.hpp", "kernels.hpp"]),
     "sparse_gate_decode": (r"sparse_gate_kernel<[^>]*, true,", ["sparse.hip", "common.hpp", "kernels.hpp"]),

@@ -77,9 +77,11 @@ float scale_log2(const lisa_dims *d) {
 
 // ---- prefill workspace ------------------------------------------------------
 struct PrefillWs {
-    size_t idx, dS, P, total;
+    size_t idx, dS, P, kpk, total;
 };
-PrefillWs prefill_ws(const lisa_dims *d, int B, int n) {
+// n query rows against nk key positions (nk = past + n; 0 when the indexer
+// does not run)
+PrefillWs prefill_ws(const lisa_dims *d, int B, int n, int nk) {
     const size_t G = d->num_kv_heads, Hq = d->num_q_heads, D = d->head_dim;
     const size_t nC = ((size_t)n + 63) / 64;
     PrefillWs w;
@@ -90,6 +92,8 @@ PrefillWs prefill_ws(const lisa_dims *d, int B, int n) {
     off += align_up((size_t)B * G * nC * D * D * 4);
     w.P = off;
     off += align_up((size_t)B * Hq * nC * D * D * elt_bytes(d->dtype));
+    w.kpk = off;
+    off += align_up(nk > 0 ? lisa::indexer_packed_bytes(B, nk, (int)G, d->idx_dim, d->dtype) : 0);
     w.total = off;
     return w;
 }
@@ -113,11 +117,11 @@ DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
 
 // ---- optional per-stage timing (benchmarking) -------------------------------
 enum Stage {
-    ST_LIN_STATE, ST_LIN_SCAN, ST_LIN_OUT, ST_INDEXER, ST_SPARSE_PREFILL,
+    ST_LIN_STATE, ST_LIN_SCAN, ST_LIN_OUT, ST_IDX_PACK, ST_INDEXER, ST_SPARSE_PREFILL,
     ST_DEC_SCORE_STATE, ST_DEC_SELECT, ST_SPARSE_DECODE, ST_COUNT
 };
 const char *const kStageNames[ST_COUNT] = {
-    "linear_chunk_state", "linear_prefix_scan", "linear_chunk_output", "indexer_topm",
+    "linear_chunk_state", "linear_prefix_scan", "linear_chunk_output", "indexer_pack", "indexer_topm",
     "sparse_gate_prefill", "decode_score_state", "decode_select", "sparse_gate_decode"};
 
 struct Timing {
@@ -189,7 +193,20 @@ lisa_status lisa_prefill_workspace_bytes(const lisa_dims *dims, int32_t B, int32
     if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
     if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
-    *bytes = prefill_ws(dims, B, n).total;
+    *bytes = prefill_ws(dims, B, n, n).total;
+    return ok();
+}
+
+lisa_status lisa_prefill_continue_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t past,
+                                                  int32_t n, size_t *bytes) {
+    lisa_status st = check_dims(dims, true, true);
+    if (st) return st;
+    if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (B < 0 || n < 0 || past < 0)
+        return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, past=%d, n=%d must be >= 0", B, past, n);
+    if ((int64_t)past + n > 32768)
+        return fail(LISA_ERR_UNSUPPORTED, "past + n = %lld above the supported 32768", (long long)past + n);
+    *bytes = prefill_ws(dims, B, n, past + n).total;
     return ok();
 }
 
@@ -249,7 +266,8 @@ lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t
     LISA_OPT(state_out, "state_out");
     LISA_OPT(topm_out, "topm_out");
     LISA_NEED(workspace, "workspace");
-    const PrefillWs w = prefill_ws(dims, B, n);
+    // the window variant asks for what lisa_prefill_workspace_bytes gives (it needs less)
+    const PrefillWs w = prefill_ws(dims, B, n, window ? n : past + n);
     if (workspace_bytes < w.total)
         return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -293,9 +311,13 @@ lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t
     ia.HI = dims->idx_heads;
     ia.M = dims->top_m;
     ia.past = past;
-    if (!window)
+    ia.k_packed = ws + w.kpk;
+    if (!window) {
+        LISA_HIP(timed(ST_IDX_PACK, s, [&] { return lisa::launch_indexer_pack(ia, dims->dtype, dims->idx_dim, s); }),
+                 "indexer key-pack launch");
         LISA_HIP(timed(ST_INDEXER, s, [&] { return lisa::launch_indexer_prefill(ia, dims->dtype, dims->idx_dim, s); }),
                  "indexer launch");
+    }
 
     lisa::SparseArgs sa{};
     sa.q = q;

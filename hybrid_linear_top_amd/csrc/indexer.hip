@@ -10,8 +10,11 @@
 //  * A work-group is one wave that owns 8 consecutive queries of one group.
 //    It streams the group's keys (L2-resident: every XCD serves a single
 //    group) in tiles of 64, loading the MFMA B fragments straight from memory
-//    one tile ahead, and scores each tile with 16 v_mfma_f32_16x16x32_bf16
-//    issued back to back.  The A operand rows are (query, indexer head) pairs
+//    two tiles ahead, and scores each tile with 16 v_mfma_f32_16x16x32_bf16
+//    issued back to back.  The keys are first re-laid out (pack_keys_kernel)
+//    so that every fragment load of a wave reads 1 KB of consecutive bytes:
+//    read in place, each load touches 16 key rows for 64 bytes each, and the
+//    scan is then bound by the address units rather than by anything else.  The A operand rows are (query, indexer head) pairs
 //    laid out so that the four accumulator rows a lane receives are the four
 //    heads of one query: the ReLU and the w-weighted head sum are lane-local.
 //  * Column n of key block cb holds key k0 + 4n + cb, so each lane scores
@@ -266,6 +269,39 @@ __device__ __attribute__((noinline)) TrimResult trim_buffer(CandBuf buf, int c, 
     return TrimResult{c, th};
 }
 
+// Packed key tiles: for batch b and group g, tile kt holds keys 64kt..64kt+63
+// as 4 x KD fragments (key block cb, K step kc), each 64 lanes x 8 elements in
+// lane order, where lane (grp, col) carries elements kc*32 + grp*8 .. +7 of key
+// 64kt + 4col + cb -- exactly what that lane feeds the MFMA.  Keys past the
+// last one are zeros.
+template <typename T, int DI>
+__global__ __launch_bounds__(256) void pack_keys_kernel(const T *__restrict__ k_idx, T *__restrict__ packed,
+                                                        int64_t total, int nk, int G, int ntiles) {
+    constexpr int KD = DI / 32;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one lane-fragment of 8 elements
+    if (i >= total) return;
+    const int lane = (int)(i & 63);
+    int64_t r = i >> 6;
+    const int kc = (int)(r % KD);
+    r /= KD;
+    const int cb = (int)(r & 3);
+    r >>= 2;
+    const int kt = (int)(r % ntiles);
+    r /= ntiles;
+    const int g = (int)(r % G), b = (int)(r / G);
+    const int key = kt * kKT + 4 * (lane & 15) + cb;
+    Frag<T> f;
+    if (key < nk) f.load(k_idx + (((size_t)b * nk + key) * G + g) * DI + kc * 32 + (lane >> 4) * 8);
+    else f.zero();
+    T *dst = packed + (size_t)i * 8;
+    if constexpr (std::is_same<T, uint16_t>::value) {
+        *reinterpret_cast<u32x4 *>(dst) = f.v;
+    } else {
+        reinterpret_cast<f32x4 *>(dst)[0] = f.lo;
+        reinterpret_cast<f32x4 *>(dst)[1] = f.hi;
+    }
+}
+
 template <typename T, int DI, int HH, int CAP, int QB>
 struct IdxCfg {
     static constexpr int KD = DI / 32;      // MFMA K-steps
@@ -302,9 +338,9 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     const int ntiles = t_hi / kKT + 1;
 
     const T *qI = reinterpret_cast<const T *>(a.q_idx);
-    const T *kI = reinterpret_cast<const T *>(a.k_idx) + ((size_t)b * nk * G + g) * DI;
+    const int ntk = (nk + kKT - 1) / kKT;  // key tiles
+    const T *kI = reinterpret_cast<const T *>(a.k_packed) + ((size_t)b * G + g) * ntk * kKT * DI;
     const T *wI = reinterpret_cast<const T *>(a.w_idx);
-    const size_t krs = (size_t)G * DI;  // key row stride
 
     // ---- per-lane constants: A fragments, head weights, query rows -----------
     Frag<T> af[QB][HH][C::KD];
@@ -342,21 +378,22 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         tau[qb] = tq[qb] < nk ? -INFINITY : INFINITY;  // padding queries accept nothing
     }
 
-    // B fragments of one key tile: key 4*col + cb, dims 32*kc + 8*grp .. +7,
-    // through a per-tile buffer descriptor (keys >= nk read as zeros)
+    // B fragments of one packed key tile: key 4*col + cb, dims 32*kc + 8*grp
+    // .. +7, through a per-tile buffer descriptor (tiles past the last read
+    // as zeros)
     constexpr uint32_t EB = Elt<T>::kBytes;
-    const uint32_t key_bytes = (uint32_t)nk * (uint32_t)krs * EB;
-    uint32_t voff[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) voff[cb] = ((uint32_t)(4 * col + cb) * (uint32_t)krs + grp * 8) * EB;
+    constexpr uint32_t kTileBytes = kKT * DI * EB, kFragBytes = 64 * 8 * EB;
+    const uint32_t all_bytes = (uint32_t)ntk * kTileBytes;
+    const uint32_t voff = (uint32_t)lane * 8 * EB;
     auto load_b = [&](int kt, Frag<T> (&bf)[4][C::KD]) {
-        const uint32_t tile_off = (uint32_t)kt * kKT * (uint32_t)krs * EB;
+        const uint32_t tile_off = (uint32_t)kt * kTileBytes;
         const rsrc_t r = make_rsrc(reinterpret_cast<const unsigned char *>(kI) + tile_off,
-                                   key_bytes > tile_off ? key_bytes - tile_off : 0u);
+                                   all_bytes > tile_off ? all_bytes - tile_off : 0u);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int kc = 0; kc < C::KD; ++kc) frag_buf_load(bf[cb][kc], r, voff[cb] + kc * 32 * EB);
+            for (int kc = 0; kc < C::KD; ++kc)
+                frag_buf_load(bf[cb][kc], r, voff + (uint32_t)(cb * C::KD + kc) * kFragBytes);
     };
 
 
@@ -610,6 +647,28 @@ hipError_t by_shape(const IndexerArgs &a, int dI, hipStream_t s) {
 }
 
 }  // namespace
+
+template <typename T>
+hipError_t pack(const IndexerArgs &a, int dI, hipStream_t s) {
+    const int nk = a.past + a.n, ntiles = (nk + kKT - 1) / kKT;
+    const int64_t total = (int64_t)a.B * a.G * ntiles * kKT * dI / 8;  // lane-fragments
+    const dim3 grid((unsigned)((total + 255) / 256));
+    const T *src = reinterpret_cast<const T *>(a.k_idx);
+    T *dst = reinterpret_cast<T *>(a.k_packed);
+    if (dI == 64) hipLaunchKernelGGL((pack_keys_kernel<T, 64>), grid, dim3(256), 0, s, src, dst, total, nk, a.G, ntiles);
+    else hipLaunchKernelGGL((pack_keys_kernel<T, 32>), grid, dim3(256), 0, s, src, dst, total, nk, a.G, ntiles);
+    return hipGetLastError();
+}
+
+size_t indexer_packed_bytes(int B, int nk, int G, int dI, int dtype) {
+    const size_t ntiles = ((size_t)nk + kKT - 1) / kKT;
+    return (size_t)B * G * ntiles * kKT * dI * (dtype == 1 ? 2 : 4);
+}
+
+hipError_t launch_indexer_pack(const IndexerArgs &a, int dtype, int dI, hipStream_t s) {
+    if (a.B * a.n == 0) return hipSuccess;
+    return dtype == 1 ? pack<uint16_t>(a, dI, s) : pack<float>(a, dI, s);
+}
 
 hipError_t launch_indexer_prefill(const IndexerArgs &a, int dtype, int dI, hipStream_t s) {
     if (a.B * a.n == 0) return hipSuccess;

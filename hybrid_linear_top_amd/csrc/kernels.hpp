@@ -90,10 +90,13 @@ struct IndexerArgs {
     const void *q_idx;   // [B,n,G,HI,dI]
     const void *k_idx;   // [B,past+n,G,dI]
     const void *w_idx;   // [B,n,G,HI]
+    void *k_packed;      // workspace: k_idx re-laid out per key tile (indexer_packed_bytes)
     int32_t *idx;        // [B,n,G,M]: key positions in 0..past+t
     int B, n, G, HI, M;
     int past;            // query t (0-based among the n) sits at position past + t
 };
+size_t indexer_packed_bytes(int B, int nk, int G, int dI, int dtype);
+hipError_t launch_indexer_pack(const IndexerArgs &a, int dtype, int dI, hipStream_t s);
 hipError_t launch_indexer_prefill(const IndexerArgs &a, int dtype, int dI, hipStream_t s);
 
 }  // namespace lisa

@@ -23,7 +23,8 @@ LISA_ERR_HIP = 4
 LISA_F32 = 0
 LISA_BF16 = 1
 
-EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill", "lisa_prefill_continue",
+EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill_continue_workspace_bytes", "lisa_prefill",
+           "lisa_prefill_continue",
            "lisa_prefill_window", "lisa_decode_step_window", "lisa_decode_step_paged",
            "lisa_decode_workspace_bytes",
            "lisa_decode_step", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
@@ -52,6 +53,8 @@ def _load(path: str = LIB_PATH):
     dp = ctypes.POINTER(LisaDims)
     lib.lisa_prefill_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
     lib.lisa_prefill_workspace_bytes.restype = ctypes.c_int
+    lib.lisa_prefill_continue_workspace_bytes.argtypes = [dp, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.lisa_prefill_continue_workspace_bytes.restype = ctypes.c_int
     lib.lisa_prefill.argtypes = [dp, i32, i32] + [vp] * 7 + [vp, vp, vp, vp, vp, sz, vp]
     lib.lisa_prefill.restype = ctypes.c_int
     lib.lisa_prefill_continue.argtypes = [dp, i32, i32, i32] + [vp] * 7 + [vp, vp, vp, vp, vp, sz, vp]
@@ -96,6 +99,12 @@ def lisa_last_error() -> str:
 
 def lisa_build_info() -> str:
     return _lib.lisa_build_info().decode()
+
+
+def lisa_prefill_continue_workspace_bytes(dims: LisaDims, B: int, past: int, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.lisa_prefill_continue_workspace_bytes(ctypes.byref(dims), B, past, n, ctypes.byref(out)))
+    return out.value
 
 
 def lisa_prefill_workspace_bytes(dims: LisaDims, B: int, n: int) -> int:
@@ -235,7 +244,7 @@ def prefill_continue(dims: LisaDims, past: int, q, k_cache, v_cache, q_idx, k_id
                                 dtype=torch.float32, device=dev)
     if topm_out is None:
         topm_out = torch.empty((B, n, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev)
-    wsb = lisa_prefill_workspace_bytes(dims, B, n)
+    wsb = lisa_prefill_continue_workspace_bytes(dims, B, past, n)
     if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     _check(lisa_prefill_continue(dims, B, past, n, _ptr(q), _ptr(k_cache), _ptr(v_cache),

@@ -90,6 +90,12 @@ typedef struct {
 lisa_status lisa_prefill_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
                                          size_t *bytes);
 
+/* Workspace needed by lisa_prefill_continue for n new tokens after `past`
+ * cached ones (the indexer keeps a re-laid-out copy of all past + n indexer
+ * keys).  past == 0 gives lisa_prefill_workspace_bytes. */
+lisa_status lisa_prefill_continue_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t past,
+                                                  int32_t n, size_t *bytes);
+
 /*
  * Whole-prompt forward pass of one LISA layer (all four parts above).
  *   q      [B, n, Hq, d]          k, v  [B, n, Hkv, d]
@@ -124,7 +130,7 @@ lisa_status lisa_prefill(const lisa_dims *dims, int32_t B, int32_t n, const void
  *   out    [B, n, Hq, d]; state_out [B, Hq, d, d] fp32 or NULL: S after the
  *          last token; topm_out [B, n, G, M] int32 or NULL: positions in
  *          0..past+t, ascending, -1 padded.
- * The workspace is lisa_prefill_workspace_bytes(dims, B, n) (n new tokens).
+ * The workspace is lisa_prefill_continue_workspace_bytes(dims, B, past, n).
  * past + n <= 32768; n == 0 or B == 0 is a valid no-op; past == 0 is
  * lisa_prefill.
  */

@@ -248,3 +248,18 @@ def test_paged_limits():
     assert _paged(d, B=0, q=0) == lisa.LISA_OK
     need = lisa.lisa_decode_workspace_bytes(d, 2, 100)
     assert _paged(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
+
+
+def test_continue_workspace_query():
+    d = _dims()
+    # past == 0 is the prefill query; more cached keys need more workspace
+    assert lisa.lisa_prefill_continue_workspace_bytes(d, 1, 0, 512) == lisa.lisa_prefill_workspace_bytes(d, 1, 512)
+    assert lisa.lisa_prefill_continue_workspace_bytes(d, 1, 4096, 512) > lisa.lisa_prefill_workspace_bytes(d, 1, 512)
+    assert lisa.lisa_prefill_continue_workspace_bytes(d, 2, 4096, 512) > lisa.lisa_prefill_continue_workspace_bytes(d, 1, 4096, 512)
+    with pytest.raises(lisa.LisaError):
+        lisa.lisa_prefill_continue_workspace_bytes(d, 1, 32768, 1)
+    with pytest.raises(lisa.LisaError):
+        lisa.lisa_prefill_continue_workspace_bytes(d, 1, -1, 8)
+    # a continue call given only the n-token prefill workspace is refused
+    need = lisa.lisa_prefill_continue_workspace_bytes(d, 1, 4096, 64)
+    assert _cont(d, past=4096, n=64, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
