@@ -7,11 +7,12 @@
 // of the full context (arxivdaily page, English abstract), the lower index
 // winning ties.  The n^2/2 scores never leave the chip:
 //
-//  * A work-group is one wave that owns 8 consecutive queries of one group.
+//  * A work-group is one wave that owns 4 consecutive queries of one group.
 //    It streams the group's keys (L2-resident: every XCD serves a single
 //    group) in tiles of 64, loading the MFMA B fragments straight from memory
-//    two tiles ahead, and scores each tile with 16 v_mfma_f32_16x16x32_bf16
-//    issued back to back.  The keys are first re-laid out (pack_keys_kernel)
+//    one tile ahead, and scores each tile with 8 v_mfma_f32_16x16x32_bf16
+//    issued back to back.  Four queries per wave and two fragment buffers keep
+//    a wave at 166 VGPRs and 12 KB of LDS, so 12 waves share a CU.  The keys are first re-laid out (pack_keys_kernel)
 //    so that every fragment load of a wave reads 1 KB of consecutive bytes:
 //    read in place, each load touches 16 key rows for 64 bytes each, and the
 //    scan is then bound by the address units rather than by anything else.  The A operand rows are (query, indexer head) pairs
@@ -43,7 +44,7 @@ namespace {
 
 constexpr int kKT = 64;  // keys per tile
 #ifndef LISA_IDX_QB
-#define LISA_IDX_QB 2  // query quads per wave (4 queries each)
+#define LISA_IDX_QB 1  // query quads per wave (4 queries each)
 #endif
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         }
     };
 
-    Frag<T> b0[4][C::KD], b1[4][C::KD], b2[4][C::KD];
+    Frag<T> b0[4][C::KD], b1[4][C::KD];
     // tiles below kd hold only keys < qw0 <= every query of the wave
     const int kd = qw0 / kKT;
     // Prefetches are never skipped: a tile past the end is fetched through an
@@ -566,9 +567,9 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         }
     }
 
-    // ---- scan: every tile, three fragment buffers rotating (tiles kt+1 and
-    // kt+2 load while kt computes); a second pass redoes exactly the queries
-    // whose sampled threshold turned out too high ------------------------------
+    // ---- scan: every tile, two fragment buffers alternating (tile kt+1 loads
+    // while kt computes); a second pass redoes exactly the queries whose
+    // sampled threshold turned out too high --------------------------------------
     auto step = [&](int kt, const Frag<T> (&bc)[4][C::KD]) {
         if (kt >= kd) tile_step(kt, bc, std::true_type{});
         else tile_step(kt, bc, std::false_type{});
@@ -576,16 +577,12 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
         load_b(0, b0);
-        load_b(tile_or_null(1, ntiles), b1);
-        for (int kt = 0; kt < ntiles; kt += 3) {
-            load_b(tile_or_null(kt + 2, ntiles), b2);
+        for (int kt = 0; kt < ntiles; kt += 2) {
+            load_b(tile_or_null(kt + 1, ntiles), b1);
             step(kt, b0);
             if (kt + 1 >= ntiles) break;
-            load_b(tile_or_null(kt + 3, ntiles), b0);
+            load_b(tile_or_null(kt + 2, ntiles), b0);
             step(kt + 1, b1);
-            if (kt + 2 >= ntiles) break;
-            load_b(tile_or_null(kt + 4, ntiles), b1);
-            step(kt + 2, b2);
         }
         if (ns == 0) break;  // started from -inf: already exact
         uint64_t redo = 0;
@@ -633,7 +630,7 @@ hipError_t launch(const IndexerArgs &a, hipStream_t s) {
 
 template <typename T, int DI, int HH>
 hipError_t by_m(const IndexerArgs &a, hipStream_t s) {
-    // per-wave LDS: 8 candidate buffers of CAP 8-byte entries
+    // per-wave LDS: 4 candidate buffers of CAP 6-byte entries
     if (a.M <= 128) return launch<T, DI, HH, 256>(a, s);
     if (a.M <= 256) return launch<T, DI, HH, 448>(a, s);
     return launch<T, DI, HH, 1024>(a, s);
