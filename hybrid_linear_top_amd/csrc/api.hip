@@ -398,6 +398,7 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     da.w_idx = w_idx;
     da.cu = cu_ctx;
     da.map = map;
+    da.pool_rows = pool_rows;
     da.state = state;
     da.olin = olin;
     da.scores = scores;

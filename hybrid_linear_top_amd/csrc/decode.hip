@@ -7,9 +7,9 @@
 //     (the indexer scans the full context with a ReLU'd dot product: arxivdaily
 //     page for arXiv 2607.19358, English abstract; gptget.net analysis,
 //     method-details section).  This stream is the largest HBM consumer of a
-//     decode step, so it is laid out for coalescing: each wave reads whole
-//     128/256-byte key rows, 16 bytes per lane, and reduces the per-lane
-//     partial dot products across the lanes of a row.
+//     decode step; the dot products run on MFMA in the prefill indexer's
+//     layout, so the per-token work is a few VALU operations and the groups
+//     stay bound by memory.
 //   * state groups do the linear-attention step of one query head:
 //     S_t = S_{t-1} + k_t v_t^T in place and o_lin = q_t^T S_t (identity
 //     feature map and state matrix S_t, O(1) per token: gptget.net,
@@ -26,103 +26,117 @@ namespace lisa {
 
 namespace {
 
-// Widen one 16-byte chunk (8 bf16 or 4 fp32) to fp32.
-template <typename T> struct Chunk;
-template <> struct Chunk<uint16_t> {
-    __device__ static __forceinline__ void widen(const u32x4 &x, float *f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(x[i] << 16);
-            f[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
-        }
-    }
-};
-template <> struct Chunk<float> {
-    __device__ static __forceinline__ void widen(const u32x4 &x, float *f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(x[i]);
-    }
-};
-
-// Sum over aligned groups of N lanes (N = 4, 8 or 16), result in every lane.
-template <int N>
-__device__ __forceinline__ float row_sum(float p) {
-    p += dpp_f32<0xB1>(p);                      // lanes i^1
-    p += dpp_f32<0x4E>(p);                      // lanes i^2
-    if constexpr (N >= 8) p += dpp_f32<0x141>(p);   // other quad of the 8
-    if constexpr (N >= 16) p += dpp_f32<0x140>(p);  // other half of the row
-    return p;
-}
-
+// Scores of one 128-token tile of one sequence, all groups.  A wave task is
+// 64 tokens of one group: four 16x16x32 MFMA blocks per K step with the
+// query's indexer heads as the A rows (rows past H_I are zero) and 16 tokens
+// as the B columns, exactly as the prefill indexer lays out a query and its
+// keys; lane (0, col) then holds the heads' dot products for token col and
+// forms the score with the same ReLU'd, weighted sum in the same order.
+// The key rows are read whole -- each load instruction covers complete
+// 128-byte lines, which streams HBM about 1.5x faster than the fragment
+// layout's half lines -- and pass through the wave's LDS slice (XOR-swizzled
+// 16-byte pieces, conflict-free both ways) on their way to the B fragments.
 template <typename T, int DI, int HIPAD>
-__device__ void score_group(const DecodeScoreArgs &a, int sb) {
-    constexpr int EPC = 16 / Elt<T>::kBytes;  // elements per 16-byte chunk
-    constexpr int CPR = DI / EPC;             // lanes per key row
-    constexpr int RPI = 64 / CPR;             // rows per wave iteration
-    constexpr int TPW = 64;                   // tokens per wave task
-    constexpr int NIT = TPW / RPI;
+__device__ void score_group(const DecodeScoreArgs &a, int sb, u32x4 *stage) {
+    constexpr int KD = DI / 32;
+    constexpr int TPW = 64;                  // tokens per wave task
+    constexpr uint32_t EB = Elt<T>::kBytes;
+    constexpr int PPR = DI * (int)EB / 16;   // 16-byte pieces per key row (4, 8 or 16)
+    constexpr int RPI = 64 / PPR;            // key rows per load instruction
+    constexpr int NLD = TPW / RPI;           // load instructions per task
+    constexpr int SWS = PPR == 4 ? 2 : PPR == 8 ? 1 : 0;  // swizzle: piece ^ ((row >> SWS) & (PPR - 1))
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
     const int b = sb / a.tiles_per_seq, tile = sb % a.tiles_per_seq;
-    const int64_t row0 = a.map.table ? 0 : a.cu[b];
-    const int32_t *ptab = a.map.table ? a.map.table + (size_t)b * a.map.max_blocks : nullptr;
+    const bool paged = a.map.table != nullptr;
+    const int64_t row0 = paged ? 0 : a.cu[b];
     const int L = cache_len(a.map, b, a.max_ctx);
     const int tok0 = tile * kDecodeTile;
     if (tok0 >= L) return;
     const int tok_end = min(tok0 + kDecodeTile, L);
-    const int c = lane % CPR, rr = lane / CPR;
-    const int G = a.G;
+    const int G = a.G, HI = a.HI;
     const int ntask = G * (kDecodeTile / TPW);
-    const T *qI = reinterpret_cast<const T *>(a.q_idx);
-    const T *wI = reinterpret_cast<const T *>(a.w_idx);
-    const T *kI = reinterpret_cast<const T *>(a.k_idx_cache);
+    // Every load below is unconditional, through a buffer descriptor that
+    // turns the lanes with nothing to read into zeros: a load under a branch
+    // would make the compiler wait for all loads in flight.
+    const uint32_t row_bytes = (uint32_t)G * DI * EB;
+    const rsrc_t krs = make_rsrc(reinterpret_cast<const T *>(a.k_idx_cache) + (size_t)row0 * G * DI,
+                                 (uint32_t)(paged ? a.pool_rows : L) * row_bytes);
+    // the page-table row (empty for packed caches: those lookups read zeros)
+    const rsrc_t trs = make_rsrc(paged ? (const void *)(a.map.table + (size_t)b * a.map.max_blocks) : (const void *)a.cu,
+                                 paged ? (uint32_t)a.map.max_blocks * 4u : 0u);
+    const int lb = a.map.log2_block;
+    float *out_b = a.scores + (size_t)b * G * a.max_ctx;
+    u32x4 *slice = stage + wave * TPW * PPR;  // this wave's 64 rows
+    const int lrow = lane / PPR, lpc = lane % PPR;  // row and piece this lane loads
+
     for (int task = wave; task < ntask; task += 4) {
-        const int g = task % G, sub = task / G;
-        const int tb = tok0 + sub * TPW;
-        if (tb >= tok_end) continue;
-        u32x4 raw[NIT];
+        const int g = task % G, tb = tok0 + (task / G) * TPW;
+        const size_t qrow = ((size_t)b * G + g) * HI;
+        // query heads and weights (rows past H_I read as zeros), page lookups
+        const rsrc_t qrs = make_rsrc(reinterpret_cast<const T *>(a.q_idx) + qrow * DI, (uint32_t)HI * DI * EB);
+        const rsrc_t wrs = make_rsrc(reinterpret_cast<const T *>(a.w_idx) + qrow, (uint32_t)HI * EB);
+        Frag<T> af[KD];
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int tok = tb + it * RPI + rr;
-            if (tok < tok_end)
-                raw[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                    kI + ((size_t)cache_row(a.map, row0, ptab, tok) * G + g) * DI + c * EPC));
-            else
-                raw[it] = u32x4{0u, 0u, 0u, 0u};
-        }
-        // query rows and head weights: unconditional loads (heads past HI
-        // re-read the last head and get weight 0) so they fly together
-        float qv[HIPAD][EPC];
+        for (int kc = 0; kc < KD; ++kc) frag_buf_load(af[kc], qrs, (uint32_t)(col * DI + kc * 32 + grp * 8) * EB);
         float wv[HIPAD];
-        u32x4 qraw[HIPAD];
-        T wraw[HIPAD];
 #pragma unroll
         for (int j = 0; j < HIPAD; ++j) {
-            const int jj = min(j, a.HI - 1);
-            qraw[j] = *reinterpret_cast<const u32x4 *>(qI + ((size_t)(b * G + g) * a.HI + jj) * DI + c * EPC);
-            wraw[j] = wI[(size_t)(b * G + g) * a.HI + jj];
+            if constexpr (EB == 2)
+                wv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wrs, (uint32_t)j * 2u, 0u, 0) << 16);
+            else
+                wv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wrs, (uint32_t)j * 4u, 0u, 0));
+        }
+        int32_t blk[NLD];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int tok = min(tb + j * RPI + lrow, L - 1);
+            blk[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(trs, (uint32_t)(tok >> lb) * 4u, 0u, 0);
+        }
+        // whole key rows: instruction j reads rows j*RPI .. j*RPI + RPI - 1
+        u32x4 raw[NLD];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int tok = tb + j * RPI + lrow;
+            const uint32_t rrow = paged ? ((uint32_t)blk[j] << lb) + (uint32_t)(tok & ((1 << lb) - 1)) : (uint32_t)tok;
+            const uint32_t off = tok < tok_end ? rrow * row_bytes + (uint32_t)g * DI * EB + (uint32_t)lpc * 16u : kOffNone;
+            raw[j] = buf_load16(krs, off);
         }
 #pragma unroll
-        for (int j = 0; j < HIPAD; ++j) {
-            wv[j] = j < a.HI ? Elt<T>::to_f32(wraw[j]) : 0.0f;
-            Chunk<T>::widen(qraw[j], qv[j]);
+        for (int j = 0; j < NLD; ++j) {
+            const int r = j * RPI + lrow;
+            slice[r * PPR + (lpc ^ ((r >> SWS) & (PPR - 1)))] = raw[j];
         }
-        float *out = a.scores + (size_t)(b * G + g) * a.max_ctx;
+        wave_lds_sync();
+        float *out = out_b + (size_t)g * a.max_ctx;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            float kf[EPC];
-            Chunk<T>::widen(raw[it], kf);
-            float score = 0.0f;
+        for (int cb = 0; cb < 4; ++cb) {
+            const int r = 16 * cb + col;
+            const int sw = (r >> SWS) & (PPR - 1);
+            f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < HIPAD; ++j) {
-                float p = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) p = fmaf(qv[j][e], kf[e], p);
-                p = row_sum<CPR>(p);
-                score = fmaf(wv[j], fmaxf(p, 0.0f), score);
+            for (int kc = 0; kc < KD; ++kc) {
+                Frag<T> bfr;
+                if constexpr (EB == 2) {
+                    bfr.v = slice[r * PPR + ((kc * 4 + grp) ^ sw)];
+                } else {
+                    bfr.lo = __builtin_bit_cast(f32x4, slice[r * PPR + ((kc * 8 + 2 * grp) ^ sw)]);
+                    bfr.hi = __builtin_bit_cast(f32x4, slice[r * PPR + ((kc * 8 + 2 * grp + 1) ^ sw)]);
+                }
+                acc = mma16(af[kc], bfr, acc);
             }
-            const int tok = tb + it * RPI + rr;
-            if (c == 0 && tok < tok_end) out[tok] = score;
+            float sc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc = fmaf(wv[i], fmaxf(acc[i], 0.0f), sc);
+            if constexpr (HIPAD > 4) {
+                // heads 4..7 sit in the rows of lane col + 16: continue the same chain
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc = fmaf(wv[4 + i], fmaxf(__shfl_down(acc[i], 16), 0.0f), sc);
+            }
+            const int tok = tb + r;
+            if (grp == 0 && tok < tok_end) out[tok] = sc;
         }
+        wave_lds_sync();  // the slice is rewritten by the next task
     }
 }
 
@@ -184,11 +198,14 @@ __device__ void state_group(const DecodeScoreArgs &a, int u, float *smem) {
 
 template <typename T, int D, int DI, int HIPAD>
 __global__ __launch_bounds__(256) void decode_score_state_kernel(DecodeScoreArgs a, int n_state) {
-    __shared__ float smem[3 * 128 + 16 * 128];
+    // state groups: 3 vectors + the reduction rows; score groups: 64 key rows per wave
+    constexpr int kStateBytes = (3 * 128 + 16 * 128) * 4;
+    constexpr int kStageBytes = 4 * 64 * DI * (int)Elt<T>::kBytes;
+    __shared__ u32x4 smem[(kStateBytes > kStageBytes ? kStateBytes : kStageBytes) / 16];
     if ((int)blockIdx.x < n_state)
-        state_group<T, D>(a, blockIdx.x, smem);
+        state_group<T, D>(a, blockIdx.x, reinterpret_cast<float *>(smem));
     else
-        score_group<T, DI, HIPAD>(a, blockIdx.x - n_state);
+        score_group<T, DI, HIPAD>(a, blockIdx.x - n_state, smem);
 }
 
 // ---------------------------------------------------------------------------

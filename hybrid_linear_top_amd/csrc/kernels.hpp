@@ -36,13 +36,14 @@ struct DecodeScoreArgs {
     const void *w_idx;        // [B,G,HI]
     const int64_t *cu;        // [B+1] device
     CacheMap map;
+    int64_t pool_rows;        // paged caches: rows in the page pool
     float *state;             // [B,Hq,d,d] in/out
     float *olin;              // [B,Hq,d] workspace
     float *scores;            // [B,G,max_ctx] workspace
     int B, Hq, G, HI, max_ctx;
     int tiles_per_seq;        // ceil(max_ctx / kDecodeTile)
 };
-constexpr int kDecodeTile = 256;  // tokens per score work-group
+constexpr int kDecodeTile = 128;  // tokens per score work-group
 
 hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI,
                                      hipStream_t s);
