@@ -21,6 +21,9 @@ namespace lisa {
 namespace {
 
 constexpr int kC = 64;  // chunk length
+#ifndef LISA_SCAN_U
+#define LISA_SCAN_U 32
+#endif
 
 // Half-fragment helpers: 4 consecutive elements into the low / high half.
 __device__ __forceinline__ void load_halves(Frag<uint16_t> &f, const uint16_t *p0, const uint16_t *p1) {
@@ -105,32 +108,36 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(LinearArgs a) {
     if (e4 >= Q4) return;
     const int g = bg % a.G, b = bg / a.G;
     const int j = (4 * e4) / D, i0 = (4 * e4) % D;  // transposed layout: element (j, i0..i0+3)
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(a.dS + (size_t)bg * a.nC * D * D) + e4;
+    // chunk c's float4 e4 of this group's dS: loads past the last chunk read
+    // zeros through the descriptor, so a batch of U loads is always in flight
+    const rsrc_t srs = make_rsrc(a.dS + (size_t)bg * a.nC * D * D, (uint32_t)a.nC * D * D * 4u);
     T *P = reinterpret_cast<T *>(a.P);
     f32x4 run = {0, 0, 0, 0};
     const size_t pbase = a.per_head ? ((size_t)b * a.Hq + g * a.r) : ((size_t)b * a.G + g);
-    constexpr int U = 4;
+    constexpr int U = LISA_SCAN_U;
+#pragma unroll 1
     for (int c0 = 0; c0 < a.nC; c0 += U) {
         f32x4 x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            x[u] = (c0 + u < a.nC) ? src[(size_t)(c0 + u) * Q4] : f32x4{0, 0, 0, 0};
+            x[u] = __builtin_bit_cast(f32x4, buf_load16(srs, ((uint32_t)(c0 + u) * Q4 + (uint32_t)e4) * 16u));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + u;
-            if (c >= a.nC) break;
-            if (!a.per_head) {
-                T *dst = P + (pbase * a.nC + c) * D * D + 4 * e4;
+            if (c < a.nC) {
+                if (!a.per_head) {
+                    T *dst = P + (pbase * a.nC + c) * D * D + 4 * e4;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dst[q] = Elt<T>::from_f32(run[q]);
-            } else {
-                // S_{c-1} = S0 + running sum, S0 read transposed from [i][j]
-                for (int hh = 0; hh < a.r; ++hh) {
-                    const float *S0 = a.state_in + (pbase + hh) * D * D;
-                    T *dst = P + ((pbase + hh) * a.nC + c) * D * D + 4 * e4;
+                    for (int q = 0; q < 4; ++q) dst[q] = Elt<T>::from_f32(run[q]);
+                } else {
+                    // S_{c-1} = S0 + running sum, S0 read transposed from [i][j]
+                    for (int hh = 0; hh < a.r; ++hh) {
+                        const float *S0 = a.state_in + (pbase + hh) * D * D;
+                        T *dst = P + ((pbase + hh) * a.nC + c) * D * D + 4 * e4;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        dst[q] = Elt<T>::from_f32(run[q] + S0[(size_t)(i0 + q) * D + j]);
+                        for (int q = 0; q < 4; ++q)
+                            dst[q] = Elt<T>::from_f32(run[q] + S0[(size_t)(i0 + q) * D + j]);
+                    }
                 }
             }
             run += x[u];
