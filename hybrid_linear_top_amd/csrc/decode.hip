@@ -140,17 +140,33 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb, u32x4 *stage) {
     }
 }
 
+// Linear-attention step of one query head, one column slice of its state:
+// state group uu is (sequence b, head h, slice part), the slice being value
+// columns [part*D/CS, (part+1)*D/CS) of S (all D rows), so o_lin's columns
+// of the slice are complete within the group.  The state loads are issued
+// before anything else, as they wait for nothing.
 template <typename T, int D>
-__device__ void state_group(const DecodeScoreArgs &a, int u, float *smem) {
+__device__ void state_group(const DecodeScoreArgs &a, int uu, float *smem) {
+    constexpr int CS = D / 32;        // column slices per head
+    constexpr int NQ = D / 4;         // float4 columns of a state row
+    constexpr int NQP = NQ / CS;      // float4 columns of the slice
+    constexpr int RG = 256 / NQP;     // row groups
+    constexpr int RPT = D / RG;       // rows per thread
     const int tid = threadIdx.x;
+    const int part = uu % CS, u = uu / CS;
     const int Hq = a.Hq, b = u / Hq, h = u % Hq;
     const int g = (int)(((int64_t)h * a.G) / Hq);
+    const int jq = part * NQP + tid % NQP, rg = tid / NQP;
+    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + ((size_t)b * Hq + h) * D * D);
+    f32x4 sv[RPT];
+#pragma unroll
+    for (int s = 0; s < RPT; ++s) sv[s] = __builtin_nontemporal_load(&S[(rg + RG * s) * NQ + jq]);
     const int64_t row0 = a.map.table ? 0 : a.cu[b];
     const int32_t *ptab = a.map.table ? a.map.table + (size_t)b * a.map.max_blocks : nullptr;
     const int L = cache_len(a.map, b, a.max_ctx);
-    float *olin = a.olin + ((size_t)b * Hq + h) * D;
+    float *olin = a.olin + ((size_t)b * Hq + h) * D + part * NQP * 4;
     if (L < 1) {
-        if (tid < D) olin[tid] = 0.0f;
+        if (tid < NQP * 4) olin[tid] = 0.0f;
         return;
     }
     const int64_t trow = cache_row(a.map, row0, ptab, L - 1);
@@ -164,13 +180,7 @@ __device__ void state_group(const DecodeScoreArgs &a, int u, float *smem) {
         qq[tid] = Elt<T>::to_f32(qp[((size_t)b * Hq + h) * D + tid]);
     }
     __syncthreads();
-    constexpr int NQ = D / 4, RG = 256 / NQ, RPT = D / RG;
-    const int jq = tid % NQ, rg = tid / NQ;
     const f32x4 v4 = *reinterpret_cast<const f32x4 *>(vv + 4 * jq);
-    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + ((size_t)b * Hq + h) * D * D);
-    f32x4 sv[RPT];
-#pragma unroll
-    for (int s = 0; s < RPT; ++s) sv[s] = __builtin_nontemporal_load(&S[(rg + RG * s) * NQ + jq]);
     f32x4 o = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < RPT; ++s) {
@@ -187,11 +197,11 @@ __device__ void state_group(const DecodeScoreArgs &a, int u, float *smem) {
         o[2] = fmaf(qi, x[2], o[2]);
         o[3] = fmaf(qi, x[3], o[3]);
     }
-    *reinterpret_cast<f32x4 *>(red + rg * D + 4 * jq) = o;
+    *reinterpret_cast<f32x4 *>(red + rg * (NQP * 4) + 4 * (tid % NQP)) = o;
     __syncthreads();
-    if (tid < D) {
+    if (tid < NQP * 4) {
         float acc = 0.0f;
-        for (int r = 0; r < RG; ++r) acc += red[r * D + tid];
+        for (int r = 0; r < RG; ++r) acc += red[r * (NQP * 4) + tid];
         olin[tid] = acc;
     }
 }
@@ -199,7 +209,7 @@ __device__ void state_group(const DecodeScoreArgs &a, int u, float *smem) {
 template <typename T, int D, int DI, int HIPAD>
 __global__ __launch_bounds__(256) void decode_score_state_kernel(DecodeScoreArgs a, int n_state) {
     // state groups: 3 vectors + the reduction rows; score groups: 64 key rows per wave
-    constexpr int kStateBytes = (3 * 128 + 16 * 128) * 4;
+    constexpr int kStateBytes = (3 * 128 + 1024) * 4;
     constexpr int kStageBytes = 4 * 64 * DI * (int)Elt<T>::kBytes;
     __shared__ u32x4 smem[(kStateBytes > kStageBytes ? kStateBytes : kStageBytes) / 16];
     if ((int)blockIdx.x < n_state)
@@ -745,7 +755,7 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
 
 template <typename T, int D, int DI, int HIPAD>
 hipError_t launch_ss(const DecodeScoreArgs &a, hipStream_t s) {
-    const int n_state = a.B * a.Hq;
+    const int n_state = a.B * a.Hq * (D / 32);  // column slices of every head's state
     const int n_score = a.B * a.tiles_per_seq;
     hipLaunchKernelGGL((decode_score_state_kernel<T, D, DI, HIPAD>), dim3(n_state + n_score),
                        dim3(256), 0, s, a, n_state);
