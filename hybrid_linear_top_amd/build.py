@@ -16,7 +16,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "sparse.hip", "linear.hip", "indexer.hip"]
+SOURCES = ["api.hip", "decode.hip", "sparse.hip", "linear.hip", "indexer.hip", "backward.hip"]
 
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I", INCLUDE,
          # packed fp32 arithmetic is kept off on this part

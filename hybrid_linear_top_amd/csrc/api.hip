@@ -519,6 +519,183 @@ lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int6
                        gate, state, out, nullptr, workspace, workspace_bytes, stream, true);
 }
 
+// ---- backward --------------------------------------------------------------------
+namespace {
+struct BwdWs {
+    size_t olin, Gl, Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, total;
+};
+BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
+    const size_t Hq = d->num_q_heads, D = d->head_dim, eb = elt_bytes(d->dtype);
+    const size_t nC = ((size_t)n + 63) / 64;
+    const size_t act = align_up((size_t)B * n * Hq * D * eb);
+    const size_t st = align_up((size_t)B * Hq * D * D * 4);
+    BwdWs w;
+    size_t off = 0;
+    size_t *acts[] = {&w.olin, &w.Gl, &w.Grev, &w.qrev, &w.vrep, &w.krep, &w.dqlin, &w.ok, &w.ov};
+    for (size_t *x : acts) {
+        *x = off;
+        off += act;
+    }
+    w.sinT = off;
+    off += st;
+    w.dsoT = off;
+    off += st;
+    // the chunked passes: up to Hq groups (each head its own group in the reversed passes)
+    w.dS = off;
+    off += align_up((size_t)B * Hq * nC * D * D * 4);
+    w.P = off;
+    off += align_up((size_t)B * Hq * nC * D * D * eb);
+    w.total = off;
+    return w;
+}
+
+// one causal chunked linear-attention pass: out = o_lin of (q, k, v, state_in)
+lisa_status linear_pass(const lisa_dims *dims, int B, int n, int Hq, int G, const void *q, const void *k,
+                        const void *v, const float *state_in, float *state_out, void *out,
+                        unsigned char *ws, const BwdWs &w, hipStream_t s) {
+    lisa::LinearArgs la{};
+    la.q = q;
+    la.k = k;
+    la.v = v;
+    la.state_in = state_in;
+    la.state_out = state_out;
+    la.dS = reinterpret_cast<float *>(ws + w.dS);
+    la.P = ws + w.P;
+    la.out = out;
+    la.B = B;
+    la.n = n;
+    la.Hq = Hq;
+    la.G = G;
+    la.r = Hq / G;
+    la.nC = (n + 63) / 64;
+    la.kv_rows = n;
+    la.kv_off = 0;
+    la.per_head = state_in != nullptr;
+    const int D = dims->head_dim;
+    LISA_HIP(lisa::launch_linear_chunk_state(la, dims->dtype, D, s), "backward chunk-state launch");
+    LISA_HIP(lisa::launch_linear_prefix_scan(la, dims->dtype, D, s), "backward prefix-scan launch");
+    LISA_HIP(lisa::launch_linear_chunk_output(la, dims->dtype, D, s), "backward chunk-output launch");
+    return ok();
+}
+}  // namespace
+
+lisa_status lisa_prefill_backward_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
+                                                  size_t *bytes) {
+    lisa_status st = check_dims(dims, true);
+    if (st) return st;
+    if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
+    if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
+    *bytes = bwd_ws(dims, B, n).total;
+    return ok();
+}
+
+lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, const void *q,
+                                  const void *k, const void *v, const void *gate,
+                                  const float *state_in, const int32_t *topm, const void *d_out,
+                                  const float *d_state_out, float *dq, float *dk, float *dv,
+                                  float *dgate, float *d_state_in, void *workspace,
+                                  size_t workspace_bytes, lisa_stream_t stream) {
+    lisa_status st = check_dims(dims, true);
+    if (st) return st;
+    if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
+    if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
+    const int G = dims->num_kv_heads, Hq = dims->num_q_heads, D = dims->head_dim, M = dims->top_m;
+    if (Hq / G > 16)
+        return fail(LISA_ERR_UNSUPPORTED, "%d query heads per group: the backward handles up to 16", Hq / G);
+    if (lisa::sparse_bwd_lds_bytes(Hq / G, M, D) > 65536)
+        return fail(LISA_ERR_UNSUPPORTED, "top_m %d with %d heads per group exceeds the backward's LDS", M, Hq / G);
+    if ((int64_t)B * n == 0) return ok();
+    LISA_NEED(q, "q");
+    LISA_NEED(k, "k");
+    LISA_NEED(v, "v");
+    LISA_NEED(gate, "gate");
+    LISA_NEED(topm, "topm");
+    LISA_NEED(d_out, "d_out");
+    LISA_NEED(dq, "dq");
+    LISA_NEED(dk, "dk");
+    LISA_NEED(dv, "dv");
+    LISA_NEED(dgate, "dgate");
+    LISA_OPT(state_in, "state_in");
+    LISA_OPT(d_state_out, "d_state_out");
+    LISA_OPT(d_state_in, "d_state_in");
+    LISA_NEED(workspace, "workspace");
+    const BwdWs w = bwd_ws(dims, B, n);
+    if (workspace_bytes < w.total)
+        return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+
+    lisa::BwdPrepArgs pa{};
+    pa.q = q;
+    pa.k = k;
+    pa.v = v;
+    pa.z = gate;
+    pa.dout = d_out;
+    pa.Gl = ws + w.Gl;
+    pa.Grev = ws + w.Grev;
+    pa.qrev = ws + w.qrev;
+    pa.vrep = ws + w.vrep;
+    pa.krep = ws + w.krep;
+    pa.B = B;
+    pa.n = n;
+    pa.Hq = Hq;
+    pa.G = G;
+    pa.d = D;
+    LISA_HIP(lisa::launch_bwd_prep(pa, dims->dtype, s), "backward operand launch");
+    float *sinT = state_in ? reinterpret_cast<float *>(ws + w.sinT) : nullptr;
+    float *dsoT = d_state_out ? reinterpret_cast<float *>(ws + w.dsoT) : nullptr;
+    if (sinT) LISA_HIP(lisa::launch_transpose_states(state_in, sinT, (int64_t)B * Hq, D, s), "transpose launch");
+    if (dsoT) LISA_HIP(lisa::launch_transpose_states(d_state_out, dsoT, (int64_t)B * Hq, D, s), "transpose launch");
+
+    // o_lin of the forward (the gate needs it), then the three gradient passes
+    st = linear_pass(dims, B, n, Hq, G, q, k, v, state_in, nullptr, ws + w.olin, ws, w, s);
+    if (st) return st;
+    st = linear_pass(dims, B, n, Hq, G, ws + w.Gl, v, k, sinT, nullptr, ws + w.dqlin, ws, w, s);
+    if (st) return st;
+    st = linear_pass(dims, B, n, Hq, Hq, ws + w.vrep, ws + w.Grev, ws + w.qrev, dsoT, nullptr, ws + w.ok, ws, w, s);
+    if (st) return st;
+    st = linear_pass(dims, B, n, Hq, Hq, ws + w.krep, ws + w.qrev, ws + w.Grev, d_state_out, d_state_in,
+                     ws + w.ov, ws, w, s);
+    if (st) return st;
+
+    lisa::BwdCombineArgs ca{};
+    ca.dq_lin = ws + w.dqlin;
+    ca.o_k = ws + w.ok;
+    ca.o_v = ws + w.ov;
+    ca.dq = dq;
+    ca.dk = dk;
+    ca.dv = dv;
+    ca.B = B;
+    ca.n = n;
+    ca.Hq = Hq;
+    ca.G = G;
+    ca.d = D;
+    LISA_HIP(lisa::launch_bwd_combine(ca, dims->dtype, s), "backward combine launch");
+
+    lisa::SparseBwdArgs sb{};
+    sb.q = q;
+    sb.k = k;
+    sb.v = v;
+    sb.z = gate;
+    sb.dout = d_out;
+    sb.olin = ws + w.olin;
+    sb.idx = topm;
+    sb.dq = dq;
+    sb.dk = dk;
+    sb.dv = dv;
+    sb.dgate = dgate;
+    sb.B = B;
+    sb.n = n;
+    sb.Hq = Hq;
+    sb.G = G;
+    sb.r = Hq / G;
+    sb.M = M;
+    sb.scale = (float)(dims->softmax_scale > 0.0f ? (double)dims->softmax_scale : 1.0 / std::sqrt((double)D));
+    LISA_HIP(lisa::launch_sparse_bwd(sb, dims->dtype, D, s), "sparse backward launch");
+    return ok();
+}
+
 lisa_status lisa_stage_timing(int32_t enable) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     g_timing.enabled = enable != 0;

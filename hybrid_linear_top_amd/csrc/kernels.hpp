@@ -100,4 +100,29 @@ size_t indexer_packed_bytes(int B, int nk, int G, int dI, int dtype);
 hipError_t launch_indexer_pack(const IndexerArgs &a, int dtype, int dI, hipStream_t s);
 hipError_t launch_indexer_prefill(const IndexerArgs &a, int dtype, int dI, hipStream_t s);
 
+// ---- prefill backward ----------------------------------------------------------
+struct BwdPrepArgs {
+    const void *q, *k, *v, *z, *dout;   // q, z, dout per head [B,n,Hq,(d)]; k, v [B,n,G,d]
+    void *Gl, *Grev, *qrev, *vrep, *krep;  // [B,n,Hq,d] in the layer dtype
+    int B, n, Hq, G, d;
+};
+struct BwdCombineArgs {
+    const void *dq_lin, *o_k, *o_v;     // [B,n,Hq,d] layer dtype (o_k, o_v in reversed time)
+    float *dq;                          // [B,n,Hq,d]
+    float *dk, *dv;                     // [B,n,G,d]
+    int B, n, Hq, G, d;
+};
+struct SparseBwdArgs {
+    const void *q, *k, *v, *z, *dout, *olin;  // layer dtype
+    const int32_t *idx;                       // [B,n,G,M] the forward's sets
+    float *dq, *dk, *dv, *dgate;              // dq += ; dk, dv atomically += ; dgate =
+    int B, n, Hq, G, r, M;
+    float scale;
+};
+size_t sparse_bwd_lds_bytes(int r, int M, int d);
+hipError_t launch_bwd_prep(const BwdPrepArgs &a, int dtype, hipStream_t s);
+hipError_t launch_transpose_states(const float *src, float *dst, int64_t nmat, int d, hipStream_t s);
+hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s);
+hipError_t launch_sparse_bwd(const SparseBwdArgs &a, int dtype, int d, hipStream_t s);
+
 }  // namespace lisa

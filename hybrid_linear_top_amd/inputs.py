@@ -175,3 +175,16 @@ def make_decode_inputs(cfg: LayerConfig, seed: int | None = None, B: int | None 
     out["B"] = B
     out["max_ctx"] = int(L.max()) if B else 0
     return out
+
+
+def make_backward_inputs(cfg: LayerConfig, seed: int | None = None, with_states: bool = True) -> dict:
+    """Upstream gradients for the backward pass: d_out [B,n,Hq,d] in the layer
+    dtype, d_state_out and an initial state [B,Hq,d,d] fp32 (or None)."""
+    seed = (cfg.seed if seed is None else seed) + 1000
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, n, d = cfg.B, cfg.n, cfg.d
+    out = {"d_out": _normal(rng, (B, n, cfg.Hq, d), 1.0, cfg.dtype), "d_state_out": None, "state_in": None}
+    if with_states:
+        out["d_state_out"] = (rng.standard_normal((B, cfg.Hq, d, d), dtype=np.float32) * 0.1).astype(np.float32)
+        out["state_in"] = (rng.standard_normal((B, cfg.Hq, d, d), dtype=np.float32) * 0.1).astype(np.float32)
+    return out

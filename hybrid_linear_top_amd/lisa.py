@@ -26,7 +26,8 @@ LISA_BF16 = 1
 EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill_continue_workspace_bytes", "lisa_prefill",
            "lisa_prefill_continue",
            "lisa_prefill_window", "lisa_decode_step_window", "lisa_decode_step_paged",
-           "lisa_decode_workspace_bytes",
+           "lisa_decode_workspace_bytes", "lisa_prefill_backward_workspace_bytes",
+           "lisa_prefill_backward",
            "lisa_decode_step", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
            "lisa_build_info"]
 
@@ -66,6 +67,11 @@ def _load(path: str = LIB_PATH):
     lib.lisa_decode_step_paged.argtypes = [dp, i32, vp, vp, i32, i32, i32, i32] + [vp] * 7 + \
         [vp, vp, vp, vp, sz, vp]
     lib.lisa_decode_step_paged.restype = ctypes.c_int
+    lib.lisa_prefill_backward_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
+    lib.lisa_prefill_backward_workspace_bytes.restype = ctypes.c_int
+    lib.lisa_prefill_backward.argtypes = [dp, i32, i32] + [vp] * 4 + [vp, vp, vp, vp] + [vp] * 5 + \
+        [vp, sz, vp]
+    lib.lisa_prefill_backward.restype = ctypes.c_int
     lib.lisa_decode_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
     lib.lisa_decode_workspace_bytes.restype = ctypes.c_int
     lib.lisa_decode_step.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp, sz, vp]
@@ -105,6 +111,20 @@ def lisa_prefill_continue_workspace_bytes(dims: LisaDims, B: int, past: int, n: 
     out = ctypes.c_size_t(0)
     _check(_lib.lisa_prefill_continue_workspace_bytes(ctypes.byref(dims), B, past, n, ctypes.byref(out)))
     return out.value
+
+
+def lisa_prefill_backward_workspace_bytes(dims: LisaDims, B: int, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.lisa_prefill_backward_workspace_bytes(ctypes.byref(dims), B, n, ctypes.byref(out)))
+    return out.value
+
+
+def lisa_prefill_backward(dims, B, n, q, k, v, gate, state_in, topm, d_out, d_state_out, dq, dk, dv,
+                          dgate, d_state_in, workspace, workspace_bytes, stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_prefill_backward(ctypes.byref(dims), B, n, q, k, v, gate, state_in, topm, d_out,
+                                      d_state_out, dq, dk, dv, dgate, d_state_in, workspace,
+                                      workspace_bytes, stream)
 
 
 def lisa_prefill_workspace_bytes(dims: LisaDims, B: int, n: int) -> int:
@@ -289,6 +309,30 @@ def decode_step_window(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache
                                    _ptr(v_cache), _ptr(gate), _ptr(state), _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def prefill_backward(dims: LisaDims, q, k, v, gate, topm, d_out, state_in=None, d_state_out=None,
+                     want_state_grad=False, workspace=None, stream=None):
+    """Gradients of <d_out, out> + <d_state_out, state_out> (torch device
+    tensors as for prefill; topm the forward's sets).  Returns (dq, dk, dv,
+    dgate, d_state_in or None), all fp32."""
+    import torch
+    B, n = int(q.shape[0]), int(q.shape[1])
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty(tuple(q.shape), **f32)
+    dk = torch.empty(tuple(k.shape), **f32)
+    dv = torch.empty(tuple(v.shape), **f32)
+    dgate = torch.empty(tuple(gate.shape), **f32)
+    dsi = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim), **f32) if want_state_grad else None
+    wsb = lisa_prefill_backward_workspace_bytes(dims, B, n)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(lisa_prefill_backward(dims, B, n, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(state_in),
+                                 _ptr(topm), _ptr(d_out), _ptr(d_state_out), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(dgate), _ptr(dsi), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    return dq, dk, dv, dgate, dsi
 
 
 def decode_step_paged(dims: LisaDims, lengths, block_table, block_size: int, max_ctx: int, q, k_pages,

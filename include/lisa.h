@@ -157,6 +157,36 @@ lisa_status lisa_prefill_window(const lisa_dims *dims, int32_t B, int32_t past, 
                                 float *state_out, void *workspace, size_t workspace_bytes,
                                 lisa_stream_t stream);
 
+/*
+ * Backward pass of lisa_prefill: the gradients of
+ *     L = <d_out, out> + <d_state_out, state_out>
+ * with respect to q, k, v, the gate logits and state_in, obtained from the
+ * layer's definition (gptget.net analysis of arXiv 2607.19358,
+ * method-details section) by the chain rule, with the selected sets held at
+ * the forward's.  A top-M set is a piecewise-constant function of q_idx,
+ * k_idx and w_idx, so those inputs get no gradient and are not taken.
+ *   q, k, v, gate, state_in   as given to lisa_prefill (state_in may be NULL)
+ *   topm         [B, n, G, M] int32: the forward's topm_out for these inputs
+ *                (entries outside 0..t are skipped)
+ *   d_out        [B, n, Hq, d] in the layer dtype
+ *   d_state_out  [B, Hq, d, d] fp32 or NULL (zero)
+ *   dq  [B, n, Hq, d]; dk, dv [B, n, Hkv, d]; dgate [B, n, Hq]; all fp32,
+ *       written (dk and dv are accumulated with atomics, so their last bits
+ *       may differ from run to run)
+ *   d_state_in  [B, Hq, d, d] fp32 or NULL
+ * Up to 16 query heads per group; top_m * heads-per-group bounded by the
+ * kernel's LDS (UNSUPPORTED beyond).  The workspace is
+ * lisa_prefill_backward_workspace_bytes(dims, B, n).
+ */
+lisa_status lisa_prefill_backward_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
+                                                  size_t *bytes);
+lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, const void *q,
+                                  const void *k, const void *v, const void *gate,
+                                  const float *state_in, const int32_t *topm, const void *d_out,
+                                  const float *d_state_out, float *dq, float *dk, float *dv,
+                                  float *dgate, float *d_state_in, void *workspace,
+                                  size_t workspace_bytes, lisa_stream_t stream);
+
 /* Workspace needed by lisa_decode_step for B sequences of at most max_ctx
  * visible tokens each. */
 lisa_status lisa_decode_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t max_ctx,

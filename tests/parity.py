@@ -352,3 +352,37 @@ def window_decode_parity(cfg, inp, report=None):
     for key in res:
         assert res[key] <= tol, res
     return res
+
+
+# ---- backward ------------------------------------------------------------------
+BWD_TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def backward_parity(cfg, inp, binp, report=None):
+    """GPU forward (for the sets), GPU backward, oracle backward on the same
+    sets; normwise errors of dq, dk, dv, dgate and d_state_in."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    from oracle import backward as obwd
+    dims = lisa.dims_from_config(cfg)
+    dv_ = lisa.to_device
+    dt = cfg.dtype
+    S0 = binp["state_in"]
+    _, _, idx = run_prefill(cfg, inp, state_in=S0)
+    got = lisa.prefill_backward(dims, dv_(inp["q"]), dv_(inp["k"]), dv_(inp["v"]), dv_(inp["gate"]),
+                                dv_(idx), dv_(binp["d_out"]),
+                                state_in=None if S0 is None else dv_(S0),
+                                d_state_out=None if binp["d_state_out"] is None else dv_(binp["d_state_out"]),
+                                want_state_grad=True)
+    torch.cuda.synchronize()
+    got = [lisa.from_device(x).astype(np.float64) for x in got]
+    w = lambda x: orc.widen(inp[x], dt)  # noqa: E731
+    ref = obwd.prefill_backward(w("q"), w("k"), w("v"), w("gate"), idx, orc.widen(binp["d_out"], dt),
+                                state_in=S0, d_state_out=binp["d_state_out"])
+    names = ("dq", "dk", "dv", "dz", "d_state_in")
+    res = {f"e_{nm}": normwise(g, ref[nm]) for nm, g in zip(names, got)}
+    if report is not None:
+        report.update(res)
+    for key, val in res.items():
+        assert val <= BWD_TOL[dt], res
+    return res

@@ -263,3 +263,36 @@ def test_continue_workspace_query():
     # a continue call given only the n-token prefill workspace is refused
     need = lisa.lisa_prefill_continue_workspace_bytes(d, 1, 4096, 64)
     assert _cont(d, past=4096, n=64, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
+
+
+def _bwd(d, B=1, n=64, ws_bytes=1 << 40, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, state_in=0, topm=FAKE, d_out=FAKE, d_state_out=0,
+             dq=FAKE, dk=FAKE, dv=FAKE, dgate=FAKE, d_state_in=0, workspace=FAKE)
+    p.update(ptrs)
+    return lisa.lisa_prefill_backward(d, B, n, p["q"], p["k"], p["v"], p["gate"], p["state_in"], p["topm"],
+                                      p["d_out"], p["d_state_out"], p["dq"], p["dk"], p["dv"], p["dgate"],
+                                      p["d_state_in"], p["workspace"], ws_bytes, 0)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "gate", "topm", "d_out", "dq", "dk", "dv", "dgate",
+                                  "workspace"])
+def test_backward_null_pointer(name):
+    assert _bwd(_dims(), **{name: 0}) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert name in lisa.lisa_last_error()
+
+
+def test_backward_limits():
+    d = _dims()
+    assert _bwd(d, state_in=FAKE + 4) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _bwd(d, d_state_in=FAKE + 8) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _bwd(d, n=-1) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert _bwd(d, n=32769) == lisa.LISA_ERR_UNSUPPORTED
+    assert _bwd(_dims(Hq=34, Hkv=2)) == lisa.LISA_ERR_UNSUPPORTED
+    assert _bwd(_dims(Hq=32, Hkv=1, M=512)) == lisa.LISA_ERR_UNSUPPORTED   # 32 heads per group
+    assert _bwd(d, n=0, q=0, workspace=0) == lisa.LISA_OK
+    assert _bwd(d, B=0, q=0) == lisa.LISA_OK
+    need = lisa.lisa_prefill_backward_workspace_bytes(d, 1, 64)
+    assert need > 0
+    assert _bwd(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
+    # workspace grows with the sequence
+    assert lisa.lisa_prefill_backward_workspace_bytes(d, 1, 4096) > need

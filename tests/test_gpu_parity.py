@@ -311,3 +311,24 @@ def test_prefill_then_decode_matches_longer_prefill():
     assert np.array_equal(idx_d[0], idx_full[0, n])
     assert parity.normwise(out_d[0], out_full[0, n]) <= 1e-2
     assert parity.normwise(st_d, st_full) <= 1e-3
+
+
+# ---- backward ------------------------------------------------------------------
+BACKWARD = [
+    (_pcfg(200, 4, 2, 64, 4, 32, 16), True),
+    (_pcfg(300, 12, 2, 128, 4, 64, 64, seed=2), True),
+    (_pcfg(130, 8, 2, 64, 2, 32, 37, dtype="f32", seed=3), True),
+    (_pcfg(257, 7, 7, 128, 4, 64, 256, seed=4), False),      # no state in or out, M > n
+    (_pcfg(1000, 8, 2, 128, 4, 64, 256, seed=5), True),
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD, ids=lambda c: c[0].name + ("_states" if c[1] else ""))
+def test_prefill_backward(case):
+    cfg, states = case
+    _say("backward", cfg.name, "states", states, "seed", cfg.seed)
+    inp = gen.make_prefill_inputs(cfg)
+    binp = gen.make_backward_inputs(cfg, with_states=states)
+    rep = {}
+    parity.backward_parity(cfg, inp, binp, report=rep)
+    _say("  ", rep)
