@@ -91,6 +91,7 @@ STAGE_KERNELS = {
     "linear_chunk_output": (r"chunk_output_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
     "decode_score_state": (r"decode_score_state_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
     "decode_select": (r"decode_topm_kernel<|decode_select_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
+    "bwd_sparse": (r"sparse_bwd_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
 }
 
 
@@ -314,6 +315,73 @@ def bench_decode(args):
     return res
 
 
+def backward_bytes(cfg, n, B):
+    """Algorithmic bytes of the sparse backward: per (position, group, valid
+    slot) the K and V rows read once and the fp32 dK and dV rows updated."""
+    pairs = B * cfg.Hkv * sum(min(cfg.M, t + 1) for t in range(n))
+    return pairs * (2 * cfg.d * 2 + 2 * cfg.d * 4)
+
+
+def bench_backward(args, pre):
+    import torch
+    from hybrid_linear_top_amd import inputs as gen, lisa
+    cfg, inp = pre["cfg"], pre["inp"]
+    dims = lisa.dims_from_config(cfg)
+    B, n = inp["B"], inp["n"]
+    binp = gen.make_backward_inputs(cfg)
+    x = {k: lisa.to_device(inp[k]) for k in ("q", "k", "v", "q_idx", "k_idx", "w_idx", "gate")}
+    s0 = lisa.to_device(binp["state_in"])
+    _, _, idx = lisa.prefill(dims, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], x["w_idx"], x["gate"],
+                             state_in=s0)
+    dO, dS = lisa.to_device(binp["d_out"]), lisa.to_device(binp["d_state_out"])
+    ws = torch.empty(lisa.lisa_prefill_backward_workspace_bytes(dims, B, n), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(c):
+        lisa.prefill_backward(dims, x["q"], x["k"], x["v"], x["gate"], idx, dO, state_in=s0,
+                              d_state_out=dS, want_state_grad=True, workspace=ws)
+
+    ms = timed_loop(step, args.bwd_steps, 1, 1)
+    stages = stage_pass(step, args.bwd_steps, 1)
+    bb = backward_bytes(cfg, n, B)
+    roof = roofline_entry("bwd_sparse", stages["bwd_sparse"], bb, "hbm", traffic_from_profiles("bwd_sparse"))
+    res = {
+        "workload": f"lisa_prefill_backward qwen2.5-7b-shaped B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
+                    f"d={cfg.d} M={cfg.M} bf16 (sets from the forward; d_state_out and state_in given)",
+        "tokens_per_s": B * n / (ms * 1e-3), "ms": ms, "roofline": roof,
+        "stages": {k: {"ms": round(v, 5)} for k, v in stages.items()},
+    }
+    del x, ws, idx
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_backward(pre, n_sample=1024):
+    """The fp64 backward oracle (numpy loops) on the first n_sample positions
+    of the same inputs, with the oracle's own sets for them."""
+    import numpy as np
+    from oracle import oracle as orc, backward as obwd
+    from hybrid_linear_top_amd import inputs as gen
+    cfg, inp = pre["cfg"], pre["inp"]
+    sub = {k: (v[:, :n_sample] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    sub["n"] = n_sample
+    fwd = orc.prefill(sub, cfg)
+    binp = gen.make_backward_inputs(cfg)
+    w = lambda key: orc.widen(sub[key], cfg.dtype)  # noqa: E731
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        obwd.prefill_backward(w("q"), w("k"), w("v"), w("gate"), fwd["idx"],
+                              orc.widen(binp["d_out"][:, :n_sample], cfg.dtype),
+                              state_in=binp["state_in"], d_state_out=binp["d_state_out"])
+        secs = time.perf_counter() - t0
+    return {"value": round(inp["B"] * n_sample / secs, 3), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 backward oracle (numpy loops, BLAS held to one thread) on the first "
+                      f"{n_sample} positions of the same inputs ({secs:.1f}s)",
+            "seconds_measured": round(secs, 2)}
+
+
 def cpu_prefill(res):
     """The fp64 oracle's full prefill call on the same n=16384 inputs (all rows;
     input widening excluded from the timed region)."""
@@ -359,6 +427,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--decode-warmup", type=int, default=20)
+    ap.add_argument("--bwd-steps", type=int, default=3)
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -389,12 +459,19 @@ def main():
     print(f"[bench] prefill {pre['ms']:.3f} ms/call, stages {pre['stages']}", file=sys.stderr, flush=True)
     dec = bench_decode(args)
     print(f"[bench] decode {dec['ms'] * 1e3:.1f} us/step, stages {dec['stages']}", file=sys.stderr, flush=True)
-    cpu_p = cpu_d = None
+    bwd = None
+    if not args.no_backward:
+        bwd = bench_backward(args, pre)
+        print(f"[bench] backward {bwd['ms']:.2f} ms/call, stages {bwd['stages']}", file=sys.stderr, flush=True)
+    cpu_p = cpu_d = cpu_b = None
     if not args.no_cpu_baseline:
         cpu_p = cpu_prefill(pre)
         print(f"[bench] cpu prefill baseline {cpu_p}", file=sys.stderr, flush=True)
         cpu_d = cpu_decode(dec)
         print(f"[bench] cpu decode baseline {cpu_d}", file=sys.stderr, flush=True)
+        if bwd is not None:
+            cpu_b = cpu_backward(pre)
+            print(f"[bench] cpu backward baseline {cpu_b}", file=sys.stderr, flush=True)
     line = {
         "metric": METRIC,
         "value": round(pre["tokens_per_s"], 1),
@@ -419,6 +496,11 @@ def main():
             "steps": args.decode_steps, "warmup": args.decode_warmup,
             "ms_per_step": round(dec["ms"], 5), "roofline": dec["roofline"],
             "step_roofline": dec["step_roofline"], "stages": dec["stages"], "cpu_baseline": cpu_d,
+        },
+        "backward": None if bwd is None else {
+            "workload": bwd["workload"], "value": round(bwd["tokens_per_s"], 1), "unit": "tokens/s",
+            "steps": args.bwd_steps, "ms_per_step": round(bwd["ms"], 4), "roofline": bwd["roofline"],
+            "stages": bwd["stages"], "cpu_baseline": cpu_b,
         },
         "wall_s": round(time.time() - t_start, 1),
     }

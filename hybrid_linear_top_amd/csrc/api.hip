@@ -118,11 +118,14 @@ DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
 // ---- optional per-stage timing (benchmarking) -------------------------------
 enum Stage {
     ST_LIN_STATE, ST_LIN_SCAN, ST_LIN_OUT, ST_IDX_PACK, ST_INDEXER, ST_SPARSE_PREFILL,
-    ST_DEC_SCORE_STATE, ST_DEC_SELECT, ST_SPARSE_DECODE, ST_COUNT
+    ST_DEC_SCORE_STATE, ST_DEC_SELECT, ST_SPARSE_DECODE,
+    ST_BWD_OPER, ST_BWD_LINEAR, ST_BWD_COMBINE, ST_BWD_SPARSE, ST_COUNT
 };
 const char *const kStageNames[ST_COUNT] = {
     "linear_chunk_state", "linear_prefix_scan", "linear_chunk_output", "indexer_pack", "indexer_topm",
-    "sparse_gate_prefill", "decode_score_state", "decode_select", "sparse_gate_decode"};
+    "sparse_gate_prefill", "decode_score_state", "decode_select", "sparse_gate_decode",
+    "bwd_operands", "bwd_linear", "bwd_combine", "bwd_sparse",
+};
 
 struct Timing {
     std::mutex mu;
@@ -550,7 +553,7 @@ BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
 }
 
 // one causal chunked linear-attention pass: out = o_lin of (q, k, v, state_in)
-lisa_status linear_pass(const lisa_dims *dims, int B, int n, int Hq, int G, const void *q, const void *k,
+hipError_t linear_pass(const lisa_dims *dims, int B, int n, int Hq, int G, const void *q, const void *k,
                         const void *v, const float *state_in, float *state_out, void *out,
                         unsigned char *ws, const BwdWs &w, hipStream_t s) {
     lisa::LinearArgs la{};
@@ -572,10 +575,10 @@ lisa_status linear_pass(const lisa_dims *dims, int B, int n, int Hq, int G, cons
     la.kv_off = 0;
     la.per_head = state_in != nullptr;
     const int D = dims->head_dim;
-    LISA_HIP(lisa::launch_linear_chunk_state(la, dims->dtype, D, s), "backward chunk-state launch");
-    LISA_HIP(lisa::launch_linear_prefix_scan(la, dims->dtype, D, s), "backward prefix-scan launch");
-    LISA_HIP(lisa::launch_linear_chunk_output(la, dims->dtype, D, s), "backward chunk-output launch");
-    return ok();
+    hipError_t e = lisa::launch_linear_chunk_state(la, dims->dtype, D, s);
+    if (e == hipSuccess) e = lisa::launch_linear_prefix_scan(la, dims->dtype, D, s);
+    if (e == hipSuccess) e = lisa::launch_linear_chunk_output(la, dims->dtype, D, s);
+    return e;
 }
 }  // namespace
 
@@ -642,22 +645,29 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     pa.Hq = Hq;
     pa.G = G;
     pa.d = D;
-    LISA_HIP(lisa::launch_bwd_prep(pa, dims->dtype, s), "backward operand launch");
     float *sinT = state_in ? reinterpret_cast<float *>(ws + w.sinT) : nullptr;
     float *dsoT = d_state_out ? reinterpret_cast<float *>(ws + w.dsoT) : nullptr;
-    if (sinT) LISA_HIP(lisa::launch_transpose_states(state_in, sinT, (int64_t)B * Hq, D, s), "transpose launch");
-    if (dsoT) LISA_HIP(lisa::launch_transpose_states(d_state_out, dsoT, (int64_t)B * Hq, D, s), "transpose launch");
-
+    LISA_HIP(timed(ST_BWD_OPER, s, [&] {
+                 hipError_t e = lisa::launch_bwd_prep(pa, dims->dtype, s);
+                 if (e == hipSuccess && sinT) e = lisa::launch_transpose_states(state_in, sinT, (int64_t)B * Hq, D, s);
+                 if (e == hipSuccess && dsoT) e = lisa::launch_transpose_states(d_state_out, dsoT, (int64_t)B * Hq, D, s);
+                 return e;
+             }),
+             "backward operand launch");
     // o_lin of the forward (the gate needs it), then the three gradient passes
-    st = linear_pass(dims, B, n, Hq, G, q, k, v, state_in, nullptr, ws + w.olin, ws, w, s);
-    if (st) return st;
-    st = linear_pass(dims, B, n, Hq, G, ws + w.Gl, v, k, sinT, nullptr, ws + w.dqlin, ws, w, s);
-    if (st) return st;
-    st = linear_pass(dims, B, n, Hq, Hq, ws + w.vrep, ws + w.Grev, ws + w.qrev, dsoT, nullptr, ws + w.ok, ws, w, s);
-    if (st) return st;
-    st = linear_pass(dims, B, n, Hq, Hq, ws + w.krep, ws + w.qrev, ws + w.Grev, d_state_out, d_state_in,
-                     ws + w.ov, ws, w, s);
-    if (st) return st;
+    LISA_HIP(timed(ST_BWD_LINEAR, s, [&] {
+                 hipError_t e = linear_pass(dims, B, n, Hq, G, q, k, v, state_in, nullptr, ws + w.olin, ws, w, s);
+                 if (e == hipSuccess)
+                     e = linear_pass(dims, B, n, Hq, G, ws + w.Gl, v, k, sinT, nullptr, ws + w.dqlin, ws, w, s);
+                 if (e == hipSuccess)
+                     e = linear_pass(dims, B, n, Hq, Hq, ws + w.vrep, ws + w.Grev, ws + w.qrev, dsoT, nullptr,
+                                     ws + w.ok, ws, w, s);
+                 if (e == hipSuccess)
+                     e = linear_pass(dims, B, n, Hq, Hq, ws + w.krep, ws + w.qrev, ws + w.Grev, d_state_out,
+                                     d_state_in, ws + w.ov, ws, w, s);
+                 return e;
+             }),
+             "backward linear-pass launch");
 
     lisa::BwdCombineArgs ca{};
     ca.dq_lin = ws + w.dqlin;
@@ -671,7 +681,8 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     ca.Hq = Hq;
     ca.G = G;
     ca.d = D;
-    LISA_HIP(lisa::launch_bwd_combine(ca, dims->dtype, s), "backward combine launch");
+    LISA_HIP(timed(ST_BWD_COMBINE, s, [&] { return lisa::launch_bwd_combine(ca, dims->dtype, s); }),
+             "backward combine launch");
 
     lisa::SparseBwdArgs sb{};
     sb.q = q;
@@ -692,7 +703,8 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     sb.r = Hq / G;
     sb.M = M;
     sb.scale = (float)(dims->softmax_scale > 0.0f ? (double)dims->softmax_scale : 1.0 / std::sqrt((double)D));
-    LISA_HIP(lisa::launch_sparse_bwd(sb, dims->dtype, D, s), "sparse backward launch");
+    LISA_HIP(timed(ST_BWD_SPARSE, s, [&] { return lisa::launch_sparse_bwd(sb, dims->dtype, D, s); }),
+             "sparse backward launch");
     return ok();
 }
 

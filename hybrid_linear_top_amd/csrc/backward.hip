@@ -40,35 +40,43 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // ---- operands of the linear-branch passes ------------------------------------
-// One thread per element of [B, n, Hq, d]:
+// One thread per 8 consecutive elements of [B, n, Hq, d] (d is a multiple of 8):
 //   G    = (1 - gamma) d_out                 (same position and head)
 //   Grev = G,  qrev = q,  vrep = v of the head's group, krep = k of the group,
 //          all at position n - 1 - t (reversed time).
 template <typename T>
+struct alignas(16) Vec8 {
+    T x[8];
+};
+
+template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a) {
-    const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= total) return;
+    const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d / 8;
+    const int64_t e8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e8 >= total) return;
+    const int64_t e = e8 * 8;
     const int dd = (int)(e % a.d);
     int64_t r = e / a.d;
     const int h = (int)(r % a.Hq);
     r /= a.Hq;
     const int t = (int)(r % a.n), b = (int)(r / a.n);
     const int g = (int)(((int64_t)h * a.G) / a.Hq);
-    const T *dout = reinterpret_cast<const T *>(a.dout);
-    const T *q = reinterpret_cast<const T *>(a.q);
-    const T *k = reinterpret_cast<const T *>(a.k);
-    const T *v = reinterpret_cast<const T *>(a.v);
-    const T *z = reinterpret_cast<const T *>(a.z);
-    const float gam = sigmoidf(Elt<T>::to_f32(z[((size_t)b * a.n + t) * a.Hq + h]));
-    const T gv = Elt<T>::from_f32((1.0f - gam) * Elt<T>::to_f32(dout[e]));
-    const size_t rev = (((size_t)b * a.n + (a.n - 1 - t)) * a.Hq + h) * a.d + dd;
+    using V = Vec8<T>;
+    const float gam = sigmoidf(Elt<T>::to_f32(reinterpret_cast<const T *>(a.z)[((size_t)b * a.n + t) * a.Hq + h]));
+    const V dov = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.dout) + e);
+    const V qv = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.q) + e);
     const size_t kv = (((size_t)b * a.n + t) * a.G + g) * a.d + dd;
-    reinterpret_cast<T *>(a.Gl)[e] = gv;
-    reinterpret_cast<T *>(a.Grev)[rev] = gv;
-    reinterpret_cast<T *>(a.qrev)[rev] = q[e];
-    reinterpret_cast<T *>(a.vrep)[rev] = v[kv];
-    reinterpret_cast<T *>(a.krep)[rev] = k[kv];
+    const V kvv = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.k) + kv);
+    const V vvv = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.v) + kv);
+    V gv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gv.x[i] = Elt<T>::from_f32((1.0f - gam) * Elt<T>::to_f32(dov.x[i]));
+    const size_t rev = (((size_t)b * a.n + (a.n - 1 - t)) * a.Hq + h) * a.d + dd;
+    *reinterpret_cast<V *>(reinterpret_cast<T *>(a.Gl) + e) = gv;
+    *reinterpret_cast<V *>(reinterpret_cast<T *>(a.Grev) + rev) = gv;
+    *reinterpret_cast<V *>(reinterpret_cast<T *>(a.qrev) + rev) = qv;
+    *reinterpret_cast<V *>(reinterpret_cast<T *>(a.vrep) + rev) = vvv;
+    *reinterpret_cast<V *>(reinterpret_cast<T *>(a.krep) + rev) = kvv;
 }
 
 // [B*H] d x d fp32 matrices transposed (dst[m][j][i] = src[m][i][j])
@@ -80,13 +88,25 @@ __global__ __launch_bounds__(256) void transpose_states_kernel(const float *src,
     dst[(m * d + j) * d + i] = src[e];
 }
 
-// dq = dq_lin; dk[b,t,g] = sum_{h in g} o_k[b, n-1-t, h]; dv likewise (fp32)
+// dq = dq_lin; dk[b,t,g] = sum_{h in g} o_k[b, n-1-t, h]; dv likewise (fp32);
+// one thread per 8 consecutive elements
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdCombineArgs a) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     const int64_t nq = (int64_t)a.B * a.n * a.Hq * a.d;
     const int64_t nk = (int64_t)a.B * a.n * a.G * a.d;
-    if (e < nq) a.dq[e] = Elt<T>::to_f32(reinterpret_cast<const T *>(a.dq_lin)[e]);
+    using V = Vec8<T>;
+    if (e < nq) {
+        const V x = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.dq_lin) + e);
+        f32x4 lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo[i] = Elt<T>::to_f32(x.x[i]);
+            hi[i] = Elt<T>::to_f32(x.x[4 + i]);
+        }
+        *reinterpret_cast<f32x4 *>(a.dq + e) = lo;
+        *reinterpret_cast<f32x4 *>(a.dq + e + 4) = hi;
+    }
     if (e >= nk) return;
     const int dd = (int)(e % a.d);
     int64_t r = e / a.d;
@@ -94,16 +114,24 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdCombineArgs a) {
     r /= a.G;
     const int t = (int)(r % a.n), b = (int)(r / a.n);
     const int rr = a.Hq / a.G;
-    const T *ok = reinterpret_cast<const T *>(a.o_k);
-    const T *ov = reinterpret_cast<const T *>(a.o_v);
-    float sk = 0.0f, sv = 0.0f;
+    float sk[8], sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sk[i] = sv[i] = 0.0f;
     for (int j = 0; j < rr; ++j) {
         const size_t at = (((size_t)b * a.n + (a.n - 1 - t)) * a.Hq + g * rr + j) * a.d + dd;
-        sk += Elt<T>::to_f32(ok[at]);
-        sv += Elt<T>::to_f32(ov[at]);
+        const V ok = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.o_k) + at);
+        const V ov = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.o_v) + at);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sk[i] += Elt<T>::to_f32(ok.x[i]);
+            sv[i] += Elt<T>::to_f32(ov.x[i]);
+        }
     }
-    a.dk[e] = sk;
-    a.dv[e] = sv;
+#pragma unroll
+    for (int i = 0; i < 8; i += 4) {
+        *reinterpret_cast<f32x4 *>(a.dk + e + i) = f32x4{sk[i], sk[i + 1], sk[i + 2], sk[i + 3]};
+        *reinterpret_cast<f32x4 *>(a.dv + e + i) = f32x4{sv[i], sv[i + 1], sv[i + 2], sv[i + 3]};
+    }
 }
 
 // ---- sparse branch and gate ----------------------------------------------------
@@ -300,13 +328,13 @@ __global__ __launch_bounds__(64) void sparse_bwd_kernel(SparseBwdArgs a) {
 
 template <typename T>
 hipError_t prep_t(const BwdPrepArgs &a, hipStream_t s) {
-    const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d;
+    const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d / 8;
     hipLaunchKernelGGL((bwd_prep_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <typename T>
 hipError_t combine_t(const BwdCombineArgs &a, hipStream_t s) {
-    const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d;  // >= the dk / dv element count
+    const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d / 8;  // >= the dk / dv count / 8
     hipLaunchKernelGGL((bwd_combine_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }

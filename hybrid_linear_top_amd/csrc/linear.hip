@@ -114,6 +114,18 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(LinearArgs a) {
     T *P = reinterpret_cast<T *>(a.P);
     f32x4 run = {0, 0, 0, 0};
     const size_t pbase = a.per_head ? ((size_t)b * a.Hq + g * a.r) : ((size_t)b * a.G + g);
+    // per-head initial states: this thread's four elements of each head's S0
+    // (read transposed from [i][j] once) kept in a thread-private LDS slot
+    extern __shared__ f32x4 s0l[];  // [r][256] when per_head
+    if (a.per_head) {
+        for (int hh = 0; hh < a.r; ++hh) {
+            const float *S0 = a.state_in + (pbase + hh) * D * D;
+            f32x4 t;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t[q] = S0[(size_t)(i0 + q) * D + j];
+            s0l[hh * 256 + threadIdx.x] = t;
+        }
+    }
     constexpr int U = LISA_SCAN_U;
 #pragma unroll 1
     for (int c0 = 0; c0 < a.nC; c0 += U) {
@@ -130,13 +142,12 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(LinearArgs a) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) dst[q] = Elt<T>::from_f32(run[q]);
                 } else {
-                    // S_{c-1} = S0 + running sum, S0 read transposed from [i][j]
+                    // S_{c-1} = S0 + running sum
                     for (int hh = 0; hh < a.r; ++hh) {
-                        const float *S0 = a.state_in + (pbase + hh) * D * D;
+                        const f32x4 s0 = s0l[hh * 256 + threadIdx.x];
                         T *dst = P + ((pbase + hh) * a.nC + c) * D * D + 4 * e4;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            dst[q] = Elt<T>::from_f32(run[q] + S0[(size_t)(i0 + q) * D + j]);
+                        for (int q = 0; q < 4; ++q) dst[q] = Elt<T>::from_f32(run[q] + s0[q]);
                     }
                 }
             }
@@ -264,7 +275,8 @@ hipError_t run_state(const LinearArgs &a, hipStream_t s) {
 template <typename T, int D>
 hipError_t run_scan(const LinearArgs &a, hipStream_t s) {
     constexpr int BPG = (D * D / 4 + 255) / 256;
-    hipLaunchKernelGGL((prefix_scan_kernel<T, D>), dim3(a.B * a.G * BPG), dim3(256), 0, s, a);
+    const size_t lds = a.per_head ? (size_t)a.r * 256 * sizeof(f32x4) : 0;
+    hipLaunchKernelGGL((prefix_scan_kernel<T, D>), dim3(a.B * a.G * BPG), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 template <typename T, int D>
