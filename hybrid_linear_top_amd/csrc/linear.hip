@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool PH>  // PH: per-head prefixes (a.per_head)
 __global__ __launch_bounds__(256) void prefix_scan_kernel(LinearArgs a) {
     constexpr int Q4 = D * D / 4;  // float4 columns per state
     constexpr int BPG = (Q4 + 255) / 256;
@@ -113,11 +113,11 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(LinearArgs a) {
     const rsrc_t srs = make_rsrc(a.dS + (size_t)bg * a.nC * D * D, (uint32_t)a.nC * D * D * 4u);
     T *P = reinterpret_cast<T *>(a.P);
     f32x4 run = {0, 0, 0, 0};
-    const size_t pbase = a.per_head ? ((size_t)b * a.Hq + g * a.r) : ((size_t)b * a.G + g);
+    const size_t pbase = PH ? ((size_t)b * a.Hq + g * a.r) : ((size_t)b * a.G + g);
     // per-head initial states: this thread's four elements of each head's S0
     // (read transposed from [i][j] once) kept in a thread-private LDS slot
     extern __shared__ f32x4 s0l[];  // [r][256] when per_head
-    if (a.per_head) {
+    if (PH) {
         for (int hh = 0; hh < a.r; ++hh) {
             const float *S0 = a.state_in + (pbase + hh) * D * D;
             f32x4 t;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(LinearArgs a) {
         for (int u = 0; u < U; ++u) {
             const int c = c0 + u;
             if (c < a.nC) {
-                if (!a.per_head) {
+                if (!PH) {
                     T *dst = P + (pbase * a.nC + c) * D * D + 4 * e4;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) dst[q] = Elt<T>::from_f32(run[q]);
@@ -275,8 +275,11 @@ hipError_t run_state(const LinearArgs &a, hipStream_t s) {
 template <typename T, int D>
 hipError_t run_scan(const LinearArgs &a, hipStream_t s) {
     constexpr int BPG = (D * D / 4 + 255) / 256;
-    const size_t lds = a.per_head ? (size_t)a.r * 256 * sizeof(f32x4) : 0;
-    hipLaunchKernelGGL((prefix_scan_kernel<T, D>), dim3(a.B * a.G * BPG), dim3(256), lds, s, a);
+    if (a.per_head)
+        hipLaunchKernelGGL((prefix_scan_kernel<T, D, true>), dim3(a.B * a.G * BPG), dim3(256),
+                           (size_t)a.r * 256 * sizeof(f32x4), s, a);
+    else
+        hipLaunchKernelGGL((prefix_scan_kernel<T, D, false>), dim3(a.B * a.G * BPG), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <typename T, int D>

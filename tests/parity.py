@@ -386,3 +386,33 @@ def backward_parity(cfg, inp, binp, report=None):
     for key, val in res.items():
         assert val <= BWD_TOL[dt], res
     return res
+
+
+def backward_sampled_parity(cfg, inp, binp, rows, keys, report=None):
+    """Full-length backward: GPU forward (for the sets) and GPU backward over
+    all positions, checked against the oracle's per-row form at sampled query
+    rows (dq, dz) and key rows (dk, dv); normwise over the sampled rows."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    from oracle import backward as obwd
+    dims = lisa.dims_from_config(cfg)
+    dv_ = lisa.to_device
+    dt = cfg.dtype
+    S0, dS = binp["state_in"], binp["d_state_out"]
+    _, _, idx = run_prefill(cfg, inp, state_in=S0)
+    got = lisa.prefill_backward(dims, dv_(inp["q"]), dv_(inp["k"]), dv_(inp["v"]), dv_(inp["gate"]),
+                                dv_(idx), dv_(binp["d_out"]),
+                                state_in=None if S0 is None else dv_(S0),
+                                d_state_out=None if dS is None else dv_(dS), want_state_grad=False)
+    torch.cuda.synchronize()
+    dq, dk, dv, dz = (lisa.from_device(x).astype(np.float64) for x in got[:4])
+    w = lambda x: orc.widen(inp[x], dt)  # noqa: E731
+    ref = obwd.prefill_backward_rows(w("q"), w("k"), w("v"), w("gate"), idx, orc.widen(binp["d_out"], dt),
+                                     rows, keys, state_in=S0, d_state_out=dS)
+    res = {"e_dq": normwise(dq[:, rows], ref["dq"]), "e_dz": normwise(dz[:, rows], ref["dz"]),
+           "e_dk": normwise(dk[:, keys], ref["dk"]), "e_dv": normwise(dv[:, keys], ref["dv"])}
+    if report is not None:
+        report.update(res)
+    for key, val in res.items():
+        assert val <= BWD_TOL[dt], res
+    return res

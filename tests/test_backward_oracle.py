@@ -48,3 +48,27 @@ def test_backward_mutant_is_caught(name):
         except (AssertionError, IndexError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches mutant {name}"
+
+
+def test_backward_rows_equal_full():
+    """The per-row form (used at lengths the full oracle cannot reach) gives
+    the full oracle's values at every query row and key row, with and
+    without states, on inputs with ragged sets (M < n) and full ones."""
+    import numpy as np
+    from oracle import oracle as orc
+    from tests.backward_pins import _cfg, _forward, _setup
+    for n, M, states in ((40, 7, True), (23, 32, False), (33, 5, True)):
+        cfg = _cfg(n=n, Hq=6, Hkv=2, d=8, M=M, seed=n)
+        inp, x, extra = _setup(cfg)
+        S0 = extra["state_in"] if states else None
+        dS = extra["d_state_out"] if states else None
+        fwd = _forward(cfg, inp, x, S0, orc.load())
+        full = bwd.prefill_backward(x["q"], x["k"], x["v"], x["gate"], fwd["idx"], extra["d_out"],
+                                    state_in=S0, d_state_out=dS)
+        every = list(range(n))
+        part = bwd.prefill_backward_rows(x["q"], x["k"], x["v"], x["gate"], fwd["idx"], extra["d_out"],
+                                         every, every[::-1], state_in=S0, d_state_out=dS)
+        for name in ("dq", "dz"):
+            np.testing.assert_allclose(part[name], full[name], rtol=1e-12, atol=1e-13)
+        for name in ("dk", "dv"):
+            np.testing.assert_allclose(part[name], full[name][:, ::-1], rtol=1e-12, atol=1e-13)

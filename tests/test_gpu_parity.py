@@ -323,6 +323,21 @@ BACKWARD = [
 ]
 
 
+def test_prefill_backward_16k_sampled():
+    """The backward at the benchmark's 16K, 7B-shaped workload and launch
+    configuration: dq, dz at sampled query rows and dk, dv at sampled keys
+    (the first, the last, both sides of the t = M boundary, mid-sequence)."""
+    cfg = gen.CONFIGS[3]
+    _say("backward 16K sampled", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    binp = gen.make_backward_inputs(cfg)
+    rows = [0, 1, cfg.M - 1, cfg.M, 5000, cfg.n // 2, cfg.n - 1]
+    keys = [0, 1, cfg.M, 9000, cfg.n - 2, cfg.n - 1]
+    rep = {}
+    parity.backward_sampled_parity(cfg, inp, binp, rows, keys, report=rep)
+    _say("  ", rep)
+
+
 @pytest.mark.parametrize("case", BACKWARD, ids=lambda c: c[0].name + ("_states" if c[1] else ""))
 def test_prefill_backward(case):
     cfg, states = case
