@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "LISA layer tokens/s at 16K ctx (decode + prefill); % of HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs, 2.4 GHz), TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -92,6 +93,8 @@ STAGE_KERNELS = {
     "decode_score_state": (r"decode_score_state_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
     "decode_select": (r"decode_topm_kernel<|decode_select_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
     "bwd_sparse": (r"sparse_bwd_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
+    "bwd_sparse_query": (r"sparse_bwd_q_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
+    "bwd_sparse_keys": (r"sparse_bwd_kv_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
 }
 
 
@@ -197,6 +200,9 @@ def roofline_entry(kernel, ms, work, bound, traffic=None):
     if bound == "hbm":
         achieved = work / (ms * 1e-3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
+    elif bound == "alu":
+        achieved = work / (ms * 1e-3) / 1e12
+        peak, unit = FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
     else:
         achieved = work / (ms * 1e-3) / 1e12
         peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
@@ -315,11 +321,13 @@ def bench_decode(args):
     return res
 
 
-def backward_bytes(cfg, n, B):
-    """Algorithmic bytes of the sparse backward: per (position, group, valid
-    slot) the K and V rows read once and the fp32 dK and dV rows updated."""
-    pairs = B * cfg.Hkv * sum(min(cfg.M, t + 1) for t in range(n))
-    return pairs * (2 * cfg.d * 2 + 2 * cfg.d * 4)
+def backward_flops(cfg, n, B):
+    """Algorithmic flops of the sparse branch's backward per (query head,
+    selected key): the logit and d_out.v dots and the dq terms on the query
+    side (3 x 2d), the dk and dv terms on the key side (2 x 2d)."""
+    ph = B * cfg.Hq * pairs(n, cfg.M)
+    return {"bwd_sparse_query": 6 * cfg.d * ph, "bwd_sparse_keys": 4 * cfg.d * ph,
+            "bwd_sparse": 10 * cfg.d * ph}
 
 
 def bench_backward(args, pre):
@@ -343,8 +351,12 @@ def bench_backward(args, pre):
 
     ms = timed_loop(step, args.bwd_steps, 1, 1)
     stages = stage_pass(step, args.bwd_steps, 1)
-    bb = backward_bytes(cfg, n, B)
-    roof = roofline_entry("bwd_sparse", stages["bwd_sparse"], bb, "hbm", traffic_from_profiles("bwd_sparse"))
+    fl = backward_flops(cfg, n, B)
+    dom = max(stages, key=stages.get)
+    # the query side runs on bf16 MFMA; the key side is fp32 VALU work whose
+    # ceiling in practice is the L2 atomic rate
+    bound = "mfma" if dom == "bwd_sparse_query" else "alu"
+    roof = roofline_entry(dom, stages[dom], fl.get(dom, 0), bound, traffic_from_profiles(dom))
     res = {
         "workload": f"lisa_prefill_backward qwen2.5-7b-shaped B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                     f"d={cfg.d} M={cfg.M} bf16 (sets from the forward; d_state_out and state_in given)",

@@ -119,12 +119,12 @@ DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
 enum Stage {
     ST_LIN_STATE, ST_LIN_SCAN, ST_LIN_OUT, ST_IDX_PACK, ST_INDEXER, ST_SPARSE_PREFILL,
     ST_DEC_SCORE_STATE, ST_DEC_SELECT, ST_SPARSE_DECODE,
-    ST_BWD_OPER, ST_BWD_LINEAR, ST_BWD_COMBINE, ST_BWD_SPARSE, ST_COUNT
+    ST_BWD_OPER, ST_BWD_LINEAR, ST_BWD_COMBINE, ST_BWD_SPARSE, ST_BWD_SPARSE_Q, ST_BWD_SPARSE_KV, ST_COUNT
 };
 const char *const kStageNames[ST_COUNT] = {
     "linear_chunk_state", "linear_prefix_scan", "linear_chunk_output", "indexer_pack", "indexer_topm",
     "sparse_gate_prefill", "decode_score_state", "decode_select", "sparse_gate_decode",
-    "bwd_operands", "bwd_linear", "bwd_combine", "bwd_sparse",
+    "bwd_operands", "bwd_linear", "bwd_combine", "bwd_sparse", "bwd_sparse_query", "bwd_sparse_keys",
 };
 
 struct Timing {
@@ -525,7 +525,7 @@ lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int6
 // ---- backward --------------------------------------------------------------------
 namespace {
 struct BwdWs {
-    size_t olin, Gl, Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, total;
+    size_t olin, Gl, Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, coef, total;
 };
 BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     const size_t Hq = d->num_q_heads, D = d->head_dim, eb = elt_bytes(d->dtype);
@@ -548,6 +548,9 @@ BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     off += align_up((size_t)B * Hq * nC * D * D * 4);
     w.P = off;
     off += align_up((size_t)B * Hq * nC * D * D * eb);
+    // bf16: per-slot coefficients of the sparse branch, [B,n,G,M,2r] fp32
+    w.coef = off;
+    if (d->dtype == LISA_BF16) off += align_up((size_t)B * n * Hq * d->top_m * 2 * 4);
     w.total = off;
     return w;
 }
@@ -606,7 +609,7 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     const int G = dims->num_kv_heads, Hq = dims->num_q_heads, D = dims->head_dim, M = dims->top_m;
     if (Hq / G > 16)
         return fail(LISA_ERR_UNSUPPORTED, "%d query heads per group: the backward handles up to 16", Hq / G);
-    if (lisa::sparse_bwd_lds_bytes(Hq / G, M, D) > 65536)
+    if (dims->dtype != LISA_BF16 && lisa::sparse_bwd_lds_bytes(Hq / G, M, D) > 65536)
         return fail(LISA_ERR_UNSUPPORTED, "top_m %d with %d heads per group exceeds the backward's LDS", M, Hq / G);
     if ((int64_t)B * n == 0) return ok();
     LISA_NEED(q, "q");
@@ -703,8 +706,16 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     sb.r = Hq / G;
     sb.M = M;
     sb.scale = (float)(dims->softmax_scale > 0.0f ? (double)dims->softmax_scale : 1.0 / std::sqrt((double)D));
-    LISA_HIP(timed(ST_BWD_SPARSE, s, [&] { return lisa::launch_sparse_bwd(sb, dims->dtype, D, s); }),
-             "sparse backward launch");
+    if (dims->dtype == LISA_BF16) {
+        sb.coef = reinterpret_cast<float *>(ws + w.coef);
+        LISA_HIP(timed(ST_BWD_SPARSE_Q, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, true, s); }),
+                 "sparse backward (query side) launch");
+        LISA_HIP(timed(ST_BWD_SPARSE_KV, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, false, s); }),
+                 "sparse backward (key side) launch");
+    } else {
+        LISA_HIP(timed(ST_BWD_SPARSE, s, [&] { return lisa::launch_sparse_bwd(sb, dims->dtype, D, s); }),
+                 "sparse backward launch");
+    }
     return ok();
 }
 

@@ -326,6 +326,369 @@ __global__ __launch_bounds__(64) void sparse_bwd_kernel(SparseBwdArgs a) {
             for (int j = 0; j < DPL; ++j) a.dq[hrow + h * D + lane + 64 * j] += a.scale * dqa[h][j];
 }
 
+// ---- sparse branch, bf16: query side on MFMA, key side by a sorted walk -----
+//
+// Query side (sparse_bwd_q_kernel), one wave per unit (b, t, g), two sweeps
+// over the unit's selected slots in steps of 32, each step gathering the K
+// and V rows into LDS (row-coalesced, as the forward does):
+//   sweep 1: S^T = K_sel Q^T and DP^T = V_sel dO^T on MFMA; per head the
+//            running max, the normaliser l and E = sum p (dO . v) (= dO . o_sp)
+//            with online rescaling;
+//   sweep 2: the same two products again, p = exp(x - m) / l,
+//            ds = gamma p (dO . v - E); the per-slot coefficients (scale ds,
+//            gamma p) of every head go to the workspace for the key side, and
+//            dq^T += K_sel^T ds^T on MFMA (K read back transposed from LDS).
+// The gate gradient is gamma (1 - gamma) (E - dO . o_lin).
+//
+// Key side (sparse_bwd_kv_kernel): a work-group takes Qb consecutive
+// positions of one group, with their q and d_out rows staged in LDS.  Their
+// (key, position, slot) entries are sorted by key in LDS (each position's set
+// is ascending, so only the merge levels of a bitonic sort run), and each wave
+// walks a contiguous stretch of the sorted entries:
+//   dk_s += sum_h (scale ds_h) q_h,  dv_s += sum_h (gamma p_h) dO_h
+// accumulating while the key stays the same and adding the sum into the key's
+// row with fp32 atomics when it changes.  Neighbouring positions share many
+// selected keys, so this adds each key row once per work-group instead of
+// once per selecting position (the atomics' throughput is what bounds the
+// one-wave-per-position form).
+typedef __bf16 bwd_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bwd_bf16x4 bwd_lds_bf16x4;
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): in each 16-lane block,
+// lane l gets element l % 4 of the 4-element row piece addressed by lane
+// 4e + l / 4, e = 0..3
+__device__ __forceinline__ u32x2 bwd_read_tr16(const unsigned char *lds_byte_ptr) {
+    bwd_lds_bf16x4 *p = (bwd_lds_bf16x4 *)(__attribute__((address_space(3))) unsigned char *)(
+        (__attribute__((address_space(3))) void *)lds_byte_ptr);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
+    constexpr int LPR = D * 2 / 16;   // lanes per gathered row (16 bytes each)
+    constexpr int RPI = 64 / LPR;     // rows per load instruction
+    constexpr int NI = 32 / RPI;      // load instructions per 32 rows (per tensor)
+    constexpr int KC = D / 32, MB = D / 16;
+    constexpr int KRB = D * 2 + 32;   // K rows: fragment reads and transposed reads
+    constexpr int VRB = D * 2 + 16;   // V rows: fragment reads
+    __shared__ __attribute__((aligned(16))) unsigned char lds[32 * KRB + 32 * VRB + 32 * 4];
+    unsigned char *ldk = lds, *ldv = lds + 32 * KRB;
+    uint32_t *flg = reinterpret_cast<uint32_t *>(lds + 32 * KRB + 32 * VRB);
+    const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
+    const int G = a.G, r = a.r, M = a.M, n = a.n;
+    // group-major units, a contiguous range per XCD (as in the forward)
+    const int lu = xcd_remap(blockIdx.x, gridDim.x);
+    const int u = (lu % (a.B * n)) * G + lu / (a.B * n);
+    const int g = u % G, bt = u / G, b = bt / n, t = bt % n;
+    const int nvalid = min(M, t + 1);
+    const size_t hrow = ((size_t)bt * a.Hq + g * r) * D;
+    const uint16_t *qrows = reinterpret_cast<const uint16_t *>(a.q) + hrow;
+    const uint16_t *dorows = reinterpret_cast<const uint16_t *>(a.dout) + hrow;
+    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k) + ((size_t)b * n * G + g) * D;
+    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v) + ((size_t)b * n * G + g) * D;
+    const uint32_t row_bytes = (uint32_t)G * D * 2;
+    const uint32_t vis_bytes = (uint32_t)(t + 1) * row_bytes;
+    const rsrc_t krs = make_rsrc(kbase, vis_bytes), vrs = make_rsrc(vbase, vis_bytes);
+    const rsrc_t irs = make_rsrc(a.idx + (size_t)u * M, (uint32_t)M * 4u);
+    const float scale_log2 = a.scale * 1.4426950408889634f;
+
+    Frag<uint16_t> qf[KC], dof[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        if (col < r) {
+            qf[kc].load(qrows + (size_t)col * D + kc * 32 + grp * 8);
+            dof[kc].load(dorows + (size_t)col * D + kc * 32 + grp * 8);
+        } else {
+            qf[kc].zero();
+            dof[kc].zero();
+        }
+    }
+    const float gam = col < r ? sigmoidf(bf16_bits_to_f32(
+                                    reinterpret_cast<const uint16_t *>(a.z)[(size_t)bt * a.Hq + g * r + col]))
+                              : 0.0f;
+
+    // this lane fetches piece (lane % LPR) of rows rho0 .. rho0 + NI - 1 of a step
+    const int rsub = lane / LPR, piece = lane % LPR, rho0 = rsub * NI;
+    const int nsteps = (nvalid + 31) / 32;
+    u32x4 kp[NI], vp[NI];
+    uint32_t okbits = 0;  // bit i: row rho0 + i of the step in flight is a valid slot
+    auto gather = [&](int j) {
+        okbits = 0;
+        uint32_t off[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int slot = j * 32 + rho0 + i;
+            const int s = (int)__builtin_amdgcn_raw_buffer_load_b32(irs, (uint32_t)slot * 4u, 0u, 0);
+            const bool ok = slot < nvalid && s >= 0 && s <= t;
+            okbits |= ok ? (1u << i) : 0u;
+            off[i] = ok ? (uint32_t)s * row_bytes + piece * 16 : kOffNone;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) kp[i] = buf_load16(krs, off[i]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) vp[i] = buf_load16(vrs, off[i]);
+    };
+    const uint32_t kw = (uint32_t)rho0 * KRB + piece * 16, vw = (uint32_t)rho0 * VRB + piece * 16;
+    const uint32_t kfr = (uint32_t)col * KRB + grp * 16, vfr = (uint32_t)col * VRB + grp * 16;
+    const uint32_t ktr = (uint32_t)(grp * 4 + (col >> 2)) * KRB + (col & 3) * 8;
+    // stage the gathered rows of step j, issue the gather of step j + 1, and
+    // form S^T (acc) and DP^T (dacc) of the step's two 16-slot blocks; valid[e]
+    // tells whether slot kb*16 + 4*grp + i (e = 4 kb + i) is a selected key
+    f32x4 acc[2], dacc[2];
+    bool valid[8];
+    auto step = [&](int j) {
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            *reinterpret_cast<u32x4 *>(ldk + kw + i * KRB) = kp[i];
+            *reinterpret_cast<u32x4 *>(ldv + vw + i * VRB) = vp[i];
+            if (piece == 0) flg[rho0 + i] = (okbits >> i) & 1u;
+        }
+        if (j + 1 < nsteps) gather(j + 1);
+        wave_lds_sync();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            acc[kb] = f32x4{0, 0, 0, 0};
+            dacc[kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                Frag<uint16_t> kf, vf;
+                kf.v = *reinterpret_cast<const u32x4 *>(ldk + kfr + kb * 16 * KRB + kc * 64);
+                vf.v = *reinterpret_cast<const u32x4 *>(ldv + vfr + kb * 16 * VRB + kc * 64);
+                acc[kb] = mma16(kf, qf[kc], acc[kb]);
+                dacc[kb] = mma16(vf, dof[kc], dacc[kb]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) valid[kb * 4 + i] = flg[kb * 16 + grp * 4 + i] != 0u;
+        }
+    };
+
+    // ---- sweep 1: max, normaliser and E per head (column) ----------------------
+    float m_run = -INFINITY, l_part = 0.0f, e_part = 0.0f;
+    gather(0);
+    for (int j = 0; j < nsteps; ++j) {
+        step(j);
+        float x[8], cmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[e] = valid[e] ? acc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+            cmax = fmaxf(cmax, x[e]);
+        }
+        cmax = wave_max_across16(cmax);
+        const float m_new = fmaxf(m_run, cmax);
+        if (m_new != -INFINITY) {
+            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_part *= alpha;
+            e_part *= alpha;
+            m_run = m_new;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = valid[e] ? __builtin_amdgcn_exp2f(x[e] - m_run) : 0.0f;
+                l_part += p;
+                e_part = fmaf(p, dacc[e >> 2][e & 3], e_part);
+            }
+        }
+    }
+    const float l = wave_sum_across16(l_part);
+    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+    const float E = wave_sum_across16(e_part) * inv_l;
+
+    // ---- sweep 2: coefficients and dq ---------------------------------------------
+    f32x4 o[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) o[mb] = f32x4{0, 0, 0, 0};
+    float *coefu = a.coef + (size_t)u * M * 2 * r;
+    gather(0);
+    for (int j = 0; j < nsteps; ++j) {
+        step(j);
+        float dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = valid[e] ? __builtin_amdgcn_exp2f(acc[e >> 2][e & 3] * scale_log2 - m_run) * inv_l : 0.0f;
+            const float ds = gam * p * (dacc[e >> 2][e & 3] - E);
+            dsv[e] = ds;
+            if (valid[e] && col < r) {
+                const int slot = j * 32 + (e >> 2) * 16 + grp * 4 + (e & 3);
+                coefu[(size_t)slot * 2 * r + col] = a.scale * ds;
+                coefu[(size_t)slot * 2 * r + r + col] = gam * p;
+            }
+        }
+        Frag<uint16_t> dsf;
+        dsf.set(dsv);  // K-element e <-> slot (e < 4 ? 4*grp + e : 16 + 4*grp + e - 4)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const u32x2 lo = bwd_read_tr16(ldk + ktr + mb * 32);
+            const u32x2 hi = bwd_read_tr16(ldk + ktr + 16 * KRB + mb * 32);
+            Frag<uint16_t> kt;
+            kt.v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            o[mb] = mma16(kt, dsf, o[mb]);
+        }
+    }
+
+    // ---- epilogue: dq (lane (col = head, grp) holds dims 16 mb + 4 grp + i), dgate
+    float dot = 0.0f;
+    if (col < r) {
+        float *dqp = a.dq + hrow + (size_t)col * D;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x4 *pp = reinterpret_cast<f32x4 *>(dqp + mb * 16 + grp * 4);
+            *pp = *pp + o[mb] * a.scale;
+        }
+        const uint16_t *dor = dorows + (size_t)col * D + grp * (D / 4);
+        const uint16_t *olr = reinterpret_cast<const uint16_t *>(a.olin) + hrow + (size_t)col * D + grp * (D / 4);
+#pragma unroll
+        for (int c = 0; c < D / 4; c += 8) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(dor + c);
+            const u32x4 y = *reinterpret_cast<const u32x4 *>(olr + c);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                dot = fmaf(bf16_bits_to_f32(x[w] & 0xFFFFu), bf16_bits_to_f32(y[w] & 0xFFFFu), dot);
+                dot = fmaf(bf16_bits_to_f32(x[w] >> 16), bf16_bits_to_f32(y[w] >> 16), dot);
+            }
+        }
+    }
+    dot = wave_sum_across16(dot);
+    if (col < r && grp == 0) a.dgate[(size_t)bt * a.Hq + g * r + col] = gam * (1.0f - gam) * (E - dot);
+}
+
+// Key side.  LDS: the sorted entries (Qb * Mp words, Mp = M rounded up to a
+// power of two), then the q and d_out rows of the Qb positions (bf16
+// [Qb][r][D] each).  An entry is key << 17 | position-in-block << 9 | slot;
+// 0xFFFFFFFF marks no entry and sorts last.
+constexpr int kKvThreads = 512;
+constexpr int kKvLdsBytes = 160 * 1024;
+constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) void sparse_bwd_kv_kernel(SparseBwdArgs a, int Qb, int lgMp) {
+    __shared__ __attribute__((aligned(16))) uint32_t sm[kKvLdsBytes / 4];
+    constexpr int DPL = D / 64;  // dims per lane: 2 * lane + c (D = 128) or lane (D = 64)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = a.G, r = a.r, M = a.M, n = a.n, Hq = a.Hq;
+    const int Mp = 1 << lgMp, E = Qb * Mp;
+    const int nblk = (n + Qb - 1) / Qb;
+    const int bg = blockIdx.x / nblk, tb = blockIdx.x % nblk;
+    const int g = bg % G, b = bg / G;
+    const int t0 = tb * Qb, nq = min(Qb, n - t0);
+    uint32_t *ent = sm;
+    uint16_t *qs = reinterpret_cast<uint16_t *>(sm + E);
+    uint16_t *dos = qs + (size_t)Qb * r * D;
+
+    // entries: position tl's run of Mp is ascending for even tl and reversed
+    // for odd tl, the input a bitonic merge of size 2 Mp expects
+    for (int i = tid; i < E; i += kKvThreads) {
+        const int tl = i >> lgMp, pos = i & (Mp - 1);
+        const int slot = (tl & 1) ? Mp - 1 - pos : pos;
+        uint32_t e = kNoEntry;
+        const int t = t0 + tl;
+        if (tl < nq && slot < min(M, t + 1)) {
+            const int s = a.idx[(((size_t)b * n + t) * G + g) * M + slot];
+            if (s >= 0 && s <= t) e = ((uint32_t)s << 17) | ((uint32_t)tl << 9) | (uint32_t)slot;
+        }
+        ent[i] = e;
+    }
+    // q and d_out rows of the block's positions (r heads of the group are contiguous)
+    {
+        const int per = r * D / 8;  // 16-byte pieces per position and tensor
+        for (int i = tid; i < nq * per; i += kKvThreads) {
+            const int tl = i / per, c = i % per;
+            const size_t src = (((size_t)b * n + t0 + tl) * Hq + g * r) * D + c * 8;
+            reinterpret_cast<u32x4 *>(qs)[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + src);
+            reinterpret_cast<u32x4 *>(dos)[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.dout) + src);
+        }
+    }
+    __syncthreads();
+    // bitonic merge levels 2 Mp .. E (ascending overall)
+    for (int k = 2 * Mp; k <= E; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int p = tid; p < E / 2; p += kKvThreads) {
+                const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+                const int l = i | j;
+                const uint32_t x = ent[i], y = ent[l];
+                const bool up = (i & k) == 0;
+                if ((x > y) == up) {
+                    ent[i] = y;
+                    ent[l] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // walk: wave w takes sorted entries [w E / W, (w + 1) E / W)
+    constexpr int W = kKvThreads / 64;
+    const int e0 = wave * (E / W), e1 = e0 + E / W;
+    const size_t unit0 = ((size_t)b * n + t0) * G + g;  // unit of the block's first position
+    float gk[DPL], gv[DPL];
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) gk[c] = gv[c] = 0.0f;
+    int cur = -1;
+    // D = 128: lane m accumulates dims 2m, 2m + 1; the atomics want lane l to
+    // hold dims l and l + 64, so each instruction adds one contiguous 256-byte run
+    auto flush = [&]() {
+        if (cur < 0) return;
+        const size_t row = (((size_t)b * n + cur) * G + g) * D;
+        if constexpr (D == 128) {
+            const int src0 = lane >> 1, src1 = 32 + (lane >> 1);
+            const bool odd = lane & 1;
+            const float k0 = __shfl(gk[0], src0), k1 = __shfl(gk[1], src0);
+            const float k2 = __shfl(gk[0], src1), k3 = __shfl(gk[1], src1);
+            const float v0 = __shfl(gv[0], src0), v1 = __shfl(gv[1], src0);
+            const float v2 = __shfl(gv[0], src1), v3 = __shfl(gv[1], src1);
+            unsafeAtomicAdd(a.dk + row + lane, odd ? k1 : k0);
+            unsafeAtomicAdd(a.dk + row + 64 + lane, odd ? k3 : k2);
+            unsafeAtomicAdd(a.dv + row + lane, odd ? v1 : v0);
+            unsafeAtomicAdd(a.dv + row + 64 + lane, odd ? v3 : v2);
+        } else {
+            unsafeAtomicAdd(a.dk + row + lane, gk[0]);
+            unsafeAtomicAdd(a.dv + row + lane, gv[0]);
+        }
+#pragma unroll
+        for (int c = 0; c < DPL; ++c) gk[c] = gv[c] = 0.0f;
+    };
+    constexpr int U = 8;  // entries whose coefficients load together
+    for (int base = e0; base < e1; base += U) {
+        uint32_t ev[U];
+        float cv[U];
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            ev[x] = __builtin_amdgcn_readfirstlane(ent[base + x]);
+            cv[x] = 0.0f;
+            if (ev[x] != kNoEntry && lane < 2 * r) {
+                const int tl = (ev[x] >> 9) & 255, slot = ev[x] & 511;
+                cv[x] = a.coef[((unit0 + (size_t)tl * G) * M + slot) * 2 * r + lane];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            if (ev[x] == kNoEntry) continue;
+            const int s = (int)(ev[x] >> 17), tl = (ev[x] >> 9) & 255;
+            if (s != cur) {
+                flush();
+                cur = s;
+            }
+            const uint16_t *qr = qs + (size_t)tl * r * D;
+            const uint16_t *dr = dos + (size_t)tl * r * D;
+            for (int h = 0; h < r; ++h) {
+                const float cds = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), h));
+                const float cpv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), r + h));
+                if constexpr (D == 128) {
+                    const uint32_t qv = *reinterpret_cast<const uint32_t *>(qr + h * D + 2 * lane);
+                    const uint32_t dv = *reinterpret_cast<const uint32_t *>(dr + h * D + 2 * lane);
+                    gk[0] = fmaf(cds, bf16_bits_to_f32(qv & 0xFFFFu), gk[0]);
+                    gk[DPL - 1] = fmaf(cds, bf16_bits_to_f32(qv >> 16), gk[DPL - 1]);
+                    gv[0] = fmaf(cpv, bf16_bits_to_f32(dv & 0xFFFFu), gv[0]);
+                    gv[DPL - 1] = fmaf(cpv, bf16_bits_to_f32(dv >> 16), gv[DPL - 1]);
+                } else {
+                    gk[0] = fmaf(cds, bf16_bits_to_f32(qr[h * D + lane]), gk[0]);
+                    gv[0] = fmaf(cpv, bf16_bits_to_f32(dr[h * D + lane]), gv[0]);
+                }
+            }
+        }
+    }
+    flush();
+}
+
 template <typename T>
 hipError_t prep_t(const BwdPrepArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d / 8;
@@ -363,6 +726,33 @@ hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s)
     if ((int64_t)a.B * a.n == 0) return hipSuccess;
     return dtype == 1 ? combine_t<uint16_t>(a, s) : combine_t<float>(a, s);
 }
+int sparse_bwd_key_block(int r, int M, int d) {
+    int Mp = 1;
+    while (Mp < M) Mp <<= 1;
+    for (int Qb = 128; Qb >= 1; Qb >>= 1)
+        if ((size_t)Qb * Mp * 4 + (size_t)2 * Qb * r * d * 2 <= (size_t)kKvLdsBytes && Qb * Mp >= 8 * (kKvThreads / 64))
+            return Qb;
+    return 0;
+}
+
+hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_side, hipStream_t s) {
+    if ((int64_t)a.B * a.n == 0) return hipSuccess;
+    if (query_side) {
+        const dim3 grid((unsigned)((int64_t)a.B * a.n * a.G));
+        if (d == 128) hipLaunchKernelGGL((sparse_bwd_q_kernel<128>), grid, dim3(64), 0, s, a);
+        else hipLaunchKernelGGL((sparse_bwd_q_kernel<64>), grid, dim3(64), 0, s, a);
+        return hipGetLastError();
+    }
+    const int Qb = sparse_bwd_key_block(a.r, a.M, d);
+    if (Qb == 0) return hipErrorInvalidValue;
+    int lgMp = 0;
+    while ((1 << lgMp) < a.M) ++lgMp;
+    const dim3 grid((unsigned)((int64_t)a.B * a.G * ((a.n + Qb - 1) / Qb)));
+    if (d == 128) hipLaunchKernelGGL((sparse_bwd_kv_kernel<128>), grid, dim3(kKvThreads), 0, s, a, Qb, lgMp);
+    else hipLaunchKernelGGL((sparse_bwd_kv_kernel<64>), grid, dim3(kKvThreads), 0, s, a, Qb, lgMp);
+    return hipGetLastError();
+}
+
 hipError_t launch_sparse_bwd(const SparseBwdArgs &a, int dtype, int d, hipStream_t s) {
     if ((int64_t)a.B * a.n == 0) return hipSuccess;
     if (a.r > kMaxR) return hipErrorInvalidValue;

@@ -116,13 +116,18 @@ struct SparseBwdArgs {
     const void *q, *k, *v, *z, *dout, *olin;  // layer dtype
     const int32_t *idx;                       // [B,n,G,M] the forward's sets
     float *dq, *dk, *dv, *dgate;              // dq += ; dk, dv atomically += ; dgate =
+    float *coef;                              // bf16 path: [B,n,G,M,2r] (scale ds, gamma p) per slot
     int B, n, Hq, G, r, M;
     float scale;
 };
 size_t sparse_bwd_lds_bytes(int r, int M, int d);
+// queries per work-group of the key-side pass (0: the shape does not fit its LDS)
+int sparse_bwd_key_block(int r, int M, int d);
 hipError_t launch_bwd_prep(const BwdPrepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_transpose_states(const float *src, float *dst, int64_t nmat, int d, hipStream_t s);
 hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s);
 hipError_t launch_sparse_bwd(const SparseBwdArgs &a, int dtype, int d, hipStream_t s);
+// bf16: the query side (dq, dgate, coefficients) or the key side (dk, dv)
+hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_side, hipStream_t s);
 
 }  // namespace lisa
