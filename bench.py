@@ -130,15 +130,22 @@ def traffic_summary(fetch_db, write_db, out_json, out_md, command):
 
     def per_kernel(db, counter):
         cur = sqlite3.connect(db).cursor()
-        rows = list(cur.execute("select kernel_name, value from counters_collection "
+        rows = list(cur.execute("select kernel_name, value, dispatch_id from counters_collection "
                                 "where counter_name = ?", (counter,)))
-        cal = [v for nm, v in rows if "copyBuffer" in nm and v > 1e5]
+        cal = [v for nm, v, _ in rows if "copyBuffer" in nm and v > 1e5]
         if not cal:
             raise SystemExit(f"{db}: no calibration copy found (run bench.py --copy-calibration)")
         factor = (1 << 30) / (sum(cal) / len(cal) * 1024.0)
+        # the benchmark runs prefill, then decode, then the backward (which
+        # runs a prefill with an initial state and the linear kernels on its
+        # own operands): prefill stages count only the dispatches before the
+        # first decode kernel
+        dec_ids = [i for nm, _, i in rows if re.search(r"decode_score_state_kernel<", nm)]
+        first_dec = min(dec_ids) if dec_ids else float("inf")
         out = {}
         for stage, (pat, _) in STAGE_KERNELS.items():
-            vals = [v for nm, v in rows if re.search(pat, nm)]
+            prefill_stage = stage.startswith(("linear", "indexer", "sparse_gate_prefill"))
+            vals = [v for nm, v, i in rows if re.search(pat, nm) and (not prefill_stage or i < first_dec)]
             if vals:
                 out[stage] = (sum(vals) / len(vals) * 1024.0 * factor, len(vals))
         return out, factor
@@ -157,7 +164,7 @@ def traffic_summary(fetch_db, write_db, out_json, out_md, command):
     with open(out_json, "w") as f:
         json.dump(data, f, indent=1)
     with open(out_md, "w") as f:
-        f.write("# HBM traffic per launch: 16K prefill and 16K decode step\n\n")
+        f.write("# HBM traffic per launch: 16K prefill, 16K decode step, 16K backward\n\n")
         f.write("rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in a pass of its own:\n\n")
         f.write("```\n" + command + "\n```\n\n")
         f.write(f"Scale factors from the 1 GiB device copy: FETCH_SIZE x {ff:.3f}, "
@@ -450,7 +457,7 @@ def main():
         cmd = ("cd /tmp && export TMPDIR=/tmp && for c in FETCH_SIZE WRITE_SIZE; do "
                "timeout -s KILL 180 rocprofv3 --pmc $c -d $REPO/gpurun_out/pmc_$c -o run -- "
                "python3 $REPO/bench.py --steps 2 --warmup 1 --decode-steps 9 --decode-warmup 1 "
-               "--no-cpu-baseline --copy-calibration; done; cd $REPO && python3 bench.py "
+               "--bwd-steps 1 --no-cpu-baseline --copy-calibration; done; cd $REPO && python3 bench.py "
                "--traffic-summary gpurun_out/pmc_FETCH_SIZE/run_results.db "
                "gpurun_out/pmc_WRITE_SIZE/run_results.db")
         data = traffic_summary(*args.traffic_summary, os.path.join(PROFILES, "traffic.json"),

@@ -525,7 +525,7 @@ lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int6
 // ---- backward --------------------------------------------------------------------
 namespace {
 struct BwdWs {
-    size_t olin, Gl, Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, coef, total;
+    size_t olin, Gl, Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, coef, sorted, total;
 };
 BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     const size_t Hq = d->num_q_heads, D = d->head_dim, eb = elt_bytes(d->dtype);
@@ -551,6 +551,8 @@ BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     // bf16: per-slot coefficients of the sparse branch, [B,n,G,M,2r] fp32
     w.coef = off;
     if (d->dtype == LISA_BF16) off += align_up((size_t)B * n * Hq * d->top_m * 2 * 4);
+    w.sorted = off;
+    if (d->dtype == LISA_BF16) off += align_up(lisa::sparse_bwd_sorted_bytes(B, n, d->num_kv_heads, d->top_m));
     w.total = off;
     return w;
 }
@@ -708,6 +710,7 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     sb.scale = (float)(dims->softmax_scale > 0.0f ? (double)dims->softmax_scale : 1.0 / std::sqrt((double)D));
     if (dims->dtype == LISA_BF16) {
         sb.coef = reinterpret_cast<float *>(ws + w.coef);
+        sb.sorted = reinterpret_cast<uint32_t *>(ws + w.sorted);
         LISA_HIP(timed(ST_BWD_SPARSE_Q, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, true, s); }),
                  "sparse backward (query side) launch");
         LISA_HIP(timed(ST_BWD_SPARSE_KV, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, false, s); }),

@@ -340,16 +340,14 @@ __global__ __launch_bounds__(64) void sparse_bwd_kernel(SparseBwdArgs a) {
 //            dq^T += K_sel^T ds^T on MFMA (K read back transposed from LDS).
 // The gate gradient is gamma (1 - gamma) (E - dO . o_lin).
 //
-// Key side (sparse_bwd_kv_kernel): a work-group takes Qb consecutive
-// positions of one group, with their q and d_out rows staged in LDS.  Their
-// (key, position, slot) entries are sorted by key in LDS (each position's set
-// is ascending, so only the merge levels of a bitonic sort run), and each wave
-// walks a contiguous stretch of the sorted entries:
+// Key side (sparse_bwd_sort_kernel, sparse_bwd_walk_kernel): the
+// (key, position, slot) entries of a block of consecutive positions of one
+// group are sorted by key, and waves walk contiguous stretches of them:
 //   dk_s += sum_h (scale ds_h) q_h,  dv_s += sum_h (gamma p_h) dO_h
 // accumulating while the key stays the same and adding the sum into the key's
 // row with fp32 atomics when it changes.  Neighbouring positions share many
-// selected keys, so this adds each key row once per work-group instead of
-// once per selecting position (the atomics' throughput is what bounds the
+// selected keys, so a key row is added about once per block instead of once
+// per selecting position (the atomics' throughput is what bounds the
 // one-wave-per-position form).
 typedef __bf16 bwd_bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bwd_bf16x4 bwd_lds_bf16x4;
@@ -551,32 +549,28 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
     if (col < r && grp == 0) a.dgate[(size_t)bt * a.Hq + g * r + col] = gam * (1.0f - gam) * (E - dot);
 }
 
-// Key side.  LDS: the sorted entries (Qb * Mp words, Mp = M rounded up to a
-// power of two), then the q and d_out rows of the Qb positions (bf16
-// [Qb][r][D] each).  An entry is key << 17 | position-in-block << 9 | slot;
-// 0xFFFFFFFF marks no entry and sorts last.
-constexpr int kKvThreads = 512;
-constexpr int kKvLdsBytes = 160 * 1024;
+// Key side, step 1 (sparse_bwd_sort_kernel): one work-group per block of Qb
+// consecutive positions of one group sorts the block's (key, position, slot)
+// entries by key in LDS and writes them out.  An entry is
+// key << 17 | position-in-block << 9 | slot; 0xFFFFFFFF marks no entry and
+// sorts last.  Each position's run of Mp entries (M rounded up to a power
+// of two) is ascending, so runs are laid out alternately ascending and
+// reversed and only the merge levels of a bitonic sort run.
+constexpr int kSortThreads = 1024;
+constexpr int kSortMaxEntries = 32768;  // 128 KB of LDS
 constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
 
-template <int D>
-__global__ __launch_bounds__(kKvThreads) void sparse_bwd_kv_kernel(SparseBwdArgs a, int Qb, int lgMp) {
-    __shared__ __attribute__((aligned(16))) uint32_t sm[kKvLdsBytes / 4];
-    constexpr int DPL = D / 64;  // dims per lane: 2 * lane + c (D = 128) or lane (D = 64)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = a.G, r = a.r, M = a.M, n = a.n, Hq = a.Hq;
+__global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwdArgs a, int Qb, int lgMp,
+                                                                       uint32_t *sorted) {
+    __shared__ uint32_t ent[kSortMaxEntries];
+    const int tid = threadIdx.x;
+    const int G = a.G, M = a.M, n = a.n;
     const int Mp = 1 << lgMp, E = Qb * Mp;
     const int nblk = (n + Qb - 1) / Qb;
     const int bg = blockIdx.x / nblk, tb = blockIdx.x % nblk;
     const int g = bg % G, b = bg / G;
     const int t0 = tb * Qb, nq = min(Qb, n - t0);
-    uint32_t *ent = sm;
-    uint16_t *qs = reinterpret_cast<uint16_t *>(sm + E);
-    uint16_t *dos = qs + (size_t)Qb * r * D;
-
-    // entries: position tl's run of Mp is ascending for even tl and reversed
-    // for odd tl, the input a bitonic merge of size 2 Mp expects
-    for (int i = tid; i < E; i += kKvThreads) {
+    for (int i = tid; i < E; i += kSortThreads) {
         const int tl = i >> lgMp, pos = i & (Mp - 1);
         const int slot = (tl & 1) ? Mp - 1 - pos : pos;
         uint32_t e = kNoEntry;
@@ -587,26 +581,14 @@ __global__ __launch_bounds__(kKvThreads) void sparse_bwd_kv_kernel(SparseBwdArgs
         }
         ent[i] = e;
     }
-    // q and d_out rows of the block's positions (r heads of the group are contiguous)
-    {
-        const int per = r * D / 8;  // 16-byte pieces per position and tensor
-        for (int i = tid; i < nq * per; i += kKvThreads) {
-            const int tl = i / per, c = i % per;
-            const size_t src = (((size_t)b * n + t0 + tl) * Hq + g * r) * D + c * 8;
-            reinterpret_cast<u32x4 *>(qs)[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + src);
-            reinterpret_cast<u32x4 *>(dos)[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.dout) + src);
-        }
-    }
     __syncthreads();
-    // bitonic merge levels 2 Mp .. E (ascending overall)
     for (int k = 2 * Mp; k <= E; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int p = tid; p < E / 2; p += kKvThreads) {
+            for (int p = tid; p < E / 2; p += kSortThreads) {
                 const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
                 const int l = i | j;
                 const uint32_t x = ent[i], y = ent[l];
-                const bool up = (i & k) == 0;
-                if ((x > y) == up) {
+                if ((x > y) == ((i & k) == 0)) {
                     ent[i] = y;
                     ent[l] = x;
                 }
@@ -614,11 +596,50 @@ __global__ __launch_bounds__(kKvThreads) void sparse_bwd_kv_kernel(SparseBwdArgs
             __syncthreads();
         }
     }
+    uint32_t *dst = sorted + (size_t)blockIdx.x * E;
+    for (int i = tid; i < E; i += kSortThreads) dst[i] = ent[i];
+}
 
-    // walk: wave w takes sorted entries [w E / W, (w + 1) E / W)
-    constexpr int W = kKvThreads / 64;
-    const int e0 = wave * (E / W), e1 = e0 + E / W;
-    const size_t unit0 = ((size_t)b * n + t0) * G + g;  // unit of the block's first position
+// Key side, step 2 (sparse_bwd_walk_kernel): the sorted entries of a block
+// are split over the waves of kWalkSlices consecutive work-groups, which the
+// XCD remap places on one XCD, so the block's q and d_out rows (Qb * r * D
+// * 4 bytes) are fetched into that XCD's L2 once and then served from it.
+// Each wave walks a contiguous stretch: while the key stays the same it
+// accumulates in registers, and when it changes it adds the row once.
+constexpr int kWalkThreads = 256;
+constexpr int kWalkPerWave = 256;  // sorted entries per wave
+
+template <int D, int RMAX>
+__global__ __launch_bounds__(kWalkThreads) void sparse_bwd_walk_kernel(SparseBwdArgs a, int Qb, int E,
+                                                                       const uint32_t *sorted) {
+    constexpr int DPL = D / 64;  // dims per lane while accumulating: 2 lane + c (D = 128) or lane
+    constexpr int U = 8;         // entries whose loads are issued together
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = a.G, r = a.r, M = a.M, n = a.n, Hq = a.Hq;
+    const int slices = (E + kWalkPerWave * (kWalkThreads / 64) - 1) / (kWalkPerWave * (kWalkThreads / 64));
+    const int lu = xcd_remap(blockIdx.x, gridDim.x);
+    const int blk = lu / slices, slice = lu % slices;
+    const int nblk = (n + Qb - 1) / Qb;
+    const int bg = blk / nblk, tb = blk % nblk;
+    const int g = bg % G, b = bg / G;
+    const int t0 = tb * Qb, nq = min(Qb, n - t0);
+    const int start = (slice * (kWalkThreads / 64) + wave) * kWalkPerWave;
+    if (start >= E) return;
+    const int len = min(kWalkPerWave, E - start);
+    // len is 128 or 256 (E is Qb * Mp >= 128 and a stretch starts at a
+    // multiple of 256), so batches of U never pass the end; entries are
+    // wave-uniform and read through scalar loads
+    const uint32_t *__restrict__ ent = sorted + (size_t)blk * E + start;
+    const size_t unit0 = ((size_t)b * n + t0) * G + g;                          // unit of position t0
+    const uint16_t *q0 = reinterpret_cast<const uint16_t *>(a.q) + (((size_t)b * n + t0) * Hq + g * r) * D;
+    const uint16_t *d0 = reinterpret_cast<const uint16_t *>(a.dout) + (((size_t)b * n + t0) * Hq + g * r) * D;
+    const int loff = D == 128 ? 2 * lane : lane;
+    // every load goes through a buffer descriptor unconditionally (offsets of
+    // missing entries and heads fall outside and read zeros): a guarded load
+    // compiles to a branch with a full wait, serializing the batch
+    const rsrc_t qrs = make_rsrc(q0, (uint32_t)nq * Hq * D * 2u), drs = make_rsrc(d0, (uint32_t)nq * Hq * D * 2u);
+    const rsrc_t crs = make_rsrc(a.coef + unit0 * M * 2 * r, (uint32_t)nq * G * M * 2 * r * 4u);
+
     float gk[DPL], gv[DPL];
 #pragma unroll
     for (int c = 0; c < DPL; ++c) gk[c] = gv[c] = 0.0f;
@@ -646,42 +667,60 @@ __global__ __launch_bounds__(kKvThreads) void sparse_bwd_kv_kernel(SparseBwdArgs
 #pragma unroll
         for (int c = 0; c < DPL; ++c) gk[c] = gv[c] = 0.0f;
     };
-    constexpr int U = 8;  // entries whose coefficients load together
-    for (int base = e0; base < e1; base += U) {
+    // the entry words of the next batch load while this batch's rows do
+    uint32_t evn[U];
+#pragma unroll
+    for (int x = 0; x < U; ++x) evn[x] = ent[x];
+    for (int base = 0; base < len; base += U) {
         uint32_t ev[U];
         float cv[U];
+        uint32_t qv[U][RMAX], dv[U][RMAX];
 #pragma unroll
         for (int x = 0; x < U; ++x) {
-            ev[x] = __builtin_amdgcn_readfirstlane(ent[base + x]);
-            cv[x] = 0.0f;
-            if (ev[x] != kNoEntry && lane < 2 * r) {
-                const int tl = (ev[x] >> 9) & 255, slot = ev[x] & 511;
-                cv[x] = a.coef[((unit0 + (size_t)tl * G) * M + slot) * 2 * r + lane];
+            ev[x] = __builtin_amdgcn_readfirstlane(evn[x]);
+            evn[x] = ent[min(base + U + x, len - 1)];
+        }
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            const bool ok = ev[x] != kNoEntry;
+            const uint32_t tl = (ev[x] >> 9) & 255u, slot = ev[x] & 511u;
+            const uint32_t coff = ok && lane < 2 * r ? ((tl * G * M + slot) * 2 * r + lane) * 4u : kOffNone;
+            cv[x] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(crs, coff, 0u, 0));
+            const uint32_t roff = (tl * Hq * D + loff) * 2u;
+#pragma unroll
+            for (int h = 0; h < RMAX; ++h) {
+                const uint32_t off = ok && h < r ? roff + h * D * 2u : kOffNone;
+                if constexpr (D == 128) {
+                    qv[x][h] = __builtin_amdgcn_raw_buffer_load_b32(qrs, off, 0u, 0);
+                    dv[x][h] = __builtin_amdgcn_raw_buffer_load_b32(drs, off, 0u, 0);
+                } else {
+                    qv[x][h] = __builtin_amdgcn_raw_buffer_load_b16(qrs, off, 0u, 0);
+                    dv[x][h] = __builtin_amdgcn_raw_buffer_load_b16(drs, off, 0u, 0);
+                }
             }
         }
 #pragma unroll
         for (int x = 0; x < U; ++x) {
             if (ev[x] == kNoEntry) continue;
-            const int s = (int)(ev[x] >> 17), tl = (ev[x] >> 9) & 255;
+            const int s = (int)(ev[x] >> 17);
             if (s != cur) {
                 flush();
                 cur = s;
             }
-            const uint16_t *qr = qs + (size_t)tl * r * D;
-            const uint16_t *dr = dos + (size_t)tl * r * D;
-            for (int h = 0; h < r; ++h) {
-                const float cds = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), h));
-                const float cpv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), r + h));
-                if constexpr (D == 128) {
-                    const uint32_t qv = *reinterpret_cast<const uint32_t *>(qr + h * D + 2 * lane);
-                    const uint32_t dv = *reinterpret_cast<const uint32_t *>(dr + h * D + 2 * lane);
-                    gk[0] = fmaf(cds, bf16_bits_to_f32(qv & 0xFFFFu), gk[0]);
-                    gk[DPL - 1] = fmaf(cds, bf16_bits_to_f32(qv >> 16), gk[DPL - 1]);
-                    gv[0] = fmaf(cpv, bf16_bits_to_f32(dv & 0xFFFFu), gv[0]);
-                    gv[DPL - 1] = fmaf(cpv, bf16_bits_to_f32(dv >> 16), gv[DPL - 1]);
-                } else {
-                    gk[0] = fmaf(cds, bf16_bits_to_f32(qr[h * D + lane]), gk[0]);
-                    gv[0] = fmaf(cpv, bf16_bits_to_f32(dr[h * D + lane]), gv[0]);
+#pragma unroll
+            for (int h = 0; h < RMAX; ++h) {
+                if (h < r) {
+                    const float cds = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), h));
+                    const float cpv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), r + h));
+                    if constexpr (D == 128) {
+                        gk[0] = fmaf(cds, bf16_bits_to_f32(qv[x][h] & 0xFFFFu), gk[0]);
+                        gk[DPL - 1] = fmaf(cds, bf16_bits_to_f32(qv[x][h] >> 16), gk[DPL - 1]);
+                        gv[0] = fmaf(cpv, bf16_bits_to_f32(dv[x][h] & 0xFFFFu), gv[0]);
+                        gv[DPL - 1] = fmaf(cpv, bf16_bits_to_f32(dv[x][h] >> 16), gv[DPL - 1]);
+                    } else {
+                        gk[0] = fmaf(cds, bf16_bits_to_f32(qv[x][h]), gk[0]);
+                        gv[0] = fmaf(cpv, bf16_bits_to_f32(dv[x][h]), gv[0]);
+                    }
                 }
             }
         }
@@ -727,12 +766,29 @@ hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s)
     return dtype == 1 ? combine_t<uint16_t>(a, s) : combine_t<float>(a, s);
 }
 int sparse_bwd_key_block(int r, int M, int d) {
+    (void)r;
+    (void)d;
     int Mp = 1;
     while (Mp < M) Mp <<= 1;
     for (int Qb = 128; Qb >= 1; Qb >>= 1)
-        if ((size_t)Qb * Mp * 4 + (size_t)2 * Qb * r * d * 2 <= (size_t)kKvLdsBytes && Qb * Mp >= 8 * (kKvThreads / 64))
-            return Qb;
+        if (Qb * Mp <= kSortMaxEntries) return Qb;
     return 0;
+}
+
+size_t sparse_bwd_sorted_bytes(int B, int n, int G, int M) {
+    int Mp = 1;
+    while (Mp < M) Mp <<= 1;
+    const int Qb = sparse_bwd_key_block(1, M, 128);
+    if (Qb == 0) return 0;
+    return (size_t)B * G * ((n + Qb - 1) / Qb) * Qb * Mp * 4;
+}
+
+template <int D>
+hipError_t launch_walk(const SparseBwdArgs &a, int Qb, int E, const uint32_t *sorted, dim3 grid, hipStream_t s) {
+    if (a.r <= 4) hipLaunchKernelGGL((sparse_bwd_walk_kernel<D, 4>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
+    else if (a.r <= 8) hipLaunchKernelGGL((sparse_bwd_walk_kernel<D, 8>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
+    else hipLaunchKernelGGL((sparse_bwd_walk_kernel<D, 16>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
+    return hipGetLastError();
 }
 
 hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_side, hipStream_t s) {
@@ -744,13 +800,17 @@ hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_sid
         return hipGetLastError();
     }
     const int Qb = sparse_bwd_key_block(a.r, a.M, d);
-    if (Qb == 0) return hipErrorInvalidValue;
+    if (Qb == 0 || !a.sorted) return hipErrorInvalidValue;
     int lgMp = 0;
     while ((1 << lgMp) < a.M) ++lgMp;
-    const dim3 grid((unsigned)((int64_t)a.B * a.G * ((a.n + Qb - 1) / Qb)));
-    if (d == 128) hipLaunchKernelGGL((sparse_bwd_kv_kernel<128>), grid, dim3(kKvThreads), 0, s, a, Qb, lgMp);
-    else hipLaunchKernelGGL((sparse_bwd_kv_kernel<64>), grid, dim3(kKvThreads), 0, s, a, Qb, lgMp);
-    return hipGetLastError();
+    const int E = Qb << lgMp;
+    const int nb = a.B * a.G * ((a.n + Qb - 1) / Qb);
+    hipLaunchKernelGGL(sparse_bwd_sort_kernel, dim3((unsigned)nb), dim3(kSortThreads), 0, s, a, Qb, lgMp, a.sorted);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int per_wg = kWalkPerWave * (kWalkThreads / 64);
+    const dim3 grid((unsigned)((int64_t)nb * ((E + per_wg - 1) / per_wg)));
+    return d == 128 ? launch_walk<128>(a, Qb, E, a.sorted, grid, s) : launch_walk<64>(a, Qb, E, a.sorted, grid, s);
 }
 
 hipError_t launch_sparse_bwd(const SparseBwdArgs &a, int dtype, int d, hipStream_t s) {

@@ -117,12 +117,15 @@ struct SparseBwdArgs {
     const int32_t *idx;                       // [B,n,G,M] the forward's sets
     float *dq, *dk, *dv, *dgate;              // dq += ; dk, dv atomically += ; dgate =
     float *coef;                              // bf16 path: [B,n,G,M,2r] (scale ds, gamma p) per slot
+    uint32_t *sorted;                         // bf16 path: per block of positions, its sorted entries
     int B, n, Hq, G, r, M;
     float scale;
 };
 size_t sparse_bwd_lds_bytes(int r, int M, int d);
-// queries per work-group of the key-side pass (0: the shape does not fit its LDS)
+// positions per block of the key-side pass (0: the shape does not fit)
 int sparse_bwd_key_block(int r, int M, int d);
+// workspace of the key side's sorted entries
+size_t sparse_bwd_sorted_bytes(int B, int n, int G, int M);
 hipError_t launch_bwd_prep(const BwdPrepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_transpose_states(const float *src, float *dst, int64_t nmat, int d, hipStream_t s);
 hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s);

@@ -167,16 +167,20 @@ lisa_status lisa_prefill_window(const lisa_dims *dims, int32_t B, int32_t past, 
  * k_idx and w_idx, so those inputs get no gradient and are not taken.
  *   q, k, v, gate, state_in   as given to lisa_prefill (state_in may be NULL)
  *   topm         [B, n, G, M] int32: the forward's topm_out for these inputs
- *                (entries outside 0..t are skipped)
+ *                (entries outside 0..t are skipped; sets that are not
+ *                ascending give the same result, only more slowly)
  *   d_out        [B, n, Hq, d] in the layer dtype
  *   d_state_out  [B, Hq, d, d] fp32 or NULL (zero)
  *   dq  [B, n, Hq, d]; dk, dv [B, n, Hkv, d]; dgate [B, n, Hq]; all fp32,
  *       written (dk and dv are accumulated with atomics, so their last bits
  *       may differ from run to run)
  *   d_state_in  [B, Hq, d, d] fp32 or NULL
- * Up to 16 query heads per group; top_m * heads-per-group bounded by the
- * kernel's LDS (UNSUPPORTED beyond).  The workspace is
- * lisa_prefill_backward_workspace_bytes(dims, B, n).
+ * Up to 16 query heads per group; for fp32, top_m * heads-per-group is
+ * bounded by the kernel's LDS (UNSUPPORTED beyond).  The workspace is
+ * lisa_prefill_backward_workspace_bytes(dims, B, n): nine activation-sized
+ * buffers and the chunk states of the linear passes, plus (bf16) 8 * top_m
+ * bytes per position and query head for the sparse branch's per-slot
+ * coefficients.
  */
 lisa_status lisa_prefill_backward_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t n,
                                                   size_t *bytes);
