@@ -549,27 +549,33 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
     if (col < r && grp == 0) a.dgate[(size_t)bt * a.Hq + g * r + col] = gam * (1.0f - gam) * (E - dot);
 }
 
-// Key side, step 1 (sparse_bwd_sort_kernel): one work-group per block of Qb
-// consecutive positions of one group sorts the block's (key, position, slot)
-// entries by key in LDS and writes them out.  An entry is
+// Key side, step 1: the entries of each walk block of Qw = 256 consecutive
+// positions of one group, sorted by key.  An entry is
 // key << 17 | position-in-block << 9 | slot; 0xFFFFFFFF marks no entry and
-// sorts last.  Each position's run of Mp entries (M rounded up to a power
-// of two) is ascending, so runs are laid out alternately ascending and
-// reversed and only the merge levels of a bitonic sort run.
+// sorts last.  sparse_bwd_sort_kernel sorts Qs = min(Qw, 32768 / Mp)
+// positions in LDS (Mp = M rounded up to a power of two): each position's
+// run of Mp entries is ascending, so runs are laid out alternately ascending
+// and reversed and only the merge levels of a bitonic sort run.  Pairs of
+// sorted lists are then merged in global memory (sparse_bwd_merge_kernel)
+// until a list covers Qw positions.
 constexpr int kSortThreads = 1024;
 constexpr int kSortMaxEntries = 32768;  // 128 KB of LDS
 constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
 
-__global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwdArgs a, int Qb, int lgMp,
+constexpr int kWalkBlock = 256;  // Qw
+
+__global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwdArgs a, int Qs, int lgMp,
                                                                        uint32_t *sorted) {
     __shared__ uint32_t ent[kSortMaxEntries];
     const int tid = threadIdx.x;
     const int G = a.G, M = a.M, n = a.n;
-    const int Mp = 1 << lgMp, E = Qb * Mp;
-    const int nblk = (n + Qb - 1) / Qb;
-    const int bg = blockIdx.x / nblk, tb = blockIdx.x % nblk;
+    const int Mp = 1 << lgMp, E = Qs * Mp;
+    const int per = kWalkBlock / Qs;                       // sort blocks per walk block
+    const int nrun = (n + kWalkBlock - 1) / kWalkBlock * per;
+    const int bg = blockIdx.x / nrun, rr = blockIdx.x % nrun;
     const int g = bg % G, b = bg / G;
-    const int t0 = tb * Qb, nq = min(Qb, n - t0);
+    const int sub = rr % per;
+    const int t0 = (rr / per) * kWalkBlock + sub * Qs, nq = min(Qs, n - t0);  // nq <= 0: padding run
     for (int i = tid; i < E; i += kSortThreads) {
         const int tl = i >> lgMp, pos = i & (Mp - 1);
         const int slot = (tl & 1) ? Mp - 1 - pos : pos;
@@ -577,7 +583,8 @@ __global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwd
         const int t = t0 + tl;
         if (tl < nq && slot < min(M, t + 1)) {
             const int s = a.idx[(((size_t)b * n + t) * G + g) * M + slot];
-            if (s >= 0 && s <= t) e = ((uint32_t)s << 17) | ((uint32_t)tl << 9) | (uint32_t)slot;
+            if (s >= 0 && s <= t)
+                e = ((uint32_t)s << 17) | ((uint32_t)(sub * Qs + tl) << 9) | (uint32_t)slot;
         }
         ent[i] = e;
     }
@@ -598,6 +605,32 @@ __global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwd
     }
     uint32_t *dst = sorted + (size_t)blockIdx.x * E;
     for (int i = tid; i < E; i += kSortThreads) dst[i] = ent[i];
+}
+
+// Merge neighbouring sorted lists of L entries into lists of 2L (merge path:
+// each thread finds where its 16 outputs start on both inputs by a binary
+// search, then merges them; ties take the first list).  total is a multiple
+// of 2L and of 16.
+constexpr int kMergePer = 16;
+__global__ __launch_bounds__(256) void sparse_bwd_merge_kernel(const uint32_t *src, uint32_t *dst, int L,
+                                                               int64_t total) {
+    const int64_t o0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kMergePer;
+    if (o0 >= total) return;
+    const int64_t pair = o0 / (2 * (int64_t)L);
+    const int d = (int)(o0 - pair * 2 * L);
+    const uint32_t *A = src + pair * 2 * L, *Bl = A + L;
+    int lo = max(0, d - L), hi = min(d, L);
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (A[mid] <= Bl[d - mid - 1]) lo = mid + 1;
+        else hi = mid;
+    }
+    int i = lo, j = d - lo;
+#pragma unroll
+    for (int k = 0; k < kMergePer; ++k) {
+        const bool takeA = j >= L || (i < L && A[i] <= Bl[j]);
+        dst[o0 + k] = takeA ? A[i++] : Bl[j++];
+    }
 }
 
 // Key side, step 2 (sparse_bwd_walk_kernel): the sorted entries of a block
@@ -626,9 +659,8 @@ __global__ __launch_bounds__(kWalkThreads) void sparse_bwd_walk_kernel(SparseBwd
     const int start = (slice * (kWalkThreads / 64) + wave) * kWalkPerWave;
     if (start >= E) return;
     const int len = min(kWalkPerWave, E - start);
-    // len is 128 or 256 (E is Qb * Mp >= 128 and a stretch starts at a
-    // multiple of 256), so batches of U never pass the end; entries are
-    // wave-uniform and read through scalar loads
+    // len is 256 (E = 256 Mp and a stretch starts at a multiple of 256), so
+    // batches of U never pass the end; entries are wave-uniform
     const uint32_t *__restrict__ ent = sorted + (size_t)blk * E + start;
     const size_t unit0 = ((size_t)b * n + t0) * G + g;                          // unit of position t0
     const uint16_t *q0 = reinterpret_cast<const uint16_t *>(a.q) + (((size_t)b * n + t0) * Hq + g * r) * D;
@@ -768,19 +800,21 @@ hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s)
 int sparse_bwd_key_block(int r, int M, int d) {
     (void)r;
     (void)d;
-    int Mp = 1;
-    while (Mp < M) Mp <<= 1;
-    for (int Qb = 128; Qb >= 1; Qb >>= 1)
-        if (Qb * Mp <= kSortMaxEntries) return Qb;
-    return 0;
+    return M >= 1 && M <= 512 ? kWalkBlock : 0;
 }
 
+namespace {
+int lg_mp(int M) {
+    int lg = 0;
+    while ((1 << lg) < M) ++lg;
+    return lg;
+}
+int sort_block(int M) { return min(kWalkBlock, kSortMaxEntries >> lg_mp(M)); }
+}  // namespace
+
 size_t sparse_bwd_sorted_bytes(int B, int n, int G, int M) {
-    int Mp = 1;
-    while (Mp < M) Mp <<= 1;
-    const int Qb = sparse_bwd_key_block(1, M, 128);
-    if (Qb == 0) return 0;
-    return (size_t)B * G * ((n + Qb - 1) / Qb) * Qb * Mp * 4;
+    const size_t one = (size_t)B * G * ((n + kWalkBlock - 1) / kWalkBlock) * kWalkBlock * ((size_t)1 << lg_mp(M)) * 4;
+    return sort_block(M) < kWalkBlock ? 2 * one : one;  // merge passes ping-pong
 }
 
 template <int D>
@@ -799,18 +833,26 @@ hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_sid
         else hipLaunchKernelGGL((sparse_bwd_q_kernel<64>), grid, dim3(64), 0, s, a);
         return hipGetLastError();
     }
-    const int Qb = sparse_bwd_key_block(a.r, a.M, d);
-    if (Qb == 0 || !a.sorted) return hipErrorInvalidValue;
-    int lgMp = 0;
-    while ((1 << lgMp) < a.M) ++lgMp;
-    const int E = Qb << lgMp;
-    const int nb = a.B * a.G * ((a.n + Qb - 1) / Qb);
-    hipLaunchKernelGGL(sparse_bwd_sort_kernel, dim3((unsigned)nb), dim3(kSortThreads), 0, s, a, Qb, lgMp, a.sorted);
+    if (sparse_bwd_key_block(a.r, a.M, d) == 0 || !a.sorted) return hipErrorInvalidValue;
+    const int lgMp = lg_mp(a.M), Qs = sort_block(a.M);
+    const int E = kWalkBlock << lgMp;                       // entries per walk block
+    const int nb = a.B * a.G * ((a.n + kWalkBlock - 1) / kWalkBlock);
+    const int64_t total = (int64_t)nb * E;
+    uint32_t *buf[2] = {a.sorted, a.sorted + total};
+    hipLaunchKernelGGL(sparse_bwd_sort_kernel, dim3((unsigned)(nb * (kWalkBlock / Qs))), dim3(kSortThreads), 0, s,
+                       a, Qs, lgMp, buf[0]);
     hipError_t e = hipGetLastError();
+    int cur = 0;
+    for (int L = Qs << lgMp; e == hipSuccess && L < E; L *= 2, cur ^= 1) {
+        hipLaunchKernelGGL(sparse_bwd_merge_kernel, dim3((unsigned)((total / kMergePer + 255) / 256)), dim3(256), 0, s,
+                           buf[cur], buf[cur ^ 1], L, total);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     const int per_wg = kWalkPerWave * (kWalkThreads / 64);
     const dim3 grid((unsigned)((int64_t)nb * ((E + per_wg - 1) / per_wg)));
-    return d == 128 ? launch_walk<128>(a, Qb, E, a.sorted, grid, s) : launch_walk<64>(a, Qb, E, a.sorted, grid, s);
+    return d == 128 ? launch_walk<128>(a, kWalkBlock, E, buf[cur], grid, s)
+                    : launch_walk<64>(a, kWalkBlock, E, buf[cur], grid, s);
 }
 
 hipError_t launch_sparse_bwd(const SparseBwdArgs &a, int dtype, int d, hipStream_t s) {
