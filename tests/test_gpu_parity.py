@@ -320,6 +320,12 @@ BACKWARD = [
     (_pcfg(130, 8, 2, 64, 2, 32, 37, dtype="f32", seed=3), True),
     (_pcfg(257, 7, 7, 128, 4, 64, 256, seed=4), False),      # no state in or out, M > n
     (_pcfg(1000, 8, 2, 128, 4, 64, 256, seed=5), True),
+    (_pcfg(300, 8, 2, 128, 4, 64, 64, B=2, seed=6), True),     # batch of two
+    (_pcfg(700, 4, 2, 128, 4, 64, 512, seed=7), True),         # M = 512: two merge passes
+    (_pcfg(600, 6, 3, 64, 4, 32, 300, seed=8), False),         # M not a power of two, d = 64
+    (_pcfg(50, 4, 1, 128, 2, 32, 1, seed=9), True),            # M = 1
+    (_pcfg(1, 4, 2, 128, 2, 32, 16, seed=10), True),           # one position
+    (_pcfg(129, 32, 2, 64, 2, 32, 40, seed=11), True),         # 16 heads per group
 ]
 
 
