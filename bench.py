@@ -94,7 +94,7 @@ STAGE_KERNELS = {
     "decode_select": (r"decode_topm_kernel<|decode_select_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
     "bwd_sparse": (r"sparse_bwd_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
     "bwd_sparse_query": (r"sparse_bwd_q_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
-    "bwd_sparse_keys": (r"sparse_bwd_kv_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
+    "bwd_sparse_keys": (r"sparse_bwd_walk_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
 }
 
 

@@ -119,12 +119,14 @@ DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
 enum Stage {
     ST_LIN_STATE, ST_LIN_SCAN, ST_LIN_OUT, ST_IDX_PACK, ST_INDEXER, ST_SPARSE_PREFILL,
     ST_DEC_SCORE_STATE, ST_DEC_SELECT, ST_SPARSE_DECODE,
-    ST_BWD_OPER, ST_BWD_LINEAR, ST_BWD_COMBINE, ST_BWD_SPARSE, ST_BWD_SPARSE_Q, ST_BWD_SPARSE_KV, ST_COUNT
+    ST_BWD_OPER, ST_BWD_LINEAR, ST_BWD_COMBINE, ST_BWD_SPARSE, ST_BWD_SPARSE_Q, ST_BWD_SORT, ST_BWD_SPARSE_KV,
+    ST_COUNT
 };
 const char *const kStageNames[ST_COUNT] = {
     "linear_chunk_state", "linear_prefix_scan", "linear_chunk_output", "indexer_pack", "indexer_topm",
     "sparse_gate_prefill", "decode_score_state", "decode_select", "sparse_gate_decode",
-    "bwd_operands", "bwd_linear", "bwd_combine", "bwd_sparse", "bwd_sparse_query", "bwd_sparse_keys",
+    "bwd_operands", "bwd_linear", "bwd_combine", "bwd_sparse", "bwd_sparse_query", "bwd_sparse_sort",
+    "bwd_sparse_keys",
 };
 
 struct Timing {
@@ -711,9 +713,11 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     if (dims->dtype == LISA_BF16) {
         sb.coef = reinterpret_cast<float *>(ws + w.coef);
         sb.sorted = reinterpret_cast<uint32_t *>(ws + w.sorted);
-        LISA_HIP(timed(ST_BWD_SPARSE_Q, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, true, s); }),
+        LISA_HIP(timed(ST_BWD_SPARSE_Q, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, 0, s); }),
                  "sparse backward (query side) launch");
-        LISA_HIP(timed(ST_BWD_SPARSE_KV, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, false, s); }),
+        LISA_HIP(timed(ST_BWD_SORT, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, 1, s); }),
+                 "sparse backward (key sort) launch");
+        LISA_HIP(timed(ST_BWD_SPARSE_KV, s, [&] { return lisa::launch_sparse_bwd_split(sb, D, 2, s); }),
                  "sparse backward (key side) launch");
     } else {
         LISA_HIP(timed(ST_BWD_SPARSE, s, [&] { return lisa::launch_sparse_bwd(sb, dims->dtype, D, s); }),

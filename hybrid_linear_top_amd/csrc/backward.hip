@@ -825,9 +825,9 @@ hipError_t launch_walk(const SparseBwdArgs &a, int Qb, int E, const uint32_t *so
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_side, hipStream_t s) {
+hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, int part, hipStream_t s) {
     if ((int64_t)a.B * a.n == 0) return hipSuccess;
-    if (query_side) {
+    if (part == 0) {
         const dim3 grid((unsigned)((int64_t)a.B * a.n * a.G));
         if (d == 128) hipLaunchKernelGGL((sparse_bwd_q_kernel<128>), grid, dim3(64), 0, s, a);
         else hipLaunchKernelGGL((sparse_bwd_q_kernel<64>), grid, dim3(64), 0, s, a);
@@ -839,16 +839,20 @@ hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_sid
     const int nb = a.B * a.G * ((a.n + kWalkBlock - 1) / kWalkBlock);
     const int64_t total = (int64_t)nb * E;
     uint32_t *buf[2] = {a.sorted, a.sorted + total};
-    hipLaunchKernelGGL(sparse_bwd_sort_kernel, dim3((unsigned)(nb * (kWalkBlock / Qs))), dim3(kSortThreads), 0, s,
-                       a, Qs, lgMp, buf[0]);
-    hipError_t e = hipGetLastError();
-    int cur = 0;
-    for (int L = Qs << lgMp; e == hipSuccess && L < E; L *= 2, cur ^= 1) {
-        hipLaunchKernelGGL(sparse_bwd_merge_kernel, dim3((unsigned)((total / kMergePer + 255) / 256)), dim3(256), 0, s,
-                           buf[cur], buf[cur ^ 1], L, total);
-        e = hipGetLastError();
+    int cur = 0;  // the buffer the last merge pass writes
+    for (int L = Qs << lgMp; L < E; L *= 2) cur ^= 1;
+    if (part == 1) {
+        hipLaunchKernelGGL(sparse_bwd_sort_kernel, dim3((unsigned)(nb * (kWalkBlock / Qs))), dim3(kSortThreads), 0,
+                           s, a, Qs, lgMp, buf[0]);
+        hipError_t e = hipGetLastError();
+        int from = 0;
+        for (int L = Qs << lgMp; e == hipSuccess && L < E; L *= 2, from ^= 1) {
+            hipLaunchKernelGGL(sparse_bwd_merge_kernel, dim3((unsigned)((total / kMergePer + 255) / 256)), dim3(256),
+                               0, s, buf[from], buf[from ^ 1], L, total);
+            e = hipGetLastError();
+        }
+        return e;
     }
-    if (e != hipSuccess) return e;
     const int per_wg = kWalkPerWave * (kWalkThreads / 64);
     const dim3 grid((unsigned)((int64_t)nb * ((E + per_wg - 1) / per_wg)));
     return d == 128 ? launch_walk<128>(a, kWalkBlock, E, buf[cur], grid, s)

@@ -130,7 +130,8 @@ hipError_t launch_bwd_prep(const BwdPrepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_transpose_states(const float *src, float *dst, int64_t nmat, int d, hipStream_t s);
 hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s);
 hipError_t launch_sparse_bwd(const SparseBwdArgs &a, int dtype, int d, hipStream_t s);
-// bf16: the query side (dq, dgate, coefficients) or the key side (dk, dv)
-hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, bool query_side, hipStream_t s);
+// bf16, in this order: part 0 the query side (dq, dgate, coefficients),
+// part 1 the key side's sort, part 2 its walk (dk, dv)
+hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, int part, hipStream_t s);
 
 }  // namespace lisa

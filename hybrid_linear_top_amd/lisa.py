@@ -193,7 +193,7 @@ def lisa_stage_timing(enable: bool) -> None:
 
 def lisa_stage_timing_read(reset: bool = True) -> dict:
     """{stage name: (launches, total_ms)} for every stage with launches."""
-    N = 16
+    N = 32
     names = (ctypes.c_char_p * N)()
     launches = (ctypes.c_int64 * N)()
     total = (ctypes.c_double * N)()
