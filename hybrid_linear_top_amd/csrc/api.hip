@@ -527,7 +527,7 @@ lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int6
 // ---- backward --------------------------------------------------------------------
 namespace {
 struct BwdWs {
-    size_t olin, Gl, Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, coef, sorted, total;
+    size_t Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, coef, sorted, total;
 };
 BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     const size_t Hq = d->num_q_heads, D = d->head_dim, eb = elt_bytes(d->dtype);
@@ -536,7 +536,7 @@ BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     const size_t st = align_up((size_t)B * Hq * D * D * 4);
     BwdWs w;
     size_t off = 0;
-    size_t *acts[] = {&w.olin, &w.Gl, &w.Grev, &w.qrev, &w.vrep, &w.krep, &w.dqlin, &w.ok, &w.ov};
+    size_t *acts[] = {&w.Grev, &w.qrev, &w.vrep, &w.krep, &w.dqlin, &w.ok, &w.ov};
     for (size_t *x : acts) {
         *x = off;
         off += act;
@@ -642,7 +642,6 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     pa.v = v;
     pa.z = gate;
     pa.dout = d_out;
-    pa.Gl = ws + w.Gl;
     pa.Grev = ws + w.Grev;
     pa.qrev = ws + w.qrev;
     pa.vrep = ws + w.vrep;
@@ -661,11 +660,10 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
                  return e;
              }),
              "backward operand launch");
-    // o_lin of the forward (the gate needs it), then the three gradient passes
+    // three passes: R_t = S_t d_out (dq_lin = (1 - gamma) R, and q . R = d_out . o_lin
+    // for the gate), then dk and dv of the linear branch in reversed time
     LISA_HIP(timed(ST_BWD_LINEAR, s, [&] {
-                 hipError_t e = linear_pass(dims, B, n, Hq, G, q, k, v, state_in, nullptr, ws + w.olin, ws, w, s);
-                 if (e == hipSuccess)
-                     e = linear_pass(dims, B, n, Hq, G, ws + w.Gl, v, k, sinT, nullptr, ws + w.dqlin, ws, w, s);
+                 hipError_t e = linear_pass(dims, B, n, Hq, G, d_out, v, k, sinT, nullptr, ws + w.dqlin, ws, w, s);
                  if (e == hipSuccess)
                      e = linear_pass(dims, B, n, Hq, Hq, ws + w.vrep, ws + w.Grev, ws + w.qrev, dsoT, nullptr,
                                      ws + w.ok, ws, w, s);
@@ -677,6 +675,7 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
              "backward linear-pass launch");
 
     lisa::BwdCombineArgs ca{};
+    ca.z = gate;
     ca.dq_lin = ws + w.dqlin;
     ca.o_k = ws + w.ok;
     ca.o_v = ws + w.ov;
@@ -697,7 +696,7 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     sb.v = v;
     sb.z = gate;
     sb.dout = d_out;
-    sb.olin = ws + w.olin;
+    sb.rlin = ws + w.dqlin;
     sb.idx = topm;
     sb.dq = dq;
     sb.dk = dk;

@@ -41,9 +41,8 @@ __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(
 
 // ---- operands of the linear-branch passes ------------------------------------
 // One thread per 8 consecutive elements of [B, n, Hq, d] (d is a multiple of 8):
-//   G    = (1 - gamma) d_out                 (same position and head)
-//   Grev = G,  qrev = q,  vrep = v of the head's group, krep = k of the group,
-//          all at position n - 1 - t (reversed time).
+//   Grev = (1 - gamma) d_out,  qrev = q,  vrep = v of the head's group,
+//          krep = k of the group, all at position n - 1 - t (reversed time).
 template <typename T>
 struct alignas(16) Vec8 {
     T x[8];
@@ -72,7 +71,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) gv.x[i] = Elt<T>::from_f32((1.0f - gam) * Elt<T>::to_f32(dov.x[i]));
     const size_t rev = (((size_t)b * a.n + (a.n - 1 - t)) * a.Hq + h) * a.d + dd;
-    *reinterpret_cast<V *>(reinterpret_cast<T *>(a.Gl) + e) = gv;
     *reinterpret_cast<V *>(reinterpret_cast<T *>(a.Grev) + rev) = gv;
     *reinterpret_cast<V *>(reinterpret_cast<T *>(a.qrev) + rev) = qv;
     *reinterpret_cast<V *>(reinterpret_cast<T *>(a.vrep) + rev) = vvv;
@@ -88,8 +86,8 @@ __global__ __launch_bounds__(256) void transpose_states_kernel(const float *src,
     dst[(m * d + j) * d + i] = src[e];
 }
 
-// dq = dq_lin; dk[b,t,g] = sum_{h in g} o_k[b, n-1-t, h]; dv likewise (fp32);
-// one thread per 8 consecutive elements
+// dq = (1 - gamma) dq_lin; dk[b,t,g] = sum_{h in g} o_k[b, n-1-t, h]; dv
+// likewise (fp32); one thread per 8 consecutive elements
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdCombineArgs a) {
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
@@ -98,11 +96,12 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdCombineArgs a) {
     using V = Vec8<T>;
     if (e < nq) {
         const V x = *reinterpret_cast<const V *>(reinterpret_cast<const T *>(a.dq_lin) + e);
+        const float om = 1.0f - sigmoidf(Elt<T>::to_f32(reinterpret_cast<const T *>(a.z)[e / a.d]));
         f32x4 lo, hi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            lo[i] = Elt<T>::to_f32(x.x[i]);
-            hi[i] = Elt<T>::to_f32(x.x[4 + i]);
+            lo[i] = om * Elt<T>::to_f32(x.x[i]);
+            hi[i] = om * Elt<T>::to_f32(x.x[4 + i]);
         }
         *reinterpret_cast<f32x4 *>(a.dq + e) = lo;
         *reinterpret_cast<f32x4 *>(a.dq + e + 4) = hi;
@@ -252,12 +251,13 @@ __global__ __launch_bounds__(64) void sparse_bwd_kernel(SparseBwdArgs a) {
             if (h < r) dl[slot * r + h] = gam[h] * pl[slot * r + h] * (dl[slot * r + h] - eh[h]);
     }
     {
-        const T *olp = reinterpret_cast<const T *>(a.olin) + hrow;
+        // d_out . o_lin = d_out . S_t^T q = q . (S_t d_out)
+        const T *rlp = reinterpret_cast<const T *>(a.rlin) + hrow;
 #pragma unroll
         for (int h = 0; h < kMaxR; ++h) {
             if (h < r) {
                 float dot = 0.0f;
-                for (int dd = lane; dd < D; dd += 64) dot = fmaf(dos[h * D + dd], Elt<T>::to_f32(olp[h * D + dd]), dot);
+                for (int dd = lane; dd < D; dd += 64) dot = fmaf(qs[h * D + dd], Elt<T>::to_f32(rlp[h * D + dd]), dot);
                 dot = wave_sum(dot);
                 if (lane == 0) a.dgate[(size_t)bt * Hq + g * r + h] = gam[h] * (1.0f - gam[h]) * (eh[h] - dot);
             }
@@ -532,8 +532,9 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
             f32x4 *pp = reinterpret_cast<f32x4 *>(dqp + mb * 16 + grp * 4);
             *pp = *pp + o[mb] * a.scale;
         }
-        const uint16_t *dor = dorows + (size_t)col * D + grp * (D / 4);
-        const uint16_t *olr = reinterpret_cast<const uint16_t *>(a.olin) + hrow + (size_t)col * D + grp * (D / 4);
+        // d_out . o_lin = d_out . S_t^T q = q . (S_t d_out)
+        const uint16_t *dor = qrows + (size_t)col * D + grp * (D / 4);
+        const uint16_t *olr = reinterpret_cast<const uint16_t *>(a.rlin) + hrow + (size_t)col * D + grp * (D / 4);
 #pragma unroll
         for (int c = 0; c < D / 4; c += 8) {
             const u32x4 x = *reinterpret_cast<const u32x4 *>(dor + c);

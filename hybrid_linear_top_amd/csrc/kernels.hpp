@@ -103,17 +103,20 @@ hipError_t launch_indexer_prefill(const IndexerArgs &a, int dtype, int dI, hipSt
 // ---- prefill backward ----------------------------------------------------------
 struct BwdPrepArgs {
     const void *q, *k, *v, *z, *dout;   // q, z, dout per head [B,n,Hq,(d)]; k, v [B,n,G,d]
-    void *Gl, *Grev, *qrev, *vrep, *krep;  // [B,n,Hq,d] in the layer dtype
+    void *Grev, *qrev, *vrep, *krep;    // [B,n,Hq,d] in the layer dtype
     int B, n, Hq, G, d;
 };
 struct BwdCombineArgs {
-    const void *dq_lin, *o_k, *o_v;     // [B,n,Hq,d] layer dtype (o_k, o_v in reversed time)
+    const void *z;                      // gate logits [B,n,Hq]
+    const void *dq_lin, *o_k, *o_v;     // [B,n,Hq,d] layer dtype: S_t d_out (not yet scaled
+                                        // by 1 - gamma); o_k, o_v in reversed time
     float *dq;                          // [B,n,Hq,d]
     float *dk, *dv;                     // [B,n,G,d]
     int B, n, Hq, G, d;
 };
 struct SparseBwdArgs {
-    const void *q, *k, *v, *z, *dout, *olin;  // layer dtype
+    const void *q, *k, *v, *z, *dout;         // layer dtype
+    const void *rlin;                         // [B,n,Hq,d] S_t d_out (q . rlin = d_out . o_lin)
     const int32_t *idx;                       // [B,n,G,M] the forward's sets
     float *dq, *dk, *dv, *dgate;              // dq += ; dk, dv atomically += ; dgate =
     float *coef;                              // bf16 path: [B,n,G,M,2r] (scale ds, gamma p) per slot

@@ -177,7 +177,7 @@ lisa_status lisa_prefill_window(const lisa_dims *dims, int32_t B, int32_t past, 
  *   d_state_in  [B, Hq, d, d] fp32 or NULL
  * Up to 16 query heads per group; for fp32, top_m * heads-per-group is
  * bounded by the kernel's LDS (UNSUPPORTED beyond).  The workspace is
- * lisa_prefill_backward_workspace_bytes(dims, B, n): nine activation-sized
+ * lisa_prefill_backward_workspace_bytes(dims, B, n): seven activation-sized
  * buffers and the chunk states of the linear passes, plus (bf16) 8 * top_m
  * bytes per position and query head for the sparse branch's per-slot
  * coefficients.
