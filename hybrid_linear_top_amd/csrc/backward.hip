@@ -608,30 +608,64 @@ __global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwd
     for (int i = tid; i < E; i += kSortThreads) dst[i] = ent[i];
 }
 
-// Merge neighbouring sorted lists of L entries into lists of 2L (merge path:
-// each thread finds where its 16 outputs start on both inputs by a binary
-// search, then merges them; ties take the first list).  total is a multiple
-// of 2L and of 16.
+// Merge neighbouring sorted lists of L entries into lists of 2L (merge
+// path; ties take the first list).  A work-group makes kMergeTile consecutive
+// outputs: two lanes find where the tile starts and ends on both inputs by a
+// binary search in global memory, the work-group stages those input ranges
+// (kMergeTile entries in all) in LDS, and each thread merges its kMergePer
+// outputs from LDS after a second search there.  2L is a multiple of
+// kMergeTile.
 constexpr int kMergePer = 16;
-__global__ __launch_bounds__(256) void sparse_bwd_merge_kernel(const uint32_t *src, uint32_t *dst, int L,
-                                                               int64_t total) {
-    const int64_t o0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kMergePer;
-    if (o0 >= total) return;
-    const int64_t pair = o0 / (2 * (int64_t)L);
-    const int d = (int)(o0 - pair * 2 * L);
-    const uint32_t *A = src + pair * 2 * L, *Bl = A + L;
+constexpr int kMergeTile = 256 * kMergePer;
+
+// number of entries of A among the first d outputs of merge(A, B), |A| = |B| = L
+template <typename P>
+__device__ __forceinline__ int merge_split(P A, P Bl, int L, int d) {
     int lo = max(0, d - L), hi = min(d, L);
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (A[mid] <= Bl[d - mid - 1]) lo = mid + 1;
         else hi = mid;
     }
-    int i = lo, j = d - lo;
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void sparse_bwd_merge_kernel(const uint32_t *src, uint32_t *dst, int L,
+                                                               int64_t total) {
+    __shared__ uint32_t buf[kMergeTile];
+    __shared__ int split[2];
+    const int64_t t0 = (int64_t)blockIdx.x * kMergeTile;
+    if (t0 >= total) return;
+    const int64_t pair = t0 / (2 * (int64_t)L);
+    const int d0 = (int)(t0 - pair * 2 * L);
+    const uint32_t *A = src + pair * 2 * L, *Bl = A + L;
+    if (threadIdx.x < 2) split[threadIdx.x] = merge_split(A, Bl, L, d0 + (int)threadIdx.x * kMergeTile);
+    __syncthreads();
+    const int a0 = split[0], a1 = split[1];
+    const int b0 = d0 - a0, b1 = d0 + kMergeTile - a1;
+    const int na = a1 - a0, nb = b1 - b0;  // na + nb = kMergeTile
+    for (int i = threadIdx.x; i < kMergeTile; i += 256) buf[i] = i < na ? A[a0 + i] : Bl[b0 + i - na];
+    __syncthreads();
+    // this thread's outputs: local diagonal dl of merge(buf[0, na), buf[na, na + nb))
+    const int dl = threadIdx.x * kMergePer;
+    int lo = max(0, dl - nb), hi = min(dl, na);
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (buf[mid] <= buf[na + dl - mid - 1]) lo = mid + 1;
+        else hi = mid;
+    }
+    int i = lo, j = dl - lo;
+    uint32_t out[kMergePer];
 #pragma unroll
     for (int k = 0; k < kMergePer; ++k) {
-        const bool takeA = j >= L || (i < L && A[i] <= Bl[j]);
-        dst[o0 + k] = takeA ? A[i++] : Bl[j++];
+        const bool takeA = j >= nb || (i < na && buf[i] <= buf[na + j]);
+        out[k] = takeA ? buf[i++] : buf[na + j++];
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMergePer; ++k) buf[dl + k] = out[k];
+    __syncthreads();
+    for (int k = threadIdx.x; k < kMergeTile; k += 256) dst[t0 + k] = buf[k];
 }
 
 // Key side, step 2 (sparse_bwd_walk_kernel): the sorted entries of a block
@@ -848,8 +882,8 @@ hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, int part, hipS
         hipError_t e = hipGetLastError();
         int from = 0;
         for (int L = Qs << lgMp; e == hipSuccess && L < E; L *= 2, from ^= 1) {
-            hipLaunchKernelGGL(sparse_bwd_merge_kernel, dim3((unsigned)((total / kMergePer + 255) / 256)), dim3(256),
-                               0, s, buf[from], buf[from ^ 1], L, total);
+            hipLaunchKernelGGL(sparse_bwd_merge_kernel, dim3((unsigned)((total + kMergeTile - 1) / kMergeTile)),
+                               dim3(256), 0, s, buf[from], buf[from ^ 1], L, total);
             e = hipGetLastError();
         }
         return e;
