@@ -555,68 +555,17 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
 // key << 17 | position-in-block << 9 | slot; 0xFFFFFFFF marks no entry and
 // sorts last.  sparse_bwd_sort_kernel sorts Qs = min(Qw, 32768 / Mp)
 // positions in LDS (Mp = M rounded up to a power of two): each position's
-// run of Mp entries is ascending, so runs are laid out alternately ascending
-// and reversed and only the merge levels of a bitonic sort run.  Pairs of
-// sorted lists are then merged in global memory (sparse_bwd_merge_kernel)
-// until a list covers Qw positions.
+// run of Mp entries is already ascending, so the runs are merged pairwise,
+// level by level, in place (each thread computes its outputs of a level by
+// merge path into registers, then all write back).  Pairs of sorted lists
+// are then merged in global memory (sparse_bwd_merge_kernel) until a list
+// covers Qw positions.
 constexpr int kSortThreads = 1024;
 constexpr int kSortMaxEntries = 32768;  // 128 KB of LDS
 constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
 
 constexpr int kWalkBlock = 256;  // Qw
-
-__global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwdArgs a, int Qs, int lgMp,
-                                                                       uint32_t *sorted) {
-    __shared__ uint32_t ent[kSortMaxEntries];
-    const int tid = threadIdx.x;
-    const int G = a.G, M = a.M, n = a.n;
-    const int Mp = 1 << lgMp, E = Qs * Mp;
-    const int per = kWalkBlock / Qs;                       // sort blocks per walk block
-    const int nrun = (n + kWalkBlock - 1) / kWalkBlock * per;
-    const int bg = blockIdx.x / nrun, rr = blockIdx.x % nrun;
-    const int g = bg % G, b = bg / G;
-    const int sub = rr % per;
-    const int t0 = (rr / per) * kWalkBlock + sub * Qs, nq = min(Qs, n - t0);  // nq <= 0: padding run
-    for (int i = tid; i < E; i += kSortThreads) {
-        const int tl = i >> lgMp, pos = i & (Mp - 1);
-        const int slot = (tl & 1) ? Mp - 1 - pos : pos;
-        uint32_t e = kNoEntry;
-        const int t = t0 + tl;
-        if (tl < nq && slot < min(M, t + 1)) {
-            const int s = a.idx[(((size_t)b * n + t) * G + g) * M + slot];
-            if (s >= 0 && s <= t)
-                e = ((uint32_t)s << 17) | ((uint32_t)(sub * Qs + tl) << 9) | (uint32_t)slot;
-        }
-        ent[i] = e;
-    }
-    __syncthreads();
-    for (int k = 2 * Mp; k <= E; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int p = tid; p < E / 2; p += kSortThreads) {
-                const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
-                const int l = i | j;
-                const uint32_t x = ent[i], y = ent[l];
-                if ((x > y) == ((i & k) == 0)) {
-                    ent[i] = y;
-                    ent[l] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
-    uint32_t *dst = sorted + (size_t)blockIdx.x * E;
-    for (int i = tid; i < E; i += kSortThreads) dst[i] = ent[i];
-}
-
-// Merge neighbouring sorted lists of L entries into lists of 2L (merge
-// path; ties take the first list).  A work-group makes kMergeTile consecutive
-// outputs: two lanes find where the tile starts and ends on both inputs by a
-// binary search in global memory, the work-group stages those input ranges
-// (kMergeTile entries in all) in LDS, and each thread merges its kMergePer
-// outputs from LDS after a second search there.  2L is a multiple of
-// kMergeTile.
-constexpr int kMergePer = 16;
-constexpr int kMergeTile = 256 * kMergePer;
+constexpr int kSortPer = kSortMaxEntries / kSortThreads;  // outputs per thread and level at most
 
 // number of entries of A among the first d outputs of merge(A, B), |A| = |B| = L
 template <typename P>
@@ -629,6 +578,107 @@ __device__ __forceinline__ int merge_split(P A, P Bl, int L, int d) {
     }
     return lo;
 }
+
+
+__global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwdArgs a, int Qs, int lgMp,
+                                                                       uint32_t *sorted) {
+    // entry i lives at word i + i / 16: threads of a merge level read about 16
+    // entries apart, which unpadded would put a wave on four LDS banks
+    __shared__ uint32_t ent[kSortMaxEntries + kSortMaxEntries / 16];
+    struct View {
+        uint32_t *w;
+        int o;
+        __device__ uint32_t operator[](int i) const { return w[o + i + ((o + i) >> 4)]; }
+    };
+    const int tid = threadIdx.x;
+    const int G = a.G, M = a.M, n = a.n;
+    const int Mp = 1 << lgMp, E = Qs * Mp;
+    const int per = kWalkBlock / Qs;                       // sort blocks per walk block
+    const int nrun = (n + kWalkBlock - 1) / kWalkBlock * per;
+    const int bg = blockIdx.x / nrun, rr = blockIdx.x % nrun;
+    const int g = bg % G, b = bg / G;
+    const int sub = rr % per;
+    const int t0 = (rr / per) * kWalkBlock + sub * Qs, nq = min(Qs, n - t0);  // nq <= 0: padding run
+    // the block's index rows through one descriptor, every load unconditional
+    // (a guarded load compiles to a branch with a full wait per load)
+    const rsrc_t irs = make_rsrc(a.idx + (((size_t)b * n + max(t0, 0)) * G + g) * M,
+                                 nq > 0 ? (uint32_t)nq * G * M * 4u : 0u);
+    uint32_t sv[kSortPer];
+#pragma unroll
+    for (int k = 0; k < kSortPer; ++k) {
+        const int i = tid + k * kSortThreads;
+        const int tl = i >> lgMp, slot = i & (Mp - 1);
+        const bool in = i < E && tl < nq && slot < min(M, t0 + tl + 1);
+        sv[k] = __builtin_amdgcn_raw_buffer_load_b32(irs, in ? (uint32_t)(tl * G * M + slot) * 4u : kOffNone, 0u, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kSortPer; ++k) {
+        const int i = tid + k * kSortThreads;
+        const int tl = i >> lgMp, slot = i & (Mp - 1), t = t0 + tl;
+        const int s = (int)sv[k];
+        const bool in = i < E && tl < nq && slot < min(M, t + 1) && s >= 0 && s <= t;
+        if (i < E)
+            ent[i + (i >> 4)] = in ? ((uint32_t)s << 17) | ((uint32_t)(sub * Qs + tl) << 9) | (uint32_t)slot : kNoEntry;
+    }
+    __syncthreads();
+    // merge levels: runs of R into runs of 2R; thread tid makes outputs
+    // [tid * per, (tid + 1) * per) of the level
+    const int opt = E >= kSortThreads ? E / kSortThreads : 1;
+    const int o0 = tid * opt;
+    for (int R = Mp; R < E; R <<= 1) {
+        uint32_t out[kSortPer];
+        if (o0 < E) {
+            int i = 0, j = 0;
+            View A{ent, 0}, Bl{ent, 0};
+            uint32_t ha = 0, hb = 0;  // the heads A[i], B[j] (kNoEntry when a side is used up)
+#pragma unroll
+            for (int k = 0; k < kSortPer; ++k) {
+                if (k < opt) {
+                    const int o = o0 + k;
+                    if (k == 0 || (o & (2 * R - 1)) == 0) {  // first output, or a new pair of runs
+                        const int p = o / (2 * R), d = o - p * 2 * R;
+                        A = View{ent, p * 2 * R};
+                        Bl = View{ent, p * 2 * R + R};
+                        i = merge_split(A, Bl, R, d);
+                        j = d - i;
+                        ha = i < R ? A[i] : kNoEntry;
+                        hb = j < R ? Bl[j] : kNoEntry;
+                    }
+                    // ties take A; a used-up side never wins (i + j < 2R here)
+                    const bool takeA = j >= R || (i < R && ha <= hb);
+                    if (takeA) {
+                        out[k] = ha;
+                        ++i;
+                        ha = i < R ? A[i] : kNoEntry;
+                    } else {
+                        out[k] = hb;
+                        ++j;
+                        hb = j < R ? Bl[j] : kNoEntry;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (o0 < E) {
+#pragma unroll
+            for (int k = 0; k < kSortPer; ++k)
+                if (k < opt) ent[o0 + k + ((o0 + k) >> 4)] = out[k];
+        }
+        __syncthreads();
+    }
+    uint32_t *dst = sorted + (size_t)blockIdx.x * E;
+    for (int i = tid; i < E; i += kSortThreads) dst[i] = ent[i + (i >> 4)];
+}
+
+// Merge neighbouring sorted lists of L entries into lists of 2L (merge
+// path; ties take the first list).  A work-group makes kMergeTile consecutive
+// outputs: two lanes find where the tile starts and ends on both inputs by a
+// binary search in global memory, the work-group stages those input ranges
+// (kMergeTile entries in all) in LDS, and each thread merges its kMergePer
+// outputs from LDS after a second search there.  2L is a multiple of
+// kMergeTile.
+constexpr int kMergePer = 16;
+constexpr int kMergeTile = 256 * kMergePer;
 
 __global__ __launch_bounds__(256) void sparse_bwd_merge_kernel(const uint32_t *src, uint32_t *dst, int L,
                                                                int64_t total) {
