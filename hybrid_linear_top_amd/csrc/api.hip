@@ -550,7 +550,7 @@ BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     off += align_up((size_t)B * Hq * nC * D * D * 4);
     w.P = off;
     off += align_up((size_t)B * Hq * nC * D * D * eb);
-    // bf16: per-slot coefficients of the sparse branch, [B,n,G,M,2r] fp32
+    // bf16: per-slot coefficients of the sparse branch, [B,n,G,M,r,2] fp32
     w.coef = off;
     if (d->dtype == LISA_BF16) off += align_up((size_t)B * n * Hq * d->top_m * 2 * 4);
     w.sorted = off;

@@ -507,8 +507,7 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
             dsv[e] = ds;
             if (valid[e] && col < r) {
                 const int slot = j * 32 + (e >> 2) * 16 + grp * 4 + (e & 3);
-                coefu[(size_t)slot * 2 * r + col] = a.scale * ds;
-                coefu[(size_t)slot * 2 * r + r + col] = gam * p;
+                *reinterpret_cast<float2 *>(coefu + ((size_t)slot * r + col) * 2) = float2{a.scale * ds, gam * p};
             }
         }
         Frag<uint16_t> dsf;
@@ -827,8 +826,8 @@ __global__ __launch_bounds__(kWalkThreads) void sparse_bwd_walk_kernel(SparseBwd
 #pragma unroll
             for (int h = 0; h < RMAX; ++h) {
                 if (h < r) {
-                    const float cds = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), h));
-                    const float cpv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), r + h));
+                    const float cds = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), 2 * h));
+                    const float cpv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[x]), 2 * h + 1));
                     if constexpr (D == 128) {
                         gk[0] = fmaf(cds, bf16_bits_to_f32(qv[x][h] & 0xFFFFu), gk[0]);
                         gk[DPL - 1] = fmaf(cds, bf16_bits_to_f32(qv[x][h] >> 16), gk[DPL - 1]);

@@ -119,7 +119,7 @@ struct SparseBwdArgs {
     const void *rlin;                         // [B,n,Hq,d] S_t d_out (q . rlin = d_out . o_lin)
     const int32_t *idx;                       // [B,n,G,M] the forward's sets
     float *dq, *dk, *dv, *dgate;              // dq += ; dk, dv atomically += ; dgate =
-    float *coef;                              // bf16 path: [B,n,G,M,2r] (scale ds, gamma p) per slot
+    float *coef;                              // bf16 path: [B,n,G,M,r,2] (scale ds, gamma p) per slot and head
     uint32_t *sorted;                         // bf16 path: per block of positions, its sorted entries
     int B, n, Hq, G, r, M;
     float scale;
