@@ -527,7 +527,7 @@ lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int6
 // ---- backward --------------------------------------------------------------------
 namespace {
 struct BwdWs {
-    size_t Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dsoT, dS, P, coef, sorted, total;
+    size_t Grev, qrev, vrep, krep, dqlin, ok, ov, sinT, dS, P, coef, sorted, total;
 };
 BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
     const size_t Hq = d->num_q_heads, D = d->head_dim, eb = elt_bytes(d->dtype);
@@ -542,8 +542,6 @@ BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
         off += act;
     }
     w.sinT = off;
-    off += st;
-    w.dsoT = off;
     off += st;
     // the chunked passes: up to Hq groups (each head its own group in the reversed passes)
     w.dS = off;
@@ -560,9 +558,12 @@ BwdWs bwd_ws(const lisa_dims *d, int B, int n) {
 }
 
 // one causal chunked linear-attention pass: out = o_lin of (q, k, v, state_in)
+// output_only: the chunk-output kernel alone, on the prefix states the previous
+// pass left in the workspace, read transposed (they are those of the
+// transposed recurrence)
 hipError_t linear_pass(const lisa_dims *dims, int B, int n, int Hq, int G, const void *q, const void *k,
                         const void *v, const float *state_in, float *state_out, void *out,
-                        unsigned char *ws, const BwdWs &w, hipStream_t s) {
+                        unsigned char *ws, const BwdWs &w, hipStream_t s, bool output_only = false) {
     lisa::LinearArgs la{};
     la.q = q;
     la.k = k;
@@ -582,6 +583,10 @@ hipError_t linear_pass(const lisa_dims *dims, int B, int n, int Hq, int G, const
     la.kv_off = 0;
     la.per_head = state_in != nullptr;
     const int D = dims->head_dim;
+    if (output_only) {
+        la.state_t = 1;
+        return lisa::launch_linear_chunk_output(la, dims->dtype, D, s);
+    }
     hipError_t e = lisa::launch_linear_chunk_state(la, dims->dtype, D, s);
     if (e == hipSuccess) e = lisa::launch_linear_prefix_scan(la, dims->dtype, D, s);
     if (e == hipSuccess) e = lisa::launch_linear_chunk_output(la, dims->dtype, D, s);
@@ -652,11 +657,9 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     pa.G = G;
     pa.d = D;
     float *sinT = state_in ? reinterpret_cast<float *>(ws + w.sinT) : nullptr;
-    float *dsoT = d_state_out ? reinterpret_cast<float *>(ws + w.dsoT) : nullptr;
     LISA_HIP(timed(ST_BWD_OPER, s, [&] {
                  hipError_t e = lisa::launch_bwd_prep(pa, dims->dtype, s);
                  if (e == hipSuccess && sinT) e = lisa::launch_transpose_states(state_in, sinT, (int64_t)B * Hq, D, s);
-                 if (e == hipSuccess && dsoT) e = lisa::launch_transpose_states(d_state_out, dsoT, (int64_t)B * Hq, D, s);
                  return e;
              }),
              "backward operand launch");
@@ -664,12 +667,15 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     // for the gate), then dk and dv of the linear branch in reversed time
     LISA_HIP(timed(ST_BWD_LINEAR, s, [&] {
                  hipError_t e = linear_pass(dims, B, n, Hq, G, d_out, v, k, sinT, nullptr, ws + w.dqlin, ws, w, s);
-                 if (e == hipSuccess)
-                     e = linear_pass(dims, B, n, Hq, Hq, ws + w.vrep, ws + w.Grev, ws + w.qrev, dsoT, nullptr,
-                                     ws + w.ok, ws, w, s);
+                 // dv: H_s = dS_out + sum_{t >= s} q_t G_t^T is the state of the
+                 // reversed recurrence k' = q, v' = G; dk reads the same prefixes
+                 // transposed (k' = G, v' = q), so it needs only the output kernel
                  if (e == hipSuccess)
                      e = linear_pass(dims, B, n, Hq, Hq, ws + w.krep, ws + w.qrev, ws + w.Grev, d_state_out,
                                      d_state_in, ws + w.ov, ws, w, s);
+                 if (e == hipSuccess)
+                     e = linear_pass(dims, B, n, Hq, Hq, ws + w.vrep, ws + w.Grev, ws + w.qrev, d_state_out,
+                                     nullptr, ws + w.ok, ws, w, s, true);
                  return e;
              }),
              "backward linear-pass launch");

@@ -81,6 +81,8 @@ struct LinearArgs {
     int B, n, Hq, G, r, nC;
     int kv_rows, kv_off;
     int per_head;                // 1 if state_in != null (prefix states per query head)
+    int state_t;                 // chunk output only: P holds the prefixes untransposed
+                                 // (those of the transposed recurrence), read transposed
 };
 hipError_t launch_linear_chunk_state(const LinearArgs &a, int dtype, int d, hipStream_t s);
 hipError_t launch_linear_prefix_scan(const LinearArgs &a, int dtype, int d, hipStream_t s);

@@ -51,6 +51,19 @@ __device__ __forceinline__ void stage_transposed(T *dst, int ts, const T *src, s
     }
 }
 
+// Copy a D x D matrix transposed into LDS rows ds apart: dst[j][i] = src[i][j].
+template <typename T, int D>
+__device__ __forceinline__ void stage_square_transposed(T *dst, int ds, const T *src) {
+    constexpr int EPC = 16 / Elt<T>::kBytes, CPR = D / EPC;
+    for (int q = threadIdx.x; q < D * CPR; q += 256) {
+        const int row = q % D, cc = q / D;
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(src + (size_t)row * D + cc * EPC);
+        const T *e = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) dst[(cc * EPC + i) * ds + row] = e[i];
+    }
+}
+
 // Copy rows x D (row-major, rows rstride apart) into LDS rows ds apart.
 template <typename T, int D>
 __device__ __forceinline__ void stage_rows(T *dst, int ds, const T *src, size_t rstride, int rows,
@@ -187,7 +200,8 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
     stage_rows<T, D>(ks_, KS, kp, rstride, kC, valid);
     stage_transposed<T, D>(vt_, VTS, vp, rstride, valid);
     const size_t pgrp = a.per_head ? ((size_t)b * a.Hq + g * a.r) : ((size_t)b * a.G + g);
-    stage_rows<T, D>(st_, SS, P + (pgrp * a.nC + c) * D * D, D, D, D);
+    if (a.state_t) stage_square_transposed<T, D>(st_, SS, P + (pgrp * a.nC + c) * D * D);
+    else stage_rows<T, D>(st_, SS, P + (pgrp * a.nC + c) * D * D, D, D, D);
     __syncthreads();
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
@@ -199,7 +213,8 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
         const int h = g * a.r + hh;
         if (a.per_head && hh > 0) {
             __syncthreads();
-            stage_rows<T, D>(st_, SS, P + ((pgrp + hh) * a.nC + c) * D * D, D, D, D);
+            if (a.state_t) stage_square_transposed<T, D>(st_, SS, P + ((pgrp + hh) * a.nC + c) * D * D);
+            else stage_rows<T, D>(st_, SS, P + ((pgrp + hh) * a.nC + c) * D * D, D, D, D);
             __syncthreads();
         }
         Frag<T> qb[KD];
