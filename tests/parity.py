@@ -358,9 +358,19 @@ def window_decode_parity(cfg, inp, report=None):
 BWD_TOL = {"bf16": 1e-2, "f32": 1e-4}
 
 
-def backward_parity(cfg, inp, binp, report=None):
-    """GPU forward (for the sets), GPU backward, oracle backward on the same
-    sets; normwise errors of dq, dk, dv, dgate and d_state_in."""
+def window_sets(B, n, G, M):
+    """The sliding-window variant's sets: position t attends to
+    max(0, t - M + 1) .. t, ascending, -1 padded."""
+    idx = np.full((B, n, G, M), -1, dtype=np.int32)
+    for t in range(n):
+        lo = max(0, t - M + 1)
+        idx[:, t, :, :t + 1 - lo] = np.arange(lo, t + 1, dtype=np.int32)
+    return idx
+
+
+def backward_parity(cfg, inp, binp, report=None, sets=None):
+    """GPU forward (for the sets, unless given), GPU backward, oracle backward
+    on the same sets; normwise errors of dq, dk, dv, dgate and d_state_in."""
     import torch
     from hybrid_linear_top_amd import lisa
     from oracle import backward as obwd
@@ -368,7 +378,7 @@ def backward_parity(cfg, inp, binp, report=None):
     dv_ = lisa.to_device
     dt = cfg.dtype
     S0 = binp["state_in"]
-    _, _, idx = run_prefill(cfg, inp, state_in=S0)
+    idx = sets if sets is not None else run_prefill(cfg, inp, state_in=S0)[2]
     got = lisa.prefill_backward(dims, dv_(inp["q"]), dv_(inp["k"]), dv_(inp["v"]), dv_(inp["gate"]),
                                 dv_(idx), dv_(binp["d_out"]),
                                 state_in=None if S0 is None else dv_(S0),

@@ -353,3 +353,19 @@ def test_prefill_backward(case):
     rep = {}
     parity.backward_parity(cfg, inp, binp, report=rep)
     _say("  ", rep)
+
+
+@pytest.mark.parametrize("case", [(_pcfg(400, 8, 2, 128, 4, 64, 96, seed=21), True),
+                                  (_pcfg(150, 4, 1, 64, 4, 32, 256, dtype="f32", seed=22), False)],
+                         ids=lambda c: c[0].name)
+def test_prefill_backward_window_sets(case):
+    """The backward of the sliding-window variant: the window's sets passed as
+    topm (the backward takes any sets; the window ones are dense bands)."""
+    cfg, states = case
+    _say("backward window sets", cfg.name, "states", states)
+    inp = gen.make_prefill_inputs(cfg)
+    binp = gen.make_backward_inputs(cfg, with_states=states)
+    rep = {}
+    parity.backward_parity(cfg, inp, binp, report=rep,
+                           sets=parity.window_sets(cfg.B, cfg.n, cfg.Hkv, cfg.M))
+    _say("  ", rep)
