@@ -369,3 +369,65 @@ def test_prefill_backward_window_sets(case):
     parity.backward_parity(cfg, inp, binp, report=rep,
                            sets=parity.window_sets(cfg.B, cfg.n, cfg.Hkv, cfg.M))
     _say("  ", rep)
+
+
+def _random_cases(seed, count):
+    """Seeded random shapes within the supported ranges (a sweep beside the
+    hand-picked cases: ragged n and M, every head-group ratio, both dtypes)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        G = int(rng.choice([1, 2, 4]))
+        r = int(rng.choice([1, 2, 3, 5, 7, 8, 16]))
+        d = int(rng.choice([64, 128]))
+        dI = int(rng.choice([32, 64]))
+        HI = int(rng.integers(1, 9))
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        out.append((G, r, d, dI, HI, dtype, int(rng.integers(1_000_000))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(77, 16), ids=lambda c: f"G{c[0]}r{c[1]}d{c[2]}s{c[6]}")
+def test_prefill_random_shapes(case):
+    G, r, d, dI, HI, dtype, seed = case
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 700))
+    M = int(rng.integers(1, 513))
+    B = int(rng.choice([1, 1, 2]))
+    cfg = _pcfg(n, G * r, G, d, HI, dI, M, dtype=dtype, B=B, seed=seed % 1000)
+    _say("prefill random", cfg.name, "B", B, "seed", cfg.seed)
+    rep = {}
+    parity.prefill_parity(cfg, gen.make_prefill_inputs(cfg), report=rep)
+    _say("  ", rep)
+
+
+@pytest.mark.parametrize("case", _random_cases(78, 16), ids=lambda c: f"G{c[0]}r{c[1]}d{c[2]}s{c[6]}")
+def test_decode_random_shapes(case):
+    G, r, d, dI, HI, dtype, seed = case
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 6))
+    M = int(rng.integers(1, 2049))
+    lengths = [int(x) for x in rng.integers(1, 12000, size=B)]
+    cfg, L = _dcfg(G * r, G, d, HI, dI, M, lengths, dtype=dtype, seed=seed % 1000)
+    _say("decode random", cfg.name, "seed", cfg.seed)
+    rep = {}
+    parity.decode_parity(cfg, gen.make_decode_inputs(cfg, lengths=L), report=rep)
+    _say("  ", rep)
+
+
+@pytest.mark.parametrize("case", _random_cases(79, 12), ids=lambda c: f"G{c[0]}r{c[1]}d{c[2]}s{c[6]}")
+def test_backward_random_shapes(case):
+    G, r, d, dI, HI, dtype, seed = case
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 500))
+    M = int(rng.integers(1, 513))
+    if dtype == "f32":
+        M = min(M, 128)  # the fp32 kernel's LDS holds M * r logits
+    B = int(rng.choice([1, 2]))
+    cfg = _pcfg(n, G * r, G, d, HI, dI, M, dtype=dtype, B=B, seed=seed % 1000)
+    states = bool(rng.random() < 0.5)
+    _say("backward random", cfg.name, "B", B, "states", states, "seed", cfg.seed)
+    rep = {}
+    parity.backward_parity(cfg, gen.make_prefill_inputs(cfg), gen.make_backward_inputs(cfg, with_states=states),
+                           report=rep)
+    _say("  ", rep)
