@@ -431,3 +431,51 @@ def test_backward_random_shapes(case):
     parity.backward_parity(cfg, gen.make_prefill_inputs(cfg), gen.make_backward_inputs(cfg, with_states=states),
                            report=rep)
     _say("  ", rep)
+
+
+@pytest.mark.parametrize("case", _random_cases(80, 8), ids=lambda c: f"G{c[0]}r{c[1]}d{c[2]}s{c[6]}")
+def test_prefill_continue_random_shapes(case):
+    G, r, d, dI, HI, dtype, seed = case
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 700))
+    past = int(rng.integers(0, n))
+    M = int(rng.integers(1, 513))
+    cfg = _pcfg(n, G * r, G, d, HI, dI, M, dtype=dtype, B=int(rng.choice([1, 2])), seed=seed % 1000)
+    _say("prefill continue random", cfg.name, "past", past, "seed", cfg.seed)
+    rep = {}
+    parity.prefill_parity(cfg, gen.make_prefill_inputs(cfg), past=past, report=rep)
+    _say("  ", rep)
+
+
+@pytest.mark.parametrize("case", _random_cases(81, 8), ids=lambda c: f"G{c[0]}r{c[1]}d{c[2]}s{c[6]}")
+def test_window_random_shapes(case):
+    G, r, d, dI, HI, dtype, seed = case
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 700))
+    past = int(rng.integers(0, n))
+    M = int(rng.integers(1, 2049))
+    cfg = _pcfg(n, G * r, G, d, 1, 32, M, dtype=dtype, seed=seed % 1000)
+    _say("prefill window random", cfg.name, "past", past, "seed", cfg.seed)
+    rep = {}
+    parity.window_prefill_parity(cfg, gen.make_prefill_inputs(cfg), past=past, report=rep)
+    _say("  ", rep)
+    lengths = [int(x) for x in rng.integers(1, 6000, size=int(rng.integers(1, 5)))]
+    dcfg, L = _dcfg(G * r, G, d, 1, 32, M, lengths, dtype=dtype, seed=seed % 1000)
+    _say("decode window random", dcfg.name, "seed", dcfg.seed)
+    rep = {}
+    parity.window_decode_parity(dcfg, gen.make_decode_inputs(dcfg, lengths=L), report=rep)
+    _say("  ", rep)
+
+
+@pytest.mark.parametrize("case", _random_cases(82, 8), ids=lambda c: f"G{c[0]}r{c[1]}d{c[2]}s{c[6]}")
+def test_decode_paged_random_shapes(case):
+    G, r, d, dI, HI, dtype, seed = case
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(1, 9000, size=int(rng.integers(1, 5)))]
+    M = int(rng.integers(1, 2049))
+    bs = int(2 ** rng.integers(0, 13))
+    cfg, L = _dcfg(G * r, G, d, HI, dI, M, lengths, dtype=dtype, seed=seed % 1000)
+    _say("decode paged random", cfg.name, "block", bs, "seed", cfg.seed)
+    rep = {}
+    parity.paged_decode_parity(cfg, gen.make_decode_inputs(cfg, lengths=L), bs, seed=cfg.seed, report=rep)
+    _say("  ", rep)
