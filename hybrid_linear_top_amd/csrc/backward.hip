@@ -6,21 +6,26 @@
 // the forward's (a top-M set is piecewise constant in q_I, k_I and w, which
 // therefore get no gradient).  With G_t = (1 - gamma_t) d_out_t per head:
 //
-//  * gate:   dz = gamma (1 - gamma) (d_out . o_sp - d_out . o_lin);
-//  * linear branch, three causal linear-attention passes run by the forward
+//  * gate:   dz = gamma (1 - gamma) (d_out . o_sp - d_out . o_lin), where
+//            d_out . o_lin = q . (S_t d_out);
+//  * linear branch, causal linear-attention passes run by the forward
 //    chunked kernels on rearranged operands:
-//      dq_t = S_t G_t                   = attention(q'=G, k'=v, v'=k, S0'=S0^T)
+//      R_t  = S_t d_out_t               = attention(q'=d_out, k'=v, v'=k, S0'=S0^T),
+//      dq_t = (1 - gamma) R_t;
 //      dk_s = H_s v_s,  dv_s = H_s^T k_s, H_s = dS_out + sum_{t >= s} q_t G_t^T
-//        -- in reversed time these are causal too: per head,
-//           dk: q'=v, k'=G, v'=q, S0'=dS_out^T;  dv: q'=k, k'=q, v'=G,
-//           S0'=dS_out, whose final state is d_state_in;
-//        each head its own group there, then summed over the heads of a group;
-//  * sparse branch, one wave per (position, group) (sparse_bwd_kernel): the
-//    softmax weights p of the r heads are recomputed from the gathered K rows,
-//    ds = gamma p (d_out . v_s - d_out . o_sp), dq += scale sum_s ds k_s, and
-//    dk_s += scale sum_h ds q_h, dv_s += sum_h p gamma d_out_h are added
-//    into the key rows with fp32 atomics (the selected keys of different
-//    positions collide at random, so no other owner exists for a key row).
+//        -- in reversed time these are causal too, per head (each head its
+//           own group there, then summed over the heads of a group):
+//           dv: q'=k, k'=q, v'=G, S0'=dS_out, whose final state is d_state_in;
+//           dk: q'=v, k'=G, v'=q carries the transposed state, so it is the
+//           output kernel alone on dv's prefix states read transposed;
+//  * sparse branch: ds = gamma p (d_out . v_s - d_out . o_sp),
+//      dq += scale sum_s ds k_s,
+//      dk_s += scale sum_h ds_h q_h,  dv_s += sum_h gamma_h p_h d_out_h.
+//    bf16: a query-side kernel on MFMA (softmax statistics, ds, dq and the
+//    per-slot coefficients) and a key side that sorts the entries of blocks
+//    of positions by key and walks them, adding each key row about once per
+//    block with fp32 atomics (details at the kernels).  fp32: one wave per
+//    (position, group) with the atomics per selected key (sparse_bwd_kernel).
 #include "common.hpp"
 #include "kernels.hpp"
 
