@@ -289,6 +289,9 @@ def test_backward_limits():
     assert _bwd(d, n=32769) == lisa.LISA_ERR_UNSUPPORTED
     assert _bwd(_dims(Hq=34, Hkv=2)) == lisa.LISA_ERR_UNSUPPORTED
     assert _bwd(_dims(Hq=32, Hkv=1, M=512)) == lisa.LISA_ERR_UNSUPPORTED   # 32 heads per group
+    # fp32 keeps M * r logits per wave in LDS; bf16 has no such bound
+    assert _bwd(_dims(Hq=16, Hkv=1, M=512, dtype="f32")) == lisa.LISA_ERR_UNSUPPORTED
+    assert "LDS" in lisa.lisa_last_error()
     assert _bwd(d, n=0, q=0, workspace=0) == lisa.LISA_OK
     assert _bwd(d, B=0, q=0) == lisa.LISA_OK
     need = lisa.lisa_prefill_backward_workspace_bytes(d, 1, 64)
