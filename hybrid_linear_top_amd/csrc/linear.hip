@@ -36,16 +36,28 @@ __device__ __forceinline__ void load_halves(Frag<float> &f, const float *p0, con
     f.hi = *reinterpret_cast<const f32x4 *>(p1);
 }
 
+// The staging copies below issue all of a thread's loads before any LDS
+// write, unconditionally (rows past `valid` re-read row valid - 1 and are
+// zeroed afterwards; valid >= 1): a guarded load in the loop had compiled to
+// one full wait per iteration.
+
 // Copy a [64 tokens x D] tile (rows rstride apart in global memory; rows
 // >= valid are zero) into LDS transposed: dst[dim * ts + tok].
 template <typename T, int D>
 __device__ __forceinline__ void stage_transposed(T *dst, int ts, const T *src, size_t rstride, int valid) {
-    constexpr int EPC = 16 / Elt<T>::kBytes, CPR = D / EPC;
-    for (int q = threadIdx.x; q < kC * CPR; q += 256) {
-        const int tok = q % kC, cc = q / kC;
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (tok < valid) raw = *reinterpret_cast<const u32x4 *>(src + (size_t)tok * rstride + cc * EPC);
-        const T *e = reinterpret_cast<const T *>(&raw);
+    constexpr int EPC = 16 / Elt<T>::kBytes, CPR = D / EPC, N = kC * CPR / 256;
+    static_assert(kC * CPR % 256 == 0, "whole rounds of 256 threads");
+    u32x4 raw[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int q = threadIdx.x + k * 256, tok = q % kC, cc = q / kC;
+        raw[k] = *reinterpret_cast<const u32x4 *>(src + (size_t)min(tok, valid - 1) * rstride + cc * EPC);
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int q = threadIdx.x + k * 256, tok = q % kC, cc = q / kC;
+        const u32x4 v = tok < valid ? raw[k] : u32x4{0u, 0u, 0u, 0u};
+        const T *e = reinterpret_cast<const T *>(&v);
 #pragma unroll
         for (int i = 0; i < EPC; ++i) dst[(cc * EPC + i) * ts + tok] = e[i];
     }
@@ -54,26 +66,39 @@ __device__ __forceinline__ void stage_transposed(T *dst, int ts, const T *src, s
 // Copy a D x D matrix transposed into LDS rows ds apart: dst[j][i] = src[i][j].
 template <typename T, int D>
 __device__ __forceinline__ void stage_square_transposed(T *dst, int ds, const T *src) {
-    constexpr int EPC = 16 / Elt<T>::kBytes, CPR = D / EPC;
-    for (int q = threadIdx.x; q < D * CPR; q += 256) {
-        const int row = q % D, cc = q / D;
-        const u32x4 raw = *reinterpret_cast<const u32x4 *>(src + (size_t)row * D + cc * EPC);
-        const T *e = reinterpret_cast<const T *>(&raw);
+    constexpr int EPC = 16 / Elt<T>::kBytes, CPR = D / EPC, N = D * CPR / 256;
+    static_assert(D * CPR % 256 == 0, "whole rounds of 256 threads");
+    u32x4 raw[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int q = threadIdx.x + k * 256, row = q % D, cc = q / D;
+        raw[k] = *reinterpret_cast<const u32x4 *>(src + (size_t)row * D + cc * EPC);
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int q = threadIdx.x + k * 256, row = q % D, cc = q / D;
+        const T *e = reinterpret_cast<const T *>(&raw[k]);
 #pragma unroll
         for (int i = 0; i < EPC; ++i) dst[(cc * EPC + i) * ds + row] = e[i];
     }
 }
 
-// Copy rows x D (row-major, rows rstride apart) into LDS rows ds apart.
-template <typename T, int D>
-__device__ __forceinline__ void stage_rows(T *dst, int ds, const T *src, size_t rstride, int rows,
-                                           int valid) {
-    constexpr int EPC = 16 / Elt<T>::kBytes, CPR = D / EPC;
-    for (int q = threadIdx.x; q < rows * CPR; q += 256) {
-        const int row = q / CPR, cc = q % CPR;
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (row < valid) raw = *reinterpret_cast<const u32x4 *>(src + (size_t)row * rstride + cc * EPC);
-        *reinterpret_cast<u32x4 *>(dst + row * ds + cc * EPC) = raw;
+// Copy ROWS x D (row-major, rows rstride apart) into LDS rows ds apart; rows
+// >= valid are zero.
+template <typename T, int D, int ROWS>
+__device__ __forceinline__ void stage_rows(T *dst, int ds, const T *src, size_t rstride, int valid) {
+    constexpr int EPC = 16 / Elt<T>::kBytes, CPR = D / EPC, N = ROWS * CPR / 256;
+    static_assert(ROWS * CPR % 256 == 0, "whole rounds of 256 threads");
+    u32x4 raw[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int q = threadIdx.x + k * 256, row = q / CPR, cc = q % CPR;
+        raw[k] = *reinterpret_cast<const u32x4 *>(src + (size_t)min(row, valid - 1) * rstride + cc * EPC);
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int q = threadIdx.x + k * 256, row = q / CPR, cc = q % CPR;
+        *reinterpret_cast<u32x4 *>(dst + row * ds + cc * EPC) = row < valid ? raw[k] : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -197,11 +222,11 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
     const T *kp = reinterpret_cast<const T *>(a.k) + (((size_t)b * a.kv_rows + a.kv_off + t0) * a.G + g) * D;
     const T *vp = reinterpret_cast<const T *>(a.v) + (((size_t)b * a.kv_rows + a.kv_off + t0) * a.G + g) * D;
     const T *P = reinterpret_cast<const T *>(a.P);
-    stage_rows<T, D>(ks_, KS, kp, rstride, kC, valid);
+    stage_rows<T, D, kC>(ks_, KS, kp, rstride, valid);
     stage_transposed<T, D>(vt_, VTS, vp, rstride, valid);
     const size_t pgrp = a.per_head ? ((size_t)b * a.Hq + g * a.r) : ((size_t)b * a.G + g);
     if (a.state_t) stage_square_transposed<T, D>(st_, SS, P + (pgrp * a.nC + c) * D * D);
-    else stage_rows<T, D>(st_, SS, P + (pgrp * a.nC + c) * D * D, D, D, D);
+    else stage_rows<T, D, D>(st_, SS, P + (pgrp * a.nC + c) * D * D, D, D);
     __syncthreads();
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
@@ -209,20 +234,30 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
     const int tq = w * 16 + col;  // this lane's query row in the chunk (B-operand column)
     const T *qbase = reinterpret_cast<const T *>(a.q);
     T *obase = reinterpret_cast<T *>(a.out);
+    // this lane's query row of every head: head hh + 1's fragments load while
+    // head hh is computed
+    const T *qrow = qbase + (((size_t)b * a.n + t0 + min(tq, valid - 1)) * a.Hq + g * a.r) * D + grp * 8;
+    Frag<T> qn[KD];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) qn[ks].load(qrow + ks * 32);
     for (int hh = 0; hh < a.r; ++hh) {
         const int h = g * a.r + hh;
         if (a.per_head && hh > 0) {
             __syncthreads();
             if (a.state_t) stage_square_transposed<T, D>(st_, SS, P + ((pgrp + hh) * a.nC + c) * D * D);
-            else stage_rows<T, D>(st_, SS, P + ((pgrp + hh) * a.nC + c) * D * D, D, D, D);
+            else stage_rows<T, D, D>(st_, SS, P + ((pgrp + hh) * a.nC + c) * D * D, D, D);
             __syncthreads();
         }
         Frag<T> qb[KD];
 #pragma unroll
         for (int ks = 0; ks < KD; ++ks) {
-            if (tq < valid) qb[ks].load(qbase + (((size_t)b * a.n + t0 + tq) * a.Hq + h) * D + ks * 32 + grp * 8);
-            else qb[ks].zero();
+            qb[ks] = qn[ks];
+            if (tq >= valid) qb[ks].zero();  // rows past the chunk end (their loads read row valid - 1)
         }
+        // (unconditional: the last head loads its own row again)
+        const int hn = min(hh + 1, a.r - 1);
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) qn[ks].load(qrow + (size_t)hn * D + ks * 32);
         // A^T[tk][tq] = K Q^T for key blocks at or below the diagonal
         f32x4 att[4];
 #pragma unroll
