@@ -479,3 +479,78 @@ def test_decode_paged_random_shapes(case):
     rep = {}
     parity.paged_decode_parity(cfg, gen.make_decode_inputs(cfg, lengths=L), bs, seed=cfg.seed, report=rep)
     _say("  ", rep)
+
+
+def test_graph_replay():
+    """A serving loop captures the calls in a HIP graph: the library enqueues
+    only kernels on the caller's stream (no allocation, memset or sync), so a
+    captured prefill and a captured decode step replay to the eager results
+    bit for bit, replay after replay, with eager work (the decode state reset
+    from a saved copy) between the replays."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    dv = lisa.to_device
+    pcfg = _pcfg(700, 8, 2, 128, 4, 64, 128, seed=51)
+    pinp = gen.make_prefill_inputs(pcfg)
+    dims = lisa.dims_from_config(pcfg)
+    x = {k: dv(pinp[k]) for k in ("q", "k", "v", "q_idx", "k_idx", "w_idx", "gate")}
+    B, n = pinp["B"], pinp["n"]
+    ws = torch.empty(lisa.lisa_prefill_workspace_bytes(dims, B, n), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x["q"])
+    st = torch.empty((B, pcfg.Hq, pcfg.d, pcfg.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, n, pcfg.Hkv, pcfg.M), dtype=torch.int32, device="cuda")
+
+    def prefill():
+        lisa.prefill(dims, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], x["w_idx"], x["gate"],
+                     out=out, state_out=st, topm_out=idx, workspace=ws)
+
+    prefill()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, st, idx)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        prefill()
+    for rep in range(3):
+        for t in (out, st, idx):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("prefill graph replay", rep)
+        for a, b in zip((out, st, idx), ref):
+            assert torch.equal(a, b)
+
+    dcfg, lengths = _dcfg(12, 2, 128, 4, 64, 256, [300, 1000, 4000], seed=52)
+    dinp = gen.make_decode_inputs(dcfg, lengths=lengths)
+    ddims = lisa.dims_from_config(dcfg)
+    y = {k: dv(dinp[k]) for k in ("cu_ctx", "q", "k_cache", "v_cache", "q_idx", "k_idx_cache", "w_idx", "gate",
+                                  "state")}
+    state0 = y["state"].clone()
+    dws = torch.empty(lisa.lisa_decode_workspace_bytes(ddims, dinp["B"], dinp["max_ctx"]), dtype=torch.uint8,
+                      device="cuda")
+    dout = torch.empty_like(y["q"])
+    didx = torch.empty((dinp["B"], dcfg.Hkv, dcfg.M), dtype=torch.int32, device="cuda")
+
+    def step():
+        lisa.decode_step(ddims, y["cu_ctx"], dinp["max_ctx"], y["q"], y["k_cache"], y["v_cache"], y["q_idx"],
+                         y["k_idx_cache"], y["w_idx"], y["gate"], y["state"], out=dout, topm_out=didx,
+                         workspace=dws)
+
+    step()
+    torch.cuda.synchronize()
+    dref = [t.clone() for t in (dout, y["state"], didx)]
+    y["state"].copy_(state0)
+    torch.cuda.synchronize()
+    dg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dg):
+        step()
+    for rep in range(3):
+        y["state"].copy_(state0)  # the step advances the state in place
+        dout.zero_()
+        didx.zero_()
+        torch.cuda.synchronize()
+        dg.replay()
+        torch.cuda.synchronize()
+        _say("decode graph replay", rep)
+        for a, b in zip((dout, y["state"], didx), dref):
+            assert torch.equal(a, b)
