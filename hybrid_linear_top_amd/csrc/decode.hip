@@ -445,9 +445,10 @@ __device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32
 
 // ---------------------------------------------------------------------------
 // Top-M select of one (sequence, group) with few block barriers: NT threads,
-// the keys in registers, wave w owning the contiguous positions
-// w*EPT*64 .. (w+1)*EPT*64 - 1.
-//  0. long sequences (L >= 8M) try a shortcut first (described at the code);
+// the keys in registers, thread t holding positions k*NT + t (k < EPT), so
+// every load instruction reads consecutive scores and (k, thread) order is
+// position order.
+//  0. a shortcut first, when 2M <= CAP (described at the code);
 //  1. key range by wave reductions (one barrier);
 //  2. 2048-bin histogram passes over the live key range (bins are
 //     (key - lo) >> shift), the bin holding the M-th largest key found by
@@ -461,7 +462,7 @@ __device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32
 //     the lowest `need` positions of it are taken;
 //  4. wave 0 walks the bitmaps in position order (contiguous words per lane,
 //     one wave scan of their counts) and writes the set ascending.
-template <int NT, int EPT>
+template <int NT, int EPT, int CAP>
 __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, CacheMap map,
                                                          int G, int M, int max_ctx, int32_t *idx) {
     constexpr int NW = NT / 64;
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
     __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
     __shared__ uint32_t bitmap[NWORD];   // selected outright
     __shared__ uint32_t eqmap[NWORD];    // boundary keys that are all equal (ties)
-    __shared__ uint32_t red[2 * NW];
+    __shared__ uint32_t red[2 * NW + 2];
     __shared__ uint32_t cand_key[64], cand_pos[64];
     __shared__ uint32_t found[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -482,115 +483,146 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
         for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
         return;
     }
-    // wave w holds positions w*EPT*64 + k*64 + lane: each wave owns one
-    // contiguous range, so (wave, round, lane) order is position order.  All
-    // loads are unconditional (positions >= L read zeros through the
-    // descriptor) so they are in flight together.
-    const int wbase = wave * (EPT * 64);
-    auto pos_of = [&](int k) { return wbase + k * 64 + lane; };
+    // All loads are unconditional (positions past L read zeros through the
+    // descriptor), so they are in flight together.  The launch guarantees
+    // NT * EPT >= L.
+    auto pos_of = [&](int k) { return k * NT + tid; };
+    auto valid = [&](int k) { return pos_of(k) < L; };
     const rsrc_t srs = make_rsrc(sc, (uint32_t)L * 4u);
     uint32_t keyreg[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k)
         keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)pos_of(k) * 4u, 0u, 0);
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, tmax = 0u;
+    bool active = false;  // this thread holds a key
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        const int s = pos_of(k);
         keyreg[k] = order_key(__uint_as_float(keyreg[k]));
-        if (s < L) {
+        if (valid(k)) {
             kmin = min(kmin, keyreg[k]);
             kmax = max(kmax, keyreg[k]);
+            active = true;
         }
     }
+    tmax = kmax;  // this thread's largest key
 
-    // ---- shortcut: per-wave thresholds, candidates packed for one wave ----
-    // Each wave picks a threshold T_w from its own keys (the R-th largest of
-    // its lanes' two largest, R a few standard deviations above the wave's
-    // expected share of the top M) and keeps its keys >= T_w.  If the kept
-    // keys number between M and 1024 they are packed in position order, and
-    // one wave finds their M-th largest theta.  When no T_w exceeds theta,
-    // every key >= theta was kept, so the top M (ties to the lower position)
-    // are exactly the kept ones that rank in the first M; otherwise, or when
-    // the count is out of range, the exact passes below run.
-    constexpr int CAP = 1024;
-    __shared__ uint32_t wcnt[NW], wthr[NW], verdict;
+    // ---- shortcut: a threshold from the threads' maxima ----------------------
+    // The M-th largest of the threads' maxima is at or below the M-th largest
+    // key (the maxima are keys of distinct positions), so every key of the
+    // top M lies at or above any T with at least M maxima >= T.  One
+    // histogram pass over the maxima gives such a T (the lower edge of the
+    // bin where the count from the top reaches M); the keys >= T -- about M
+    // plus the threads holding two or more of the top M -- are packed in
+    // position order (per (round k, wave) counts, one block scan over that
+    // k-major grid, ballot ranks within a wave), and one wave selects their M
+    // largest exactly (ties to the lower position).  When more than CAP keys
+    // pass T the exact passes below run instead.
+    static_assert(EPT * NW <= NT, "one scan entry per thread");
     __shared__ uint32_t fkey[CAP], fpos[CAP];
-    if (L >= 8 * M) {
-        const int nv = min(max(L - wbase, 0), EPT * 64);  // this wave's valid keys
-        uint32_t a1 = 0u, a2 = 0u;                       // this lane's two largest
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) {
-            const uint32_t u = pos_of(k) < L ? keyreg[k] : 0u;
-            a2 = max(a2, min(a1, u));
-            a1 = max(a1, u);
-        }
-        const float mu = (float)M * (float)nv / (float)L;
-        const uint32_t R = (uint32_t)fminf(128.0f, ceilf(mu + 4.0f * sqrtf(mu) + 4.0f));
-        uint32_t T = 0u;  // largest T with at least R of the 128 values >= T
-#pragma unroll 1
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = T | (1u << bit);
-            const uint32_t c = (uint32_t)__popcll(__ballot(a1 >= cand)) + (uint32_t)__popcll(__ballot(a2 >= cand));
-            T = c >= R ? cand : T;
-        }
-        uint32_t cw = 0;
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) cw += (uint32_t)__popcll(__ballot(pos_of(k) < L && keyreg[k] >= T));
+    __shared__ uint32_t scan_tmp[NW + 1];
+    __shared__ uint32_t kbase[EPT * NW];
+    const bool shortcut = 2 * M <= CAP;
+    if (shortcut) {
+        const uint32_t mlo = wave_min_u32(active ? tmax : 0xFFFFFFFFu);
+        const uint32_t mhi = wave_max_u32(tmax);
         if (lane == 0) {
-            wcnt[wave] = cw;
-            wthr[wave] = nv > 0 ? T : 0u;
+            red[wave] = mlo;
+            red[NW + wave] = mhi;
         }
+        for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
         __syncthreads();
-        uint32_t C = 0, pre = 0, Tmax = 0;
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            pre += w < wave ? wcnt[w] : 0u;
-            C += wcnt[w];
-            Tmax = max(Tmax, wthr[w]);
+            lo = min(lo, red[w]);
+            hi = max(hi, red[NW + w]);
         }
-        if (C >= (uint32_t)M && C <= (uint32_t)CAP) {
+        const uint32_t span = hi >= lo ? hi - lo : 0u;
+        const int width = span == 0 ? 0 : 32 - __builtin_clz(span);
+        const int shift = width > 11 ? width - 11 : 0;
+        if (active) atomicAdd(&hist[(tmax - lo) >> shift], 1u);
+        __syncthreads();
+        if (wave == 0) {
+            // lane l owns bins 2016 - 32*l .. 2047 - 32*l, walked downwards
+            const uint32_t *hl = hist + 2016 - 32 * lane;
+            uint32_t hsum = 0;
 #pragma unroll
-            for (int k = 0; k < EPT; ++k) {
-                const int s = pos_of(k);
-                const bool sel = s < L && keyreg[k] >= T;
-                const uint64_t bm = __ballot(sel);
-                if (sel) {
-                    fkey[pre + mbcnt64(bm)] = keyreg[k];
-                    fpos[pre + mbcnt64(bm)] = (uint32_t)s;
-                }
-                pre += (uint32_t)__popcll(bm);
+            for (int q = 0; q < 8; ++q) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(hl)[q];
+                hsum += v[0] + v[1] + v[2] + v[3];
             }
-            __syncthreads();
-            if (wave == 0) {
-                constexpr int NE = CAP / 64;
-                uint32_t kr[NE];
+            const uint32_t incl = wave_inclusive_scan(hsum);
+            const uint32_t before = incl - hsum;
+            if (before < (uint32_t)M && incl >= (uint32_t)M) {
+                uint32_t run = before;
+                int fe = 0;
+                bool got = false;
 #pragma unroll
-                for (int e = 0; e < NE; ++e) kr[e] = e * 64 + lane < (int)C ? fkey[e * 64 + lane] : 0u;
-                uint32_t theta, take_eq;
-                wave_kth_u32<NE>(kr, (int)C, (uint32_t)M, hist, theta, take_eq);
-                const bool ok = Tmax <= theta;
-                if (ok) {
-                    uint32_t base = 0, eq_seen = 0;
+                for (int q = 7; q >= 0; --q) {
+                    const u32x4 v = reinterpret_cast<const u32x4 *>(hl)[q];
 #pragma unroll
-                    for (int e = 0; e < NE; ++e) {
-                        const bool valid = e * 64 + lane < (int)C;
-                        const bool gt = valid && kr[e] > theta;
-                        const bool eq = valid && kr[e] == theta;
-                        const uint64_t em = __ballot(eq);
-                        const uint32_t er = eq_seen + mbcnt64(em);
-                        eq_seen += (uint32_t)__popcll(em);
-                        const bool keep = gt || (eq && er < take_eq);
-                        const uint64_t km = __ballot(keep);
-                        const uint32_t pos = base + mbcnt64(km);
-                        base += (uint32_t)__popcll(km);
-                        if (keep && pos < (uint32_t)M) out[pos] = (int32_t)fpos[e * 64 + lane];
+                    for (int e = 3; e >= 0; --e) {
+                        const bool hit = !got && run + v[e] >= (uint32_t)M;
+                        fe = hit ? 4 * q + e : fe;
+                        got = got || hit;
+                        run += v[e];
                     }
                 }
-                if (lane == 0) verdict = ok ? 1u : 0u;
+                red[2 * NW] = lo + ((uint32_t)(2016 - 32 * lane + fe) << shift);
+            }
+            // fewer than M threads hold keys: no bin reaches M
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            if (lane == 0) red[2 * NW + 1] = total >= (uint32_t)M ? 1u : 0u;
+        }
+        __syncthreads();
+        const uint32_t T = red[2 * NW];
+        const bool have_T = red[2 * NW + 1] != 0u;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const uint32_t c = (uint32_t)__popcll(__ballot(valid(k) && keyreg[k] >= T));
+            if (lane == 0) kbase[k * NW + wave] = c;
+        }
+        __syncthreads();
+        uint32_t C;
+        const uint32_t mine = tid < EPT * NW ? kbase[tid] : 0u;
+        const uint32_t ex = block_exclusive_scan<NT>(mine, scan_tmp, &C);
+        if (tid < EPT * NW) kbase[tid] = ex;
+        __syncthreads();
+        if (have_T && C >= (uint32_t)M && C <= (uint32_t)CAP) {
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const bool sel = valid(k) && keyreg[k] >= T;
+                const uint64_t bm = __ballot(sel);
+                if (sel) {
+                    const uint32_t p = kbase[k * NW + wave] + mbcnt64(bm);
+                    fkey[p] = keyreg[k];
+                    fpos[p] = (uint32_t)pos_of(k);
+                }
             }
             __syncthreads();
-            if (verdict) return;
+            if (wave != 0) return;
+            constexpr int NE = CAP / 64;
+            uint32_t kr[NE];
+#pragma unroll
+            for (int e = 0; e < NE; ++e) kr[e] = e * 64 + lane < (int)C ? fkey[e * 64 + lane] : 0u;
+            uint32_t theta, take_eq;
+            wave_kth_u32<NE>(kr, (int)C, (uint32_t)M, hist, theta, take_eq);
+            uint32_t base = 0, eq_seen = 0;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const bool in = e * 64 + lane < (int)C;
+                const bool gt = in && kr[e] > theta;
+                const bool eq = in && kr[e] == theta;
+                const uint64_t em = __ballot(eq);
+                const uint32_t er = eq_seen + mbcnt64(em);
+                eq_seen += (uint32_t)__popcll(em);
+                const bool keep = gt || (eq && er < take_eq);
+                const uint64_t km = __ballot(keep);
+                const uint32_t pos = base + mbcnt64(km);
+                base += (uint32_t)__popcll(km);
+                if (keep && pos < (uint32_t)M) out[pos] = (int32_t)fpos[e * 64 + lane];
+            }
+            return;
         }
     }
 
@@ -626,9 +658,8 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
         const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
-            const int s = pos_of(k);
             const uint32_t u = keyreg[k];
-            if (s < L && u >= lo && (uint64_t)u < hi_excl) atomicAdd(&hist[(u - lo) >> shift], 1u);
+            if (valid(k) && u >= lo && (uint64_t)u < hi_excl) atomicAdd(&hist[(u - lo) >> shift], 1u);
         }
         __syncthreads();
         if (wave == 0) {
@@ -688,8 +719,8 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
     for (int k = 0; k < EPT; ++k) {
         const int s = pos_of(k);
         const uint32_t u = keyreg[k];
-        if (s < L && (uint64_t)u >= bin_hi) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
-        if (cnt_b > 0 && s < L && u >= bin_lo && (uint64_t)u < bin_hi) {
+        if (valid(k) && (uint64_t)u >= bin_hi) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
+        if (cnt_b > 0 && valid(k) && u >= bin_lo && (uint64_t)u < bin_hi) {
             if (tied) {
                 atomicOr(&eqmap[s >> 5], 1u << (s & 31));
             } else {
@@ -788,15 +819,15 @@ hipError_t launch_decode_select(const float *scores, const CacheMap &cu, int B, 
                            max_ctx, idx);                                                         \
         return hipGetLastError();                                                                 \
     }
-#define LISA_TOPM(NT_, E)                                                                         \
+#define LISA_TOPM(NT_, E, CAP_)                                                                   \
     if (max_ctx <= (E) * (NT_)) {                                                                 \
-        hipLaunchKernelGGL((decode_topm_kernel<NT_, E>), grid, dim3(NT_), 0, s, scores, cu, G, M,   \
-                           max_ctx, idx);                                                         \
+        hipLaunchKernelGGL((decode_topm_kernel<NT_, E, CAP_>), grid, dim3(NT_), 0, s, scores, cu, G, \
+                           M, max_ctx, idx);                                                      \
         return hipGetLastError();                                                                 \
     }
-    // keys per thread stay in registers: 1024 threads (128 VGPRs) for short
-    // contexts, 768 threads (170 VGPRs) for longer ones
-    LISA_TOPM(1024, 8) LISA_TOPM(1024, 17) LISA_SEL(768, 43) LISA_SEL(768, 86)
+    // keys per thread stay in registers: 1024 threads (128 VGPRs) up to 33,792
+    // positions, 768 threads (170 VGPRs) for longer ones
+    LISA_TOPM(1024, 8, 1024) LISA_TOPM(1024, 17, 1024) LISA_TOPM(1024, 33, 1024) LISA_SEL(768, 86)
 #undef LISA_SEL
 #undef LISA_TOPM
     return hipErrorInvalidValue;  // longer contexts are rejected by the API layer

@@ -114,6 +114,10 @@ DECODE_SMALL = [
     _dcfg(8, 2, 64, 8, 64, 100, [999, 1001, 5000], dtype="f32", seed=3),
     _dcfg(16, 1, 128, 6, 64, 2048, [3000, 2048, 2049], seed=4),
     _dcfg(4, 1, 64, 4, 32, 256, [40000, 3, 33100], seed=5),   # longest-context select variant
+    # the 33-keys-per-thread top-M, at its largest context and just above the
+    # 17-keys-per-thread one's
+    _dcfg(4, 1, 64, 4, 32, 512, [33792, 17409, 9000], seed=6),
+    _dcfg(4, 2, 64, 2, 32, 64, [17409, 25000], seed=7),
 ]
 
 
@@ -159,6 +163,22 @@ def test_ties_lowest_index_wins():
         exp = np.concatenate([np.arange(m), -np.ones(cfg.M - m)]).astype(np.int32)
         assert np.array_equal(idx[0, t, 0], exp) and np.array_equal(idx[0, t, 1], exp), t
     dcfg, L = _dcfg(4, 2, 64, 4, 32, 100, [50, 100, 101, 3000])
+    _say("decode all-ties", dcfg.name)
+    dinp = gen.make_decode_inputs(dcfg, lengths=L)
+    dinp["w_idx"] = np.zeros_like(dinp["w_idx"])
+    _, _, didx = parity.run_decode(dcfg, dinp)
+    for b, Lb in enumerate(L):
+        m = min(dcfg.M, Lb)
+        exp = np.concatenate([np.arange(m), -np.ones(dcfg.M - m)]).astype(np.int32)
+        assert np.array_equal(didx[b, 0], exp) and np.array_equal(didx[b, 1], exp), b
+
+
+@pytest.mark.parametrize("lengths", [[8000, 300], [17000], [33792, 18000], [40000, 5]],
+                         ids=["ctx8000", "ctx17000", "ctx33792", "ctx40000"])
+def test_decode_ties_every_select_variant(lengths):
+    """w = 0 at contexts that pick each top-M kernel variant: every score is
+    exactly 0, so each set is the first min(M, L) positions."""
+    dcfg, L = _dcfg(4, 2, 64, 4, 32, 512, lengths, seed=8)
     _say("decode all-ties", dcfg.name)
     dinp = gen.make_decode_inputs(dcfg, lengths=L)
     dinp["w_idx"] = np.zeros_like(dinp["w_idx"])
