@@ -176,6 +176,30 @@ def traffic_summary(fetch_db, write_db, out_json, out_md, command):
     return data
 
 
+def kernel_stats_summary(db, out_md):
+    """Per-kernel durations from a rocprofv3 --kernel-trace database, one row
+    per (kernel, grid size): the 16K and the ragged decode batches launch the
+    same kernels with different grids."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    rows = list(cur.execute("select name, grid_x, count(*), sum(duration), avg(duration) from kernels "
+                            "group by name, grid_x order by sum(duration) desc"))
+    total = sum(r[3] for r in rows) or 1
+    with open(out_md, "w") as f:
+        f.write("# Kernel durations: 16K prefill (Qwen2.5-7B-shaped), 16K decode step (Qwen2.5-1.5B-shaped), "
+                "7B-shaped ragged decode step, 16K backward (7B-shaped)\n\n")
+        f.write("Command (run from the repository root on one MI355X):\n\n```\n"
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_stats "
+                "-o run -- python3 $REPO/bench.py\ncd $REPO && python3 bench.py --kernel-stats "
+                "gpurun_out/prof_stats/run_results.db profiles/kernel_stats_prefill16k_decode16k.md\n```\n\n")
+        f.write("rocprofv3 kernel-trace durations in microseconds, one row per kernel and launch grid "
+                "(grid_x in work-items):\n\n")
+        f.write("| kernel | grid_x | calls | total us | average us | % |\n|---|---|---|---|---|---|\n")
+        for name, gx, n, tot, avg in rows:
+            short = name.replace("lisa::(anonymous namespace)::", "").replace("void ", "")
+            f.write(f"| `{short}` | {gx} | {n} | {tot / 1e3:.1f} | {avg / 1e3:.2f} | {100.0 * tot / total:.1f} |\n")
+
+
 # ---------------------------------------------------------------------------
 def timed_loop(fn, steps, warmup, copies):
     import torch
@@ -277,15 +301,21 @@ def bench_prefill(args):
     return res
 
 
-def bench_decode(args):
+def bench_decode(args, cid=2):
+    """The decode step of CONFIGS[cid]: 2 is the 16K Qwen2.5-1.5B-shaped batch
+    of 16, 4 the Qwen2.5-7B-shaped ragged batch of 32 (contexts U[4096, 32768])."""
     import numpy as np
     import torch
     from hybrid_linear_top_amd import inputs as gen, lisa
-    cfg = gen.CONFIGS[2]
+    cfg = gen.CONFIGS[cid]
     inp = gen.make_decode_inputs(cfg)
     dims = lisa.dims_from_config(cfg)
     B = inp["B"]
-    copies = 9  # 9 x ~96 MB of bytes read per step >= 3 x the 256 MB Infinity Cache
+    by = decode_bytes(cfg, inp["lengths"])
+    # input copies rotate so that their bytes read per step add up to at
+    # least 3 x the 256 MB Infinity Cache (9 x ~96 MB at 16K, 2 x ~427 MB
+    # for the ragged batch)
+    copies = max(2, -(-3 * 256 * 2**20 // by["total"]))
     cu = lisa.to_device(inp["cu_ctx"])
     shared = {k: lisa.to_device(inp[k]) for k in ("q", "q_idx", "w_idx", "gate")}
     per = [{k: lisa.to_device(inp[k]) for k in ("k_cache", "v_cache", "k_idx_cache", "state")}
@@ -303,7 +333,6 @@ def bench_decode(args):
 
     ms = timed_loop(step, args.decode_steps, args.decode_warmup, copies)
     stages = stage_pass(step, max(copies, min(args.decode_steps, 45)), copies)
-    by = decode_bytes(cfg, inp["lengths"])
     stage_rows = {}
     for k, v in stages.items():
         b = by.get(k, 0)
@@ -314,8 +343,12 @@ def bench_decode(args):
     # (the select pass works on the scores already in the workspace)
     dom = max((k for k in stages if by.get(k)), key=stages.get)
     roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm", traffic_from_profiles(dom))
+    L = inp["lengths"]
+    ctx = (f"ctx=16384+1" if cid == 2 else
+           f"ragged ctx U[4096,32768]+1 (sum {int(L.sum())}, max {int(L.max())})")
+    shape = "qwen2.5-1.5b-shaped" if cid == 2 else "qwen2.5-7b-shaped"
     res = {
-        "workload": f"lisa_decode_step qwen2.5-1.5b-shaped B={B} ctx=16384+1 Hq={cfg.Hq} "
+        "workload": f"lisa_decode_step {shape} B={B} {ctx} Hq={cfg.Hq} "
                     f"Hkv={cfg.Hkv} d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} bf16",
         "tokens_per_s": B / (ms * 1e-3), "ms": ms, "roofline": roof, "stages": stage_rows,
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": by["total"],
@@ -449,15 +482,24 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=3)
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the 7B-shaped ragged decode batch (its kernels share names with the "
+                         "16K decode's, so counter runs leave it out)")
+    ap.add_argument("--kernel-stats", nargs=2, metavar=("DB", "OUT_MD"),
+                    help="write a per-kernel duration table from a rocprofv3 --kernel-trace "
+                         "database and exit")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
+    if args.kernel_stats:
+        kernel_stats_summary(*args.kernel_stats)
+        return
     if args.traffic_summary:
         cmd = ("cd /tmp && export TMPDIR=/tmp && for c in FETCH_SIZE WRITE_SIZE; do "
                "timeout -s KILL 180 rocprofv3 --pmc $c -d $REPO/gpurun_out/pmc_$c -o run -- "
                "python3 $REPO/bench.py --steps 2 --warmup 1 --decode-steps 9 --decode-warmup 1 "
-               "--bwd-steps 1 --no-cpu-baseline --copy-calibration; done; cd $REPO && python3 bench.py "
+               "--bwd-steps 1 --no-ragged --no-cpu-baseline --copy-calibration; done; cd $REPO && python3 bench.py "
                "--traffic-summary gpurun_out/pmc_FETCH_SIZE/run_results.db "
                "gpurun_out/pmc_WRITE_SIZE/run_results.db")
         data = traffic_summary(*args.traffic_summary, os.path.join(PROFILES, "traffic.json"),
@@ -478,6 +520,11 @@ def main():
     print(f"[bench] prefill {pre['ms']:.3f} ms/call, stages {pre['stages']}", file=sys.stderr, flush=True)
     dec = bench_decode(args)
     print(f"[bench] decode {dec['ms'] * 1e3:.1f} us/step, stages {dec['stages']}", file=sys.stderr, flush=True)
+    rag = None
+    if not args.no_ragged:
+        rag = bench_decode(args, cid=4)
+        print(f"[bench] ragged decode {rag['ms'] * 1e3:.1f} us/step, stages {rag['stages']}", file=sys.stderr,
+              flush=True)
     bwd = None
     if not args.no_backward:
         bwd = bench_backward(args, pre)
@@ -515,6 +562,12 @@ def main():
             "steps": args.decode_steps, "warmup": args.decode_warmup,
             "ms_per_step": round(dec["ms"], 5), "roofline": dec["roofline"],
             "step_roofline": dec["step_roofline"], "stages": dec["stages"], "cpu_baseline": cpu_d,
+        },
+        "decode_ragged": None if rag is None else {
+            "workload": rag["workload"], "value": round(rag["tokens_per_s"], 1), "unit": "tokens/s",
+            "steps": args.decode_steps, "warmup": args.decode_warmup,
+            "ms_per_step": round(rag["ms"], 5), "roofline": rag["roofline"],
+            "step_roofline": rag["step_roofline"], "stages": rag["stages"],
         },
         "backward": None if bwd is None else {
             "workload": bwd["workload"], "value": round(bwd["tokens_per_s"], 1), "unit": "tokens/s",
