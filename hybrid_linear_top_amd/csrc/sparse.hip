@@ -14,9 +14,10 @@
 //
 // The r heads are padded to the 16 columns of a 16x16x32 MFMA tile.  The M
 // selected slots are split over the NW waves of the work-group (32 slots per
-// step; prefill uses 4 waves per unit, decode up to 16 since it has few
-// units); the waves' partial (max, sum, O) are merged in LDS, then the gate
-// gamma = sigmoid(z) mixes o_sparse with o_lin and the result is stored.
+// step; prefill uses 4 waves per unit, decode 4 or 8, and 16 only for
+// M > 512, since it has few units); the waves' partial (max, sum, O) are
+// merged in LDS, then the gate gamma = sigmoid(z) mixes o_sparse with o_lin
+// and the result is stored.
 // Each step issues the gathered K fragment loads and the V row loads
 // together, so both gathers are in flight before the first MFMA.
 #include "common.hpp"
@@ -100,6 +101,35 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
     for (int kc = 0; kc < KC; ++kc) {
         if (col < r) qf[kc].load(qrows + (size_t)col * D + kc * 32 + grp * 8);
         else qf[kc].zero();
+    }
+
+    // The epilogue's gate logits and o_lin (thread t mixes elements
+    // t + j*NW*64 of the unit's r x D outputs), through descriptors that read
+    // zeros past the end.  Up to 8 waves they load now, in flight during the
+    // gathers instead of after the merge; the 16-wave variant has no
+    // registers to spare (1024 threads) and loads them in the epilogue.
+    constexpr int NPF = (16 * D + NW * 64 - 1) / (NW * 64);  // r <= 16
+    constexpr bool kEarly = NW <= 8;
+    float zv[NPF], linv[NPF];
+    constexpr uint32_t LB = DECODE ? 4u : Elt<T>::kBytes;  // o_lin is fp32 in decode
+    const rsrc_t lrs = make_rsrc(reinterpret_cast<const unsigned char *>(linp) + lin_off * LB,
+                                 (uint32_t)(r * D) * LB);
+    const rsrc_t zrs = make_rsrc(zp, (uint32_t)r * Elt<T>::kBytes);
+    auto load_epilogue = [&](int j) {
+        const uint32_t e = (uint32_t)(threadIdx.x + j * NW * 64);
+        const uint32_t hh = e / D;
+        if constexpr (Elt<T>::kBytes == 2)
+            zv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(zrs, hh * 2u, 0u, 0) << 16);
+        else
+            zv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zrs, hh * 4u, 0u, 0));
+        if constexpr (LB == 4)
+            linv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, e * 4u, 0u, 0));
+        else
+            linv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lrs, e * 2u, 0u, 0) << 16);
+    };
+    if constexpr (kEarly) {
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) load_epilogue(j);
     }
 
     f32x4 o[MB];
@@ -232,7 +262,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) wm[32 + col * (D + 1) + mb * 16 + grp * 4 + i] = o[mb][i];
     __syncthreads();
-    for (int e = threadIdx.x; e < r * D; e += NW * 64) {
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) {
+        const int e = threadIdx.x + j * NW * 64;
+        if (e >= r * D) break;
+        if constexpr (!kEarly) load_epilogue(j);
         const int hh = e / D, dim = e % D;
         float mx = -INFINITY;
 #pragma unroll
@@ -248,12 +282,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
             }
         }
         const float osp = den > 0.0f ? num / den : 0.0f;
-        const float z = Elt<T>::to_f32(zp[hh]);
-        const float gam = 1.0f / (1.0f + expf(-z));
-        float lin;
-        if (DECODE) lin = reinterpret_cast<const float *>(linp)[lin_off + e];
-        else lin = Elt<T>::to_f32(reinterpret_cast<const T *>(linp)[lin_off + e]);
-        outp[e] = Elt<T>::from_f32(gam * osp + (1.0f - gam) * lin);
+        const float gam = 1.0f / (1.0f + expf(-zv[j]));
+        outp[e] = Elt<T>::from_f32(gam * osp + (1.0f - gam) * linv[j]);
     }
 }
 
@@ -492,7 +522,7 @@ hipError_t dispatch_d(const SparseArgs &a, bool decode, hipStream_t s) {
             hipLaunchKernelGGL((sparse_gate_kernel<T, D, false, 4>), grid, dim3(256), 0, s, a);
     } else if (a.M <= 4 * kChunk) {
         hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 4>), grid, dim3(256), 0, s, a);
-    } else if (a.M <= 8 * kChunk) {
+    } else if (a.M <= 16 * kChunk) {
         hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
     } else if constexpr (sizeof(T) == 4 && D == 128) {  // 16 waves of fp32 rows exceed the LDS
         hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
