@@ -476,23 +476,25 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
     __shared__ uint32_t found[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bg = blockIdx.x, b = bg / G;
-    const int L = cache_len(map, b, max_ctx);
     const float *sc = scores + (size_t)bg * max_ctx;
+    // The score loads are issued first, before the sequence length is known:
+    // the row holds max_ctx entries (the descriptor reads zeros past them)
+    // and positions at or past L are masked below, so the loads need not
+    // wait for the length lookup.  All of them are unconditional and in
+    // flight together.  The launch guarantees NT * EPT >= max_ctx.
+    auto pos_of = [&](int k) { return k * NT + tid; };
+    const rsrc_t srs = make_rsrc(sc, (uint32_t)max_ctx * 4u);
+    uint32_t keyreg[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+        keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)pos_of(k) * 4u, 0u, 0);
+    const int L = cache_len(map, b, max_ctx);
+    auto valid = [&](int k) { return pos_of(k) < L; };
     int32_t *out = idx + (size_t)bg * M;
     if (L <= M) {
         for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
         return;
     }
-    // All loads are unconditional (positions past L read zeros through the
-    // descriptor), so they are in flight together.  The launch guarantees
-    // NT * EPT >= L.
-    auto pos_of = [&](int k) { return k * NT + tid; };
-    auto valid = [&](int k) { return pos_of(k) < L; };
-    const rsrc_t srs = make_rsrc(sc, (uint32_t)L * 4u);
-    uint32_t keyreg[EPT];
-#pragma unroll
-    for (int k = 0; k < EPT; ++k)
-        keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)pos_of(k) * 4u, 0u, 0);
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, tmax = 0u;
     bool active = false;  // this thread holds a key
 #pragma unroll

@@ -56,6 +56,22 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
     const int lu = xcd_remap(blockIdx.x, gridDim.x);
     const int G = a.G, r = a.r, M = a.M;
     const int u = DECODE ? lu : (lu % (a.B * a.n)) * G + lu / (a.B * a.n);
+    // The wave's slot range, and the selected positions of its first step,
+    // loaded before anything that waits on the sequence length (a descriptor
+    // over the unit's M entries; none for the window sets, which use no idx).
+    const int per_wave = ((M + NW - 1) / NW + kChunk - 1) / kChunk * kChunk;
+    const int s_begin = wave * per_wave, s_end = min(M, s_begin + per_wave);
+    // (the 16-wave variant, at its register limit, reads them in the loop)
+    constexpr bool kEarlyIdx = NW <= 8;
+    int32_t idx0[2] = {0, 0};
+    if constexpr (kEarlyIdx) {
+        const rsrc_t irs = make_rsrc(a.window ? a.q : (const void *)(a.idx + (size_t)u * M),
+                                     a.window ? 0u : (uint32_t)M * 4u);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            idx0[kb] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                irs, (uint32_t)(s_begin + kb * 16 + (lane & 15)) * 4u, 0u, 0);
+    }
 
     const T *qrows, *kbase, *vbase;
     int smax;    // largest valid key position of the unit (defensive bound on gathered rows)
@@ -138,8 +154,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     T *vs = reinterpret_cast<T *>(smem) + (size_t)wave * kChunk * VS;
-    const int per_wave = ((M + NW - 1) / NW + kChunk - 1) / kChunk * kChunk;
-    const int s_begin = wave * per_wave, s_end = min(M, s_begin + per_wave);
     const int s_stop = min(s_end, nvalid);
     // buffer descriptors over the unit's visible K and V rows: slots that are
     // padding or out of range read as zeros without a branch
@@ -156,7 +170,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int slot = cs + kb * 16 + col;
-            const int s = slot >= s_stop ? -1 : a.window ? max(0, smax - M + 1) + slot : idxp[slot];
+            const int s = slot >= s_stop ? -1
+                          : a.window ? max(0, smax - M + 1) + slot
+                                     : (kEarlyIdx && cs == s_begin ? idx0[kb] : idxp[slot]);
             const uint32_t rrow = DECODE && tb ? (uint32_t)cache_row(a.map, 0, tb, min(max(s, 0), max(smax, 0))) : (uint32_t)s;
             const uint32_t roff = (s >= 0 && s <= smax) ? rrow * row_bytes + grp * 8 * EB : kOffNone;
 #pragma unroll
