@@ -301,6 +301,13 @@ def bench_prefill(args):
     return res
 
 
+def rotating_copies(bytes_per_step):
+    """Input copies to rotate over so that the bytes read between repeats of
+    a copy add up to at least 3 x the 256 MB Infinity Cache (9 x ~96 MB for
+    the 16K decode, 2 x ~427 MB for the ragged batch); at least 2."""
+    return max(2, -(-3 * 256 * 2**20 // bytes_per_step))
+
+
 def bench_decode(args, cid=2):
     """The decode step of CONFIGS[cid]: 2 is the 16K Qwen2.5-1.5B-shaped batch
     of 16, 4 the Qwen2.5-7B-shaped ragged batch of 32 (contexts U[4096, 32768])."""
@@ -312,10 +319,7 @@ def bench_decode(args, cid=2):
     dims = lisa.dims_from_config(cfg)
     B = inp["B"]
     by = decode_bytes(cfg, inp["lengths"])
-    # input copies rotate so that their bytes read per step add up to at
-    # least 3 x the 256 MB Infinity Cache (9 x ~96 MB at 16K, 2 x ~427 MB
-    # for the ragged batch)
-    copies = max(2, -(-3 * 256 * 2**20 // by["total"]))
+    copies = rotating_copies(by["total"])
     cu = lisa.to_device(inp["cu_ctx"])
     shared = {k: lisa.to_device(inp[k]) for k in ("q", "q_idx", "w_idx", "gate")}
     per = [{k: lisa.to_device(inp[k]) for k in ("k_cache", "v_cache", "k_idx_cache", "state")}
