@@ -89,6 +89,20 @@ def test_prefill_config1_full():
     _say("  ", rep)
 
 
+def test_prefill_max_length_sampled_rows():
+    """n = 32768, the longest prefill (candidate indices are 16-bit): rows
+    near the end select among every position up to 32767."""
+    cfg = _pcfg(32768, 4, 2, 64, 2, 32, 256, seed=11)
+    _say("prefill", cfg.name, "(sampled rows, full state)")
+    inp = gen.make_prefill_inputs(cfg)
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 255, 256, 16383, 16384, 32700, 32766, 32767]
+                      + rng.integers(16384, cfg.n, size=12).tolist()))
+    rep = {}
+    parity.prefill_parity(cfg, inp, rows=rows, report=rep)
+    _say("  ", rep)
+
+
 def test_prefill_config3_sampled_rows():
     cfg = gen.CONFIGS[3]
     _say("prefill", cfg.name, "(sampled rows, full state)")
@@ -118,6 +132,7 @@ DECODE_SMALL = [
     # 17-keys-per-thread one's
     _dcfg(4, 1, 64, 4, 32, 512, [33792, 17409, 9000], seed=6),
     _dcfg(4, 2, 64, 2, 32, 64, [17409, 25000], seed=7),
+    _dcfg(2, 1, 64, 1, 32, 256, [65536, 100], seed=9),         # the longest decode context
 ]
 
 
@@ -173,8 +188,8 @@ def test_ties_lowest_index_wins():
         assert np.array_equal(didx[b, 0], exp) and np.array_equal(didx[b, 1], exp), b
 
 
-@pytest.mark.parametrize("lengths", [[8000, 300], [17000], [33792, 18000], [40000, 5]],
-                         ids=["ctx8000", "ctx17000", "ctx33792", "ctx40000"])
+@pytest.mark.parametrize("lengths", [[8000, 300], [17000], [33792, 18000], [40000, 5], [65536]],
+                         ids=["ctx8000", "ctx17000", "ctx33792", "ctx40000", "ctx65536"])
 def test_decode_ties_every_select_variant(lengths):
     """w = 0 at contexts that pick each top-M kernel variant: every score is
     exactly 0, so each set is the first min(M, L) positions."""
