@@ -13,6 +13,13 @@
 #include "lisa.h"
 #include "kernels.hpp"
 
+namespace lisa {
+DispatchEvents &dispatch_events() {
+    static thread_local DispatchEvents d;
+    return d;
+}
+}  // namespace lisa
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -147,18 +154,27 @@ struct Timing {
 Timing g_timing;
 
 // Launch through `fn`, bracketed by an event pair when timing is enabled.
+// The stage's launches carry the events (lisa::launch_kernel): a = the first
+// kernel's start, b = the last kernel's end.  A stage that launched nothing
+// records them as plain markers, so every pair completes.
 template <typename F>
 hipError_t timed(int stage, hipStream_t s, F fn) {
     if (!g_timing.enabled) return fn();
     std::lock_guard<std::mutex> lk(g_timing.mu);
     hipEvent_t a = g_timing.get(), b = g_timing.get();
     if (!a || !b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(a, s);
+    lisa::DispatchEvents &de = lisa::dispatch_events();
+    de = lisa::DispatchEvents{a, b, 0};
+    hipError_t e = fn();
+    const int launched = de.launches;
+    de = lisa::DispatchEvents{};
     if (e != hipSuccess) return e;
-    e = fn();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(b, s);
-    if (e != hipSuccess) return e;
+    if (launched == 0) {
+        e = hipEventRecord(a, s);
+        if (e != hipSuccess) return e;
+        e = hipEventRecord(b, s);
+        if (e != hipSuccess) return e;
+    }
     g_timing.pending.push_back({stage, a, b});
     return hipSuccess;
 }

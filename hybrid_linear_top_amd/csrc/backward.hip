@@ -852,19 +852,19 @@ __global__ __launch_bounds__(kWalkThreads) void sparse_bwd_walk_kernel(SparseBwd
 template <typename T>
 hipError_t prep_t(const BwdPrepArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d / 8;
-    hipLaunchKernelGGL((bwd_prep_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    launch_kernel((bwd_prep_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <typename T>
 hipError_t combine_t(const BwdCombineArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)a.B * a.n * a.Hq * a.d / 8;  // >= the dk / dv count / 8
-    hipLaunchKernelGGL((bwd_combine_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    launch_kernel((bwd_combine_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <typename T, int D>
 hipError_t sparse_t(const SparseBwdArgs &a, hipStream_t s) {
     const size_t lds = sparse_bwd_lds_bytes(a.r, a.M, D);
-    hipLaunchKernelGGL((sparse_bwd_kernel<T, D>), dim3((unsigned)((int64_t)a.B * a.n * a.G)), dim3(64), lds, s, a);
+    launch_kernel((sparse_bwd_kernel<T, D>), dim3((unsigned)((int64_t)a.B * a.n * a.G)), dim3(64), lds, s, a);
     return hipGetLastError();
 }
 
@@ -879,7 +879,7 @@ hipError_t launch_bwd_prep(const BwdPrepArgs &a, int dtype, hipStream_t s) {
 hipError_t launch_transpose_states(const float *src, float *dst, int64_t nmat, int d, hipStream_t s) {
     const int64_t total = nmat * d * d;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(transpose_states_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, src, dst, nmat, d);
+    launch_kernel(transpose_states_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, src, dst, nmat, d);
     return hipGetLastError();
 }
 hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s) {
@@ -908,9 +908,9 @@ size_t sparse_bwd_sorted_bytes(int B, int n, int G, int M) {
 
 template <int D>
 hipError_t launch_walk(const SparseBwdArgs &a, int Qb, int E, const uint32_t *sorted, dim3 grid, hipStream_t s) {
-    if (a.r <= 4) hipLaunchKernelGGL((sparse_bwd_walk_kernel<D, 4>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
-    else if (a.r <= 8) hipLaunchKernelGGL((sparse_bwd_walk_kernel<D, 8>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
-    else hipLaunchKernelGGL((sparse_bwd_walk_kernel<D, 16>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
+    if (a.r <= 4) launch_kernel((sparse_bwd_walk_kernel<D, 4>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
+    else if (a.r <= 8) launch_kernel((sparse_bwd_walk_kernel<D, 8>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
+    else launch_kernel((sparse_bwd_walk_kernel<D, 16>), grid, dim3(kWalkThreads), 0, s, a, Qb, E, sorted);
     return hipGetLastError();
 }
 
@@ -918,8 +918,8 @@ hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, int part, hipS
     if ((int64_t)a.B * a.n == 0) return hipSuccess;
     if (part == 0) {
         const dim3 grid((unsigned)((int64_t)a.B * a.n * a.G));
-        if (d == 128) hipLaunchKernelGGL((sparse_bwd_q_kernel<128>), grid, dim3(64), 0, s, a);
-        else hipLaunchKernelGGL((sparse_bwd_q_kernel<64>), grid, dim3(64), 0, s, a);
+        if (d == 128) launch_kernel((sparse_bwd_q_kernel<128>), grid, dim3(64), 0, s, a);
+        else launch_kernel((sparse_bwd_q_kernel<64>), grid, dim3(64), 0, s, a);
         return hipGetLastError();
     }
     if (sparse_bwd_key_block(a.r, a.M, d) == 0 || !a.sorted) return hipErrorInvalidValue;
@@ -931,12 +931,12 @@ hipError_t launch_sparse_bwd_split(const SparseBwdArgs &a, int d, int part, hipS
     int cur = 0;  // the buffer the last merge pass writes
     for (int L = Qs << lgMp; L < E; L *= 2) cur ^= 1;
     if (part == 1) {
-        hipLaunchKernelGGL(sparse_bwd_sort_kernel, dim3((unsigned)(nb * (kWalkBlock / Qs))), dim3(kSortThreads), 0,
+        launch_kernel(sparse_bwd_sort_kernel, dim3((unsigned)(nb * (kWalkBlock / Qs))), dim3(kSortThreads), 0,
                            s, a, Qs, lgMp, buf[0]);
         hipError_t e = hipGetLastError();
         int from = 0;
         for (int L = Qs << lgMp; e == hipSuccess && L < E; L *= 2, from ^= 1) {
-            hipLaunchKernelGGL(sparse_bwd_merge_kernel, dim3((unsigned)((total + kMergeTile - 1) / kMergeTile)),
+            launch_kernel(sparse_bwd_merge_kernel, dim3((unsigned)((total + kMergeTile - 1) / kMergeTile)),
                                dim3(256), 0, s, buf[from], buf[from ^ 1], L, total);
             e = hipGetLastError();
         }

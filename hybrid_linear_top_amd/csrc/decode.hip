@@ -790,7 +790,7 @@ template <typename T, int D, int DI, int HIPAD>
 hipError_t launch_ss(const DecodeScoreArgs &a, hipStream_t s) {
     const int n_state = a.B * a.Hq * (D / 32);  // column slices of every head's state
     const int n_score = a.B * a.tiles_per_seq;
-    hipLaunchKernelGGL((decode_score_state_kernel<T, D, DI, HIPAD>), dim3(n_state + n_score),
+    launch_kernel((decode_score_state_kernel<T, D, DI, HIPAD>), dim3(n_state + n_score),
                        dim3(256), 0, s, a, n_state);
     return hipGetLastError();
 }
@@ -817,13 +817,13 @@ hipError_t launch_decode_select(const float *scores, const CacheMap &cu, int B, 
     const dim3 grid(B * G);
 #define LISA_SEL(NT_, E)                                                                          \
     if (max_ctx <= (E) * (NT_)) {                                                                 \
-        hipLaunchKernelGGL((decode_select_kernel<NT_, E>), grid, dim3(NT_), 0, s, scores, cu, G, M, \
+        launch_kernel((decode_select_kernel<NT_, E>), grid, dim3(NT_), 0, s, scores, cu, G, M, \
                            max_ctx, idx);                                                         \
         return hipGetLastError();                                                                 \
     }
 #define LISA_TOPM(NT_, E, CAP_)                                                                   \
     if (max_ctx <= (E) * (NT_)) {                                                                 \
-        hipLaunchKernelGGL((decode_topm_kernel<NT_, E, CAP_>), grid, dim3(NT_), 0, s, scores, cu, G, \
+        launch_kernel((decode_topm_kernel<NT_, E, CAP_>), grid, dim3(NT_), 0, s, scores, cu, G, \
                            M, max_ctx, idx);                                                      \
         return hipGetLastError();                                                                 \
     }

@@ -624,7 +624,7 @@ hipError_t launch(const IndexerArgs &a, hipStream_t s) {
     constexpr int QB = LISA_IDX_QB;
     constexpr int QW = 4 * QB;
     const int nqb = (a.n + QW - 1) / QW;
-    hipLaunchKernelGGL((indexer_topm_kernel<T, DI, HH, CAP, QB>), dim3(a.B * a.G * nqb), dim3(64), 0, s, a);
+    launch_kernel((indexer_topm_kernel<T, DI, HH, CAP, QB>), dim3(a.B * a.G * nqb), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -652,8 +652,8 @@ hipError_t pack(const IndexerArgs &a, int dI, hipStream_t s) {
     const dim3 grid((unsigned)((total + 255) / 256));
     const T *src = reinterpret_cast<const T *>(a.k_idx);
     T *dst = reinterpret_cast<T *>(a.k_packed);
-    if (dI == 64) hipLaunchKernelGGL((pack_keys_kernel<T, 64>), grid, dim3(256), 0, s, src, dst, total, nk, a.G, ntiles);
-    else hipLaunchKernelGGL((pack_keys_kernel<T, 32>), grid, dim3(256), 0, s, src, dst, total, nk, a.G, ntiles);
+    if (dI == 64) launch_kernel((pack_keys_kernel<T, 64>), grid, dim3(256), 0, s, src, dst, total, nk, a.G, ntiles);
+    else launch_kernel((pack_keys_kernel<T, 32>), grid, dim3(256), 0, s, src, dst, total, nk, a.G, ntiles);
     return hipGetLastError();
 }
 

@@ -1,9 +1,36 @@
 // Launch interface between the C-ABI layer (api.hip) and the kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lisa {
+
+// ---- kernel launches ----------------------------------------------------------
+// Stage timing (lisa_stage_timing) attaches its events to the dispatches
+// themselves: while a stage is timed on this thread, the stage's first launch
+// carries the start event and every launch the stop event
+// (hipExtLaunchKernelGGL), so the pair brackets the kernels' own execution,
+// from the first one's start to the last one's end, not two marker packets
+// around them.  Otherwise launches are plain.
+struct DispatchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+    int launches = 0;
+};
+DispatchEvents &dispatch_events();  // this thread's (defined with the entry points)
+
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                          Args... args) {
+    DispatchEvents &de = dispatch_events();
+    if (de.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, de.launches == 0 ? de.start : nullptr, de.stop, 0u,
+                              static_cast<KArgs>(args)...);
+        ++de.launches;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, static_cast<KArgs>(args)...);
+    }
+}
 
 // ---- decode ---------------------------------------------------------------
 // Where position s of sequence b lives in a decode cache.  Packed caches

@@ -319,22 +319,22 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
 
 template <typename T, int D>
 hipError_t run_state(const LinearArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((chunk_state_kernel<T, D>), dim3(a.B * a.G * a.nC), dim3(256), 0, s, a);
+    launch_kernel((chunk_state_kernel<T, D>), dim3(a.B * a.G * a.nC), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <typename T, int D>
 hipError_t run_scan(const LinearArgs &a, hipStream_t s) {
     constexpr int BPG = (D * D / 4 + 255) / 256;
     if (a.per_head)
-        hipLaunchKernelGGL((prefix_scan_kernel<T, D, true>), dim3(a.B * a.G * BPG), dim3(256),
+        launch_kernel((prefix_scan_kernel<T, D, true>), dim3(a.B * a.G * BPG), dim3(256),
                            (size_t)a.r * 256 * sizeof(f32x4), s, a);
     else
-        hipLaunchKernelGGL((prefix_scan_kernel<T, D, false>), dim3(a.B * a.G * BPG), dim3(256), 0, s, a);
+        launch_kernel((prefix_scan_kernel<T, D, false>), dim3(a.B * a.G * BPG), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 template <typename T, int D>
 hipError_t run_output(const LinearArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((chunk_output_kernel<T, D>), dim3(a.B * a.G * a.nC), dim3(256), 0, s, a);
+    launch_kernel((chunk_output_kernel<T, D>), dim3(a.B * a.G * a.nC), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -533,17 +533,17 @@ hipError_t dispatch_d(const SparseArgs &a, bool decode, hipStream_t s) {
     const dim3 grid(a.units);
     if (!decode) {
         if constexpr (sizeof(T) == 2)
-            hipLaunchKernelGGL((sparse_prefill_wave_kernel<D>), grid, dim3(64), 0, s, a);
+            launch_kernel((sparse_prefill_wave_kernel<D>), grid, dim3(64), 0, s, a);
         else
-            hipLaunchKernelGGL((sparse_gate_kernel<T, D, false, 4>), grid, dim3(256), 0, s, a);
+            launch_kernel((sparse_gate_kernel<T, D, false, 4>), grid, dim3(256), 0, s, a);
     } else if (a.M <= 4 * kChunk) {
-        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 4>), grid, dim3(256), 0, s, a);
+        launch_kernel((sparse_gate_kernel<T, D, true, 4>), grid, dim3(256), 0, s, a);
     } else if (a.M <= 16 * kChunk) {
-        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
+        launch_kernel((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
     } else if constexpr (sizeof(T) == 4 && D == 128) {  // 16 waves of fp32 rows exceed the LDS
-        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
+        launch_kernel((sparse_gate_kernel<T, D, true, 8>), grid, dim3(512), 0, s, a);
     } else {
-        hipLaunchKernelGGL((sparse_gate_kernel<T, D, true, 16>), grid, dim3(1024), 0, s, a);
+        launch_kernel((sparse_gate_kernel<T, D, true, 16>), grid, dim3(1024), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -255,11 +255,15 @@ lisa_status lisa_decode_step_window(const lisa_dims *dims, int32_t B, const int6
 
 /*
  * Per-kernel timing, for benchmarking only.  While enabled (process-wide),
- * every kernel the entry points launch is bracketed by a pair of HIP events
- * recorded on the caller's stream; this adds host work per launch, so whole-
- * call timings should be taken with it disabled.  Stages, in order:
- * linear_chunk_state, linear_prefix_scan, linear_chunk_output, indexer_topm,
- * sparse_gate_prefill, decode_score_state, decode_select, sparse_gate_decode.
+ * each stage of an entry point is timed by a pair of HIP events attached to
+ * its kernel dispatches on the caller's stream (hipExtLaunchKernel): from the
+ * start of the stage's first kernel to the end of its last, so the figures
+ * are the kernels' own execution times.  This adds host work per launch, so
+ * whole-call timings should be taken with it disabled.  Stages, in order:
+ * linear_chunk_state, linear_prefix_scan, linear_chunk_output, indexer_pack,
+ * indexer_topm, sparse_gate_prefill, decode_score_state, decode_select,
+ * sparse_gate_decode, then the backward's bwd_operands, bwd_linear,
+ * bwd_combine, bwd_sparse, bwd_sparse_query, bwd_sparse_sort, bwd_sparse_keys.
  */
 lisa_status lisa_stage_timing(int32_t enable);
 
