@@ -397,24 +397,29 @@ __global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
 }
 
 // ---------------------------------------------------------------------------
-// One wave: the m-th largest of c 32-bit keys kr[e] (element e*64 + lane) by
-// four 8-bit radix passes over a 256-bin LDS histogram.  theta is that key;
-// take_eq is how many keys equal to theta belong to the top m (the earliest
-// elements, as ties go to the lower position).
+// One wave: the m-th largest of c 32-bit keys kr[e] (element e*64 + lane),
+// all of them in [lo, lo + 2^width), by radix passes of up to 8 bits over
+// key - lo from bit width - 1 down, with a 256-bin LDS histogram.  theta is
+// that key; take_eq is how many keys equal to theta belong to the top m (the
+// earliest elements, as ties go to the lower position).  Passing the live
+// range skips the high bits every key shares (and the pile-up of all keys in
+// one bin that those passes cause).
 template <int NE>
-__device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32_t *hist,
-                             uint32_t &theta, uint32_t &take_eq) {
+__device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32_t *hist, uint32_t lo,
+                             int width, uint32_t &theta, uint32_t &take_eq) {
     const int lane = threadIdx.x & 63;
-    uint32_t prefix = 0u, need = m;
+    uint32_t prefix = 0u, need = m;  // prefix: the bits of key - lo above `top`
 #pragma unroll 1
-    for (int p = 0; p < 4; ++p) {
-        const int sh = 24 - 8 * p;
+    for (int top = width; top > 0; top -= 8) {
+        const int sh = top > 8 ? top - 8 : 0;
+        const uint32_t digit_mask = (1u << (top - sh)) - 1u;
         *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
 #pragma unroll
         for (int k = 0; k < NE; ++k) {
-            const bool live = k * 64 + lane < c && (p == 0 || (kr[k] >> (sh + 8)) == prefix);
-            if (live) atomicAdd(&hist[(kr[k] >> sh) & 255u], 1u);
+            const uint32_t x = kr[k] - lo;
+            const bool live = k * 64 + lane < c && (top >= 32 || (x >> top) == prefix);
+            if (live) atomicAdd(&hist[(x >> sh) & digit_mask], 1u);
         }
         wave_lds_sync();
         const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
@@ -435,11 +440,11 @@ __device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32
         const int src = __ffsll((unsigned long long)__ballot(fb >= 0)) - 1;
         fb = __builtin_amdgcn_readlane(fb, src);
         fneed = (uint32_t)__builtin_amdgcn_readlane((int)fneed, src);
-        prefix = (prefix << 8) | (uint32_t)fb;
+        prefix = (prefix << (top - sh)) | (uint32_t)fb;
         need = fneed;
         wave_lds_sync();
     }
-    theta = prefix;
+    theta = lo + prefix;
     take_eq = need;
 }
 
@@ -608,7 +613,10 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
 #pragma unroll
             for (int e = 0; e < NE; ++e) kr[e] = e * 64 + lane < (int)C ? fkey[e * 64 + lane] : 0u;
             uint32_t theta, take_eq;
-            wave_kth_u32<NE>(kr, (int)C, (uint32_t)M, hist, theta, take_eq);
+            // every packed key lies in [T, hi]
+            const uint32_t span_c = hi - T;
+            wave_kth_u32<NE>(kr, (int)C, (uint32_t)M, hist, T, span_c == 0 ? 0 : 32 - __builtin_clz(span_c),
+                             theta, take_eq);
             uint32_t base = 0, eq_seen = 0;
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
