@@ -165,7 +165,8 @@ def traffic_summary(fetch_db, write_db, out_json, out_md, command):
         json.dump(data, f, indent=1)
     with open(out_md, "w") as f:
         f.write("# HBM traffic per launch: 16K prefill, 16K decode step, 16K backward\n\n")
-        f.write("rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in a pass of its own:\n\n")
+        f.write("rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in a pass of its own "
+                "(REPO is the repository root, OUT any scratch folder):\n\n")
         f.write("```\n" + command + "\n```\n\n")
         f.write(f"Scale factors from the 1 GiB device copy: FETCH_SIZE x {ff:.3f}, "
                 f"WRITE_SIZE x {wf:.3f}.\n\n")
@@ -188,10 +189,10 @@ def kernel_stats_summary(db, out_md):
     with open(out_md, "w") as f:
         f.write("# Kernel durations: 16K prefill (Qwen2.5-7B-shaped), 16K decode step (Qwen2.5-1.5B-shaped), "
                 "7B-shaped ragged decode step, 16K backward (7B-shaped)\n\n")
-        f.write("Command (run from the repository root on one MI355X):\n\n```\n"
-                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_stats "
+        f.write("Command (on one MI355X; REPO is the repository root, OUT any scratch folder):\n\n```\n"
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/prof_stats "
                 "-o run -- python3 $REPO/bench.py\ncd $REPO && python3 bench.py --kernel-stats "
-                "gpurun_out/prof_stats/run_results.db profiles/kernel_stats_prefill16k_decode16k.md\n```\n\n")
+                "$OUT/prof_stats/run_results.db profiles/kernel_stats_prefill16k_decode16k.md\n```\n\n")
         f.write("rocprofv3 kernel-trace durations in microseconds, one row per kernel and launch grid "
                 "(grid_x in work-items):\n\n")
         f.write("| kernel | grid_x | calls | total us | average us | % |\n|---|---|---|---|---|---|\n")
@@ -257,7 +258,7 @@ def bench_prefill(args):
     import numpy as np
     import torch
     from hybrid_linear_top_amd import inputs as gen, lisa
-    cfg = gen.CONFIGS[3]
+    cfg = gen.PREFILL_7B_16K
     inp = gen.make_prefill_inputs(cfg)
     dims = lisa.dims_from_config(cfg)
     B, n = inp["B"], inp["n"]
@@ -308,13 +309,13 @@ def rotating_copies(bytes_per_step):
     return max(2, -(-3 * 256 * 2**20 // bytes_per_step))
 
 
-def bench_decode(args, cid=2):
-    """The decode step of CONFIGS[cid]: 2 is the 16K Qwen2.5-1.5B-shaped batch
-    of 16, 4 the Qwen2.5-7B-shaped ragged batch of 32 (contexts U[4096, 32768])."""
+def bench_decode(args, ragged=False):
+    """One decode step: the 16K Qwen2.5-1.5B-shaped batch of 16, or (ragged)
+    the Qwen2.5-7B-shaped batch of 32 with contexts U[4096, 32768]."""
     import numpy as np
     import torch
     from hybrid_linear_top_amd import inputs as gen, lisa
-    cfg = gen.CONFIGS[cid]
+    cfg = gen.DECODE_7B_RAGGED if ragged else gen.DECODE_1P5B_16K
     inp = gen.make_decode_inputs(cfg)
     dims = lisa.dims_from_config(cfg)
     B = inp["B"]
@@ -348,9 +349,9 @@ def bench_decode(args, cid=2):
     dom = max((k for k in stages if by.get(k)), key=stages.get)
     roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm", traffic_from_profiles(dom))
     L = inp["lengths"]
-    ctx = (f"ctx=16384+1" if cid == 2 else
+    ctx = (f"ctx=16384+1" if not ragged else
            f"ragged ctx U[4096,32768]+1 (sum {int(L.sum())}, max {int(L.max())})")
-    shape = "qwen2.5-1.5b-shaped" if cid == 2 else "qwen2.5-7b-shaped"
+    shape = "qwen2.5-7b-shaped" if ragged else "qwen2.5-1.5b-shaped"
     res = {
         "workload": f"lisa_decode_step {shape} B={B} {ctx} Hq={cfg.Hq} "
                     f"Hkv={cfg.Hkv} d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} bf16",
@@ -501,11 +502,11 @@ def main():
         return
     if args.traffic_summary:
         cmd = ("cd /tmp && export TMPDIR=/tmp && for c in FETCH_SIZE WRITE_SIZE; do "
-               "timeout -s KILL 180 rocprofv3 --pmc $c -d $REPO/gpurun_out/pmc_$c -o run -- "
+               "timeout -s KILL 180 rocprofv3 --pmc $c -d $OUT/pmc_$c -o run -- "
                "python3 $REPO/bench.py --steps 2 --warmup 1 --decode-steps 9 --decode-warmup 1 "
                "--bwd-steps 1 --no-ragged --no-cpu-baseline --copy-calibration; done; cd $REPO && python3 bench.py "
-               "--traffic-summary gpurun_out/pmc_FETCH_SIZE/run_results.db "
-               "gpurun_out/pmc_WRITE_SIZE/run_results.db")
+               "--traffic-summary $OUT/pmc_FETCH_SIZE/run_results.db "
+               "$OUT/pmc_WRITE_SIZE/run_results.db")
         data = traffic_summary(*args.traffic_summary, os.path.join(PROFILES, "traffic.json"),
                                os.path.join(PROFILES, "hbm_traffic_prefill16k_decode16k.md"), cmd)
         print(json.dumps(data, indent=1))
@@ -526,7 +527,7 @@ def main():
     print(f"[bench] decode {dec['ms'] * 1e3:.1f} us/step, stages {dec['stages']}", file=sys.stderr, flush=True)
     rag = None
     if not args.no_ragged:
-        rag = bench_decode(args, cid=4)
+        rag = bench_decode(args, ragged=True)
         print(f"[bench] ragged decode {rag['ms'] * 1e3:.1f} us/step, stages {rag['stages']}", file=sys.stderr,
               flush=True)
     bwd = None

@@ -55,22 +55,22 @@ class LayerConfig:
         return DT_BF16 if self.dtype == "bf16" else DT_F32
 
 
-# The five workloads.  0: tiny fp32 correctness case; 1: Qwen2.5-1.5B-shaped
-# prefill at 4K; 2: 1.5B-shaped decode at 16K context; 3: Qwen2.5-7B-shaped
-# prefill at 16K; 4: 7B-shaped ragged decode, 4K..32K context, M = 512.
-CONFIGS: dict[int, LayerConfig] = {
-    0: LayerConfig("tiny_fp32_prefill_n512", "prefill", "f32", B=1, n=512, Hq=1, Hkv=1,
-                   d=64, HI=4, dI=32, M=64, chunk=64, seed=1000),
-    1: LayerConfig("qwen2.5-1.5b_prefill_n4096", "prefill", "bf16", B=1, n=4096, Hq=12,
-                   Hkv=2, d=128, HI=4, dI=64, M=256, chunk=64, seed=1001),
-    2: LayerConfig("qwen2.5-1.5b_decode_b16_ctx16k", "decode", "bf16", B=16, ctx=16384,
-                   Hq=12, Hkv=2, d=128, HI=4, dI=64, M=256, seed=1002),
-    3: LayerConfig("qwen2.5-7b_prefill_n16384", "prefill", "bf16", B=1, n=16384, Hq=28,
-                   Hkv=4, d=128, HI=4, dI=64, M=256, chunk=64, seed=1003),
-    4: LayerConfig("qwen2.5-7b_ragged_decode_b32_ctx4k-32k", "decode", "bf16", B=32,
-                   ctx_lo=4096, ctx_hi=32768, Hq=28, Hkv=4, d=128, HI=4, dI=64, M=512,
-                   seed=1004),
-}
+# The five workloads: a tiny fp32 correctness case; Qwen2.5-1.5B-shaped
+# prefill at 4K; 1.5B-shaped decode at 16K context; Qwen2.5-7B-shaped
+# prefill at 16K; 7B-shaped ragged decode, 4K..32K context, M = 512.
+TINY_F32_PREFILL = LayerConfig("tiny_fp32_prefill_n512", "prefill", "f32", B=1, n=512, Hq=1, Hkv=1,
+                               d=64, HI=4, dI=32, M=64, chunk=64, seed=1000)
+PREFILL_1P5B_4K = LayerConfig("qwen2.5-1.5b_prefill_n4096", "prefill", "bf16", B=1, n=4096, Hq=12,
+                              Hkv=2, d=128, HI=4, dI=64, M=256, chunk=64, seed=1001)
+DECODE_1P5B_16K = LayerConfig("qwen2.5-1.5b_decode_b16_ctx16k", "decode", "bf16", B=16, ctx=16384,
+                              Hq=12, Hkv=2, d=128, HI=4, dI=64, M=256, seed=1002)
+PREFILL_7B_16K = LayerConfig("qwen2.5-7b_prefill_n16384", "prefill", "bf16", B=1, n=16384, Hq=28,
+                             Hkv=4, d=128, HI=4, dI=64, M=256, chunk=64, seed=1003)
+DECODE_7B_RAGGED = LayerConfig("qwen2.5-7b_ragged_decode_b32_ctx4k-32k", "decode", "bf16", B=32,
+                               ctx_lo=4096, ctx_hi=32768, Hq=28, Hkv=4, d=128, HI=4, dI=64, M=512,
+                               seed=1004)
+WORKLOADS: dict[str, LayerConfig] = {c.name: c for c in (
+    TINY_F32_PREFILL, PREFILL_1P5B_4K, DECODE_1P5B_16K, PREFILL_7B_16K, DECODE_7B_RAGGED)}
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -26,7 +26,7 @@ def test_pair_counts_brute_force(n, M):
 
 
 def test_prefill_flops_16k_7b():
-    cfg = gen.CONFIGS[3]
+    cfg = gen.PREFILL_7B_16K
     f = bench.prefill_flops(cfg, cfg.n, 1)
     n, G, Hq, d, M, C = cfg.n, cfg.Hkv, cfg.Hq, cfg.d, cfg.M, cfg.chunk
     # indexer: 2 flops per multiply-add, H_I heads of d_I per (group, causal pair)
@@ -44,7 +44,7 @@ def test_prefill_flops_16k_7b():
 
 
 def test_decode_bytes_16k_and_ragged():
-    cfg = gen.CONFIGS[2]
+    cfg = gen.DECODE_1P5B_16K
     L = np.full(16, 16385)
     by = bench.decode_bytes(cfg, L)
     assert by["kI"] == 16 * 16385 * cfg.Hkv * cfg.dI * 2
@@ -53,7 +53,7 @@ def test_decode_bytes_16k_and_ragged():
     assert by["total"] == by["kI"] + by["kv_rows"] + by["state"] + by["small"]
     assert abs(by["total"] - 96.6e6) / 96.6e6 < 2e-3
     # the ragged batch: K/V rows are min(M, L_b) per sequence and group
-    cfg4 = gen.CONFIGS[4]
+    cfg4 = gen.DECODE_7B_RAGGED
     L4 = np.array([100, 600, 5000])
     by4 = bench.decode_bytes(cfg4, L4)
     assert by4["kv_rows"] == (100 + 512 + 512) * cfg4.Hkv * 2 * cfg4.d * 2
@@ -61,7 +61,7 @@ def test_decode_bytes_16k_and_ragged():
 
 
 def test_backward_flops_per_pair():
-    cfg = gen.CONFIGS[3]
+    cfg = gen.PREFILL_7B_16K
     fl = bench.backward_flops(cfg, cfg.n, 1)
     P = bench.pairs(cfg.n, cfg.M)
     assert fl["bwd_sparse_query"] == 6 * cfg.d * cfg.Hq * P
@@ -92,8 +92,7 @@ def test_kernel_stats_rows_per_grid(tmp_path):
 def test_rotating_copies_exceed_the_infinity_cache():
     # the decode benchmark rotates enough input copies that their bytes read
     # between repeats are at least 3 x 256 MB
-    for cid, expect in ((2, 9), (4, 2)):
-        cfg = gen.CONFIGS[cid]
+    for cfg, expect in ((gen.DECODE_1P5B_16K, 9), (gen.DECODE_7B_RAGGED, 2)):
         total = bench.decode_bytes(cfg, gen.decode_lengths(cfg))["total"]
         copies = bench.rotating_copies(total)
         assert copies * total >= 3 * 256 * 2 ** 20

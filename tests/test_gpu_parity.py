@@ -72,7 +72,7 @@ def test_prefill_with_initial_state():
 
 
 def test_prefill_config0_tiny_fp32():
-    cfg = gen.CONFIGS[0]
+    cfg = gen.TINY_F32_PREFILL
     _say("prefill", cfg.name)
     inp = gen.make_prefill_inputs(cfg)
     rep = {}
@@ -81,7 +81,7 @@ def test_prefill_config0_tiny_fp32():
 
 
 def test_prefill_config1_full():
-    cfg = gen.CONFIGS[1]
+    cfg = gen.PREFILL_1P5B_4K
     _say("prefill", cfg.name)
     inp = gen.make_prefill_inputs(cfg)
     rep = {}
@@ -104,7 +104,7 @@ def test_prefill_max_length_sampled_rows():
 
 
 def test_prefill_config3_sampled_rows():
-    cfg = gen.CONFIGS[3]
+    cfg = gen.PREFILL_7B_16K
     _say("prefill", cfg.name, "(sampled rows, full state)")
     inp = gen.make_prefill_inputs(cfg)
     rng = np.random.default_rng(3)
@@ -146,9 +146,8 @@ def test_decode_small(case):
     _say("  ", rep)
 
 
-@pytest.mark.parametrize("cid", [2, 4])
-def test_decode_configs(cid):
-    cfg = gen.CONFIGS[cid]
+@pytest.mark.parametrize("cfg", [gen.DECODE_1P5B_16K, gen.DECODE_7B_RAGGED], ids=lambda c: c.name)
+def test_decode_configs(cfg):
     _say("decode", cfg.name)
     inp = gen.make_decode_inputs(cfg)
     rep = {}
@@ -309,14 +308,14 @@ def test_decode_paged(case):
 
 
 def test_deterministic():
-    cfg = gen.CONFIGS[1]
+    cfg = gen.PREFILL_1P5B_4K
     _say("determinism", cfg.name)
     inp = gen.make_prefill_inputs(cfg)
     a = parity.run_prefill(cfg, inp)
     b = parity.run_prefill(cfg, inp)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
-    dcfg = gen.CONFIGS[2]
+    dcfg = gen.DECODE_1P5B_16K
     _say("determinism", dcfg.name)
     dinp = gen.make_decode_inputs(dcfg, B=4)
     a = parity.run_decode(dcfg, dinp)
@@ -368,7 +367,7 @@ def test_prefill_backward_16k_sampled():
     """The backward at the benchmark's 16K, 7B-shaped workload and launch
     configuration: dq, dz at sampled query rows and dk, dv at sampled keys
     (the first, the last, both sides of the t = M boundary, mid-sequence)."""
-    cfg = gen.CONFIGS[3]
+    cfg = gen.PREFILL_7B_16K
     _say("backward 16K sampled", cfg.name)
     inp = gen.make_prefill_inputs(cfg)
     binp = gen.make_backward_inputs(cfg)
