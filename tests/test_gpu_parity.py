@@ -515,6 +515,53 @@ def test_decode_paged_random_shapes(case):
     _say("  ", rep)
 
 
+def test_stage_timing_changes_nothing():
+    """With stage timing on, the kernels launch through hipExtLaunchKernel with
+    events attached: prefill, decode and backward must give the same outputs
+    as with it off (bit for bit; dk and dv, summed with fp32 atomics, to
+    rounding), and every stage must report positive, finite times."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    cfg = _pcfg(700, 8, 2, 128, 4, 64, 256, seed=12)
+    dcfg, L = _dcfg(12, 2, 128, 4, 64, 256, [3000, 20000, 100], seed=12)
+    inp = gen.make_prefill_inputs(cfg)
+    dinp = gen.make_decode_inputs(dcfg, lengths=L)
+    binp = gen.make_backward_inputs(cfg)
+    dims = lisa.dims_from_config(cfg)
+    dv_ = lisa.to_device
+
+    def run_all():
+        pre = parity.run_prefill(cfg, inp, state_in=binp["state_in"])
+        dec = parity.run_decode(dcfg, dinp)
+        g = lisa.prefill_backward(dims, dv_(inp["q"]), dv_(inp["k"]), dv_(inp["v"]), dv_(inp["gate"]),
+                                  dv_(pre[2]), dv_(binp["d_out"]), state_in=dv_(binp["state_in"]),
+                                  d_state_out=dv_(binp["d_state_out"]), want_state_grad=True)
+        torch.cuda.synchronize()
+        return list(pre) + list(dec) + [lisa.from_device(x) for x in g]
+
+    _say("stage timing off/on", cfg.name, dcfg.name)
+    ref = run_all()
+    lisa.lisa_stage_timing_read(reset=True)
+    lisa.lisa_stage_timing(True)
+    try:
+        got = run_all()
+    finally:
+        lisa.lisa_stage_timing(False)
+    stages = lisa.lisa_stage_timing_read(reset=True)
+    names = ["prefill out", "prefill state", "prefill idx", "decode out", "decode state", "decode idx",
+             "dq", "dk", "dv", "dz", "d_state_in"]
+    for nm, a, b in zip(names, ref, got):
+        if nm in ("dk", "dv"):
+            assert parity.normwise(b.astype(np.float64), a.astype(np.float64)) < 1e-6, nm
+        else:
+            assert np.array_equal(a, b), nm
+    for st in ("indexer_topm", "sparse_gate_prefill", "linear_chunk_output", "decode_score_state",
+               "decode_select", "sparse_gate_decode", "bwd_sparse_query", "bwd_sparse_keys", "bwd_linear"):
+        n, ms = stages[st]
+        assert n >= 1 and np.isfinite(ms) and ms > 0.0, (st, n, ms)
+    _say("  ", {k: round(v[1], 4) for k, v in stages.items()})
+
+
 def test_graph_replay():
     """A serving loop captures the calls in a HIP graph: the library enqueues
     only kernels on the caller's stream (no allocation, memset or sync), so a
