@@ -49,6 +49,10 @@ class LisaError(RuntimeError):
 def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m hybrid_linear_top_amd.build`")
+    # torch carries its own HIP and HSA runtimes; they must be in the process
+    # before the library's ROCm ones.  Loaded the other way round (library
+    # first, torch later), the library's launches found no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, sz, i32, i64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p
     dp = ctypes.POINTER(LisaDims)
