@@ -77,6 +77,61 @@ lisa_status check_dims(const lisa_dims *d, bool prefill, bool window = false) {
     return LISA_OK;
 }
 
+// Every kernel addresses a sequence's rows through buffer descriptors whose
+// byte extent is a 32-bit field, and every launch counts its threads in 32
+// bits.  Shapes whose spans do not fit are refused here, before any HIP call
+// (they would otherwise wrap and read zeros past the wrapped extent).
+constexpr int64_t kSpan32 = 0xFFFFFFFFll;
+constexpr int64_t kMaxUnitThreads = 1024;  // the largest work-group one unit gets
+
+// (products in 128 bits: the arguments are unvalidated 32-bit counts whose
+// products can pass 2^63)
+using wide_t = __int128;
+
+lisa_status check_spans(const lisa_dims *d, int64_t B, int64_t units, int64_t kv_rows, bool indexer) {
+    const wide_t G = d->num_kv_heads, eb = elt_bytes(d->dtype);
+    const wide_t kv_span = (wide_t)kv_rows * G * d->head_dim * eb;
+    if (kv_span > kSpan32)
+        return fail(LISA_ERR_UNSUPPORTED,
+                    "%lld K/V rows of %d groups span %.4g bytes: a buffer descriptor holds at most %lld",
+                    (long long)kv_rows, d->num_kv_heads, (double)kv_span, (long long)kSpan32);
+    const wide_t idx_span = (wide_t)kv_rows * G * d->idx_dim * eb;
+    if (indexer && idx_span > kSpan32)
+        return fail(LISA_ERR_UNSUPPORTED, "%lld indexer-key rows span %.4g bytes: at most %lld",
+                    (long long)kv_rows, (double)idx_span, (long long)kSpan32);
+    if ((wide_t)B * units * kMaxUnitThreads > kSpan32)
+        return fail(LISA_ERR_UNSUPPORTED, "%.4g (sequence, position, group) units: at most %lld per call",
+                    (double)((wide_t)B * units), (long long)(kSpan32 / kMaxUnitThreads));
+    return LISA_OK;
+}
+
+// decode: kv_rows is max_ctx for packed caches (a sequence's rows) or the
+// page pool's rows; the score scan launches a 256-thread work-group per 128
+// positions of every sequence
+lisa_status check_decode_spans(const lisa_dims *d, int64_t B, int64_t max_ctx, int64_t kv_rows) {
+    lisa_status st = check_spans(d, B, d->num_kv_heads, kv_rows, true);
+    if (st) return st;
+    if (B * ((max_ctx + 127) / 128) * 256 > kSpan32)
+        return fail(LISA_ERR_UNSUPPORTED, "B=%lld sequences of max_ctx=%lld: the score launch exceeds 2^32 threads",
+                    (long long)B, (long long)max_ctx);
+    return LISA_OK;
+}
+
+// backward: besides the forward's spans, the key side reads a block of 256
+// positions' per-slot coefficients (8 bytes per slot and query head) and
+// their q / d_out rows through one descriptor each
+lisa_status check_bwd_spans(const lisa_dims *d, int64_t B, int64_t n) {
+    lisa_status st = check_spans(d, B, n * d->num_kv_heads, n, false);
+    if (st) return st;
+    const int64_t coef = 256ll * d->num_q_heads * d->top_m * 8;
+    if (coef > kSpan32)
+        return fail(LISA_ERR_UNSUPPORTED, "%d query heads x top_m %d: a 256-position coefficient block spans %lld bytes",
+                    d->num_q_heads, d->top_m, (long long)coef);
+    if (256ll * d->num_q_heads * d->head_dim * 4 > kSpan32)
+        return fail(LISA_ERR_UNSUPPORTED, "%d query heads: a 256-position row block exceeds 4 GiB", d->num_q_heads);
+    return LISA_OK;
+}
+
 float scale_log2(const lisa_dims *d) {
     const double s = d->softmax_scale > 0.0f ? (double)d->softmax_scale : 1.0 / std::sqrt((double)d->head_dim);
     return (float)(s * 1.4426950408889634);
@@ -214,6 +269,7 @@ lisa_status lisa_prefill_workspace_bytes(const lisa_dims *dims, int32_t B, int32
     if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
     if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
+    if ((st = check_spans(dims, B, (int64_t)n * dims->num_kv_heads, n, false))) return st;
     *bytes = prefill_ws(dims, B, n, n).total;
     return ok();
 }
@@ -227,6 +283,7 @@ lisa_status lisa_prefill_continue_workspace_bytes(const lisa_dims *dims, int32_t
         return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, past=%d, n=%d must be >= 0", B, past, n);
     if ((int64_t)past + n > 32768)
         return fail(LISA_ERR_UNSUPPORTED, "past + n = %lld above the supported 32768", (long long)past + n);
+    if ((st = check_spans(dims, B, (int64_t)n * dims->num_kv_heads, (int64_t)past + n, false))) return st;
     *bytes = prefill_ws(dims, B, n, past + n).total;
     return ok();
 }
@@ -240,6 +297,7 @@ lisa_status lisa_decode_workspace_bytes(const lisa_dims *dims, int32_t B, int32_
         return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0 and max_ctx=%d >= 1", B, max_ctx);
     if (max_ctx > kMaxDecodeCtx)
         return fail(LISA_ERR_UNSUPPORTED, "max_ctx=%d above the supported %d", max_ctx, kMaxDecodeCtx);
+    if ((st = check_decode_spans(dims, B, max_ctx, max_ctx))) return st;
     *bytes = decode_ws(dims, B, max_ctx).total;
     return ok();
 }
@@ -272,6 +330,7 @@ lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t
     if ((int64_t)past + n > 32768)
         return fail(LISA_ERR_UNSUPPORTED, "past + n = %lld above the supported 32768",
                     (long long)past + n);
+    if ((st = check_spans(dims, B, (int64_t)n * dims->num_kv_heads, (int64_t)past + n, false))) return st;
     if (B == 0 || n == 0) return ok();
     LISA_NEED(q, "q");
     LISA_NEED(k, "k");
@@ -380,6 +439,7 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     if (max_ctx < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "max_ctx=%d must be >= 1", max_ctx);
     if (max_ctx > kMaxDecodeCtx)
         return fail(LISA_ERR_UNSUPPORTED, "max_ctx=%d above the supported %d", max_ctx, kMaxDecodeCtx);
+    if ((st = check_decode_spans(dims, B, max_ctx, paged ? pool_rows : max_ctx))) return st;
     if (B == 0) return ok();
     if (!paged) {
         if (!cu_ctx) return fail(LISA_ERR_INVALID_ARGUMENT, "cu_ctx is NULL");
@@ -518,9 +578,10 @@ lisa_status lisa_decode_step_paged(const lisa_dims *dims, int32_t B, const int32
                     block_size, max_ctx);
     if (num_pages < 1) return fail(LISA_ERR_INVALID_ARGUMENT, "num_pages=%d must be >= 1", num_pages);
     const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim * (dims->dtype == LISA_BF16 ? 2 : 4);
-    if ((int64_t)num_pages * block_size * row_bytes >= ((int64_t)1 << 31))
-        return fail(LISA_ERR_UNSUPPORTED, "K/V page pool of %lld bytes: at most 2 GiB is supported",
-                    (long long)num_pages * block_size * row_bytes);
+    const wide_t pool_bytes = (wide_t)num_pages * block_size * row_bytes;
+    if (pool_bytes >= ((wide_t)1 << 31))
+        return fail(LISA_ERR_UNSUPPORTED, "K/V page pool of %.4g bytes: at most 2 GiB is supported",
+                    (double)pool_bytes);
     lisa::CacheMap map{};
     map.table = block_table;
     map.lengths = lengths;
@@ -617,6 +678,7 @@ lisa_status lisa_prefill_backward_workspace_bytes(const lisa_dims *dims, int32_t
     if (!bytes) return fail(LISA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (B < 0 || n < 0) return fail(LISA_ERR_INVALID_ARGUMENT, "B=%d, n=%d must be >= 0", B, n);
     if (n > 32768) return fail(LISA_ERR_UNSUPPORTED, "n=%d above the supported 32768", n);
+    if ((st = check_bwd_spans(dims, B, n))) return st;
     *bytes = bwd_ws(dims, B, n).total;
     return ok();
 }
@@ -636,6 +698,7 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
         return fail(LISA_ERR_UNSUPPORTED, "%d query heads per group: the backward handles up to 16", Hq / G);
     if (dims->dtype != LISA_BF16 && lisa::sparse_bwd_lds_bytes(Hq / G, M, D) > 65536)
         return fail(LISA_ERR_UNSUPPORTED, "top_m %d with %d heads per group exceeds the backward's LDS", M, Hq / G);
+    if ((st = check_bwd_spans(dims, B, n))) return st;
     if ((int64_t)B * n == 0) return ok();
     LISA_NEED(q, "q");
     LISA_NEED(k, "k");

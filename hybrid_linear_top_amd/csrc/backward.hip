@@ -556,8 +556,12 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
 
 // Key side, step 1: the entries of each walk block of Qw = 256 consecutive
 // positions of one group, sorted by key.  An entry is
-// key << 17 | position-in-block << 9 | slot; 0xFFFFFFFF marks no entry and
-// sorts last.  sparse_bwd_sort_kernel sorts Qs = min(Qw, 32768 / Mp)
+// key << 17 | position-in-block << 9 | slot (key <= 32767, position < 256,
+// slot < 512: the fields fill the word).  kNoEntry marks no entry: key 32767
+// with block position 0, which no real entry can be (a key is at most its
+// position t = t0 + position, and a block's first position t0 is a multiple of
+// 256, at most 32512).  Where kNoEntry sorts does not matter: the walk skips
+// it without ending the key run it is in.  sparse_bwd_sort_kernel sorts Qs = min(Qw, 32768 / Mp)
 // positions in LDS (Mp = M rounded up to a power of two): each position's
 // run of Mp entries is already ascending, so the runs are merged pairwise,
 // level by level, in place (each thread computes its outputs of a level by
@@ -566,7 +570,8 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
 // covers Qw positions.
 constexpr int kSortThreads = 1024;
 constexpr int kSortMaxEntries = 32768;  // 128 KB of LDS
-constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
+constexpr uint32_t kNoEntry = 0x7FFFu << 17;
+constexpr uint32_t kUsedUp = 0xFFFFFFFFu;  // merge placeholder for a used-up run (never compared)
 
 constexpr int kWalkBlock = 256;  // Qw
 constexpr int kSortPer = kSortMaxEntries / kSortThreads;  // outputs per thread and level at most
@@ -634,7 +639,7 @@ __global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwd
         if (o0 < E) {
             int i = 0, j = 0;
             View A{ent, 0}, Bl{ent, 0};
-            uint32_t ha = 0, hb = 0;  // the heads A[i], B[j] (kNoEntry when a side is used up)
+            uint32_t ha = 0, hb = 0;  // the heads A[i], B[j] (kUsedUp when a side is used up)
 #pragma unroll
             for (int k = 0; k < kSortPer; ++k) {
                 if (k < opt) {
@@ -645,19 +650,19 @@ __global__ __launch_bounds__(kSortThreads) void sparse_bwd_sort_kernel(SparseBwd
                         Bl = View{ent, p * 2 * R + R};
                         i = merge_split(A, Bl, R, d);
                         j = d - i;
-                        ha = i < R ? A[i] : kNoEntry;
-                        hb = j < R ? Bl[j] : kNoEntry;
+                        ha = i < R ? A[i] : kUsedUp;
+                        hb = j < R ? Bl[j] : kUsedUp;
                     }
                     // ties take A; a used-up side never wins (i + j < 2R here)
                     const bool takeA = j >= R || (i < R && ha <= hb);
                     if (takeA) {
                         out[k] = ha;
                         ++i;
-                        ha = i < R ? A[i] : kNoEntry;
+                        ha = i < R ? A[i] : kUsedUp;
                     } else {
                         out[k] = hb;
                         ++j;
-                        hb = j < R ? Bl[j] : kNoEntry;
+                        hb = j < R ? Bl[j] : kUsedUp;
                     }
                 }
             }

@@ -16,6 +16,8 @@ name as host models: arxivdaily page for arXiv 2607.19358, English abstract,
   ``dtype=float32``), scaled in float32, then rounded once to bf16 with
   round-to-nearest-even where the configuration is bf16;
 * q, k, v ~ N(0,1)/sqrt(d); q_I, k_I ~ N(0,1); w ~ U(0,1); z ~ N(0,1);
+  (test cases for negative indexer scores map the same uniform draw u to
+  w = 2u - 1 ~ U(-1,1) or w = u - 1 ~ U(-1,0));
   decode state S ~ N(0,1) * sqrt(L_b) / d (the magnitude a zero-start
   prefill of L_b tokens at this input scale produces).
 
@@ -49,6 +51,7 @@ class LayerConfig:
     ctx_lo: int = 0      # decode: ragged lengths drawn U[ctx_lo, ctx_hi]
     ctx_hi: int = 0
     seed: int = 1000
+    w_dist: str = "u01"  # indexer head weights: "u01" U(0,1), "signed" U(-1,1), "neg" U(-1,0)
 
     @property
     def dtype_code(self) -> int:
@@ -96,6 +99,17 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     return round_bf16(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
 
+def _weights(rng, shape, cfg):
+    u = rng.random(shape, dtype=np.float32)
+    if cfg.w_dist == "signed":
+        u = u * np.float32(2) - np.float32(1)
+    elif cfg.w_dist == "neg":
+        u = u - np.float32(1)
+    elif cfg.w_dist != "u01":
+        raise ValueError(f"unknown w_dist {cfg.w_dist!r}")
+    return _store(u, cfg.dtype)
+
+
 def _normal(rng, shape, scale, dtype):
     x = rng.standard_normal(shape, dtype=np.float32)
     if scale != 1.0:
@@ -131,7 +145,7 @@ def make_prefill_inputs(cfg: LayerConfig, seed: int | None = None, n: int | None
         "v": _normal(rng, (B, n, cfg.Hkv, cfg.d), s, dt),
         "q_idx": _normal(rng, (B, n, G, cfg.HI, cfg.dI), 1.0, dt),
         "k_idx": _normal(rng, (B, n, G, cfg.dI), 1.0, dt),
-        "w_idx": _store(rng.random((B, n, G, cfg.HI), dtype=np.float32), dt),
+        "w_idx": _weights(rng, (B, n, G, cfg.HI), cfg),
         "gate": _normal(rng, (B, n, cfg.Hq), 1.0, dt),
     }
     out["B"], out["n"] = B, n
@@ -164,7 +178,7 @@ def make_decode_inputs(cfg: LayerConfig, seed: int | None = None, B: int | None 
         "v_cache": _normal(rng, (tot, cfg.Hkv, cfg.d), s, dt),
         "q_idx": _normal(rng, (B, G, cfg.HI, cfg.dI), 1.0, dt),
         "k_idx_cache": _normal(rng, (tot, G, cfg.dI), 1.0, dt),
-        "w_idx": _store(rng.random((B, G, cfg.HI), dtype=np.float32), dt),
+        "w_idx": _weights(rng, (B, G, cfg.HI), cfg),
         "gate": _normal(rng, (B, cfg.Hq), 1.0, dt),
     }
     st = rng.standard_normal((B, cfg.Hq, cfg.d, cfg.d), dtype=np.float32)

@@ -49,7 +49,24 @@
  * Supported shapes: head_dim in {64, 128}; idx_dim in {32, 64};
  * 1 <= idx_heads <= 8; num_q_heads % num_kv_heads == 0 with r <= 16;
  * chunk in {0, 64} (0 means 64); prefill: 1 <= top_m <= 512, n <= 32768;
- * decode: 1 <= top_m <= 2048, max_ctx <= 65536.
+ * decode: 1 <= top_m <= 2048, max_ctx <= 65536.  Also refused
+ * (LISA_ERR_UNSUPPORTED), because kernels address a sequence's rows through
+ * buffer descriptors with a 32-bit byte extent and count a launch's threads
+ * in 32 bits: one sequence's K/V rows (positions x num_kv_heads x head_dim
+ * x element size; in decode max_ctx positions, or the page pool's rows)
+ * above 4 GiB - 1, likewise its indexer-key rows, 2^22 or more
+ * (sequence, position, group) units in one call, and in the backward
+ * num_q_heads x top_m above 2^21 (a 256-position block of per-slot
+ * coefficients).
+ * Refusals and their reasons:
+ *   - chunk 16 or 32: the linear branch's result does not depend on the
+ *     chunk length (it only regroups the same sums), and the kernels are
+ *     tiled for 64-row MFMA blocks, so only 64 is taken;
+ *   - prefill top_m above 512: the fused indexer keeps each query's
+ *     candidates (score and index) in LDS next to its key tiles, and at
+ *     top_m = 512 that buffer already holds 1024 entries per query; larger
+ *     top_m are served by the decode step (up to 2048) and by the window
+ *     variant (up to 2048), whose selects do not live in LDS per query.
  */
 #ifndef LISA_H
 #define LISA_H
@@ -192,7 +209,9 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
                                   size_t workspace_bytes, lisa_stream_t stream);
 
 /* Workspace needed by lisa_decode_step for B sequences of at most max_ctx
- * visible tokens each. */
+ * visible tokens each.  The indexer scores are kept per sequence in rows of
+ * max_ctx entries ([B, G, max_ctx] fp32), so the size depends on B and
+ * max_ctx only: the total context length of a ragged batch is not needed. */
 lisa_status lisa_decode_workspace_bytes(const lisa_dims *dims, int32_t B, int32_t max_ctx,
                                         size_t *bytes);
 

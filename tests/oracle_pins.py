@@ -200,6 +200,71 @@ def pin_linear_closed_form(lib):
                                    atol=1e-12)
 
 
+def _chunked_linear(Q, K, V, S0, C):
+    """Chunked evaluation of the identity-feature-map linear attention
+    (gptget.net analysis, method-details section: state S_t, O(1) per step),
+    chunk by chunk: O_c = tril(Q_c K_c^T) V_c + Q_c S_{c-1},
+    S_c = S_{c-1} + K_c^T V_c.  The last chunk may be short."""
+    n = Q.shape[0]
+    S = np.array(S0, dtype=np.float64)
+    out = np.zeros((n, V.shape[1]))
+    for c0 in range(0, n, C):
+        Qc, Kc, Vc = Q[c0:c0 + C], K[c0:c0 + C], V[c0:c0 + C]
+        out[c0:c0 + C] = np.tril(Qc @ Kc.T) @ Vc + Qc @ S
+        S = S + Kc.T @ Vc
+    return out, S
+
+
+def pin_linear_chunked(lib):
+    """The oracle's recurrent linear branch (one rank-one update per token)
+    equals the chunked form at chunk sizes 1, 4, 16 and 64, with n = 150 not a
+    multiple of any of them but 1, with and without an initial state."""
+    cfg = _cfg(n=150, Hq=4, Hkv=2, d=8, HI=2, dI=8, M=4)
+    inp = make_prefill_inputs(cfg)
+    rng = np.random.default_rng(6)
+    q, k, v = (orc.widen(inp[x], "f32") for x in ("q", "k", "v"))
+    for S0 in (None, rng.standard_normal((1, cfg.Hq, cfg.d, cfg.d))):
+        r = orc.prefill(inp, cfg, state_in=S0, lib=lib)
+        for h in range(cfg.Hq):
+            g = h * cfg.Hkv // cfg.Hq
+            init = np.zeros((cfg.d, cfg.d)) if S0 is None else S0[0, h]
+            for C in (1, 4, 16, 64):
+                o, S = _chunked_linear(q[0, :, h], k[0, :, g], v[0, :, g], init, C)
+                np.testing.assert_allclose(r["olin"][0, :, h], o, rtol=1e-11, atol=1e-12)
+                np.testing.assert_allclose(r["state_out"][0, h], S, rtol=1e-11, atol=1e-12)
+
+
+def pin_topm_negative_scores(lib):
+    """Selection with head weights of both signs: the oracle's sets equal the
+    brute-force sort of its own scores, and a query whose weights are all
+    negative selects its exact-zero scores (keys anti-aligned with every
+    indexer head) first, in index order, then the negatives closest to 0."""
+    cfg = LayerConfig("pin", "prefill", "f32", B=1, n=90, Hq=2, Hkv=2, d=8, HI=3, dI=8, M=12,
+                      seed=9, w_dist="signed")
+    inp = make_prefill_inputs(cfg)
+    r = orc.prefill(inp, cfg, lib=lib)
+    qI, kI, w = (orc.widen(inp[x], "f32") for x in ("q_idx", "k_idx", "w_idx"))
+    assert (w < 0).any() and (w > 0).any()
+    for t in range(cfg.n):
+        for g in range(cfg.Hkv):
+            sc = (w[0, t, g][:, None] * np.maximum(qI[0, t, g] @ kI[0, :t + 1, g].T, 0)).sum(0)
+            assert r["idx"][0, t, g].tolist() == _brute_topm(sc.tolist(), cfg.M), (t, g)
+    # every weight negative: zeros first (lowest index), then the least negative
+    rng = np.random.default_rng(10)
+    HI, dI, T, M = 2, 4, 40, 10
+    qIn = np.abs(rng.standard_normal((HI, dI))) + 0.1
+    kIn = np.abs(rng.standard_normal((T, dI))) + 0.1   # aligned: every dot > 0, score < 0
+    kIn[::4] = -kIn[::4]                                # anti-aligned: these 10 score exactly 0
+    wn = -(rng.random(HI) + 0.1)
+    sc = orc.index_scores(qIn, wn, kIn, lib=lib)
+    assert np.all(sc <= 0.0) and np.count_nonzero(sc == 0.0) == 10
+    got = orc.topm(sc, M, lib=lib).tolist()
+    assert got == list(range(0, T, 4)), got
+    got = orc.topm(sc, M + 3, lib=lib).tolist()
+    neg = sorted((s for s in range(T) if sc[s] < 0), key=lambda s: (-sc[s], s))[:3]
+    assert got == sorted(list(range(0, T, 4)) + neg), got
+
+
 def pin_gate_limits(lib):
     cfg = _cfg(n=21, Hq=4, Hkv=2, d=8, HI=2, dI=8, M=4)
     inp = make_prefill_inputs(cfg)
@@ -326,5 +391,5 @@ def pin_window_banded(lib):
 
 ALL_PINS = [pin_golden_prefill, pin_golden_softmax, pin_golden_decode, pin_topm_bruteforce,
             pin_scores_reductions, pin_sparse_full_causal, pin_sparse_m1, pin_sparse_zero_query,
-            pin_linear_closed_form, pin_gate_limits, pin_selection_properties, pin_rows_subset,
+            pin_linear_closed_form, pin_linear_chunked, pin_topm_negative_scores, pin_gate_limits, pin_selection_properties, pin_rows_subset,
             pin_decode_matches_prefill, pin_decode_ragged_groups, pin_window_banded]

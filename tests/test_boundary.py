@@ -299,3 +299,35 @@ def test_backward_limits():
     assert _bwd(d, ws_bytes=need - 1) == lisa.LISA_ERR_WORKSPACE
     # workspace grows with the sequence
     assert lisa.lisa_prefill_backward_workspace_bytes(d, 1, 4096) > need
+
+
+def test_descriptor_spans_refused():
+    """Shapes whose per-sequence row spans or launch sizes do not fit the
+    kernels' 32-bit buffer-descriptor extents and thread counts are refused
+    with UNSUPPORTED before any HIP call (the pointers are never touched)."""
+    # K/V rows of one sequence: 32768 rows x 2048 groups x 128 fp32 = 32 GiB
+    big = _dims(Hq=2048, Hkv=2048, dtype="f32")
+    assert _prefill(big, n=32768) == lisa.LISA_ERR_UNSUPPORTED
+    assert "descriptor" in lisa.lisa_last_error()
+    assert _cont(big, past=16384, n=16384) == lisa.LISA_ERR_UNSUPPORTED
+    assert _win(big, n=32768) == lisa.LISA_ERR_UNSUPPORTED
+    assert _bwd(big, n=32768) == lisa.LISA_ERR_UNSUPPORTED
+    with pytest.raises(lisa.LisaError):
+        lisa.lisa_prefill_workspace_bytes(big, 1, 32768)
+    # decode: 65536 rows x 512 groups x 128 fp32 = 16 GiB per sequence
+    dbig = _dims(Hq=512, Hkv=512, dtype="f32", M=256)
+    assert _decode(dbig, max_ctx=65536) == lisa.LISA_ERR_UNSUPPORTED
+    assert _dwin(dbig, max_ctx=65536) == lisa.LISA_ERR_UNSUPPORTED
+    with pytest.raises(lisa.LisaError):
+        lisa.lisa_decode_workspace_bytes(dbig, 1, 65536)
+    # the same groups at a short context fit
+    assert lisa.lisa_decode_workspace_bytes(dbig, 1, 1024) > 0
+    # too many (sequence, position, group) units for one launch's thread count
+    many = _dims(Hq=64, Hkv=64)
+    assert _prefill(many, B=4, n=32768) == lisa.LISA_ERR_UNSUPPORTED
+    assert "units" in lisa.lisa_last_error()
+    assert _decode(_dims(), B=(1 << 21) + 1) == lisa.LISA_ERR_UNSUPPORTED
+    # backward: 256 positions' per-slot coefficients, 8 bytes per slot and head
+    assert _bwd(_dims(Hq=4096, Hkv=256, M=512), n=64) == lisa.LISA_ERR_UNSUPPORTED
+    assert "coefficient" in lisa.lisa_last_error()
+    assert _bwd(_dims(Hq=1024, Hkv=64, M=512), n=64, ws_bytes=1) == lisa.LISA_ERR_WORKSPACE

@@ -31,9 +31,10 @@ def _gpu():
     yield
 
 
-def _pcfg(n, Hq, Hkv, d, HI, dI, M, dtype="bf16", B=1, seed=1):
-    return LayerConfig(f"p_n{n}_h{Hq}x{Hkv}_d{d}_i{HI}x{dI}_m{M}_{dtype}", "prefill", dtype, B=B,
-                       n=n, Hq=Hq, Hkv=Hkv, d=d, HI=HI, dI=dI, M=M, seed=seed)
+def _pcfg(n, Hq, Hkv, d, HI, dI, M, dtype="bf16", B=1, seed=1, w_dist="u01"):
+    wtag = "" if w_dist == "u01" else f"_w{w_dist}"
+    return LayerConfig(f"p_n{n}_h{Hq}x{Hkv}_d{d}_i{HI}x{dI}_m{M}_{dtype}{wtag}", "prefill", dtype, B=B,
+                       n=n, Hq=Hq, Hkv=Hkv, d=d, HI=HI, dI=dI, M=M, seed=seed, w_dist=w_dist)
 
 
 PREFILL_SMALL = [
@@ -103,22 +104,22 @@ def test_prefill_max_length_sampled_rows():
     _say("  ", rep)
 
 
-def test_prefill_config3_sampled_rows():
+def test_prefill_config3_all_rows():
+    """The 16K 7B-shaped workload in the benchmark's launch configuration,
+    every row: index sets of all 16384 x 4 units, all outputs and the state."""
     cfg = gen.PREFILL_7B_16K
-    _say("prefill", cfg.name, "(sampled rows, full state)")
+    _say("prefill", cfg.name, "(all rows)")
     inp = gen.make_prefill_inputs(cfg)
-    rng = np.random.default_rng(3)
-    rows = sorted(set([0, 1, 2, 63, 64, 65, 254, 255, 256, 257, 1000, 4095, 4096, 8191, 12345,
-                       16383] + rng.integers(0, cfg.n, size=40).tolist()))
     rep = {}
-    parity.prefill_parity(cfg, inp, rows=rows, report=rep)
+    parity.prefill_parity(cfg, inp, report=rep)
     _say("  ", rep)
 
 
-def _dcfg(Hq, Hkv, d, HI, dI, M, lengths, dtype="bf16", seed=1):
-    return LayerConfig(f"d_h{Hq}x{Hkv}_d{d}_i{HI}x{dI}_m{M}_{dtype}_L{'-'.join(map(str, lengths))}",
+def _dcfg(Hq, Hkv, d, HI, dI, M, lengths, dtype="bf16", seed=1, w_dist="u01"):
+    wtag = "" if w_dist == "u01" else f"_w{w_dist}"
+    return LayerConfig(f"d_h{Hq}x{Hkv}_d{d}_i{HI}x{dI}_m{M}_{dtype}{wtag}_L{'-'.join(map(str, lengths))}",
                        "decode", dtype, B=len(lengths), Hq=Hq, Hkv=Hkv, d=d, HI=HI, dI=dI, M=M,
-                       seed=seed), np.asarray(lengths)
+                       seed=seed, w_dist=w_dist), np.asarray(lengths)
 
 
 DECODE_SMALL = [
@@ -635,3 +636,82 @@ def test_graph_replay():
         _say("decode graph replay", rep)
         for a, b in zip((dout, y["state"], didx), dref):
             assert torch.equal(a, b)
+
+
+# ---- negative indexer scores (w may be negative: scores of either sign) ----
+NEG_PREFILL = [
+    _pcfg(3000, 8, 2, 128, 4, 64, 256, seed=51, w_dist="signed"),  # n >= 4M: sampled threshold, trims
+    _pcfg(2600, 4, 2, 64, 4, 32, 64, seed=52, w_dist="neg"),       # every score <= 0; the zeros tie
+    _pcfg(1200, 6, 3, 128, 8, 64, 100, seed=53, w_dist="signed"),  # 8 indexer heads
+    _pcfg(600, 4, 1, 64, 3, 32, 512, seed=54, w_dist="neg"),       # t < M and the 1024-entry buffers
+    _pcfg(2100, 4, 2, 128, 2, 64, 37, dtype="f32", seed=55, w_dist="signed"),
+]
+
+
+@pytest.mark.parametrize("cfg", NEG_PREFILL, ids=lambda c: c.name)
+def test_prefill_negative_scores(cfg):
+    _say("prefill", cfg.name, "seed", cfg.seed)
+    inp = gen.make_prefill_inputs(cfg)
+    rep = {}
+    parity.prefill_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+@pytest.mark.parametrize("w_dist", ["signed", "neg"])
+@pytest.mark.parametrize("lengths", [[8000, 300], [17000], [33792, 18000], [40000, 5]],
+                         ids=["ctx8000", "ctx17000", "ctx33792", "ctx40000"])
+@pytest.mark.parametrize("M", [256, 512])
+def test_decode_negative_scores_every_select_variant(lengths, w_dist, M):
+    """Scores of both signs (and, with w <= 0, only of one sign with many exact
+    zeros) at contexts that pick each top-M kernel variant."""
+    cfg, L = _dcfg(4, 2, 64, 4, 32, M, lengths, seed=61, w_dist=w_dist)
+    _say("decode", cfg.name)
+    inp = gen.make_decode_inputs(cfg, lengths=L)
+    rep = {}
+    parity.decode_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+# ---- long prefill at the largest M and with 8 indexer heads -----------------
+def test_prefill_m512_long_sampled_rows():
+    """M = 512 (1024-entry candidate buffers) at n = 8192: queries past 2048
+    start from a sampled threshold, queries between 960 and 2048 trim their
+    buffers; rows sampled over both ranges, the state in full."""
+    for w_dist, seed in (("u01", 71), ("signed", 72)):
+        cfg = _pcfg(8192, 8, 2, 128, 4, 64, 512, seed=seed, w_dist=w_dist)
+        _say("prefill", cfg.name, "(sampled rows, full state)")
+        inp = gen.make_prefill_inputs(cfg)
+        rng = np.random.default_rng(seed)
+        rows = sorted(set([0, 511, 512, 959, 960, 1500, 2047, 2048, 2049, 4095, 8191]
+                          + rng.integers(960, 2048, size=24).tolist()
+                          + rng.integers(2048, cfg.n, size=24).tolist()))
+        rep = {}
+        parity.prefill_parity(cfg, inp, rows=rows, report=rep)
+        _say("  ", rep)
+
+
+def test_prefill_eight_indexer_heads_long():
+    """8 indexer heads (two head halves per query) at n = 4500, all rows."""
+    cfg = _pcfg(4500, 8, 2, 128, 8, 64, 256, seed=73)
+    _say("prefill", cfg.name)
+    inp = gen.make_prefill_inputs(cfg)
+    rep = {}
+    parity.prefill_parity(cfg, inp, report=rep)
+    _say("  ", rep)
+
+
+def test_prefill_backward_max_length_m512_window():
+    """n = 32768 and M = 512: the last key row is selected by the last
+    position, in its set's last slot (window sets), which packs the largest
+    key, block position and slot into one sort entry.  dk and dv of the last
+    keys and dq of the last rows against the oracle's per-row form."""
+    cfg = _pcfg(32768, 4, 2, 128, 4, 64, 512, seed=81)
+    _say("backward window sets", cfg.name, "(sampled rows and keys)")
+    inp = gen.make_prefill_inputs(cfg)
+    binp = gen.make_backward_inputs(cfg)
+    sets = parity.window_sets(cfg.B, cfg.n, cfg.Hkv, cfg.M)
+    rows = [0, 511, 512, 32766, 32767]
+    keys = [0, 20000, 32255, 32256, 32766, 32767]
+    rep = {}
+    parity.backward_sampled_parity(cfg, inp, binp, rows, keys, report=rep, sets=sets)
+    _say("  ", rep)
