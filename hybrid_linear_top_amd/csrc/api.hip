@@ -424,6 +424,36 @@ lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t
     return ok();
 }
 
+// ---- static scratch for lisa_decode_step_noalloc ------------------------------
+// A file-scope device array stands in for the caller's workspace.  In host
+// code its name is only a stand-in for the symbol: every host use goes
+// through the device address hipGetSymbolAddress returns, resolved once per
+// device on the first call there (with that device current) and kept.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+lisa_status device_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LISA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(LISA_ERR_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(LISA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LISA_OK;
+}
+
 // The decode path; window as in prefill_impl.  map.table == nullptr: packed
 // caches described by cu_ctx; otherwise paged caches (pool_rows rows).
 lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx, int32_t max_ctx,
@@ -431,7 +461,7 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
                         const void *k_idx_cache, const void *w_idx, const void *gate, float *state,
                         void *out, int32_t *topm_out, void *workspace, size_t workspace_bytes,
                         lisa_stream_t stream, bool window, lisa::CacheMap map = lisa::CacheMap{},
-                        int64_t pool_rows = 0) {
+                        int64_t pool_rows = 0, bool use_scratch = false) {
     const bool paged = map.table != nullptr;
     lisa_status st = check_dims(dims, false, window);
     if (st) return st;
@@ -459,10 +489,19 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     LISA_NEED(state, "state");
     LISA_NEED(out, "out");
     LISA_OPT(topm_out, "topm_out");
-    LISA_NEED(workspace, "workspace");
     const DecodeWs w = decode_ws(dims, B, max_ctx);
-    if (workspace_bytes < w.total)
-        return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+    if (use_scratch) {
+        // the kernels overwrite every scratch byte they read (no zero start)
+        if (w.total > kScratchBytes)
+            return fail(LISA_ERR_UNSUPPORTED, "this step needs %zu bytes of scratch; the static scratch holds %zu",
+                        w.total, kScratchBytes);
+        if ((st = device_scratch(&workspace))) return st;
+        workspace_bytes = kScratchBytes;
+    } else {
+        LISA_NEED(workspace, "workspace");
+        if (workspace_bytes < w.total)
+            return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const int G = dims->num_kv_heads, Hq = dims->num_q_heads, D = dims->head_dim;
@@ -554,6 +593,15 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
                              lisa_stream_t stream) {
     return decode_impl(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
                        gate, state, out, topm_out, workspace, workspace_bytes, stream, false);
+}
+
+lisa_status lisa_decode_step_noalloc(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
+                                     int32_t max_ctx, const void *q, const void *k_cache,
+                                     const void *v_cache, const void *q_idx, const void *k_idx_cache,
+                                     const void *w_idx, const void *gate, float *state, void *out,
+                                     int32_t *topm_out, lisa_stream_t stream) {
+    return decode_impl(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache, w_idx,
+                       gate, state, out, topm_out, nullptr, 0, stream, false, lisa::CacheMap{}, 0, true);
 }
 
 lisa_status lisa_decode_step_paged(const lisa_dims *dims, int32_t B, const int32_t *lengths,

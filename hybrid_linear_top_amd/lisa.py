@@ -28,7 +28,7 @@ EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill_continue_workspace_byte
            "lisa_prefill_window", "lisa_decode_step_window", "lisa_decode_step_paged",
            "lisa_decode_workspace_bytes", "lisa_prefill_backward_workspace_bytes",
            "lisa_prefill_backward",
-           "lisa_decode_step", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
+           "lisa_decode_step", "lisa_decode_step_noalloc", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
            "lisa_build_info"]
 
 
@@ -80,6 +80,8 @@ def _load(path: str = LIB_PATH):
     lib.lisa_decode_workspace_bytes.restype = ctypes.c_int
     lib.lisa_decode_step.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp, sz, vp]
     lib.lisa_decode_step.restype = ctypes.c_int
+    lib.lisa_decode_step_noalloc.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp]
+    lib.lisa_decode_step_noalloc.restype = ctypes.c_int
     lib.lisa_stage_timing.argtypes = [i32]
     lib.lisa_stage_timing.restype = ctypes.c_int
     lib.lisa_stage_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p),
@@ -189,6 +191,13 @@ def lisa_decode_step(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx
     return _lib.lisa_decode_step(ctypes.byref(dims), B, cu_ctx, max_ctx, q, k_cache, v_cache,
                                  q_idx, k_idx_cache, w_idx, gate, state, out, topm_out, workspace,
                                  workspace_bytes, stream)
+
+
+def lisa_decode_step_noalloc(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_idx, k_idx_cache,
+                             w_idx, gate, state, out, topm_out, stream) -> int:
+    """Raw call; returns the status code (0 = LISA_OK)."""
+    return _lib.lisa_decode_step_noalloc(ctypes.byref(dims), B, cu_ctx, max_ctx, q, k_cache, v_cache,
+                                         q_idx, k_idx_cache, w_idx, gate, state, out, topm_out, stream)
 
 
 def lisa_stage_timing(enable: bool) -> None:

@@ -238,6 +238,26 @@ lisa_status lisa_decode_step(const lisa_dims *dims, int32_t B, const int64_t *cu
                              lisa_stream_t stream);
 
 /*
+ * lisa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The step's scratch (indexer scores,
+ * o_lin, and the sets when topm_out is NULL) lives in a static device array
+ * of the library, 32 MiB per GPU, held until the process ends; nothing is
+ * allocated or freed.  A step needing more than that
+ * (lisa_decode_workspace_bytes(dims, B, max_ctx) > 32 MiB, e.g. B * G *
+ * max_ctx above about 8 M) returns LISA_ERR_UNSUPPORTED.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (concurrent
+ * streams or threads) race and must be serialized by the caller.  The first
+ * call on each device looks the array's device address up (a HIP call made
+ * after argument validation).  Other arguments as lisa_decode_step.
+ */
+lisa_status lisa_decode_step_noalloc(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
+                                     int32_t max_ctx, const void *q, const void *k_cache,
+                                     const void *v_cache, const void *q_idx, const void *k_idx_cache,
+                                     const void *w_idx, const void *gate, float *state, void *out,
+                                     int32_t *topm_out, lisa_stream_t stream);
+
+/*
  * lisa_decode_step on paged (block-table) caches, the layout serving systems
  * keep KV caches in (the pages say nothing about cache layouts; the result
  * is the same decode step).  The three caches are page pools of

@@ -331,3 +331,18 @@ def test_descriptor_spans_refused():
     assert _bwd(_dims(Hq=4096, Hkv=256, M=512), n=64) == lisa.LISA_ERR_UNSUPPORTED
     assert "coefficient" in lisa.lisa_last_error()
     assert _bwd(_dims(Hq=1024, Hkv=64, M=512), n=64, ws_bytes=1) == lisa.LISA_ERR_WORKSPACE
+
+
+def test_noalloc_decode_validation():
+    """The no-allocation decode step validates like lisa_decode_step and
+    refuses a step whose scratch would exceed its static 32 MiB, all before
+    any HIP call."""
+    d = _dims(Hq=28, Hkv=4, M=512)
+    args = [FAKE] * 7
+    assert lisa.lisa_decode_step_noalloc(d, 64, FAKE, 65536, *args, FAKE, FAKE, 0, 0) == lisa.LISA_ERR_UNSUPPORTED
+    assert "scratch" in lisa.lisa_last_error()
+    assert lisa.lisa_decode_step_noalloc(d, 2, 0, 100, *args, FAKE, FAKE, 0, 0) == lisa.LISA_ERR_INVALID_ARGUMENT
+    assert lisa.lisa_decode_step_noalloc(d, 2, FAKE, 65537, *args, FAKE, FAKE, 0, 0) == lisa.LISA_ERR_UNSUPPORTED
+    assert lisa.lisa_decode_step_noalloc(_dims(M=2049), 2, FAKE, 100, *args, FAKE, FAKE, 0, 0) == \
+        lisa.LISA_ERR_UNSUPPORTED
+    assert lisa.lisa_decode_step_noalloc(d, 0, 0, 100, *([0] * 7), 0, 0, 0, 0) == lisa.LISA_OK
