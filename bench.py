@@ -106,74 +106,200 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(stage):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when absent or when the kernel's sources changed since it was taken."""
+# The benchmark's phases, in the order it runs them.  With --phase-markers a
+# tiny calibration copy (probe_copy_kernel on 4 KiB) is launched before each
+# phase, so that a rocprofv3 database can be split by phase: the 16K and the
+# ragged decode batches launch the same kernels, and the backward launches
+# the forward's linear kernels on its own operands.
+PHASES = ["prefill_7b_16k", "prefill_1p5b_4k", "decode_1p5b_16k", "decode_7b_ragged", "backward_setup",
+          "backward_7b_16k"]
+MARKER_KERNEL = "probe_copy_kernel"
+
+
+def traffic_from_profiles(stage, phase):
+    """HBM bytes per launch of a stage in a phase, from the committed rocprofv3
+    counter summary; None when absent or when the kernel's sources changed
+    since the counters were taken."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get("kernels", {}).get(stage)
+    ent = data.get("phases", {}).get(phase, {}).get(stage)
     if not ent or ent.get("source_hash") != source_hash(*STAGE_KERNELS[stage][1]):
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
-def traffic_summary(fetch_db, write_db, out_json, out_md, command):
-    """Turn two rocprofv3 --pmc databases (FETCH_SIZE and WRITE_SIZE, KiB per
-    dispatch) into HBM bytes per launch.  Each counter is scaled by what it
-    reads for the 1 GiB device copy that --copy-calibration runs first (the
-    copy reads and writes 2^30 bytes)."""
+def _db_rows(db, counters=None):
+    """(phase, stage, counter, value) per dispatch of a rocprofv3 --pmc
+    database written by a run with --phase-markers."""
     import re
     import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    rows = list(cur.execute("select kernel_name, counter_name, value, dispatch_id from counters_collection"))
+    marks = sorted({i for nm, _, _, i in rows if MARKER_KERNEL in nm})
+    import bisect
+    out = []
+    for nm, cn, v, i in rows:
+        if counters and cn not in counters:
+            continue
+        if MARKER_KERNEL in nm or "copyBuffer" in nm:
+            out.append(("calibration", nm, cn, v, i))
+            continue
+        ph = bisect.bisect_left(marks, i) - 1
+        phase = PHASES[ph] if 0 <= ph < len(PHASES) else "unmarked"
+        for stage, (pat, _) in STAGE_KERNELS.items():
+            if re.search(pat, nm):
+                out.append((phase, stage, cn, v, i))
+                break
+    return out
 
-    def per_kernel(db, counter):
-        cur = sqlite3.connect(db).cursor()
-        rows = list(cur.execute("select kernel_name, value, dispatch_id from counters_collection "
-                                "where counter_name = ?", (counter,)))
-        cal = [v for nm, v, _ in rows if "copyBuffer" in nm and v > 1e5]
+
+def traffic_summary(fetch_db, write_db, out_json, out_md, command):
+    """Turn two rocprofv3 --pmc databases (FETCH_SIZE and WRITE_SIZE, KiB per
+    dispatch) into HBM bytes per launch, per phase and stage.  Each counter is
+    scaled by what it reads for the 1 GiB device copy that --copy-calibration
+    runs first (the copy reads and writes 2^30 bytes)."""
+
+    def per_stage(db, counter):
+        rows = _db_rows(db, {counter})
+        cal = [v for ph, nm, _, v, _ in rows if ph == "calibration" and "copyBuffer" in nm and v > 1e5]
         if not cal:
             raise SystemExit(f"{db}: no calibration copy found (run bench.py --copy-calibration)")
         factor = (1 << 30) / (sum(cal) / len(cal) * 1024.0)
-        # the benchmark runs prefill, then decode, then the backward (which
-        # runs a prefill with an initial state and the linear kernels on its
-        # own operands): prefill stages count only the dispatches before the
-        # first decode kernel
-        dec_ids = [i for nm, _, i in rows if re.search(r"decode_score_state_kernel<", nm)]
-        first_dec = min(dec_ids) if dec_ids else float("inf")
-        out = {}
-        for stage, (pat, _) in STAGE_KERNELS.items():
-            prefill_stage = stage.startswith(("linear", "indexer", "sparse_gate_prefill"))
-            vals = [v for nm, v, i in rows if re.search(pat, nm) and (not prefill_stage or i < first_dec)]
-            if vals:
-                out[stage] = (sum(vals) / len(vals) * 1024.0 * factor, len(vals))
-        return out, factor
+        acc = {}
+        for ph, stage, _, v, _ in rows:
+            if ph in ("calibration", "unmarked", "backward_setup"):
+                continue
+            acc.setdefault((ph, stage), []).append(v)
+        return {k: (sum(v) / len(v) * 1024.0 * factor, len(v)) for k, v in acc.items()}, factor
 
-    fetch, ff = per_kernel(fetch_db, "FETCH_SIZE")
-    write, wf = per_kernel(write_db, "WRITE_SIZE")
-    kernels = {}
-    for stage in STAGE_KERNELS:
-        if stage in fetch and stage in write:
-            kernels[stage] = {"fetch_bytes": round(fetch[stage][0]), "write_bytes": round(write[stage][0]),
-                              "hbm_bytes_per_launch": round(fetch[stage][0] + write[stage][0]),
-                              "dispatches": fetch[stage][1],
-                              "source_hash": source_hash(*STAGE_KERNELS[stage][1])}
-    data = {"command": command, "fetch_scale": round(ff, 4), "write_scale": round(wf, 4),
-            "kernels": kernels}
+    fetch, ff = per_stage(fetch_db, "FETCH_SIZE")
+    write, wf = per_stage(write_db, "WRITE_SIZE")
+    phases = {}
+    for key in fetch:
+        if key not in write:
+            continue
+        ph, stage = key
+        phases.setdefault(ph, {})[stage] = {
+            "fetch_bytes": round(fetch[key][0]), "write_bytes": round(write[key][0]),
+            "hbm_bytes_per_launch": round(fetch[key][0] + write[key][0]), "dispatches": fetch[key][1],
+            "source_hash": source_hash(*STAGE_KERNELS[stage][1])}
+    data = {"command": command, "fetch_scale": round(ff, 4), "write_scale": round(wf, 4), "phases": phases}
     with open(out_json, "w") as f:
         json.dump(data, f, indent=1)
     with open(out_md, "w") as f:
-        f.write("# HBM traffic per launch: 16K prefill, 16K decode step, 16K backward\n\n")
+        f.write("# HBM traffic per launch: prefill (16K 7B-shaped, 4K 1.5B-shaped), decode (16K 1.5B-shaped, "
+                "7B-shaped ragged), backward (16K 7B-shaped)\n\n")
         f.write("rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in a pass of its own "
-                "(REPO is the repository root, OUT any scratch folder):\n\n")
+                "(REPO is the repository root, OUT any scratch folder); dispatches are split by phase with "
+                "the marker copies the run launches between phases:\n\n")
         f.write("```\n" + command + "\n```\n\n")
         f.write(f"Scale factors from the 1 GiB device copy: FETCH_SIZE x {ff:.3f}, "
                 f"WRITE_SIZE x {wf:.3f}.\n\n")
-        f.write("| stage | dispatches | fetch MB | write MB | HBM MB per launch |\n|---|---|---|---|---|\n")
-        for stage, e in kernels.items():
-            f.write(f"| {stage} | {e['dispatches']} | {e['fetch_bytes'] / 1e6:.2f} | "
-                    f"{e['write_bytes'] / 1e6:.2f} | {e['hbm_bytes_per_launch'] / 1e6:.2f} |\n")
+        f.write("| phase | stage | dispatches | fetch MB | write MB | HBM MB per launch |\n|---|---|---|---|---|---|\n")
+        for ph in PHASES:
+            for stage, e in phases.get(ph, {}).items():
+                f.write(f"| {ph} | {stage} | {e['dispatches']} | {e['fetch_bytes'] / 1e6:.2f} | "
+                        f"{e['write_bytes'] / 1e6:.2f} | {e['hbm_bytes_per_launch'] / 1e6:.2f} |\n")
+    return data
+
+
+# Derived rocprofv3 counters (definitions of the rocprofiler-sdk counter
+# table for gfx950), two passes that each stay within one run's hardware
+# counter budget: pass 1 MfmaUtil, MfmaFlopsBF16, VALUBusy, TA_BUSY_avr,
+# OccupancyPercent, GRBM_GUI_ACTIVE (4 SQ, 1 GRBM, 1 TA counters); pass 2 LDSBankConflict,
+# TCC_HIT_sum, TCC_MISS_sum, MemUnitStalled (1 SQ, 1 GRBM, 2 TCC, 1 TCP).
+N_XCD = 8  # MI355X: 8 accelerator complex dies, 32 CUs each
+COUNTER_PASSES = [["MfmaUtil", "MfmaFlopsBF16", "VALUBusy", "TA_BUSY_avr", "OccupancyPercent", "GRBM_GUI_ACTIVE"],
+                  ["LDSBankConflict", "TCC_HIT_sum", "TCC_MISS_sum", "MemUnitStalled"]]
+COUNTER_CMD = ("cd /tmp && export TMPDIR=/tmp && "
+               "timeout -s KILL 240 rocprofv3 --pmc {counters} -d $OUT/pmc_{tag} -o run -- python3 $REPO/bench.py "
+               "--steps 2 --warmup 1 --decode-steps 9 --decode-warmup 1 --bwd-steps 1 --no-cpu-baseline "
+               "--no-peaks --phase-markers")
+
+
+def counter_summary(dbs, out_json, out_md, durations_db=None):
+    """Per (phase, stage) averages of the derived counters in COUNTER_PASSES,
+    from one rocprofv3 --pmc database per pass; with a --kernel-trace
+    database of a run with --phase-markers, also the MFMA rate each stage's
+    issued MFMA flops (MfmaFlopsBF16) make over its mean duration."""
+    acc = {}
+    for db in dbs:
+        for ph, stage, cn, v, _ in _db_rows(db):
+            if ph in ("calibration", "unmarked", "backward_setup"):
+                continue
+            acc.setdefault((ph, stage), {}).setdefault(cn, []).append(v)
+    durs = {}
+    if durations_db:
+        import bisect
+        import re
+        import sqlite3
+        cur = sqlite3.connect(durations_db).cursor()
+        kr = list(cur.execute("select name, duration, start from kernels order by start"))
+        marks = [st for nm, _, st in kr if MARKER_KERNEL in nm]
+        for nm, du, st in kr:
+            if MARKER_KERNEL in nm:
+                continue
+            ph = bisect.bisect_left(marks, st) - 1
+            if not 0 <= ph < len(PHASES):
+                continue
+            for stage, (pat, _) in STAGE_KERNELS.items():
+                if re.search(pat, nm):
+                    durs.setdefault((PHASES[ph], stage), []).append(du)
+                    break
+    out = {}
+    for (ph, stage), cs in acc.items():
+        ent = {cn: round(sum(v) / len(v), 4) for cn, v in cs.items()}
+        ent["dispatches"] = max(len(v) for v in cs.values())
+        ta, gui = ent.get("TA_BUSY_avr"), ent.get("GRBM_GUI_ACTIVE")
+        if ta is not None and gui:
+            # the raw GRBM_GUI_ACTIVE value is summed over the chip's 8 XCDs
+            # (the derived counters take its maximum, one XCD's active cycles)
+            ent["TA_busy_pct"] = round(100.0 * ta / (gui / N_XCD), 2)
+        h, m = ent.get("TCC_HIT_sum"), ent.get("TCC_MISS_sum")
+        if h is not None and m is not None and h + m > 0:
+            ent["L2_hit_pct"] = round(100.0 * h / (h + m), 2)
+        d = durs.get((ph, stage))
+        if d and ent.get("MfmaFlopsBF16"):
+            mean_ns = sum(d) / len(d)
+            ent["mean_duration_us"] = round(mean_ns / 1e3, 2)
+            ent["mfma_issued_tflops"] = round(ent["MfmaFlopsBF16"] / (mean_ns * 1e-9) / 1e12, 1)
+            ent["mfma_issued_frac_peak"] = round(ent["mfma_issued_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+        ent["source_hash"] = source_hash(*STAGE_KERNELS[stage][1])
+        out.setdefault(ph, {})[stage] = ent
+    cmds = [COUNTER_CMD.format(counters=" ".join(p), tag=f"pass{i + 1}") for i, p in enumerate(COUNTER_PASSES)]
+    cmds.append("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace -d $OUT/trace_marked -o run -- "
+                "python3 $REPO/bench.py --steps 2 --warmup 1 --decode-steps 9 --decode-warmup 1 --bwd-steps 1 "
+                "--no-cpu-baseline --no-peaks --phase-markers")
+    cmds.append("cd $REPO && python3 bench.py --counter-summary $OUT/trace_marked/run_results.db "
+                "$OUT/pmc_pass1/run_results.db $OUT/pmc_pass2/run_results.db")
+    data = {"commands": cmds, "phases": out}
+    with open(out_json, "w") as f:
+        json.dump(data, f, indent=1)
+    cols = [("MfmaUtil", "MFMA busy %"), ("mfma_issued_frac_peak", "MFMA flops / peak"),
+            ("VALUBusy", "VALU busy %"), ("TA_busy_pct", "TA busy %"),
+            ("MemUnitStalled", "mem unit stalled %"), ("L2_hit_pct", "L2 hit %"),
+            ("LDSBankConflict", "LDS bank conflict %"), ("OccupancyPercent", "occupancy %")]
+    with open(out_md, "w") as f:
+        f.write("# Hardware counters per kernel: prefill, decode and backward phases\n\n")
+        f.write("Derived rocprofv3 counters (rocprofiler-sdk definitions for gfx950), averaged over each "
+                "stage's dispatches within a phase; each pass is a run of its own (REPO is the repository "
+                "root, OUT any scratch folder):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
+        f.write("MfmaUtil = MFMA-busy cycles / (GPU-active cycles x SIMDs); MFMA flops / peak = "
+                "MfmaFlopsBF16 (512 x MFMA MOPS) over the stage's mean kernel-trace duration, against "
+                "2.5 PFLOP/s; VALUBusy = VALU-active cycles per CU / GPU-active cycles; TA busy % = busy "
+                "cycles of the texture-address unit averaged over its instances (TA_BUSY_avr) / one XCD's "
+                "GPU-active cycles (GRBM_GUI_ACTIVE, whose raw value sums the 8 XCDs, / 8); L2 hit % = "
+                "TCC_HIT / (TCC_HIT + TCC_MISS).\n\n")
+        f.write("| phase | stage | dispatches | " + " | ".join(c[1] for c in cols) + " |\n")
+        f.write("|---|---|---|" + "---|" * len(cols) + "\n")
+        for ph in PHASES:
+            for stage, e in out.get(ph, {}).items():
+                vals = [e.get(c[0]) for c in cols]
+                f.write(f"| {ph} | {stage} | {e['dispatches']} | " +
+                        " | ".join("" if v is None else f"{v:g}" for v in vals) + " |\n")
     return data
 
 
@@ -228,19 +354,79 @@ def stage_pass(fn, steps, copies):
     return {k: tot / max(cnt, 1) for k, (cnt, tot) in lisa.lisa_stage_timing_read(reset=True).items()}
 
 
+# peaks measured on this machine by the calibration kernels (measure_peaks)
+MEASURED = {}
+
+
 def roofline_entry(kernel, ms, work, bound, traffic=None):
+    measured = None
     if bound == "hbm":
         achieved = work / (ms * 1e-3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
+        measured = MEASURED.get("hbm_gbs")
     elif bound == "alu":
         achieved = work / (ms * 1e-3) / 1e12
         peak, unit = FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
     else:
         achieved = work / (ms * 1e-3) / 1e12
         peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        measured = MEASURED.get("mfma_bf16_tflops")
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel,
-            "avg_launch_ms": round(ms, 5), "algorithmic_per_launch": work}
+            "avg_launch_ms": round(ms, 5), "algorithmic_per_launch": work,
+            "measured_peak": measured, "frac_measured_peak": round(achieved / measured, 4) if measured else None}
+
+
+def measure_peaks(copy_bytes=1 << 30, mfma_iters=400, reps=5):
+    """The achievable peaks of this part, measured with the library's
+    calibration kernels: a plain streaming copy (bytes read + written per
+    second) and an MFMA loop (bf16 16x16x32, 8 waves per SIMD)."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.empty(1 << 21, dtype=torch.float32, device="cuda")
+
+    def best(fn):
+        times, work = [], 0.0
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            work = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        return work, sorted(times)[len(times) // 2]
+
+    w, ms = best(lambda: lisa.peak_probe(lisa.LISA_PROBE_COPY, src, dst, copy_bytes))
+    copy_gbs = w / (ms * 1e-3) / 1e9
+    w, ms = best(lambda: lisa.peak_probe(lisa.LISA_PROBE_READ, src, sink, copy_bytes))
+    read_gbs = w / (ms * 1e-3) / 1e9
+    MEASURED["hbm_copy_gbs"] = round(copy_gbs, 1)
+    MEASURED["hbm_read_gbs"] = round(read_gbs, 1)
+    # the better of the two is the achievable HBM rate the fractions use
+    MEASURED["hbm_gbs"] = round(max(copy_gbs, read_gbs), 1)
+    w, ms = best(lambda: lisa.peak_probe(lisa.LISA_PROBE_MFMA, None, sink, sink.numel() * 4, mfma_iters))
+    MEASURED["mfma_bf16_tflops"] = round(w / (ms * 1e-3) / 1e12, 1)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return dict(MEASURED, method="median of 5 event-timed launches of lisa_peak_probe: a copy of 1 GiB "
+                                 "(2 GiB moved), a read-only stream over 1 GiB (hbm_gbs is the "
+                                 "better of the two), and an MFMA loop (2048 x 256 threads, 400 x 8 bf16 "
+                                 "16x16x32 MFMAs per wave)")
+
+
+_MARK = {}
+
+
+def phase_marker(i):
+    """With --phase-markers: a 4 KiB calibration copy before phase i, which
+    splits a profiler database by phase (PHASES)."""
+    if not _MARK:
+        return
+    from hybrid_linear_top_amd import lisa
+    lisa.peak_probe(lisa.LISA_PROBE_COPY, _MARK["src"], _MARK["dst"], 4096)
 
 
 def cores_used():
@@ -254,15 +440,20 @@ def cores_used():
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(args):
+def bench_prefill(args, small=False):
+    """lisa_prefill on the 16K Qwen2.5-7B-shaped workload, or (small) on the
+    4K Qwen2.5-1.5B-shaped one, whose inputs are rotated over enough copies
+    that the Infinity Cache cannot hold them between repeats."""
     import numpy as np
     import torch
     from hybrid_linear_top_amd import inputs as gen, lisa
-    cfg = gen.PREFILL_7B_16K
+    cfg = gen.PREFILL_1P5B_4K if small else gen.PREFILL_7B_16K
     inp = gen.make_prefill_inputs(cfg)
     dims = lisa.dims_from_config(cfg)
     B, n = inp["B"], inp["n"]
-    copies = 2
+    per_copy = sum(inp[k].nbytes for k in ("q", "k", "v", "q_idx", "k_idx", "w_idx", "gate")) + \
+        inp["q"].nbytes + B * n * cfg.Hkv * cfg.M * 4
+    copies = rotating_copies(per_copy)
     keys = ("q", "k", "v", "q_idx", "k_idx", "w_idx", "gate")
     sets = [{k: lisa.to_device(inp[k]) for k in keys} for _ in range(copies)]
     outs = [torch.empty_like(s["q"]) for s in sets]
@@ -275,8 +466,9 @@ def bench_prefill(args):
         lisa.prefill(dims, s["q"], s["k"], s["v"], s["q_idx"], s["k_idx"], s["w_idx"], s["gate"],
                      out=outs[c], state_out=st, topm_out=idx[c], workspace=ws)
 
-    ms = timed_loop(step, args.steps, args.warmup, copies)
-    stages = stage_pass(step, max(3, min(args.steps, 10)), copies)
+    steps = args.steps * 5 if small else args.steps
+    ms = timed_loop(step, steps, args.warmup, copies)
+    stages = stage_pass(step, max(3, min(steps, 10)), copies)
     flops = prefill_flops(cfg, n, B)
     total_flops = sum(flops.values())
     stage_rows = {}
@@ -287,14 +479,20 @@ def bench_prefill(args):
                          "frac_mfma_peak": round(f / (v * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
                          if f else None}
     dom = max(stages, key=stages.get)
-    roof = roofline_entry(dom, stages[dom], flops.get(dom, 0), "mfma", traffic_from_profiles(dom))
+    phase = "prefill_1p5b_4k" if small else "prefill_7b_16k"
+    roof = roofline_entry(dom, stages[dom], flops.get(dom, 0), "mfma", traffic_from_profiles(dom, phase))
+    shape = "qwen2.5-1.5b-shaped" if small else "qwen2.5-7b-shaped"
     res = {
-        "workload": f"lisa_prefill qwen2.5-7b-shaped B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
+        "workload": f"lisa_prefill {shape} B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                     f"d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} C={cfg.chunk} bf16",
-        "tokens_per_s": B * n / (ms * 1e-3), "ms": ms, "roofline": roof, "stages": stage_rows,
+        "tokens_per_s": B * n / (ms * 1e-3), "ms": ms, "steps": steps, "copies": copies,
+        "roofline": roof, "stages": stage_rows,
         "step_roofline": {"bound": "mfma", "algorithmic_flops": total_flops,
                           "achieved_tflops": round(total_flops / (ms * 1e-3) / 1e12, 3),
-                          "frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+                          "frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "frac_measured_peak": round(total_flops / (ms * 1e-3) / 1e12 /
+                                                      MEASURED["mfma_bf16_tflops"], 4)
+                          if MEASURED.get("mfma_bf16_tflops") else None},
         "cfg": cfg, "inp": inp,
     }
     del sets, outs, idx, ws
@@ -347,7 +545,8 @@ def bench_decode(args, ragged=False):
     # the dominant kernel among those that move the step's algorithmic bytes
     # (the select pass works on the scores already in the workspace)
     dom = max((k for k in stages if by.get(k)), key=stages.get)
-    roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm", traffic_from_profiles(dom))
+    roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm",
+                          traffic_from_profiles(dom, "decode_7b_ragged" if ragged else "decode_1p5b_16k"))
     L = inp["lengths"]
     ctx = (f"ctx=16384+1" if not ragged else
            f"ragged ctx U[4096,32768]+1 (sum {int(L.sum())}, max {int(L.max())})")
@@ -358,7 +557,9 @@ def bench_decode(args, ragged=False):
         "tokens_per_s": B / (ms * 1e-3), "ms": ms, "roofline": roof, "stages": stage_rows,
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": by["total"],
                           "achieved_gbs": round(by["total"] / (ms * 1e-3) / 1e9, 1),
-                          "frac": round(by["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                          "frac": round(by["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "frac_measured_peak": round(by["total"] / (ms * 1e-3) / 1e9 / MEASURED["hbm_gbs"], 4)
+                          if MEASURED.get("hbm_gbs") else None},
         "cfg": cfg, "inp": inp,
     }
     del per, ws
@@ -389,6 +590,7 @@ def bench_backward(args, pre):
     dO, dS = lisa.to_device(binp["d_out"]), lisa.to_device(binp["d_state_out"])
     ws = torch.empty(lisa.lisa_prefill_backward_workspace_bytes(dims, B, n), dtype=torch.uint8,
                      device="cuda")
+    phase_marker(PHASES.index("backward_7b_16k"))
 
     def step(c):
         lisa.prefill_backward(dims, x["q"], x["k"], x["v"], x["gate"], idx, dO, state_in=s0,
@@ -401,7 +603,7 @@ def bench_backward(args, pre):
     # the query side runs on bf16 MFMA; the key side is fp32 VALU work whose
     # ceiling in practice is the L2 atomic rate
     bound = "mfma" if dom == "bwd_sparse_query" else "alu"
-    roof = roofline_entry(dom, stages[dom], fl.get(dom, 0), bound, traffic_from_profiles(dom))
+    roof = roofline_entry(dom, stages[dom], fl.get(dom, 0), bound, traffic_from_profiles(dom, "backward_7b_16k"))
     res = {
         "workload": f"lisa_prefill_backward qwen2.5-7b-shaped B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                     f"d={cfg.d} M={cfg.M} bf16 (sets from the forward; d_state_out and state_in given)",
@@ -494,17 +696,30 @@ def main():
                     help="write a per-kernel duration table from a rocprofv3 --kernel-trace "
                          "database and exit")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--phase-markers", action="store_true",
+                    help="launch a 4 KiB calibration copy before each phase (splits profiler databases)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DB",
+                    help="kernel-trace database of a --phase-markers run, then one rocprofv3 --pmc database "
+                         "per counter pass: write profiles/counters.json and the table, and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
     if args.kernel_stats:
         kernel_stats_summary(*args.kernel_stats)
         return
+    if args.counter_summary:
+        data = counter_summary(args.counter_summary[1:], os.path.join(PROFILES, "counters.json"),
+                               os.path.join(PROFILES, "counters_prefill_decode_backward.md"),
+                               durations_db=args.counter_summary[0])
+        print(json.dumps(data, indent=1))
+        return
     if args.traffic_summary:
         cmd = ("cd /tmp && export TMPDIR=/tmp && for c in FETCH_SIZE WRITE_SIZE; do "
                "timeout -s KILL 180 rocprofv3 --pmc $c -d $OUT/pmc_$c -o run -- "
                "python3 $REPO/bench.py --steps 2 --warmup 1 --decode-steps 9 --decode-warmup 1 "
-               "--bwd-steps 1 --no-ragged --no-cpu-baseline --copy-calibration; done; cd $REPO && python3 bench.py "
+               "--bwd-steps 1 --no-cpu-baseline --no-peaks --copy-calibration --phase-markers; done; "
+               "cd $REPO && python3 bench.py "
                "--traffic-summary $OUT/pmc_FETCH_SIZE/run_results.db "
                "$OUT/pmc_WRITE_SIZE/run_results.db")
         data = traffic_summary(*args.traffic_summary, os.path.join(PROFILES, "traffic.json"),
@@ -521,16 +736,31 @@ def main():
     if args.copy_calibration:
         nb = copy_calibration()
         print(json.dumps({"copy_calibration_bytes": nb}), flush=True)
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks()
+        print(f"[bench] measured peaks {peaks}", file=sys.stderr, flush=True)
+    if args.phase_markers:
+        _MARK["src"] = torch.zeros(1024, dtype=torch.float32, device="cuda")
+        _MARK["dst"] = torch.empty_like(_MARK["src"])
+    phase_marker(PHASES.index("prefill_7b_16k"))
     pre = bench_prefill(args)
     print(f"[bench] prefill {pre['ms']:.3f} ms/call, stages {pre['stages']}", file=sys.stderr, flush=True)
+    phase_marker(PHASES.index("prefill_1p5b_4k"))
+    pre_small = bench_prefill(args, small=True)
+    print(f"[bench] prefill (4K, 1.5B shapes) {pre_small['ms']:.4f} ms/call, stages {pre_small['stages']}",
+          file=sys.stderr, flush=True)
+    phase_marker(PHASES.index("decode_1p5b_16k"))
     dec = bench_decode(args)
     print(f"[bench] decode {dec['ms'] * 1e3:.1f} us/step, stages {dec['stages']}", file=sys.stderr, flush=True)
     rag = None
+    phase_marker(PHASES.index("decode_7b_ragged"))
     if not args.no_ragged:
         rag = bench_decode(args, ragged=True)
         print(f"[bench] ragged decode {rag['ms'] * 1e3:.1f} us/step, stages {rag['stages']}", file=sys.stderr,
               flush=True)
     bwd = None
+    phase_marker(PHASES.index("backward_setup"))
     if not args.no_backward:
         bwd = bench_backward(args, pre)
         print(f"[bench] backward {bwd['ms']:.2f} ms/call, stages {bwd['stages']}", file=sys.stderr, flush=True)
@@ -562,6 +792,13 @@ def main():
         "cpu_baseline": cpu_p,
         "step_roofline": pre["step_roofline"],
         "stages": pre["stages"],
+        "peaks_measured": peaks,
+        "prefill_1p5b_4k": {
+            "workload": pre_small["workload"], "value": round(pre_small["tokens_per_s"], 1),
+            "unit": "tokens/s", "steps": pre_small["steps"], "input_copies": pre_small["copies"],
+            "ms_per_step": round(pre_small["ms"], 5), "roofline": pre_small["roofline"],
+            "step_roofline": pre_small["step_roofline"], "stages": pre_small["stages"],
+        },
         "decode": {
             "workload": dec["workload"], "value": round(dec["tokens_per_s"], 1), "unit": "tokens/s",
             "steps": args.decode_steps, "warmup": args.decode_warmup,

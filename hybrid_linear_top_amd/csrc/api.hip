@@ -139,7 +139,7 @@ float scale_log2(const lisa_dims *d) {
 
 // ---- prefill workspace ------------------------------------------------------
 struct PrefillWs {
-    size_t idx, dS, P, kpk, total;
+    size_t idx, dS, P, kpk, cand, total;
 };
 // n query rows against nk key positions (nk = past + n; 0 when the indexer
 // does not run)
@@ -156,6 +156,8 @@ PrefillWs prefill_ws(const lisa_dims *d, int B, int n, int nk) {
     off += align_up((size_t)B * Hq * nC * D * D * elt_bytes(d->dtype));
     w.kpk = off;
     off += align_up(nk > 0 ? lisa::indexer_packed_bytes(B, nk, (int)G, d->idx_dim, d->dtype) : 0);
+    w.cand = off;
+    off += align_up(nk > 0 && d->top_m <= 512 ? lisa::indexer_cand_bytes(B, n, (int)G, d->top_m) : 0);
     w.total = off;
     return w;
 }
@@ -392,6 +394,7 @@ lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t
     ia.M = dims->top_m;
     ia.past = past;
     ia.k_packed = ws + w.kpk;
+    ia.cand = ws + w.cand;
     if (!window) {
         LISA_HIP(timed(ST_IDX_PACK, s, [&] { return lisa::launch_indexer_pack(ia, dims->dtype, dims->idx_dim, s); }),
                  "indexer key-pack launch");

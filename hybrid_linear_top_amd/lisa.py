@@ -28,7 +28,7 @@ EXPORTS = ["lisa_prefill_workspace_bytes", "lisa_prefill_continue_workspace_byte
            "lisa_prefill_window", "lisa_decode_step_window", "lisa_decode_step_paged",
            "lisa_decode_workspace_bytes", "lisa_prefill_backward_workspace_bytes",
            "lisa_prefill_backward",
-           "lisa_decode_step", "lisa_decode_step_noalloc", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
+           "lisa_decode_step", "lisa_decode_step_noalloc", "lisa_peak_probe", "lisa_stage_timing", "lisa_stage_timing_read", "lisa_last_error",
            "lisa_build_info"]
 
 
@@ -82,6 +82,8 @@ def _load(path: str = LIB_PATH):
     lib.lisa_decode_step.restype = ctypes.c_int
     lib.lisa_decode_step_noalloc.argtypes = [dp, i32, i64p, i32] + [vp] * 7 + [vp, vp, vp, vp]
     lib.lisa_decode_step_noalloc.restype = ctypes.c_int
+    lib.lisa_peak_probe.argtypes = [i32, vp, vp, sz, i32, ctypes.POINTER(ctypes.c_double), vp]
+    lib.lisa_peak_probe.restype = ctypes.c_int
     lib.lisa_stage_timing.argtypes = [i32]
     lib.lisa_stage_timing.restype = ctypes.c_int
     lib.lisa_stage_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p),
@@ -198,6 +200,22 @@ def lisa_decode_step_noalloc(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_id
     """Raw call; returns the status code (0 = LISA_OK)."""
     return _lib.lisa_decode_step_noalloc(ctypes.byref(dims), B, cu_ctx, max_ctx, q, k_cache, v_cache,
                                          q_idx, k_idx_cache, w_idx, gate, state, out, topm_out, stream)
+
+
+LISA_PROBE_COPY = 0
+LISA_PROBE_MFMA = 1
+LISA_PROBE_READ = 2
+
+
+def peak_probe(kind: int, src, dst, nbytes: int, iters: int = 0, stream=None) -> float:
+    """Enqueue a calibration kernel (lisa_peak_probe); returns its work (bytes
+    moved or flops)."""
+    work = ctypes.c_double(0.0)
+    st = _lib.lisa_peak_probe(kind, 0 if src is None else _ptr(src), _ptr(dst), int(nbytes), int(iters),
+                              ctypes.byref(work), _stream(stream))
+    if st != LISA_OK:
+        raise LisaError(st, f"lisa_peak_probe(kind={kind}) failed")
+    return work.value
 
 
 def lisa_stage_timing(enable: bool) -> None:

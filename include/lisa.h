@@ -316,6 +316,23 @@ lisa_status lisa_stage_timing(int32_t enable);
 lisa_status lisa_stage_timing_read(int32_t max_stages, const char **names, int64_t *launches,
                                    double *total_ms, int32_t *n_stages, int32_t reset);
 
+/*
+ * Roofline calibration, for benchmarking only (not part of the layer).
+ * kind LISA_PROBE_COPY: a plain streaming copy of `bytes` (a multiple of 16,
+ * 16-byte aligned buffers) from src to dst; *work = 2 * bytes moved.
+ * kind LISA_PROBE_READ: a read-only stream over `bytes` of src (dst is a
+ * sink of at least 8 MiB that is never written in practice); *work = bytes.
+ * kind LISA_PROBE_MFMA: `iters` rounds of eight independent bf16
+ * 16x16x32 MFMAs per wave on register operands, 8 waves per SIMD; dst is a
+ * sink of at least 2 MiB that is never written in practice; *work = the
+ * flops issued.  Enqueued on `stream`; the caller times it with events.
+ * Returns LISA_ERR_INVALID_ARGUMENT for a bad kind or buffer (nothing is
+ * enqueued then); the error message is not set.
+ */
+enum { LISA_PROBE_COPY = 0, LISA_PROBE_MFMA = 1, LISA_PROBE_READ = 2 };
+lisa_status lisa_peak_probe(int32_t kind, const void *src, void *dst, size_t bytes, int32_t iters,
+                            double *work, lisa_stream_t stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char *lisa_last_error(void);
 
