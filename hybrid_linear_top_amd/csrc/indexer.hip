@@ -23,24 +23,28 @@
 //    its query.
 //  * A candidate is accepted when its score is strictly above the query's
 //    threshold tau (a later equal score loses: the lowest-index tie-break).
-//    Accepted (score, key) pairs go, in key order, to a per-query staging
-//    ring in LDS (positions from an exclusive scan of the per-lane counts over
-//    the query's 16-lane row, by DPP), and from there in blocks of 64 to the
-//    query's candidate buffer in global memory (workspace).  A query's
-//    candidates are thus always in ascending key order.
-//  * When a buffer could overflow on the next tile it is trimmed in place: a
-//    256-bin histogram over the buffered scores finds the bin holding the
-//    M-th largest; the lower bins are dropped and tau becomes the largest
-//    dropped score, so at least M kept candidates beat everything rejected.
-//    When that frees too little (exact ties) an exact select keeps M.
+//    Each lane stages its accepted (score, key) pairs per query in LDS, up to
+//    kLane of them, with straight-line code (every key is written at the next
+//    free slot, which advances only past accepted ones).  When a lane could
+//    overflow on the next tile, the quad's staged pairs go to the queries'
+//    candidate buffers in global memory (workspace), each lane after the lower
+//    lanes of its query's row (a DPP scan of the counts).  Buffer order is
+//    therefore arbitrary; indices in it are distinct.
+//  * When a buffer could overflow on the next flush it is trimmed in place by
+//    streaming passes: a 256-bin histogram over the buffered scores finds the
+//    bin holding the M-th largest; the lower bins are dropped and tau becomes
+//    the largest dropped score, so at least M kept candidates beat everything
+//    rejected.  When that frees too little (exact ties) an exact select
+//    keeps M.
 //  * Late queries start from a threshold estimated from a sample of key
 //    tiles, so that only about 2 M candidates are appended; a query left
 //    with fewer than min(M, t+1) candidates (the estimate was too high) is
-//    scanned again from tau = -inf, so the result is exact whatever the
-//    sample says.
-//  * The exact select (radix select on order-preserving keys, ties to the
-//    lower buffer position = lower index) keeps min(M, t+1) candidates at the
-//    end; they are written out in buffer order, which is ascending.
+//    scanned again, first from a lower sample estimate, then from -inf, so
+//    the result is exact whatever the sample says.
+//  * At the end an exact select (radix select on order-preserving 64-bit
+//    keys: score, then the lower index) keeps min(M, t+1) candidates; they
+//    are marked in an LDS bitmap over positions 0..t and written out in
+//    position order, -1 padded.
 #include <type_traits>
 
 #include "common.hpp"
@@ -49,8 +53,8 @@
 namespace lisa {
 namespace {
 
-constexpr int kKT = 64;     // keys per tile
-constexpr int kRing = 128;  // staging-ring entries per query (LDS)
+constexpr int kKT = 64;    // keys per tile
+constexpr int kLane = 8;   // staging entries per lane and query (LDS)
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
     const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
@@ -65,68 +69,46 @@ __device__ __forceinline__ void wave_global_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// A query's buffered candidates in registers: entry k*64 + lane in slot k.
-template <int NE>
-struct Cands {
-    float sc[NE];
-    uint32_t key[NE];
-};
-
-template <int NE>
-__device__ __forceinline__ void load_cands(const u32x2 *qbuf, int c, Cands<NE> &x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int k = 0; k < NE; ++k) {
-        const int e = k * 64 + lane;
-        u32x2 v = u32x2{0u, 0u};
-        if (e < c) v = qbuf[e];
-        x.sc[k] = __uint_as_float(v[0]);
-        x.key[k] = v[1];
-    }
+// The candidate order as one 64-bit key: higher score first (order-preserving
+// bits, -0.0 = +0.0), then lower index.  A query's candidates have distinct
+// indices, so their keys are distinct.
+__device__ __forceinline__ uint64_t cand_key(float sc, uint32_t idx) {
+    return ((uint64_t)order_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
 }
 
-// Mark exactly the first m of the c candidates in the order (higher score,
-// lower buffer position).  Whole wave, uniform control flow.  Returns the
-// order key of the m-th.  The threshold is found by 256-bin histogram passes
-// over the live range of order keys, [min, max] first (buffered candidates
-// sit in a narrow band, so fixed 8-bit digits would waste passes on common
-// high bits); a pass stops as soon as the bin holding the m-th key is taken
-// whole, or holds a single key value (ties: the earliest positions win).
-template <int NE>
-__device__ uint32_t select_first(const Cands<NE> &x, int c, int m, bool (&keep)[NE], uint32_t *hist) {
+// theta = the m-th largest of the distinct keys that for_each(f) presents as
+// f(valid, key): exactly m of them are >= theta (1 <= m <= their count).
+// Radix passes of 256 bins over the live range [min, max] first (candidates
+// sit in a narrow band), each narrowing to the bin that holds the m-th key,
+// until that bin is taken whole.  Whole wave, uniform control flow.
+template <typename ForEach>
+__device__ uint64_t select_theta(ForEach &&for_each, int m, uint32_t *hist) {
     const int lane = threadIdx.x & 63;
-    // order keys are recomputed where needed rather than held (registers)
-    auto u = [&](int k) { return order_key(x.sc[k]); };
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int k = 0; k < NE; ++k) {
-        if (k * 64 + lane < c) {
-            kmin = min(kmin, u(k));
-            kmax = max(kmax, u(k));
+    // the live range from the keys' high words (DPP reductions): [min_hi.0,
+    // max_hi.ffffffff] holds every key
+    uint32_t hmin = 0xFFFFFFFFu, hmax = 0u;
+    for_each([&](bool valid, uint64_t k) {
+        if (valid) {
+            hmin = min(hmin, (uint32_t)(k >> 32));
+            hmax = max(hmax, (uint32_t)(k >> 32));
         }
-    }
-    uint32_t lo = wave_min_u32(kmin);
-    const uint32_t span = wave_max_u32(kmax) - lo;
-    int width = span == 0 ? 0 : 32 - __builtin_clz(span);  // bits of key - lo
+    });
+    uint64_t lo = (uint64_t)wave_min_u32(hmin) << 32;
+    const uint64_t span = (((uint64_t)wave_max_u32(hmax) << 32) | 0xFFFFFFFFull) - lo;
+    int width = span == 0 ? 0 : 64 - __builtin_clzll(span);  // bits of key - lo
     uint32_t need = (uint32_t)m;
-    uint32_t theta;    // keys > theta are kept, and keys == theta up to take_eq,
-    uint32_t take_eq;  // or (whole_bin) every key >= theta
-    bool whole_bin;
 #pragma unroll 1
     for (;;) {
         const int shift = width > 8 ? width - 8 : 0;
+        const uint64_t last = width >= 64 ? ~0ull : (1ull << width) - 1;  // the range is [lo, lo + last]
         *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
-        const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            const uint32_t uk = u(k);
-            if (k * 64 + lane < c && uk >= lo && (uint64_t)uk < hi_excl) atomicAdd(&hist[(uk - lo) >> shift], 1u);
-        }
+        for_each([&](bool valid, uint64_t k) {
+            if (valid && k >= lo && k - lo <= last) atomicAdd(&hist[(k - lo) >> shift], 1u);
+        });
         wave_lds_sync();
         const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
-        const uint32_t lsum = h[0] + h[1] + h[2] + h[3];
-        const uint32_t incl = wave_inclusive_scan(lsum);
+        const uint32_t incl = wave_inclusive_scan(h[0] + h[1] + h[2] + h[3]);
         const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
         uint32_t run = total - incl;  // keys in the bins of higher lanes
         int fb = -1;
@@ -145,63 +127,25 @@ __device__ uint32_t select_first(const Cands<NE> &x, int c, int m, bool (&keep)[
         fneed = (uint32_t)__builtin_amdgcn_readlane((int)fneed, src);
         fcnt = (uint32_t)__builtin_amdgcn_readlane((int)fcnt, src);
         wave_lds_sync();
-        const uint32_t blo = lo + ((uint32_t)fb << shift);
-        if (fneed == fcnt) {  // the whole bin is kept: keys >= blo are exactly the first m
-            theta = blo;
-            take_eq = 0u;
-            whole_bin = true;
-            break;
-        }
-        if (shift == 0) {  // one key value: the earliest fneed of them
-            theta = blo;
-            take_eq = fneed;
-            whole_bin = false;
-            break;
-        }
+        const uint64_t blo = lo + ((uint64_t)fb << shift);
+        // the bin taken whole: keys >= blo are exactly the first m (with
+        // distinct keys a single-value bin holds one, so this always ends)
+        if (fneed == fcnt || shift == 0) return blo;
         lo = blo;
         width = shift;
         need = fneed;
     }
-    uint32_t eq_seen = 0u, kth = 0xFFFFFFFFu;
-#pragma unroll
-    for (int k = 0; k < NE; ++k) {
-        const bool valid = k * 64 + lane < c;
-        const uint32_t uk = u(k);
-        const bool gt = valid && (whole_bin ? uk >= theta : uk > theta);
-        const bool eq = valid && !whole_bin && uk == theta;
-        const uint64_t em = __ballot(eq);
-        const uint32_t er = eq_seen + mbcnt64(em);
-        eq_seen += (uint32_t)__popcll(em);
-        keep[k] = gt || (eq && er < take_eq);
-        if (keep[k]) kth = min(kth, uk);
-    }
-    return wave_min_u32(kth);
-}
-
-// Stable compaction of the kept entries to positions 0.. (slot order =
-// buffer order); returns how many were kept.
-template <int NE, typename F>
-__device__ __forceinline__ int compact(const bool (&keep)[NE], F &&put) {
-    uint32_t base = 0u;
-#pragma unroll
-    for (int k = 0; k < NE; ++k) {
-        const uint64_t km = __ballot(keep[k]);
-        const uint32_t pos = base + mbcnt64(km);
-        base += (uint32_t)__popcll(km);
-        if (keep[k]) put(k, pos);
-    }
-    return (int)base;
 }
 
 // ---- trims: streaming passes over a query's buffer in global memory --------
 // A trim runs on the rare occasions a buffer fills up (a query rescanned from
-// tau = -inf, or adversarial scores), so it reads the buffer in chunks of 256
-// entries per pass rather than holding it in registers: the scan's own
+// a low threshold, or adversarial scores), so it reads the buffer in chunks
+// of 256 entries per pass rather than holding it in registers: the scan's own
 // registers stay live across it.
 constexpr int kChunkL = 4;  // entries per lane and chunk
 
-// f(e, valid, score, key) for every entry e < c, in order; the chunk's loads
-// are all issued before f sees any of them
+// f(valid, score, index) for every entry e < c; a chunk's loads are all
+// issued before f sees any of them
 template <typename F>
 __device__ __forceinline__ void stream_cands(const u32x2 *qbuf, int c, F &&f) {
     const int lane = threadIdx.x & 63;
@@ -214,31 +158,22 @@ __device__ __forceinline__ void stream_cands(const u32x2 *qbuf, int c, F &&f) {
             v[j] = e < c ? qbuf[e] : u32x2{0u, 0u};
         }
 #pragma unroll
-        for (int j = 0; j < kChunkL; ++j) {
-            const int e = base + j * 64 + lane;
-            f(e, e < c, __uint_as_float(v[j][0]), v[j][1]);
-        }
+        for (int j = 0; j < kChunkL; ++j) f(base + j * 64 + lane < c, __uint_as_float(v[j][0]), v[j][1]);
     }
 }
 
-// In-place stable compaction of the entries keep(score, key, rank) marks,
-// where rank counts the earlier entries for which eq(score) holds.  A kept
-// entry moves to a position at or below its own, and every position a chunk
-// writes was read by that chunk or an earlier one, so reads and writes do not
-// collide.
-template <typename K, typename E>
-__device__ int compact_stream(u32x2 *qbuf, int c, K &&keep, E &&eq) {
-    uint32_t base = 0u, eq_seen = 0u;
-    stream_cands(qbuf, c, [&](int, bool valid, float sc, uint32_t key) {
-        const bool is_eq = valid && eq(sc);
-        const uint64_t em = __ballot(is_eq);
-        const uint32_t er = eq_seen + mbcnt64(em);
-        eq_seen += (uint32_t)__popcll(em);
-        const bool kp = valid && keep(sc, is_eq, er);
+// In-place stable compaction of the entries keep(score, index) marks.  A
+// kept entry moves to a position at or below its own, and every position a
+// chunk writes was read by that chunk or an earlier one.
+template <typename K>
+__device__ int compact_stream(u32x2 *qbuf, int c, K &&keep) {
+    uint32_t base = 0u;
+    stream_cands(qbuf, c, [&](bool valid, float sc, uint32_t idx) {
+        const bool kp = valid && keep(sc, idx);
         const uint64_t km = __ballot(kp);
         const uint32_t pos = base + mbcnt64(km);
         base += (uint32_t)__popcll(km);
-        if (kp) qbuf[pos] = u32x2{__float_as_uint(sc), key};
+        if (kp) qbuf[pos] = u32x2{__float_as_uint(sc), idx};
     });
     return (int)base;
 }
@@ -248,18 +183,19 @@ struct TrimResult {
     float tau;
 };
 
-// Trim one query's c buffered candidates to about M, in place.  First a
-// 256-bin histogram over [min, max] of the scores: every bin from the one
-// holding the M-th largest up is kept, and tau becomes the largest dropped
-// score, so at least M kept candidates beat everything rejected.  When that
-// would keep more than c - need_free (exact ties, or a spread too narrow for
-// the bins), radix passes over the order keys find the M-th exactly and
-// exactly M are kept (ties: the earliest positions, the lower indices).
-__device__ __attribute__((noinline)) TrimResult trim_buffer(u32x2 *qbuf, int c, int M, int need_free,
+// Trim one query's c buffered candidates (all in its global buffer) to at
+// most max_keep and at least M, in place.  First a 256-bin histogram over
+// [min, max] of the scores: every bin from the one holding the M-th largest
+// up is kept, and tau becomes the largest dropped score, so at least M kept
+// candidates beat everything rejected.  When that would keep more than
+// max_keep (exact ties, or a spread too narrow for the bins), the exact M are
+// kept (select_theta on the candidate keys) and tau is the M-th score: a later
+// key with that score has a higher index and loses.
+__device__ __attribute__((noinline)) TrimResult trim_buffer(u32x2 *qbuf, int c, int M, int max_keep,
                                                             uint32_t *hist) {
     const int lane = threadIdx.x & 63;
     float mn = INFINITY, mx = -INFINITY;
-    stream_cands(qbuf, c, [&](int, bool valid, float sc, uint32_t) {
+    stream_cands(qbuf, c, [&](bool valid, float sc, uint32_t) {
         if (valid) {
             mn = fminf(mn, sc);
             mx = fmaxf(mx, sc);
@@ -272,7 +208,7 @@ __device__ __attribute__((noinline)) TrimResult trim_buffer(u32x2 *qbuf, int c, 
         auto bin_of = [&](float sc) { return min(255, (int)((sc - mn) * scale)); };
         *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
-        stream_cands(qbuf, c, [&](int, bool valid, float sc, uint32_t) {
+        stream_cands(qbuf, c, [&](bool valid, float sc, uint32_t) {
             if (valid) atomicAdd(&hist[bin_of(sc)], 1u);
         });
         wave_lds_sync();
@@ -294,83 +230,23 @@ __device__ __attribute__((noinline)) TrimResult trim_buffer(u32x2 *qbuf, int c, 
         fb = __builtin_amdgcn_readlane(fb, src);
         kept = (uint32_t)__builtin_amdgcn_readlane((int)kept, src);
         wave_lds_sync();
-        if (fb > 0 && (int)kept <= c - need_free) {
+        if (fb > 0 && (int)kept <= max_keep) {
             float dmax = -INFINITY;
-            stream_cands(qbuf, c, [&](int, bool valid, float sc, uint32_t) {
+            stream_cands(qbuf, c, [&](bool valid, float sc, uint32_t) {
                 if (valid && bin_of(sc) < fb) dmax = fmaxf(dmax, sc);
             });
             dmax = wave_max(dmax);
-            const int nk = compact_stream(
-                qbuf, c, [&](float sc, bool, uint32_t) { return bin_of(sc) >= fb; }, [](float) { return false; });
+            const int nk = compact_stream(qbuf, c, [&](float sc, uint32_t) { return bin_of(sc) >= fb; });
             wave_global_sync();
             return TrimResult{nk, dmax};
         }
     }
-    // exact: radix passes over the live range of order keys, as select_first
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    stream_cands(qbuf, c, [&](int, bool valid, float sc, uint32_t) {
-        if (valid) {
-            kmin = min(kmin, order_key(sc));
-            kmax = max(kmax, order_key(sc));
-        }
-    });
-    uint32_t lo = wave_min_u32(kmin);
-    const uint32_t span = wave_max_u32(kmax) - lo;
-    int width = span == 0 ? 0 : 32 - __builtin_clz(span);
-    uint32_t need = (uint32_t)M, theta, take_eq;
-    bool whole_bin;
-#pragma unroll 1
-    for (;;) {
-        const int shift = width > 8 ? width - 8 : 0;
-        *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
-        wave_lds_sync();
-        const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
-        stream_cands(qbuf, c, [&](int, bool valid, float sc, uint32_t) {
-            const uint32_t u = order_key(sc);
-            if (valid && u >= lo && (uint64_t)u < hi_excl) atomicAdd(&hist[(u - lo) >> shift], 1u);
-        });
-        wave_lds_sync();
-        const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
-        const uint32_t incl = wave_inclusive_scan(h[0] + h[1] + h[2] + h[3]);
-        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-        uint32_t run = total - incl;
-        int fb = -1;
-        uint32_t fneed = 0, fcnt = 0;
-#pragma unroll
-        for (int bb = 3; bb >= 0; --bb) {
-            if (fb < 0 && run < need && run + h[bb] >= need) {
-                fb = 4 * lane + bb;
-                fneed = need - run;
-                fcnt = h[bb];
-            }
-            run += h[bb];
-        }
-        const int src = __ffsll((unsigned long long)__ballot(fb >= 0)) - 1;
-        fb = __builtin_amdgcn_readlane(fb, src);
-        fneed = (uint32_t)__builtin_amdgcn_readlane((int)fneed, src);
-        fcnt = (uint32_t)__builtin_amdgcn_readlane((int)fcnt, src);
-        wave_lds_sync();
-        const uint32_t blo = lo + ((uint32_t)fb << shift);
-        if (fneed == fcnt || shift == 0) {
-            theta = blo;
-            whole_bin = fneed == fcnt;
-            take_eq = whole_bin ? 0u : fneed;
-            break;
-        }
-        lo = blo;
-        width = shift;
-        need = fneed;
-    }
-    const int nk = compact_stream(
-        qbuf, c,
-        [&](float sc, bool is_eq, uint32_t er) {
-            const uint32_t u = order_key(sc);
-            return (whole_bin ? u >= theta : u > theta) || (is_eq && er < take_eq);
-        },
-        [&](float sc) { return !whole_bin && order_key(sc) == theta; });
+    const uint64_t theta = select_theta(
+        [&](auto &&f) { stream_cands(qbuf, c, [&](bool valid, float sc, uint32_t idx) { f(valid, cand_key(sc, idx)); }); },
+        M, hist);
+    const int nk = compact_stream(qbuf, c, [&](float sc, uint32_t idx) { return cand_key(sc, idx) >= theta; });
     wave_global_sync();
-    // the M-th kept key bounds every later candidate: equal scores lose
-    return TrimResult{nk, key_to_float(theta)};
+    return TrimResult{nk, key_to_float((uint32_t)(theta >> 32))};
 }
 
 // Packed key tiles: for batch b and group g, tile kt holds keys 64kt..64kt+63
@@ -417,8 +293,12 @@ template <typename T, int DI, int HH, int QB, int CAPG>
 __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     using C = IdxCfg<T, DI, HH, QB, CAPG>;
     constexpr int kQW = C::QW;
-    __shared__ __attribute__((aligned(16))) u32x2 ring[kQW * kRing];
+    // per query, per lane of its 16-lane row: kLane staged candidates; the
+    // area doubles as the output bitmap of the final select (32768 bits at 4
+    // queries per wave)
+    __shared__ __attribute__((aligned(16))) u32x2 lists[kQW * 16 * kLane];
     __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+    static_assert(kQW * 16 * kLane * 8 >= 4096, "the bitmap needs 4 KB");
 
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, grp = lane >> 4;
@@ -438,7 +318,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     const int ntk = (nk + kKT - 1) / kKT;  // key tiles
     const T *kI = reinterpret_cast<const T *>(a.k_packed) + ((size_t)b * G + g) * ntk * kKT * DI;
     const T *wI = reinterpret_cast<const T *>(a.w_idx);
-    // candidate buffer of query row tr: unit (b, tr, g)
+    // candidate buffer of query qq of the wave: unit (b, row, g)
     u32x2 *const cand = reinterpret_cast<u32x2 *>(a.cand);
     auto qbuf_of = [&](int qq) { return cand + (((size_t)b * nq + (qw0 - p0 + qq)) * G + g) * CAPG; };
 
@@ -470,16 +350,18 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
             }
         }
     }
-    // per quad, for this lane's query: candidates so far (cnt), how many of
-    // them are already in the global buffer (fl), and the threshold
-    int cnt[QB], fl[QB];
+    // per quad: this lane's staged candidates (cl), its query's candidates in
+    // the global buffer (gc, the same on the query's 16 lanes) and threshold
+    int cl[QB], gc[QB];
     float tau[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        cnt[qb] = 0;
-        fl[qb] = 0;
+        cl[qb] = 0;
+        gc[qb] = 0;
         tau[qb] = tq[qb] < nk ? -INFINITY : INFINITY;  // padding queries accept nothing
     }
+    // this lane's staging list for the query of quad qb
+    auto list_of = [&](int qb) { return lists + ((qb * 4 + grp) * 16 + col) * kLane; };
 
     // B fragments of one packed key tile: key 4*col + cb, dims 32*kc + 8*grp
     // .. +7, through a per-tile buffer descriptor (tiles past the last read
@@ -499,53 +381,12 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                 frag_buf_load(bf[cb][kc], r, voff + (uint32_t)(cb * C::KD + kc) * kFragBytes);
     };
 
-    // scores of one quad for one tile: score[cb] for key k0 + 4*col + cb of query tq[qb]
-    auto quad_scores = [&](int qb, const Frag<T> (&bcur)[4][C::KD], float (&score)[4]) {
-        f32x4 acc[HH][4];
-#pragma unroll
-        for (int hh = 0; hh < HH; ++hh)
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                f32x4 x = {0, 0, 0, 0};
-#pragma unroll
-                for (int kc = 0; kc < C::KD; ++kc) x = mma16(af[qb][hh][kc], bcur[cb][kc], x);
-                acc[hh][cb] = x;
-            }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            float sc = 0.0f;
-#pragma unroll
-            for (int hh = 0; hh < HH; ++hh)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sc = fmaf(wv[qb][hh][i], fmaxf(acc[hh][cb][i], 0.0f), sc);
-            score[cb] = sc;
-        }
-    };
-
-    // Move entries [fl, fl + 64) of query qq from its ring to its global buffer.
-    auto flush64 = [&](int qq, int f) {
-        const u32x2 e = ring[qq * kRing + ((f + lane) & (kRing - 1))];
-        qbuf_of(qq)[f + lane] = e;
-    };
-    // Move the ring's remaining entries [f, c) (fewer than 64) to the buffer.
-    auto flush_rest = [&](int qq, int f, int c) {
-        if (lane < c - f) {
-            const u32x2 e = ring[qq * kRing + ((f + lane) & (kRing - 1))];
-            qbuf_of(qq)[f + lane] = e;
-        }
-    };
-
-    // The rejected keys of an append write to a per-lane sink (in the
-    // histogram, which every trim and select clears before use), so appends
-    // are straight-line code with no exec-mask branches.
-    u32x2 *const sink = reinterpret_cast<u32x2 *>(hist) + lane;
-
-    auto tile_step = [&](int kt, const Frag<T> (&bcur)[4][C::KD], auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;  // tile reaches past the first query
-        const int k0 = kt * kKT;
-        // every quad's MFMAs first, so that the matrix core runs ahead of the
-        // epilogues instead of each epilogue waiting for its quad's results
-        f32x4 acc[QB][HH][4];
+    // One tile in two halves: every quad's MFMAs (the caller then reuses the
+    // fragment registers for the next tile's loads, in flight during the
+    // epilogue), and the epilogue, score[qb][cb] for key k0 + 4*col + cb of
+    // query tq[qb].
+    using Acc = f32x4[QB][HH][4];
+    auto tile_mfma = [&](const Frag<T> (&bcur)[4][C::KD], Acc &acc) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -557,11 +398,10 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                     for (int kc = 0; kc < C::KD; ++kc) x = mma16(af[qb][hh][kc], bcur[cb][kc], x);
                     acc[qb][hh][cb] = x;
                 }
-        uint64_t flushq = 0;  // quads with a query to flush (64+ ring entries) or to trim
+    };
+    auto tile_epilogue = [&](const Acc &acc, float (&score)[QB][4]) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float score[4];
-            bool ok[4];
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
                 float sc = 0.0f;
@@ -569,63 +409,78 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                 for (int hh = 0; hh < HH; ++hh)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sc = fmaf(wv[qb][hh][i], fmaxf(acc[qb][hh][cb][i], 0.0f), sc);
-                score[cb] = sc;
-                if constexpr (DIAG) ok[cb] = (k0 + 4 * col + cb <= tq[qb]) && sc > tau[qb];
-                else ok[cb] = sc > tau[qb];
+                score[qb][cb] = sc;
             }
-            // Append in ascending key order: a query's accepted keys are
-            // ordered by (col, cb), so a lane's first position is the query's
-            // count plus the exclusive scan of the per-lane counts over its
-            // 16-lane row.
-            const uint32_t c4 = (uint32_t)ok[0] + (uint32_t)ok[1] + (uint32_t)ok[2] + (uint32_t)ok[3];
-            const uint32_t incl = row_inclusive_scan(c4);
-            const uint32_t tot = row_broadcast15(incl);
-            int pos = cnt[qb] + (int)(incl - c4);
-            u32x2 *qring = ring + (qb * 4 + grp) * kRing;
+    };
+
+    // Move quad qb's staged candidates to its queries' global buffers: a
+    // lane's entries go after those of the lower lanes of its row (exclusive
+    // scan of the counts over the row).  Then trim any buffer that another
+    // flush could overflow.
+    // The wave's candidate buffers through one descriptor: query qq's entry e
+    // is entry qq * G * CAPG + e; stores at offsets past the end are dropped,
+    // so a lane's flush needs no branch per entry.
+    const uint32_t qstride = (uint32_t)G * CAPG;
+    const rsrc_t crs = make_rsrc(qbuf_of(0), ((uint32_t)(kQW - 1) * qstride + CAPG) * 8u);
+    auto flush_quad = [&](int qb) {
+        const uint32_t incl = row_inclusive_scan((uint32_t)cl[qb]);
+        const int tot = (int)row_broadcast15(incl);
+        const uint32_t off = (uint32_t)(qb * 4 + grp) * qstride + (uint32_t)(gc[qb] + (int)incl - cl[qb]);
+        const u32x2 *const my = list_of(qb);
+        u32x2 e[kLane];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                u32x2 *dst = ok[cb] ? qring + (pos & (kRing - 1)) : sink;
-                *dst = u32x2{__float_as_uint(score[cb]), (uint32_t)(k0 + 4 * col + cb)};
-                pos += ok[cb] ? 1 : 0;
-            }
-            cnt[qb] += (int)tot;
-            flushq |= __ballot(cnt[qb] - fl[qb] >= 64 || cnt[qb] > CAPG - kKT) ? (1ull << qb) : 0ull;
-        }
-        if (!flushq) return;
-        wave_lds_sync();  // the appends are read by other lanes below
+        for (int j = 0; j < kLane; ++j) e[j] = my[j];  // all reads first: one wait
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            if (!((flushq >> qb) & 1ull)) continue;
-            const uint64_t need = __ballot(cnt[qb] - fl[qb] >= 64);
+        for (int j = 0; j < kLane; ++j)
+            __builtin_amdgcn_raw_buffer_store_b64(e[j], crs, j < cl[qb] ? (off + (uint32_t)j) * 8u : kOffNone, 0u, 0);
+        gc[qb] += tot;
+        cl[qb] = 0;
+        const uint64_t full = __ballot(gc[qb] > CAPG - 16 * kLane);
+        if (!full) return;
+        wave_global_sync();
 #pragma unroll 1
-            for (int gg = 0; gg < 4; ++gg) {
-                if (!((need >> (16 * gg)) & 1ull)) continue;
-                flush64(qb * 4 + gg, __builtin_amdgcn_readlane(fl[qb], 16 * gg));
-            }
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg)
-                if (grp == gg && ((need >> (16 * gg)) & 1ull)) fl[qb] += 64;
-            // trim any buffer that could overflow on the next tile
-            const uint64_t full = __ballot(cnt[qb] > CAPG - kKT);
-            if (!full) continue;
-#pragma unroll 1
-            for (int gg = 0; gg < 4; ++gg) {
-                if (!((full >> (16 * gg)) & 1ull)) continue;
-                const int qq = qb * 4 + gg;
-                const int c = __builtin_amdgcn_readlane(cnt[qb], 16 * gg);
-                flush_rest(qq, __builtin_amdgcn_readlane(fl[qb], 16 * gg), c);
-                wave_global_sync();
-                const TrimResult tr = trim_buffer(qbuf_of(qq), c, M, CAPG / 4, hist);
-                if (grp == gg) {
-                    cnt[qb] = tr.c;
-                    fl[qb] = tr.c;
-                    tau[qb] = tr.tau;
-                }
+        for (int gg = 0; gg < 4; ++gg) {
+            if (!((full >> (16 * gg)) & 1ull)) continue;
+            const TrimResult tr = trim_buffer(qbuf_of(qb * 4 + gg), __builtin_amdgcn_readlane(gc[qb], 16 * gg), M,
+                                              CAPG - 2 * 16 * kLane, hist);
+            if (grp == gg) {
+                gc[qb] = tr.c;
+                tau[qb] = tr.tau;
             }
         }
     };
 
-    Frag<T> b0[4][C::KD], b1[4][C::KD];
+    auto tile_step = [&](int kt, const Acc &acc, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;  // tile reaches past the first query
+        const int k0 = kt * kKT;
+        float score[QB][4];
+        tile_epilogue(acc, score);
+        uint64_t flushq = 0;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            u32x2 *const my = list_of(qb);
+            // Every key is written at the lane's next free slot, and the slot
+            // advances only past accepted ones: a rejected key is overwritten
+            // by the next key or left past the end, so staging is
+            // straight-line code (slots cl .. cl + 3 are at most 7 here).
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const uint32_t key = (uint32_t)(k0 + 4 * col + cb);
+                bool ok = score[qb][cb] > tau[qb];
+                if constexpr (DIAG) ok = ok && (int)key <= tq[qb];
+                my[cl[qb]] = u32x2{__float_as_uint(score[qb][cb]), key};
+                cl[qb] += ok ? 1 : 0;
+            }
+            // a lane can stage 4 more next tile
+            flushq |= __ballot(cl[qb] > kLane - 4) ? (1ull << qb) : 0ull;
+        }
+        if (!flushq) return;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            if ((flushq >> qb) & 1ull) flush_quad(qb);
+    };
+
+    Frag<T> bf[4][C::KD];
     // tiles below kd hold only keys < qw0 <= every query of the wave
     const int kd = qw0 / kKT;
     // Prefetches are never skipped: a tile past the end is fetched through an
@@ -636,17 +491,17 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     auto tile_or_null = [&](int kt, int lim) { return kt < lim ? kt : knull; };
 
     // ---- starting threshold from a key sample ---------------------------------
-    // With tau starting at -inf a late query appends about M*ln(t/M) keys and
-    // trims its buffer several times.  Instead, ns tiles spread over the keys
-    // below qw0 are scored first; each lane keeps its four best sample scores
-    // per query, and tau starts at (about) the R-th largest of a query's 64
-    // kept values, R chosen so that about kSlack*M of the query's t+1 keys are
-    // expected above it.  This is only a starting point: the scan below
-    // accepts what beats it, and a query left with fewer than min(M, t+1)
-    // candidates (tau was too high) is scanned again from tau = -inf.
+    // With tau starting at -inf a late query would stage every key.  Instead,
+    // ns tiles spread over the keys below qw0 are scored first; each lane keeps
+    // its four best sample scores per query, and tau starts at (about) the
+    // R-th largest of a query's 64 kept values, R chosen so that about
+    // kSlack*M of the query's t+1 keys are expected above it (tau1, for a
+    // second attempt, about twice as many).  This is only a starting point:
+    // the scan accepts what beats it, and a query left with fewer than
+    // min(M, t+1) candidates is scanned again from a lower threshold.
     constexpr float kSlack = 2.0f;
     constexpr int kRank = 32;
-    float tau1[QB];  // a lower start for queries the first estimate starves
+    float tau1[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) tau1[qb] = -INFINITY;
     int ns = 0;
@@ -660,14 +515,14 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) top[qb][i] = -INFINITY;
-        auto sample_tile = [&](const Frag<T> (&bc)[4][C::KD]) {
+        auto sample_tile = [&](const Acc &acc) {
+            float score[QB][4];
+            tile_epilogue(acc, score);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float score[4];
-                quad_scores(qb, bc, score);
+            for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
-                    float x = score[cb];  // insert into the descending top-4
+                    float x = score[qb][cb];  // insert into the descending top-4
 #pragma unroll
                     for (int i = 0; i < 3; ++i) {
                         const float hi = fmaxf(top[qb][i], x);
@@ -676,16 +531,14 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                     }
                     top[qb][3] = fmaxf(top[qb][3], x);
                 }
-            }
         };
         auto ks = [&](int i) { return ((2 * i + 1) * kd) / (2 * ns); };
-        load_b(ks(0), b0);
-        for (int i = 0; i < ns; i += 2) {
-            load_b(i + 1 < ns ? ks(i + 1) : knull, b1);
-            sample_tile(b0);
-            if (i + 1 >= ns) break;
-            load_b(i + 2 < ns ? ks(i + 2) : knull, b0);
-            sample_tile(b1);
+        load_b(ks(0), bf);
+        for (int i = 0; i < ns; ++i) {
+            Acc acc;
+            tile_mfma(bf, acc);
+            load_b(i + 1 < ns ? ks(i + 1) : knull, bf);
+            sample_tile(acc);
         }
         const float S = (float)(ns * kKT);
 #pragma unroll
@@ -697,13 +550,13 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
                 return (float)row_broadcast15(row_inclusive_scan(c));
             };
             // the largest x with at least R kept sample values >= x, by bisection
-            auto rank_value = [&](float R) {
+            auto rank_value = [&](float Rk) {
                 float lo = row_min(top[qb][3]), hi = row_max(top[qb][0]);
-                if (count_ge(hi) >= R) lo = hi;
+                if (count_ge(hi) >= Rk) lo = hi;
 #pragma unroll 1
                 for (int it = 0; it < 12; ++it) {
                     const float mid = 0.5f * (lo + hi);
-                    const bool up = count_ge(mid) >= R;
+                    const bool up = count_ge(mid) >= Rk;
                     lo = up ? mid : lo;
                     hi = up ? hi : mid;
                 }
@@ -716,31 +569,30 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         }
     }
 
-    // ---- scan: every tile, two fragment buffers alternating (tile kt+1 loads
-    // while kt computes).  A query left with fewer than min(M, t+1) candidates
+    // ---- scan: every tile; tile kt+1 loads while the epilogue of kt runs.
+    // A query left with fewer than min(M, t+1) candidates
     // had its threshold at or above its M-th score: it is scanned again from
     // the lower sample estimate tau1, and if that starves it too, from -inf;
     // the wave's other queries take nothing in those passes. --------------------
-    auto step = [&](int kt, const Frag<T> (&bc)[4][C::KD]) {
-        if (kt >= kd) tile_step(kt, bc, std::true_type{});
-        else tile_step(kt, bc, std::false_type{});
-    };
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
-        load_b(0, b0);
-        for (int kt = 0; kt < ntiles; kt += 2) {
-            load_b(tile_or_null(kt + 1, ntiles), b1);
-            step(kt, b0);
-            if (kt + 1 >= ntiles) break;
-            load_b(tile_or_null(kt + 2, ntiles), b0);
-            step(kt + 1, b1);
+        load_b(0, bf);
+#pragma unroll 1
+        for (int kt = 0; kt < ntiles; ++kt) {
+            Acc acc;
+            tile_mfma(bf, acc);
+            load_b(tile_or_null(kt + 1, ntiles), bf);
+            if (kt >= kd) tile_step(kt, acc, std::true_type{});
+            else tile_step(kt, acc, std::false_type{});
         }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) flush_quad(qb);
         if (ns == 0) break;  // started from -inf: already exact
         uint64_t redo = 0;
         bool fail[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            fail[qb] = tq[qb] < nk && cnt[qb] < min(M, tq[qb] + 1);
+            fail[qb] = tq[qb] < nk && gc[qb] < min(M, tq[qb] + 1);
             redo |= __ballot(fail[qb]);
         }
         if (!redo || pass == 2) break;
@@ -748,45 +600,87 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         for (int qb = 0; qb < QB; ++qb) {
             // kept queries take nothing more (their counts stay below a trim)
             tau[qb] = fail[qb] ? (pass == 0 ? tau1[qb] : -INFINITY) : INFINITY;
-            cnt[qb] = fail[qb] ? 0 : cnt[qb];
-            fl[qb] = fail[qb] ? 0 : fl[qb];
+            gc[qb] = fail[qb] ? 0 : gc[qb];
         }
     }
 
     // ---- final select and ordered write-out --------------------------------------
-    wave_lds_sync();  // the last tiles' appends are read by other lanes below
+    // For each query: keep the first min(M, t+1) of its c buffered candidates
+    // (any order, distinct indices) in the order (higher score, lower index),
+    // mark them in a bitmap over positions 0..t (the staging area, free now),
+    // and write them out in position order, -1 padded.  The wave takes its
+    // queries in turn; the chip's other waves keep scanning meanwhile.
+    wave_global_sync();
+    uint32_t *const bm = reinterpret_cast<uint32_t *>(lists);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll 1
         for (int gg = 0; gg < 4; ++gg) {
             const int t = qw0 + qb * 4 + gg;
             if (t >= nk) continue;
-            const int qq = qb * 4 + gg;
-            const int c = __builtin_amdgcn_readlane(cnt[qb], 16 * gg);
-            flush_rest(qq, __builtin_amdgcn_readlane(fl[qb], 16 * gg), c);
-            wave_global_sync();
+            const int c = __builtin_amdgcn_readlane(gc[qb], 16 * gg);
             const int m = min(M, t + 1);
-            Cands<C::NE> x;
-            load_cands<C::NE>(qbuf_of(qq), c, x);
-            bool keep[C::NE];
-            if (c > m) {
-                select_first<C::NE>(x, c, m, keep, hist);
-            } else {
+            const int kn = (c + 63) / 64;  // slots holding candidates
+            const u32x2 *const gb = qbuf_of(qb * 4 + gg);
+            float xs[C::NE];
+            uint32_t xi[C::NE];
 #pragma unroll
-                for (int k = 0; k < C::NE; ++k) keep[k] = k * 64 + lane < c;
+            for (int k = 0; k < C::NE; ++k) {
+                const int e = k * 64 + lane;
+                u32x2 v = u32x2{0u, 0u};
+                if (e < c) v = gb[e];
+                xs[k] = __uint_as_float(v[0]);
+                xi[k] = v[1];
             }
+            uint64_t theta = 0;  // every valid candidate is kept when c <= m
+            if (c > m)
+                theta = select_theta(
+                    [&](auto &&f) {
+#pragma unroll
+                        for (int k = 0; k < C::NE; ++k)
+                            if (k < kn) f(k * 64 + lane < c, cand_key(xs[k], xi[k]));
+                    },
+                    m, hist);
+            const int nwords = t / 32 + 1;
+            for (int w = lane; w < nwords; w += 64) bm[w] = 0u;
+            wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < C::NE; ++k)
+                if (k < kn && k * 64 + lane < c && cand_key(xs[k], xi[k]) >= theta)
+                    atomicOr(&bm[xi[k] >> 5], 1u << (xi[k] & 31));
+            wave_lds_sync();
+            // lane l reads words [l*per, (l+1)*per): its kept positions follow
+            // those of the lower lanes
+            const int per = (nwords + 63) / 64;
+            uint32_t own = 0u;
+            for (int j = 0; j < per; ++j) {
+                const int w = lane * per + j;
+                if (w < nwords) own += (uint32_t)__popc(bm[w]);
+            }
+            const uint32_t incl = wave_inclusive_scan(own);
+            const int kept = __builtin_amdgcn_readlane((int)incl, 63);
             int32_t *dst = a.idx + (((size_t)b * nq + t - p0) * G + g) * M;
-            const int kept = compact<C::NE>(keep, [&](int k, uint32_t pos) { dst[pos] = (int32_t)x.key[k]; });
+            int pos = (int)(incl - own);
+            for (int j = 0; j < per; ++j) {
+                const int w = lane * per + j;
+                if (w >= nwords) break;
+                uint32_t bits = bm[w];
+                while (bits) {
+                    dst[pos++] = w * 32 + __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                }
+            }
             for (int i = kept + lane; i < M; i += 64) dst[i] = -1;
+            wave_lds_sync();  // the bitmap is cleared for the next query
         }
     }
 }
 
-// Candidate-buffer entries per query, 4 M' + 128 for M up to M' (a query is
-// trimmed when it holds more than CAPG - 64): a query below 4 M starts from
-// -inf and appends every key, so it never trims; a later one starts from a
-// sampled threshold expected to admit about 2 M keys.
-int cand_entries(int M) { return M <= 64 ? 384 : M <= 128 ? 640 : M <= 256 ? 1152 : 2176; }
+// Candidate-buffer entries per query, 4 M' + 256 for M up to M' (a query is
+// trimmed when it holds more than CAPG - 128, room for one more flush): a
+// query below 4 M starts from -inf and stages every key, so it never trims;
+// a later one starts from a sampled threshold expected to admit about 2 M.
+int cand_entries(int M) { return M <= 64 ? 512 : M <= 128 ? 768 : M <= 256 ? 1280 : 2304; }
 
 template <typename T, int DI, int HH, int QB>
 hipError_t launch_q(const IndexerArgs &a, hipStream_t s) {
@@ -794,10 +688,10 @@ hipError_t launch_q(const IndexerArgs &a, hipStream_t s) {
     const int nqb = (a.n + QW - 1) / QW;
     const dim3 grid((unsigned)(a.B * a.G * nqb));
     switch (cand_entries(a.M)) {
-        case 384: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 384>), grid, dim3(64), 0, s, a); break;
-        case 640: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 640>), grid, dim3(64), 0, s, a); break;
-        case 1152: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 1152>), grid, dim3(64), 0, s, a); break;
-        default: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 2176>), grid, dim3(64), 0, s, a); break;
+        case 512: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 512>), grid, dim3(64), 0, s, a); break;
+        case 768: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 768>), grid, dim3(64), 0, s, a); break;
+        case 1280: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 1280>), grid, dim3(64), 0, s, a); break;
+        default: launch_kernel((indexer_topm_kernel<T, DI, HH, QB, 2304>), grid, dim3(64), 0, s, a); break;
     }
     return hipGetLastError();
 }
