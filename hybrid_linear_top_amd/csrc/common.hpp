@@ -121,6 +121,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0u, 0));
 }
+// The same with a wave-uniform part of the offset in soffset (an SGPR, so a
+// constant part costs no VGPR).  Callers keep voff + soff inside the
+// descriptor wherever the data is wanted; a zero-size descriptor reads zeros
+// whatever the offsets.
+__device__ __forceinline__ u32x4 buf_load16s(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset beyond every descriptor used here
 
 // Fill a 16x16x32 fragment from a buffer: 8 consecutive elements at byte offset voff.
@@ -130,6 +137,13 @@ __device__ __forceinline__ void frag_buf_load(Frag<uint16_t> &f, rsrc_t r, uint3
 __device__ __forceinline__ void frag_buf_load(Frag<float> &f, rsrc_t r, uint32_t voff) {
     f.lo = __builtin_bit_cast(f32x4, buf_load16(r, voff));
     f.hi = __builtin_bit_cast(f32x4, buf_load16(r, voff + 16u));
+}
+__device__ __forceinline__ void frag_buf_load(Frag<uint16_t> &f, rsrc_t r, uint32_t voff, uint32_t soff) {
+    f.v = buf_load16s(r, voff, soff);
+}
+__device__ __forceinline__ void frag_buf_load(Frag<float> &f, rsrc_t r, uint32_t voff, uint32_t soff) {
+    f.lo = __builtin_bit_cast(f32x4, buf_load16s(r, voff, soff));
+    f.hi = __builtin_bit_cast(f32x4, buf_load16s(r, voff + 16u, soff));
 }
 
 // Number of set bits of a 64-lane mask in the lanes below this one.

@@ -76,41 +76,42 @@ __device__ __forceinline__ uint64_t cand_key(float sc, uint32_t idx) {
     return ((uint64_t)order_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
 }
 
-// theta = the m-th largest of the distinct keys that for_each(f) presents as
-// f(valid, key): exactly m of them are >= theta (1 <= m <= their count).
-// Radix passes of 256 bins over the live range [min, max] first (candidates
-// sit in a narrow band), each narrowing to the bin that holds the m-th key,
-// until that bin is taken whole.  Whole wave, uniform control flow.
+// Radix select over 32-bit values: for_each(f) presents f(valid, v) (v may
+// repeat); with 1 <= m <= the number of valid values, returns lo such that
+// the values >= lo are the m largest -- exactly m of them (*need = 0) or,
+// when the m-th largest value is tied, the ones above it plus *need of those
+// equal to it (then lo is that value).  256-bin passes over [min, max] (the
+// values sit in a narrow band), each narrowing to the bin that holds the
+// m-th value, until a bin is taken whole or holds one value.  Whole wave,
+// uniform control flow.
 template <typename ForEach>
-__device__ uint64_t select_theta(ForEach &&for_each, int m, uint32_t *hist) {
+__device__ uint32_t select32(ForEach &&for_each, int m, uint32_t *hist, uint32_t *need_out) {
     const int lane = threadIdx.x & 63;
-    // the live range from the keys' high words (DPP reductions): [min_hi.0,
-    // max_hi.ffffffff] holds every key
-    uint32_t hmin = 0xFFFFFFFFu, hmax = 0u;
-    for_each([&](bool valid, uint64_t k) {
+    uint32_t vmin = 0xFFFFFFFFu, vmax = 0u;
+    for_each([&](bool valid, uint32_t v) {
         if (valid) {
-            hmin = min(hmin, (uint32_t)(k >> 32));
-            hmax = max(hmax, (uint32_t)(k >> 32));
+            vmin = min(vmin, v);
+            vmax = max(vmax, v);
         }
     });
-    uint64_t lo = (uint64_t)wave_min_u32(hmin) << 32;
-    const uint64_t span = (((uint64_t)wave_max_u32(hmax) << 32) | 0xFFFFFFFFull) - lo;
-    int width = span == 0 ? 0 : 64 - __builtin_clzll(span);  // bits of key - lo
+    uint32_t lo = wave_min_u32(vmin);
+    const uint32_t span = wave_max_u32(vmax) - lo;
+    int width = span == 0 ? 0 : 32 - __builtin_clz(span);  // bits of v - lo
     uint32_t need = (uint32_t)m;
 #pragma unroll 1
     for (;;) {
         const int shift = width > 8 ? width - 8 : 0;
-        const uint64_t last = width >= 64 ? ~0ull : (1ull << width) - 1;  // the range is [lo, lo + last]
+        const uint32_t last = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;  // the range is [lo, lo + last]
         *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
-        for_each([&](bool valid, uint64_t k) {
-            if (valid && k >= lo && k - lo <= last) atomicAdd(&hist[(k - lo) >> shift], 1u);
+        for_each([&](bool valid, uint32_t v) {
+            if (valid && v >= lo && v - lo <= last) atomicAdd(&hist[(v - lo) >> shift], 1u);
         });
         wave_lds_sync();
         const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
         const uint32_t incl = wave_inclusive_scan(h[0] + h[1] + h[2] + h[3]);
         const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-        uint32_t run = total - incl;  // keys in the bins of higher lanes
+        uint32_t run = total - incl;  // values in the bins of higher lanes
         int fb = -1;
         uint32_t fneed = 0, fcnt = 0;
 #pragma unroll
@@ -127,14 +128,37 @@ __device__ uint64_t select_theta(ForEach &&for_each, int m, uint32_t *hist) {
         fneed = (uint32_t)__builtin_amdgcn_readlane((int)fneed, src);
         fcnt = (uint32_t)__builtin_amdgcn_readlane((int)fcnt, src);
         wave_lds_sync();
-        const uint64_t blo = lo + ((uint64_t)fb << shift);
-        // the bin taken whole: keys >= blo are exactly the first m (with
-        // distinct keys a single-value bin holds one, so this always ends)
-        if (fneed == fcnt || shift == 0) return blo;
+        const uint32_t blo = lo + ((uint32_t)fb << shift);
+        if (fneed == fcnt) {  // the bin taken whole
+            *need_out = 0u;
+            return blo;
+        }
+        if (shift == 0) {  // a single tied value
+            *need_out = fneed;
+            return blo;
+        }
         lo = blo;
         width = shift;
         need = fneed;
     }
+}
+
+// theta = the m-th largest of the distinct 64-bit candidate keys (score
+// order key above, complemented index below) that for_each(f) presents as
+// f(valid, order_key(score), index): exactly m keys are >= theta.  A select
+// on the scores first; only a tie at the M-th score needs a second one, on
+// the indices of the tied candidates (lower index first).
+template <typename ForEach>
+__device__ uint64_t select_theta(ForEach &&for_each, int m, uint32_t *hist) {
+    uint32_t need = 0u;
+    const uint32_t hi = select32(
+        [&](auto &&f) { for_each([&](bool valid, uint32_t ok, uint32_t) { f(valid, ok); }); }, m, hist, &need);
+    if (need == 0u) return (uint64_t)hi << 32;
+    uint32_t none = 0u;
+    const uint32_t lo = select32(
+        [&](auto &&f) { for_each([&](bool valid, uint32_t ok, uint32_t idx) { f(valid && ok == hi, ~idx); }); },
+        (int)need, hist, &none);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // ---- trims: streaming passes over a query's buffer in global memory --------
@@ -242,7 +266,9 @@ __device__ __attribute__((noinline)) TrimResult trim_buffer(u32x2 *qbuf, int c, 
         }
     }
     const uint64_t theta = select_theta(
-        [&](auto &&f) { stream_cands(qbuf, c, [&](bool valid, float sc, uint32_t idx) { f(valid, cand_key(sc, idx)); }); },
+        [&](auto &&f) {
+            stream_cands(qbuf, c, [&](bool valid, float sc, uint32_t idx) { f(valid, order_key(sc), idx); });
+        },
         M, hist);
     const int nk = compact_stream(qbuf, c, [&](float sc, uint32_t idx) { return cand_key(sc, idx) >= theta; });
     wave_global_sync();
@@ -286,7 +312,8 @@ template <typename T, int DI, int HH, int QB, int CAPG>
 struct IdxCfg {
     static constexpr int KD = DI / 32;  // MFMA K-steps
     static constexpr int QW = 4 * QB;   // queries per wave: QB quads of 4
-    static constexpr int NE = CAPG / 64;
+    // entries per lane of the final select: room for 2 M + 128 candidates
+    static constexpr int NF = CAPG <= 512 ? 4 : CAPG <= 768 ? 6 : CAPG <= 1280 ? 10 : 18;
 };
 
 template <typename T, int DI, int HH, int QB, int CAPG>
@@ -294,11 +321,11 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     using C = IdxCfg<T, DI, HH, QB, CAPG>;
     constexpr int kQW = C::QW;
     // per query, per lane of its 16-lane row: kLane staged candidates; the
-    // area doubles as the output bitmap of the final select (32768 bits at 4
-    // queries per wave)
-    __shared__ __attribute__((aligned(16))) u32x2 lists[kQW * 16 * kLane];
+    // area doubles as the final select's bitmap with a rank per word (1024
+    // words: positions up to 32767)
+    constexpr int kListEntries = kQW * 16 * kLane > 1024 ? kQW * 16 * kLane : 1024;
+    __shared__ __attribute__((aligned(16))) u32x2 lists[kListEntries];
     __shared__ __attribute__((aligned(16))) uint32_t hist[256];
-    static_assert(kQW * 16 * kLane * 8 >= 4096, "the bitmap needs 4 KB");
 
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, grp = lane >> 4;
@@ -378,7 +405,7 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int kc = 0; kc < C::KD; ++kc)
-                frag_buf_load(bf[cb][kc], r, voff + (uint32_t)(cb * C::KD + kc) * kFragBytes);
+                frag_buf_load(bf[cb][kc], r, voff, (uint32_t)(cb * C::KD + kc) * kFragBytes);
     };
 
     // One tile in two halves: every quad's MFMAs (the caller then reuses the
@@ -608,70 +635,87 @@ __global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
     // For each query: keep the first min(M, t+1) of its c buffered candidates
     // (any order, distinct indices) in the order (higher score, lower index),
     // mark them in a bitmap over positions 0..t (the staging area, free now),
-    // and write them out in position order, -1 padded.  The wave takes its
-    // queries in turn; the chip's other waves keep scanning meanwhile.
+    // give every bitmap word the number of kept positions below it, and store
+    // each kept index at its rank, -1 padded.  The wave takes its queries in
+    // turn; the chip's other waves keep scanning meanwhile.
     wave_global_sync();
-    uint32_t *const bm = reinterpret_cast<uint32_t *>(lists);
+    // per bitmap word: {bits, kept positions in the lower words}; lane l owns
+    // words [l * per, (l + 1) * per), per even and at most 16
+    uint32_t *const bw = reinterpret_cast<uint32_t *>(lists);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll 1
         for (int gg = 0; gg < 4; ++gg) {
             const int t = qw0 + qb * 4 + gg;
             if (t >= nk) continue;
-            const int c = __builtin_amdgcn_readlane(gc[qb], 16 * gg);
+            int c = __builtin_amdgcn_readlane(gc[qb], 16 * gg);
             const int m = min(M, t + 1);
-            const int kn = (c + 63) / 64;  // slots holding candidates
-            const u32x2 *const gb = qbuf_of(qb * 4 + gg);
-            float xs[C::NE];
-            uint32_t xi[C::NE];
+            u32x2 *const gb = qbuf_of(qb * 4 + gg);
+            // the select holds C::NF entries per lane; a larger buffer (a
+            // query started from -inf, or a loose threshold) is trimmed first
+            if (c > C::NF * 64) c = trim_buffer(gb, c, m, C::NF * 64, hist).c;
+            uint32_t ok[C::NF], xi[C::NF];  // order key of the score, index
 #pragma unroll
-            for (int k = 0; k < C::NE; ++k) {
+            for (int k = 0; k < C::NF; ++k) {
                 const int e = k * 64 + lane;
                 u32x2 v = u32x2{0u, 0u};
                 if (e < c) v = gb[e];
-                xs[k] = __uint_as_float(v[0]);
+                ok[k] = order_key(__uint_as_float(v[0]));
                 xi[k] = v[1];
             }
+            auto valid = [&](int k) { return k * 64 + lane < c; };
             uint64_t theta = 0;  // every valid candidate is kept when c <= m
             if (c > m)
                 theta = select_theta(
                     [&](auto &&f) {
 #pragma unroll
-                        for (int k = 0; k < C::NE; ++k)
-                            if (k < kn) f(k * 64 + lane < c, cand_key(xs[k], xi[k]));
+                        for (int k = 0; k < C::NF; ++k) f(valid(k), ok[k], xi[k]);
                     },
                     m, hist);
-            const int nwords = t / 32 + 1;
-            for (int w = lane; w < nwords; w += 64) bm[w] = 0u;
+            uint32_t kept_mask = 0u;
+#pragma unroll
+            for (int k = 0; k < C::NF; ++k)
+                if (valid(k) && ((((uint64_t)ok[k]) << 32) | (uint64_t)~xi[k]) >= theta) kept_mask |= 1u << k;
+            const int per = (((t / 32 + 1) + 63) / 64 + 1) & ~1;
+            uint32_t *const mine = bw + 2 * lane * per;
+#pragma unroll
+            for (int j = 0; j < 16; j += 2)
+                if (j < per) *reinterpret_cast<u32x4 *>(mine + 2 * j) = u32x4{0u, 0u, 0u, 0u};
             wave_lds_sync();
 #pragma unroll
-            for (int k = 0; k < C::NE; ++k)
-                if (k < kn && k * 64 + lane < c && cand_key(xs[k], xi[k]) >= theta)
-                    atomicOr(&bm[xi[k] >> 5], 1u << (xi[k] & 31));
+            for (int k = 0; k < C::NF; ++k)
+                if ((kept_mask >> k) & 1u) atomicOr(&bw[2 * (xi[k] >> 5)], 1u << (xi[k] & 31));
             wave_lds_sync();
-            // lane l reads words [l*per, (l+1)*per): its kept positions follow
-            // those of the lower lanes
-            const int per = (nwords + 63) / 64;
             uint32_t own = 0u;
-            for (int j = 0; j < per; ++j) {
-                const int w = lane * per + j;
-                if (w < nwords) own += (uint32_t)__popc(bm[w]);
-            }
+#pragma unroll
+            for (int j = 0; j < 16; j += 2)
+                if (j < per) {
+                    const u32x4 w2 = *reinterpret_cast<const u32x4 *>(mine + 2 * j);
+                    own += (uint32_t)(__popc(w2[0]) + __popc(w2[2]));
+                }
             const uint32_t incl = wave_inclusive_scan(own);
             const int kept = __builtin_amdgcn_readlane((int)incl, 63);
-            int32_t *dst = a.idx + (((size_t)b * nq + t - p0) * G + g) * M;
-            int pos = (int)(incl - own);
-            for (int j = 0; j < per; ++j) {
-                const int w = lane * per + j;
-                if (w >= nwords) break;
-                uint32_t bits = bm[w];
-                while (bits) {
-                    dst[pos++] = w * 32 + __builtin_ctz(bits);
-                    bits &= bits - 1u;
+            uint32_t run = incl - own;
+#pragma unroll
+            for (int j = 0; j < 16; j += 2)
+                if (j < per) {
+                    u32x4 w2 = *reinterpret_cast<const u32x4 *>(mine + 2 * j);
+                    w2[1] = run;
+                    run += (uint32_t)__popc(w2[0]);
+                    w2[3] = run;
+                    run += (uint32_t)__popc(w2[2]);
+                    *reinterpret_cast<u32x4 *>(mine + 2 * j) = w2;
                 }
-            }
+            wave_lds_sync();
+            int32_t *dst = a.idx + (((size_t)b * nq + t - p0) * G + g) * M;
+#pragma unroll
+            for (int k = 0; k < C::NF; ++k)
+                if ((kept_mask >> k) & 1u) {
+                    const u32x2 e = *reinterpret_cast<const u32x2 *>(bw + 2 * (xi[k] >> 5));
+                    dst[e[1] + (uint32_t)__popc(e[0] & ((1u << (xi[k] & 31)) - 1u))] = (int32_t)xi[k];
+                }
             for (int i = kept + lane; i < M; i += 64) dst[i] = -1;
-            wave_lds_sync();  // the bitmap is cleared for the next query
+            wave_lds_sync();  // the bitmap is read before the next query clears it
         }
     }
 }
