@@ -317,7 +317,7 @@ struct IdxCfg {
 };
 
 template <typename T, int DI, int HH, int QB, int CAPG>
-__global__ __launch_bounds__(64) void indexer_topm_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1))) void indexer_topm_kernel(IndexerArgs a) {
     using C = IdxCfg<T, DI, HH, QB, CAPG>;
     constexpr int kQW = C::QW;
     // per query, per lane of its 16-lane row: kLane staged candidates; the
