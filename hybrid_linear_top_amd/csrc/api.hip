@@ -90,11 +90,16 @@ using wide_t = __int128;
 
 lisa_status check_spans(const lisa_dims *d, int64_t B, int64_t units, int64_t kv_rows, bool indexer) {
     const wide_t G = d->num_kv_heads, eb = elt_bytes(d->dtype);
-    const wide_t kv_span = (wide_t)kv_rows * G * d->head_dim * eb;
+    // (one row more: the sparse gathers address the row past the last)
+    const wide_t kv_span = ((wide_t)kv_rows + 1) * G * d->head_dim * eb;
     if (kv_span > kSpan32)
         return fail(LISA_ERR_UNSUPPORTED,
                     "%lld K/V rows of %d groups span %.4g bytes: a buffer descriptor holds at most %lld",
                     (long long)kv_rows, d->num_kv_heads, (double)kv_span, (long long)kSpan32);
+    // (the sparse gathers form row offsets with 24-bit multiplies)
+    if (G * d->head_dim * eb >= ((wide_t)1 << 24))
+        return fail(LISA_ERR_UNSUPPORTED, "a K/V position of %d groups spans %.4g bytes: at most 2^24 - 1",
+                    d->num_kv_heads, (double)(G * d->head_dim * eb));
     const wide_t idx_span = (wide_t)kv_rows * G * d->idx_dim * eb;
     if (indexer && idx_span > kSpan32)
         return fail(LISA_ERR_UNSUPPORTED, "%lld indexer-key rows span %.4g bytes: at most %lld",

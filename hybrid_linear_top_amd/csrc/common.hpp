@@ -15,12 +15,15 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 values -> packed bf16 bits (lo in bits 0..15), round to nearest
+// even: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2v_t));
 }
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
 // Element traits: storage type T is uint16_t (bf16 bit pattern) or float.
 template <typename T> struct Elt;
@@ -51,8 +54,7 @@ template <> struct Frag<uint16_t> {
     // set from 8 fp32 values (rounded to bf16)
     __device__ __forceinline__ void set(const float *x) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
     }
     __device__ __forceinline__ void set_bits(const uint16_t *x) {
 #pragma unroll

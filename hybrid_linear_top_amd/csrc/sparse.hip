@@ -401,14 +401,16 @@ void sparse_prefill_wave_kernel(SparseArgs a) {
         return x;
     };
     u32x4 kp[NI], vp[NI];
+    // Row offsets by 24-bit multiplies (positions and row bytes are below
+    // 2^24).  An index past smax, -1 padding included, is clamped to smax + 1,
+    // whose row starts at the descriptor's end and reads zeros (the host keeps
+    // one row past the last inside 32 bits).  Slots past nvalid hold such
+    // indices: -1 padding, or window positions past smax.
+    const uint32_t uend = (uint32_t)smax + 1u;
     auto gather = [&](int j, const Idx &x) {
         uint32_t off[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int s = (int)x.v[i / 4][i % 4];
-            const bool ok = j * kChunk + rho0 + i < nvalid && s >= 0 && s <= smax;
-            off[i] = ok ? (uint32_t)s * row_bytes + piece * 16 : kOffNone;
-        }
+        for (int i = 0; i < NI; ++i) off[i] = __umul24(min(x.v[i / 4][i % 4], uend), row_bytes) + piece * 16;
 #pragma unroll
         for (int i = 0; i < NI; ++i) kp[i] = buf_load16(krs, off[i]);
 #pragma unroll
@@ -458,21 +460,26 @@ void sparse_prefill_wave_kernel(SparseArgs a) {
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) acc[kb] = mma16(kf[kb][kc], qf[kc], acc[kb]);
         }
-        // online softmax over the 32 slots, per head (column)
+        // online softmax over the 32 slots, per head (column); slots past
+        // nvalid (only in the last step) get -inf
         float x[8];
-        float cmax = -INFINITY;
+        if ((j + 1) * kChunk <= nvalid) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int e = 0; e < 8; ++e) x[e] = acc[e / 4][e % 4] * a.scale_log2;
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = j * kChunk + kb * 16 + grp * 4 + i < nvalid;
-                const float v = ok ? acc[kb][i] * a.scale_log2 : -INFINITY;
-                x[kb * 4 + i] = v;
-                cmax = fmaxf(cmax, v);
-            }
+            for (int e = 0; e < 8; ++e)
+                x[e] = j * kChunk + (e / 4) * 16 + grp * 4 + e % 4 < nvalid ? acc[e / 4][e % 4] * a.scale_log2
+                                                                              : -INFINITY;
+        }
+        float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         cmax = wave_max_across16(cmax);
-        const float m_new = fmaxf(m_run, cmax);  // finite from the first step on (slot 0 is valid)
-        if (__ballot(m_new > m_run)) {
+        // The reference m_run moves only when a logit passes it by more than
+        // 8 (log2 units): p stays below 256, O / l does not depend on the
+        // reference, and the rescale of O runs on few steps.  m_run is finite
+        // from the first step on (slot 0 is valid).
+        if (__ballot(cmax > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, cmax);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_part *= alpha;
 #pragma unroll

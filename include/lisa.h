@@ -52,9 +52,11 @@
  * decode: 1 <= top_m <= 2048, max_ctx <= 65536.  Also refused
  * (LISA_ERR_UNSUPPORTED), because kernels address a sequence's rows through
  * buffer descriptors with a 32-bit byte extent and count a launch's threads
- * in 32 bits: one sequence's K/V rows (positions x num_kv_heads x head_dim
- * x element size; in decode max_ctx positions, or the page pool's rows)
- * above 4 GiB - 1, likewise its indexer-key rows, 2^22 or more
+ * in 32 bits: one sequence's K/V rows plus one (positions + 1, times
+ * num_kv_heads x head_dim x element size; in decode max_ctx positions, or the
+ * page pool's rows) above 4 GiB - 1, a position's K/V row of all groups of
+ * 16 MiB or more (row offsets are 24-bit products), the indexer-key rows
+ * above 4 GiB - 1, 2^22 or more
  * (sequence, position, group) units in one call, and in the backward
  * num_q_heads x top_m above 2^21 (a 256-position block of per-slot
  * coefficients).
@@ -62,11 +64,12 @@
  *   - chunk 16 or 32: the linear branch's result does not depend on the
  *     chunk length (it only regroups the same sums), and the kernels are
  *     tiled for 64-row MFMA blocks, so only 64 is taken;
- *   - prefill top_m above 512: the fused indexer keeps each query's
- *     candidates (score and index) in LDS next to its key tiles, and at
- *     top_m = 512 that buffer already holds 1024 entries per query; larger
- *     top_m are served by the decode step (up to 2048) and by the window
- *     variant (up to 2048), whose selects do not live in LDS per query.
+ *   - prefill top_m above 512: the fused indexer's final select holds a
+ *     query's 2 top_m + 128 best candidates in registers across the wave
+ *     (18 per lane at top_m = 512), and its workspace keeps 4 top_m + 256
+ *     candidates per query; larger top_m are served by the decode step (up
+ *     to 2048) and by the window variant (up to 2048), whose selects work
+ *     differently.
  */
 #ifndef LISA_H
 #define LISA_H
