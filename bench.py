@@ -409,12 +409,18 @@ def measure_peaks(copy_bytes=1 << 30, mfma_iters=400, reps=5):
     MEASURED["hbm_gbs"] = round(max(copy_gbs, read_gbs), 1)
     w, ms = best(lambda: lisa.peak_probe(lisa.LISA_PROBE_MFMA, None, sink, sink.numel() * 4, mfma_iters))
     MEASURED["mfma_bf16_tflops"] = round(w / (ms * 1e-3) / 1e12, 1)
+    # random 256-byte row gathers from an 8 MiB table (the K and V rows of one
+    # KV group at 16K positions) and from a 1 MiB one (L2-resident)
+    for tag, tb in (("gather_8mib_gbs", 8 << 20), ("gather_1mib_gbs", 1 << 20)):
+        w, ms = best(lambda: lisa.peak_probe(lisa.LISA_PROBE_GATHER, src, sink, tb, 8))
+        MEASURED[tag] = round(w / (ms * 1e-3) / 1e9, 1)
     del src, dst, sink
     torch.cuda.empty_cache()
     return dict(MEASURED, method="median of 5 event-timed launches of lisa_peak_probe: a copy of 1 GiB "
                                  "(2 GiB moved), a read-only stream over 1 GiB (hbm_gbs is the "
-                                 "better of the two), and an MFMA loop (2048 x 256 threads, 400 x 8 bf16 "
-                                 "16x16x32 MFMAs per wave)")
+                                 "better of the two), an MFMA loop (2048 x 256 threads, 400 x 8 bf16 "
+                                 "16x16x32 MFMAs per wave), and random 256-byte row gathers (65536 waves x "
+                                 "8 x 16 KB) from an 8 MiB and a 1 MiB table")
 
 
 _MARK = {}
@@ -478,6 +484,15 @@ def bench_prefill(args, small=False):
                          "tflops": round(f / (v * 1e-3) / 1e12, 3) if f else None,
                          "frac_mfma_peak": round(f / (v * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
                          if f else None}
+    # the sparse stage moves K and V rows from L2 by random 256-byte gathers:
+    # its rate against the gather probe at the same table size
+    if "sparse_gate_prefill" in stage_rows:
+        gbytes = B * cfg.Hkv * pairs(n, cfg.M) * 2 * cfg.d * 2
+        gbs = gbytes / (stages["sparse_gate_prefill"] * 1e-3) / 1e9
+        stage_rows["sparse_gate_prefill"]["gather_bytes"] = gbytes
+        stage_rows["sparse_gate_prefill"]["gather_gbs"] = round(gbs, 1)
+        if MEASURED.get("gather_8mib_gbs"):
+            stage_rows["sparse_gate_prefill"]["frac_measured_gather"] = round(gbs / MEASURED["gather_8mib_gbs"], 4)
     dom = max(stages, key=stages.get)
     phase = "prefill_1p5b_4k" if small else "prefill_7b_16k"
     roof = roofline_entry(dom, stages[dom], flops.get(dom, 0), "mfma", traffic_from_profiles(dom, phase))

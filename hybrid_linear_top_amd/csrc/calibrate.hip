@@ -1,7 +1,9 @@
 // Roofline calibration kernels, for measurement only (not on the LISA path):
-// a plain streaming copy, which measures the HBM bandwidth a kernel can reach
-// on this part, and an MFMA loop, which measures the bf16 matrix-core rate a
-// kernel can reach.  The benchmark reports each path's roofline fraction
+// a plain streaming copy and a read stream, which measure the HBM bandwidth
+// a kernel can reach on this part, an MFMA loop, which measures the bf16
+// matrix-core rate a kernel can reach, and random row gathers, which measure
+// the rate at which the vector memory path delivers scattered 256-byte rows
+// from a table of a given size (the sparse kernels' access pattern).  The benchmark reports each path's roofline fraction
 // against these measured peaks next to the published ones.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -69,6 +71,35 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float *sink, int iters)
 
 constexpr int kMfmaBlocks = 2048;  // 8192 waves: 8 per SIMD
 
+// Row gathers: random 256-byte rows of a table of nrows (a power of two),
+// 16 lanes per row, each wave `iters` batches of 16 loads (64 rows, 16 KB)
+// in flight together -- the access pattern of the sparse kernels' K/V
+// gathers.  Rows come from a counter-based hash of (wave, load).
+constexpr int kGatherBlocks = 16384;  // 65536 waves
+constexpr int kGatherDepth = 16;
+__global__ __launch_bounds__(256) void probe_gather_kernel(const u32x4 *__restrict__ table, uint32_t *sink,
+                                                           uint32_t row_mask, int iters) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+    const uint32_t piece = lane & 15, rsub = lane >> 4;
+    u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+    for (int it = 0; it < iters; ++it) {
+        u32x4 v[kGatherDepth];
+#pragma unroll
+        for (int i = 0; i < kGatherDepth; ++i) {
+            uint32_t x = (wave * 0x9E3779B1u) ^ ((uint32_t)(it * kGatherDepth + i) * 0x85EBCA77u) ^ (rsub * 0xC2B2AE3Du);
+            x ^= x >> 15;
+            x *= 0x2C1B3C6Du;
+            x ^= x >> 12;
+            v[i] = table[(size_t)(x & row_mask) * 16 + piece];
+        }
+#pragma unroll
+        for (int i = 0; i < kGatherDepth; ++i) acc ^= v[i];
+    }
+    const uint32_t y = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (y == 0x9E3779B9u) sink[threadIdx.x] = y;
+}
+
 }  // namespace
 }  // namespace lisa
 
@@ -97,6 +128,15 @@ extern "C" lisa_status lisa_peak_probe(int32_t kind, const void *src, void *dst,
         lisa::launch_kernel(lisa::probe_mfma_kernel, dim3(lisa::kMfmaBlocks), dim3(256), 0, s,
                             static_cast<float *>(dst), (int)iters);
         *work = (double)lisa::kMfmaBlocks * 4 * iters * lisa::kChains * (2.0 * 16 * 16 * 32);
+    } else if (kind == LISA_PROBE_GATHER) {
+        const size_t rows = bytes / 256;
+        if (!src || !dst || iters < 1 || bytes % 256 != 0 || rows == 0 || (rows & (rows - 1)) != 0 ||
+            rows > ((size_t)1 << 31) || (reinterpret_cast<uintptr_t>(src) & 15u))
+            return LISA_ERR_INVALID_ARGUMENT;
+        lisa::launch_kernel(lisa::probe_gather_kernel, dim3(lisa::kGatherBlocks), dim3(256), 0, s,
+                            reinterpret_cast<const lisa::u32x4 *>(src), static_cast<uint32_t *>(dst),
+                            (uint32_t)(rows - 1), (int)iters);
+        *work = (double)lisa::kGatherBlocks * 4 * iters * lisa::kGatherDepth * 1024.0;
     } else {
         return LISA_ERR_INVALID_ARGUMENT;
     }

@@ -205,6 +205,7 @@ def lisa_decode_step_noalloc(dims, B, cu_ctx, max_ctx, q, k_cache, v_cache, q_id
 LISA_PROBE_COPY = 0
 LISA_PROBE_MFMA = 1
 LISA_PROBE_READ = 2
+LISA_PROBE_GATHER = 3
 
 
 def peak_probe(kind: int, src, dst, nbytes: int, iters: int = 0, stream=None) -> float:

@@ -328,11 +328,16 @@ lisa_status lisa_stage_timing_read(int32_t max_stages, const char **names, int64
  * kind LISA_PROBE_MFMA: `iters` rounds of eight independent bf16
  * 16x16x32 MFMAs per wave on register operands, 8 waves per SIMD; dst is a
  * sink of at least 2 MiB that is never written in practice; *work = the
- * flops issued.  Enqueued on `stream`; the caller times it with events.
+ * flops issued.
+ * kind LISA_PROBE_GATHER: 65536 waves, each `iters` batches of 16 loads of
+ * random 256-byte rows (16 lanes a row) of the table src of `bytes` (a power
+ * of two rows of 256 bytes, 16-byte aligned); dst is a sink of at least
+ * 1 KiB that is never written in practice; *work = the bytes gathered.
+ * Enqueued on `stream`; the caller times it with events.
  * Returns LISA_ERR_INVALID_ARGUMENT for a bad kind or buffer (nothing is
  * enqueued then); the error message is not set.
  */
-enum { LISA_PROBE_COPY = 0, LISA_PROBE_MFMA = 1, LISA_PROBE_READ = 2 };
+enum { LISA_PROBE_COPY = 0, LISA_PROBE_MFMA = 1, LISA_PROBE_READ = 2, LISA_PROBE_GATHER = 3 };
 lisa_status lisa_peak_probe(int32_t kind, const void *src, void *dst, size_t bytes, int32_t iters,
                             double *work, lisa_stream_t stream);
 
