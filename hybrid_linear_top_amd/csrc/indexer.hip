@@ -387,8 +387,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
         gc[qb] = 0;
         tau[qb] = tq[qb] < nk ? -INFINITY : INFINITY;  // padding queries accept nothing
     }
-    // this lane's staging list for the query of quad qb
-    auto list_of = [&](int qb) { return lists + ((qb * 4 + grp) * 16 + col) * kLane; };
+    // this lane's staging list for the query of quad qb: entry j at
+    // list_of(qb)[64 j] (slot-major over the wave's lanes, so that the lanes'
+    // writes of one slot index fall in distinct LDS banks)
+    auto list_of = [&](int qb) { return lists + qb * kLane * 64 + lane; };
 
     // B fragments of one packed key tile: key 4*col + cb, dims 32*kc + 8*grp
     // .. +7, through a per-tile buffer descriptor (tiles past the last read
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
         const u32x2 *const my = list_of(qb);
         u32x2 e[kLane];
 #pragma unroll
-        for (int j = 0; j < kLane; ++j) e[j] = my[j];  // all reads first: one wait
+        for (int j = 0; j < kLane; ++j) e[j] = my[64 * j];  // all reads first: one wait
 #pragma unroll
         for (int j = 0; j < kLane; ++j)
             __builtin_amdgcn_raw_buffer_store_b64(e[j], crs, j < cl[qb] ? (off + (uint32_t)j) * 8u : kOffNone, 0u, 0);
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
                 const uint32_t key = (uint32_t)(k0 + 4 * col + cb);
                 bool ok = score[qb][cb] > tau[qb];
                 if constexpr (DIAG) ok = ok && (int)key <= tq[qb];
-                my[cl[qb]] = u32x2{__float_as_uint(score[qb][cb]), key};
+                my[64 * cl[qb]] = u32x2{__float_as_uint(score[qb][cb]), key};
                 cl[qb] += ok ? 1 : 0;
             }
             // a lane can stage 4 more next tile
