@@ -496,12 +496,24 @@ def bench_prefill(args, small=False):
     dom = max(stages, key=stages.get)
     phase = "prefill_1p5b_4k" if small else "prefill_7b_16k"
     roof = roofline_entry(dom, stages[dom], flops.get(dom, 0), "mfma", traffic_from_profiles(dom, phase))
+    if dom == "sparse_gate_prefill":
+        # its MFMA work is light: what bounds it is the random-row gather
+        # rate from L2 / Infinity Cache, measured by the gather probe
+        sg = stage_rows[dom]
+        roof.update({"limiter": "random 256-byte K/V row gathers from L2 and the Infinity Cache",
+                     "gather_bytes_per_launch": sg.get("gather_bytes"), "gather_gbs": sg.get("gather_gbs"),
+                     "gather_peak_measured_gbs": MEASURED.get("gather_8mib_gbs"),
+                     "frac_measured_gather": sg.get("frac_measured_gather")})
+    # the indexer, the other large kernel, against the MFMA peak as well
+    idx_roof = (roofline_entry("indexer_topm", stages["indexer_topm"], flops["indexer_topm"], "mfma",
+                               traffic_from_profiles("indexer_topm", phase))
+                if "indexer_topm" in stages and dom != "indexer_topm" else None)
     shape = "qwen2.5-1.5b-shaped" if small else "qwen2.5-7b-shaped"
     res = {
         "workload": f"lisa_prefill {shape} B={B} n={n} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                     f"d={cfg.d} indexer={cfg.HI}x{cfg.dI} M={cfg.M} C={cfg.chunk} bf16",
         "tokens_per_s": B * n / (ms * 1e-3), "ms": ms, "steps": steps, "copies": copies,
-        "roofline": roof, "stages": stage_rows,
+        "roofline": roof, "roofline_indexer": idx_roof, "stages": stage_rows,
         "step_roofline": {"bound": "mfma", "algorithmic_flops": total_flops,
                           "achieved_tflops": round(total_flops / (ms * 1e-3) / 1e12, 3),
                           "frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
