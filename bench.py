@@ -569,9 +569,12 @@ def bench_decode(args, ragged=False):
         stage_rows[k] = {"ms": round(v, 5),
                          "gbs": round(b / (v * 1e-3) / 1e9, 1) if b else None,
                          "frac_hbm_peak": round(b / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if b else None}
-    # the dominant kernel among those that move the step's algorithmic bytes
-    # (the select pass works on the scores already in the workspace)
-    dom = max((k for k in stages if by.get(k)), key=stages.get)
+    # the step is bound by its HBM stream: the kernel reported is the one
+    # that carries most of the step's algorithmic bytes (the score/state
+    # scan); the select and the sparse kernel are short latency chains on
+    # B x G work-groups, and the dispatch events of the sparse one read up to
+    # 4x its kernel-trace duration, so their event times rank nothing here
+    dom = max((k for k in stages if by.get(k)), key=lambda k: by[k])
     roof = roofline_entry(dom, stages[dom], by.get(dom, 0), "hbm",
                           traffic_from_profiles(dom, "decode_7b_ragged" if ragged else "decode_1p5b_16k"))
     L = inp["lengths"]
