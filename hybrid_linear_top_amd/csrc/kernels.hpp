@@ -94,6 +94,7 @@ struct SparseArgs {
     int window;           // 1: the set of a query at position t is max(0, t-M+1)..t (idx unused)
     float scale_log2;     // softmax scale * log2(e)
     int units;
+    int split_lo;         // set by the launch (bf16 prefill)
 };
 hipError_t launch_sparse_gate(const SparseArgs &a, int dtype, int d, bool decode, hipStream_t s);
 
