@@ -354,17 +354,6 @@ __global__ __launch_bounds__(64) void sparse_bwd_kernel(SparseBwdArgs a) {
 // selected keys, so a key row is added about once per block instead of once
 // per selecting position (the atomics' throughput is what bounds the
 // one-wave-per-position form).
-typedef __bf16 bwd_bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bwd_bf16x4 bwd_lds_bf16x4;
-
-// gfx950 transposing LDS read (ds_read_b64_tr_b16): in each 16-lane block,
-// lane l gets element l % 4 of the 4-element row piece addressed by lane
-// 4e + l / 4, e = 0..3
-__device__ __forceinline__ u32x2 bwd_read_tr16(const unsigned char *lds_byte_ptr) {
-    bwd_lds_bf16x4 *p = (bwd_lds_bf16x4 *)(__attribute__((address_space(3))) unsigned char *)(
-        (__attribute__((address_space(3))) void *)lds_byte_ptr);
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
-}
 
 template <int D>
 __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
@@ -519,8 +508,8 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
         dsf.set(dsv);  // K-element e <-> slot (e < 4 ? 4*grp + e : 16 + 4*grp + e - 4)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const u32x2 lo = bwd_read_tr16(ldk + ktr + mb * 32);
-            const u32x2 hi = bwd_read_tr16(ldk + ktr + 16 * KRB + mb * 32);
+            const u32x2 lo = lds_read_tr16(ldk + ktr + mb * 32);
+            const u32x2 hi = lds_read_tr16(ldk + ktr + 16 * KRB + mb * 32);
             Frag<uint16_t> kt;
             kt.v = u32x4{lo[0], lo[1], hi[0], hi[1]};
             o[mb] = mma16(kt, dsf, o[mb]);

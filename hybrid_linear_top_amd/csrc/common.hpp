@@ -148,6 +148,20 @@ __device__ __forceinline__ void frag_buf_load(Frag<float> &f, rsrc_t r, uint32_t
     f.hi = __builtin_bit_cast(f32x4, buf_load16s(r, voff + 16u, soff));
 }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): in each 16-lane block,
+// lane l gets element l % 4 of the 4-element (8-byte) row piece addressed by
+// lane 4e + l / 4, e = 0..3.  With lane j of the block addressing row
+// (base + j / 4) at column 4 (j % 4) + c0, lane l receives rows base ..
+// base + 3 of column c0 + l % 16: four consecutive K-elements of an MFMA
+// operand read across rows of a row-major tile.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+__device__ __forceinline__ u32x2 lds_read_tr16(const void *lds_byte_ptr) {
+    lds_bf16x4_t *p = (lds_bf16x4_t *)(__attribute__((address_space(3))) unsigned char *)(
+        (__attribute__((address_space(3))) void *)lds_byte_ptr);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
+}
+
 // Number of set bits of a 64-lane mask in the lanes below this one.
 __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

@@ -211,10 +211,15 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
     constexpr int PD = pad16<T>();
     constexpr int KS = D + PD;    // K rows (natural)
-    constexpr int VTS = kC + PD;  // V^T rows (transposed)
+    // bf16: V rows natural (32-byte pad), read transposed by ds_read_b64_tr_b16;
+    // fp32: V^T staged transposed
+    constexpr bool TRV = sizeof(T) == 2;
+    constexpr int VRS = D + 32 / (int)sizeof(T);
+    constexpr int VTS = kC + PD;
+    constexpr int VBUF = TRV ? kC * VRS : D * VTS;
     constexpr int SS = D + PD;    // S^T rows
     __shared__ __attribute__((aligned(16))) T ks_[kC * KS];
-    __shared__ __attribute__((aligned(16))) T vt_[D * VTS];
+    __shared__ __attribute__((aligned(16))) T vt_[VBUF];
     __shared__ __attribute__((aligned(16))) T st_[D * SS];
     const int blk = blockIdx.x, c = blk % a.nC, bg = blk / a.nC, g = bg % a.G, b = bg / a.G;
     const int t0 = c * kC, valid = min(kC, a.n - t0);
@@ -223,7 +228,8 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
     const T *vp = reinterpret_cast<const T *>(a.v) + (((size_t)b * a.kv_rows + a.kv_off + t0) * a.G + g) * D;
     const T *P = reinterpret_cast<const T *>(a.P);
     stage_rows<T, D, kC>(ks_, KS, kp, rstride, valid);
-    stage_transposed<T, D>(vt_, VTS, vp, rstride, valid);
+    if constexpr (TRV) stage_rows<T, D, kC>(vt_, VRS, vp, rstride, valid);
+    else stage_transposed<T, D>(vt_, VTS, vp, rstride, valid);
     const size_t pgrp = a.per_head ? ((size_t)b * a.Hq + g * a.r) : ((size_t)b * a.G + g);
     if (a.state_t) stage_square_transposed<T, D>(st_, SS, P + (pgrp * a.nC + c) * D * D);
     else stage_rows<T, D, D>(st_, SS, P + (pgrp * a.nC + c) * D * D, D, D);
@@ -292,8 +298,15 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(LinearArgs a) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 Frag<T> vf;
-                const T *row = vt_ + (mb * 16 + col) * VTS + k2 * 32 + grp * 4;
-                load_halves(vf, row, row + 16);
+                if constexpr (TRV) {
+                    // lane (col, grp): keys k2*32 + 4 grp .. +3 and +16.. of dim 16 mb + col
+                    const T *p0 = vt_ + (k2 * 32 + grp * 4 + (col >> 2)) * VRS + mb * 16 + (col & 3) * 4;
+                    const u32x2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * VRS);
+                    vf.v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    const T *row = vt_ + (mb * 16 + col) * VTS + k2 * 32 + grp * 4;
+                    load_halves(vf, row, row + 16);
+                }
                 o[mb] = mma16(vf, pf, o[mb]);
             }
         }

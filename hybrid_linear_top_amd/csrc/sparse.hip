@@ -323,14 +323,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
 // in the S^T accumulators.  K and V of a step share one LDS region (K is
 // read into registers before V overwrites it), and the next step's gathers
 // are issued as soon as both have been copied out of their registers.
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char *lds_byte_ptr) {
-    lds_bf16x4 *p = (lds_bf16x4 *)(__attribute__((address_space(3))) unsigned char *)(
-        (__attribute__((address_space(3))) void *)lds_byte_ptr);
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
-}
 
 template <int D>
 struct WaveSmem {
