@@ -168,7 +168,7 @@ PrefillWs prefill_ws(const lisa_dims *d, int B, int n, int nk) {
 }
 
 struct DecodeWs {
-    size_t scores, olin, idx, total;
+    size_t scores, olin, idx, cand, total;
 };
 DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
     const size_t G = d->num_kv_heads, Hq = d->num_q_heads, D = d->head_dim;
@@ -180,6 +180,8 @@ DecodeWs decode_ws(const lisa_dims *d, int B, int max_ctx) {
     off += align_up((size_t)B * Hq * D * 4);
     w.idx = off;
     off += align_up((size_t)B * G * d->top_m * 4);
+    w.cand = off;  // the two-part select of long contexts
+    off += align_up(lisa::decode_cand_bytes(B, (int)G, d->top_m, max_ctx));
     w.total = off;
     return w;
 }
@@ -541,7 +543,10 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     LISA_HIP(timed(ST_DEC_SCORE_STATE, s, [&] { return lisa::launch_decode_score_state(da, dims->dtype, D, dI, s); }),
              "indexer-scan/state launch");
     if (!window)
-        LISA_HIP(timed(ST_DEC_SELECT, s, [&] { return lisa::launch_decode_select(scores, map, B, G, dims->top_m, max_ctx, idx, s); }),
+        LISA_HIP(timed(ST_DEC_SELECT, s, [&] {
+                     return lisa::launch_decode_select(scores, map, B, G, dims->top_m, max_ctx, idx,
+                                                       reinterpret_cast<int32_t *>(ws + w.cand), s);
+                 }),
                  "top-M select launch");
 
     lisa::SparseArgs sa{};

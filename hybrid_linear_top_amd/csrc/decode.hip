@@ -219,184 +219,6 @@ __global__ __launch_bounds__(256) void decode_score_state_kernel(DecodeScoreArgs
 }
 
 // ---------------------------------------------------------------------------
-// Top-M select of one (sequence, group): NT threads, thread t holding the
-// order keys of positions t, t+NT, ... in registers (EPT of them).
-//  1. min / max key of the sequence;
-//  2. up to three 2048-bin histogram passes over the live key range (bins are
-//     (key - lo) >> shift, so they spread over the actual scores rather than
-//     the fixed top bits, which keeps LDS atomics uncontended), each narrowing
-//     to the bin that holds the M-th largest key; a pass stops early when that
-//     bin is taken whole;
-//  3. ordered compaction: per (round k, wave w) ballots give counts of keys
-//     above the threshold and equal to it; one block scan over the (k, w)
-//     grid, which is index order, gives every selected key its position, the
-//     lowest indices taking the ties.
-template <int NT, int EPT>
-__global__ __launch_bounds__(NT) void decode_select_kernel(const float *scores,
-                                                                    CacheMap map, int G, int M,
-                                                                    int max_ctx, int32_t *idx) {
-    constexpr int BPT = (2048 + NT - 1) / NT;  // histogram bins per thread
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wtmp[(NT / 64) + 1];
-    __shared__ uint32_t bases[2][2 * NT + 1];
-    __shared__ uint32_t found[3];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bg = blockIdx.x, b = bg / G;
-    const int L = cache_len(map, b, max_ctx);
-    const float *sc = scores + (size_t)bg * max_ctx;
-    int32_t *out = idx + (size_t)bg * M;
-    if (L <= M) {
-        for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
-        return;
-    }
-    // ---- 1. key range (unconditional loads: positions >= L read zeros) ----
-    const rsrc_t srs = make_rsrc(sc, (uint32_t)L * 4u);
-    uint32_t keyreg[EPT];
-#pragma unroll
-    for (int k = 0; k < EPT; ++k)
-        keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(k * NT + tid) * 4u, 0u, 0);
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-        const int s = k * NT + tid;
-        keyreg[k] = order_key(__uint_as_float(keyreg[k]));
-        if (s < L) {
-            kmin = min(kmin, keyreg[k]);
-            kmax = max(kmax, keyreg[k]);
-        }
-    }
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    if (lane == 0) { hist[wave] = kmin; hist[(NT / 64) + wave] = kmax; }
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t a = 0xFFFFFFFFu, c = 0u;
-        for (int w = 0; w < (NT / 64); ++w) { a = min(a, hist[w]); c = max(c, hist[(NT / 64) + w]); }
-        found[0] = a;
-        found[1] = c;
-    }
-    __syncthreads();
-    // live range [lo, lo + 2^width): every key still in play
-    uint32_t lo = found[0];
-    const uint32_t span = found[1] - lo;
-    int width = span == 0 ? 0 : 32 - __builtin_clz(span);  // bits needed for key - lo
-    uint32_t need = (uint32_t)M;
-    uint32_t T = lo;          // selection threshold: keys >= T are candidates
-    uint32_t take_eq = 0;     // keys == T taken (lowest indices first) when exact
-    bool exact = false;
-    __syncthreads();
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = width > 11 ? width - 11 : 0;
-        for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
-        __syncthreads();
-        const uint64_t hi_excl = (uint64_t)lo + ((uint64_t)1 << width);
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) {
-            const int s = k * NT + tid;
-            const uint32_t u = keyreg[k];
-            if (s < L && u >= lo && (uint64_t)u < hi_excl) atomicAdd(&hist[(u - lo) >> shift], 1u);
-        }
-        __syncthreads();
-        // thread t owns bins 2047-BPT*t downwards; unused bins are empty
-        uint32_t hb[BPT], hsum = 0;
-#pragma unroll
-        for (int e = 0; e < BPT; ++e) {
-            const int bi = 2047 - BPT * tid - e;
-            hb[e] = bi >= 0 ? hist[bi] : 0u;
-            hsum += hb[e];
-        }
-        uint32_t tot;
-        const uint32_t before = block_exclusive_scan<NT>(hsum, wtmp, &tot);
-        if (before < need && before + hsum >= need) {
-            uint32_t run = before;
-#pragma unroll
-            for (int e = 0; e < BPT; ++e) {
-                if (run + hb[e] >= need) {
-                    found[0] = 2047 - BPT * tid - e;
-                    found[1] = need - run;
-                    found[2] = hb[e];
-                    break;
-                }
-                run += hb[e];
-            }
-        }
-        __syncthreads();
-        const uint32_t bin = found[0], rem = found[1], cnt_bin = found[2];
-        __syncthreads();
-        lo = lo + (bin << shift);
-        if (rem == cnt_bin) {   // the whole bin is taken: keys >= lo are exactly the top M
-            T = lo;
-            take_eq = 0;
-            exact = false;
-            break;
-        }
-        need = rem;
-        width = shift;
-        if (shift == 0) {       // bin is a single key value: keys > lo, plus `rem` ties
-            T = lo;
-            take_eq = rem;
-            exact = true;
-            break;
-        }
-    }
-    // ---- 3. ordered compaction ----
-    // gt: key > T (exact) or key >= T (whole-bin cut); eq: key == T (exact only)
-    constexpr int nr = EPT;
-#pragma unroll
-    for (int k = 0; k < nr; ++k) {
-        const int s = k * NT + tid;
-        const uint32_t u = keyreg[k];
-        const bool valid = s < L;
-        const bool gt = valid && (exact ? u > T : u >= T);
-        const bool eq = valid && exact && u == T;
-        const uint64_t gm = __ballot(gt), em = __ballot(eq);
-        if (lane == 0) {
-            bases[0][k * (NT / 64) + wave] = (uint32_t)__popcll(gm);
-            bases[1][k * (NT / 64) + wave] = (uint32_t)__popcll(em);
-        }
-    }
-    __syncthreads();
-    constexpr int cells = nr * (NT / 64);  // two per thread
-    static_assert(cells <= 2 * NT, "compaction cells");
-    {
-        uint32_t tot;
-        const int c0 = 2 * tid;
-        const uint32_t g0 = c0 < cells ? bases[0][c0] : 0u, g1 = c0 + 1 < cells ? bases[0][c0 + 1] : 0u;
-        const uint32_t e0 = c0 < cells ? bases[1][c0] : 0u, e1 = c0 + 1 < cells ? bases[1][c0 + 1] : 0u;
-        const uint32_t gpre = block_exclusive_scan<NT>(g0 + g1, wtmp, &tot);
-        const uint32_t epre = block_exclusive_scan<NT>(e0 + e1, wtmp, &tot);
-        if (c0 < cells) {
-            bases[0][c0] = gpre;
-            bases[1][c0] = epre;
-        }
-        if (c0 + 1 < cells) {
-            bases[0][c0 + 1] = gpre + g0;
-            bases[1][c0 + 1] = epre + e0;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < nr; ++k) {
-        const int s = k * NT + tid;
-        const uint32_t u = keyreg[k];
-        const bool valid = s < L;
-        const bool gt = valid && (exact ? u > T : u >= T);
-        const bool eq = valid && exact && u == T;
-        const uint64_t gm = __ballot(gt), em = __ballot(eq);
-        const int cell = k * (NT / 64) + wave;
-        const uint32_t gb = bases[0][cell] + mbcnt64(gm);
-        const uint32_t eb = bases[1][cell] + mbcnt64(em);
-        if (gt) {
-            const uint32_t pos = gb + min(eb, take_eq);
-            if (pos < (uint32_t)M) out[pos] = s;
-        } else if (eq && eb < take_eq) {
-            const uint32_t pos = gb + eb;
-            if (pos < (uint32_t)M) out[pos] = s;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // One wave: the m-th largest of c 32-bit keys kr[e] (element e*64 + lane),
 // all of them in [lo, lo + 2^width), by radix passes of up to 8 bits over
 // key - lo from bit width - 1 down, with a 256-bin LDS histogram.  theta is
@@ -467,9 +289,14 @@ __device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32
 //     the lowest `need` positions of it are taken;
 //  4. wave 0 walks the bitmaps in position order (contiguous words per lane,
 //     one wave scan of their counts) and writes the set ascending.
+// A launch with gridDim.y = 2 selects within one of two position ranges of
+// part_len positions (part blockIdx.y covers [part_len * part,
+// part_len * (part + 1))),
+// writing the part's set (positions, ascending) to row 2 bg + part of idx;
+// decode_merge_kernel then merges the two.
 template <int NT, int EPT, int CAP>
 __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, CacheMap map,
-                                                         int G, int M, int max_ctx, int32_t *idx) {
+                                                         int G, int M, int max_ctx, int part_len, int32_t *idx) {
     constexpr int NW = NT / 64;
     constexpr int NWORD = (NT * EPT + 31) / 32;  // bitmap words
     constexpr int WPL = (NWORD + 63) / 64;       // bitmap words per lane of wave 0
@@ -481,23 +308,24 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
     __shared__ uint32_t found[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bg = blockIdx.x, b = bg / G;
-    const float *sc = scores + (size_t)bg * max_ctx;
+    const int p0 = part_len * (int)blockIdx.y;  // first position of this part
+    const float *sc = scores + (size_t)bg * max_ctx + p0;
     // The score loads are issued first, before the sequence length is known:
     // the row holds max_ctx entries (the descriptor reads zeros past them)
     // and positions at or past L are masked below, so the loads need not
     // wait for the length lookup.  All of them are unconditional and in
-    // flight together.  The launch guarantees NT * EPT >= max_ctx.
+    // flight together.  The launch guarantees NT * EPT >= part_len.
     auto pos_of = [&](int k) { return k * NT + tid; };
-    const rsrc_t srs = make_rsrc(sc, (uint32_t)max_ctx * 4u);
+    const rsrc_t srs = make_rsrc(sc, (uint32_t)(max_ctx - p0) * 4u);
     uint32_t keyreg[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k)
         keyreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)pos_of(k) * 4u, 0u, 0);
-    const int L = cache_len(map, b, max_ctx);
+    const int L = min(max(cache_len(map, b, max_ctx) - p0, 0), part_len);
     auto valid = [&](int k) { return pos_of(k) < L; };
-    int32_t *out = idx + (size_t)bg * M;
+    int32_t *out = idx + ((size_t)bg * gridDim.y + blockIdx.y) * M;
     if (L <= M) {
-        for (int i = tid; i < M; i += NT) out[i] = i < L ? i : -1;
+        for (int i = tid; i < M; i += NT) out[i] = i < L ? p0 + i : -1;
         return;
     }
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, tmax = 0u;
@@ -630,7 +458,7 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
                 const uint64_t km = __ballot(keep);
                 const uint32_t pos = base + mbcnt64(km);
                 base += (uint32_t)__popcll(km);
-                if (keep && pos < (uint32_t)M) out[pos] = (int32_t)fpos[e * 64 + lane];
+                if (keep && pos < (uint32_t)M) out[pos] = p0 + (int32_t)fpos[e * 64 + lane];
             }
             return;
         }
@@ -781,17 +609,98 @@ __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, Ca
             const int s = 32 * w + bit;
             if ((gw >> bit) & 1u) {
                 const uint32_t pos = gpos + min(epos, take);
-                if (pos < (uint32_t)M) out[pos] = s;
+                if (pos < (uint32_t)M) out[pos] = p0 + s;
                 ++gpos;
             } else {
                 if (epos < take) {
                     const uint32_t pos = gpos + epos;
-                    if (pos < (uint32_t)M) out[pos] = s;
+                    if (pos < (uint32_t)M) out[pos] = p0 + s;
                 }
                 ++epos;
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the two parts' sets of one (sequence, group): the 2M candidates
+// (positions ascending within each part, the parts in order, -1 padded) are
+// ranked by the 64-bit key (score order key, complemented position), the
+// M-th largest found by eight 8-bit radix passes of a 256-bin histogram, and
+// the kept ones written in candidate order, which is position order.
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void decode_merge_kernel(const float *scores, const int32_t *cand, int M,
+                                                          int max_ctx, int32_t *idx) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wtmp[NT / 64 + 1];
+    __shared__ uint32_t found[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bg = blockIdx.x, C = 2 * M;
+    const int32_t *cb = cand + (size_t)bg * C;
+    const float *sc = scores + (size_t)bg * max_ctx;
+    int32_t pos[E];
+    uint64_t key[E];  // 0 for no candidate; a candidate's key is at least 2^32
+    uint32_t own = 0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int i = k * NT + tid;
+        pos[k] = i < C ? cb[i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        key[k] = pos[k] >= 0 ? ((uint64_t)order_key(sc[pos[k]]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos[k])
+                             : 0ull;
+        own += pos[k] >= 0 ? 1u : 0u;
+    }
+    uint32_t nval;
+    block_exclusive_scan<NT>(own, wtmp, &nval);
+    uint64_t theta = 1ull;  // every candidate is kept when there are at most M
+    if (nval > (uint32_t)M) {
+        uint64_t prefix = 0ull;  // the bits of theta above the current digit
+        uint32_t need = (uint32_t)M;
+#pragma unroll 1
+        for (int sh = 56; sh >= 0; sh -= 8) {
+            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const bool live = key[k] != 0ull && (sh == 56 || (key[k] >> (sh + 8)) == (prefix >> (sh + 8)));
+                if (live) atomicAdd(&hist[(key[k] >> sh) & 255u], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) {
+                // lane l owns bins 4 l .. 4 l + 3; the count from the top reaches need in one of them
+                const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);
+                const uint32_t incl = wave_inclusive_scan(h[0] + h[1] + h[2] + h[3]);
+                const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+                uint32_t run = total - incl;
+#pragma unroll
+                for (int bb = 3; bb >= 0; --bb) {
+                    if (run < need && run + h[bb] >= need) {
+                        found[0] = 4 * lane + bb;
+                        found[1] = need - run;
+                    }
+                    run += h[bb];
+                }
+            }
+            __syncthreads();
+            prefix |= (uint64_t)found[0] << sh;
+            need = found[1];
+            __syncthreads();
+        }
+        theta = prefix;  // the M-th largest key: exactly M keys are >= it
+    }
+    int32_t *out = idx + (size_t)bg * M;
+    uint32_t base = 0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const bool kept = key[k] != 0ull && key[k] >= theta;
+        uint32_t tot;
+        const uint32_t at = block_exclusive_scan<NT>(kept ? 1u : 0u, wtmp, &tot);
+        if (kept) out[base + at] = pos[k];
+        base += tot;
+    }
+    for (int i = (int)base + tid; i < M; i += NT) out[i] = -1;
 }
 
 template <typename T, int D, int DI, int HIPAD>
@@ -821,24 +730,26 @@ hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d,
 }
 
 hipError_t launch_decode_select(const float *scores, const CacheMap &cu, int B, int G, int M,
-                                int max_ctx, int32_t *idx, hipStream_t s) {
+                                int max_ctx, int32_t *idx, int32_t *cand, hipStream_t s) {
     const dim3 grid(B * G);
-#define LISA_SEL(NT_, E)                                                                          \
-    if (max_ctx <= (E) * (NT_)) {                                                                 \
-        launch_kernel((decode_select_kernel<NT_, E>), grid, dim3(NT_), 0, s, scores, cu, G, M, \
-                           max_ctx, idx);                                                         \
-        return hipGetLastError();                                                                 \
+    // above 33,792 positions: two parts of 32,768 (keys in registers), then a merge
+    if (max_ctx > 33 * 1024) {
+        if (!cand || max_ctx > 2 * 32768 || M > 2048) return hipErrorInvalidValue;
+        launch_kernel((decode_topm_kernel<1024, 32, 1024>), dim3(B * G, 2), dim3(1024), 0, s, scores, cu, G, M,
+                      max_ctx, 32768, cand);
+        launch_kernel((decode_merge_kernel<1024, 4>), grid, dim3(1024), 0, s, scores, (const int32_t *)cand, M,
+                      max_ctx, idx);
+        return hipGetLastError();
     }
 #define LISA_TOPM(NT_, E, CAP_)                                                                   \
     if (max_ctx <= (E) * (NT_)) {                                                                 \
         launch_kernel((decode_topm_kernel<NT_, E, CAP_>), grid, dim3(NT_), 0, s, scores, cu, G, \
-                           M, max_ctx, idx);                                                      \
+                           M, max_ctx, max_ctx, idx);                                             \
         return hipGetLastError();                                                                 \
     }
     // keys per thread stay in registers: 1024 threads (128 VGPRs) up to 33,792
-    // positions, 768 threads (170 VGPRs) for longer ones
-    LISA_TOPM(1024, 8, 1024) LISA_TOPM(1024, 17, 1024) LISA_TOPM(1024, 33, 1024) LISA_SEL(768, 86)
-#undef LISA_SEL
+    // positions (longer contexts take the two-part path above)
+    LISA_TOPM(1024, 8, 1024) LISA_TOPM(1024, 17, 1024) LISA_TOPM(1024, 33, 1024)
 #undef LISA_TOPM
     return hipErrorInvalidValue;  // longer contexts are rejected by the API layer
 }

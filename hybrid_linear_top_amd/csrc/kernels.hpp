@@ -74,8 +74,13 @@ constexpr int kDecodeTile = 128;  // tokens per score work-group
 
 hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI,
                                      hipStream_t s);
+// cand: workspace of B * G * 2 * M int32 (decode_cand_entries), used above
+// 33,792 positions (two parts, then a merge); may be null below
 hipError_t launch_decode_select(const float *scores, const CacheMap &map, int B, int G, int M,
-                                int max_ctx, int32_t *idx, hipStream_t s);
+                                int max_ctx, int32_t *idx, int32_t *cand, hipStream_t s);
+inline size_t decode_cand_bytes(int B, int G, int M, int max_ctx) {
+    return max_ctx > 33 * 1024 ? (size_t)B * G * 2 * M * 4 : 0;
+}
 
 // ---- sparse attention + gate (prefill and decode) -------------------------
 struct SparseArgs {

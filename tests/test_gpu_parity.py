@@ -128,7 +128,10 @@ DECODE_SMALL = [
     _dcfg(28, 4, 128, 4, 64, 512, [4097, 700, 513, 20000], seed=2),
     _dcfg(8, 2, 64, 8, 64, 100, [999, 1001, 5000], dtype="f32", seed=3),
     _dcfg(16, 1, 128, 6, 64, 2048, [3000, 2048, 2049], seed=4),
-    _dcfg(4, 1, 64, 4, 32, 256, [40000, 3, 33100], seed=5),   # longest-context select variant
+    _dcfg(4, 1, 64, 4, 32, 256, [40000, 3, 33100], seed=5),   # two-part select and its merge
+    # the two-part select with M = 2048 (its parts' exact passes; 4096
+    # candidates merged), contexts at its lower edge, between and at the top
+    _dcfg(8, 2, 64, 4, 32, 2048, [33793, 47000, 65536], seed=21),
     # the 33-keys-per-thread top-M, at its largest context and just above the
     # 17-keys-per-thread one's
     _dcfg(4, 1, 64, 4, 32, 512, [33792, 17409, 9000], seed=6),
@@ -188,12 +191,15 @@ def test_ties_lowest_index_wins():
         assert np.array_equal(didx[b, 0], exp) and np.array_equal(didx[b, 1], exp), b
 
 
-@pytest.mark.parametrize("lengths", [[8000, 300], [17000], [33792, 18000], [40000, 5], [65536]],
-                         ids=["ctx8000", "ctx17000", "ctx33792", "ctx40000", "ctx65536"])
-def test_decode_ties_every_select_variant(lengths):
+@pytest.mark.parametrize("lengths,M", [([8000, 300], 512), ([17000], 512), ([33792, 18000], 512),
+                                       ([40000, 5], 512), ([65536], 512), ([40000, 34000], 2048)],
+                         ids=["ctx8000", "ctx17000", "ctx33792", "ctx40000", "ctx65536", "ctx40000_m2048"])
+def test_decode_ties_every_select_variant(lengths, M):
     """w = 0 at contexts that pick each top-M kernel variant: every score is
-    exactly 0, so each set is the first min(M, L) positions."""
-    dcfg, L = _dcfg(4, 2, 64, 4, 32, 512, lengths, seed=8)
+    exactly 0, so each set is the first min(M, L) positions (in the two-part
+    select above 33,792 positions both parts hold tied candidates, and the
+    merge must keep the first part's)."""
+    dcfg, L = _dcfg(4, 2, 64, 4, 32, M, lengths, seed=8)
     _say("decode all-ties", dcfg.name)
     dinp = gen.make_decode_inputs(dcfg, lengths=L)
     dinp["w_idx"] = np.zeros_like(dinp["w_idx"])
