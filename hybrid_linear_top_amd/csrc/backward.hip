@@ -403,22 +403,46 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
     const int rsub = lane / LPR, piece = lane % LPR, rho0 = rsub * NI;
     const int nsteps = (nvalid + 31) / 32;
     u32x4 kp[NI], vp[NI];
+    // the slots' indices load two steps ahead of their gathers (vector loads
+    // when the rows are 16-byte aligned), so no gather waits on an index load
+    struct Idx { u32x4 v[NI / 4]; };
+    const bool idx16 = (M & 3) == 0;
+    auto load_idx = [&](int j) {
+        Idx x;
+        const uint32_t o = (uint32_t)(j * 32 + rho0) * 4u;
+        if (idx16) {
+#pragma unroll
+            for (int h = 0; h < NI / 4; ++h) x.v[h] = buf_load16(irs, o + 16u * h);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                x.v[i / 4][i % 4] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(irs, o + 4u * i, 0u, 0);
+        }
+        return x;
+    };
+    Idx inext;
     uint32_t okbits = 0;  // bit i: row rho0 + i of the step in flight is a valid slot
-    auto gather = [&](int j) {
+    // row offsets by clamped 24-bit products: an index past t (or -1) reads
+    // the row past the last, zeros through the descriptor
+    const uint32_t uend = (uint32_t)t + 1u;
+    auto gather = [&](int j, const Idx &x) {
         okbits = 0;
         uint32_t off[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int slot = j * 32 + rho0 + i;
-            const int s = (int)__builtin_amdgcn_raw_buffer_load_b32(irs, (uint32_t)slot * 4u, 0u, 0);
-            const bool ok = slot < nvalid && s >= 0 && s <= t;
+            const uint32_t si = x.v[i / 4][i % 4];
+            const bool ok = j * 32 + rho0 + i < nvalid && si <= (uint32_t)t;
             okbits |= ok ? (1u << i) : 0u;
-            off[i] = ok ? (uint32_t)s * row_bytes + piece * 16 : kOffNone;
+            off[i] = __umul24(min(si, uend), row_bytes) + piece * 16;
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) kp[i] = buf_load16(krs, off[i]);
 #pragma unroll
         for (int i = 0; i < NI; ++i) vp[i] = buf_load16(vrs, off[i]);
+    };
+    auto start = [&]() {  // a sweep's first gather, and the next step's indices in flight
+        gather(0, load_idx(0));
+        inext = load_idx(1);
     };
     const uint32_t kw = (uint32_t)rho0 * KRB + piece * 16, vw = (uint32_t)rho0 * VRB + piece * 16;
     const uint32_t kfr = (uint32_t)col * KRB + grp * 16, vfr = (uint32_t)col * VRB + grp * 16;
@@ -436,7 +460,10 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
             *reinterpret_cast<u32x4 *>(ldv + vw + i * VRB) = vp[i];
             if (piece == 0) flg[rho0 + i] = (okbits >> i) & 1u;
         }
-        if (j + 1 < nsteps) gather(j + 1);
+        if (j + 1 < nsteps) {
+            gather(j + 1, inext);
+            inext = load_idx(j + 2);
+        }
         wave_lds_sync();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -457,7 +484,7 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
 
     // ---- sweep 1: max, normaliser and E per head (column) ----------------------
     float m_run = -INFINITY, l_part = 0.0f, e_part = 0.0f;
-    gather(0);
+    start();
     for (int j = 0; j < nsteps; ++j) {
         step(j);
         float x[8], cmax = -INFINITY;
@@ -490,7 +517,7 @@ __global__ __launch_bounds__(64) void sparse_bwd_q_kernel(SparseBwdArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) o[mb] = f32x4{0, 0, 0, 0};
     float *coefu = a.coef + (size_t)u * M * 2 * r;
-    gather(0);
+    start();
     for (int j = 0; j < nsteps; ++j) {
         step(j);
         float dsv[8];
