@@ -69,10 +69,11 @@ def decode_bytes(cfg, lengths):
     kv_rows = int(np.minimum(L, cfg.M).sum()) * G * 2 * d * 2
     state = B * Hq * d * d * 4 * 2
     small = B * (2 * Hq * d * 2 + G * cfg.HI * cfg.dI * 2 + G * cfg.HI * 2 + Hq * 2 + 2 * G * d * 2)
+    # the score launch streams k_I; the state step (state read and write, the
+    # new token's q, k, v) runs in the select launch, beside the selects
     return {
-        "decode_score_state": kI + state + B * (Hq * d * 2 + G * cfg.HI * cfg.dI * 2
-                                                + G * cfg.HI * 2 + 2 * G * d * 2),
-        "decode_select": 0,
+        "decode_score_state": kI + B * (G * cfg.HI * cfg.dI * 2 + G * cfg.HI * 2),
+        "decode_select": state + B * (Hq * d * 2 + 2 * G * d * 2),
         "sparse_gate_decode": kv_rows + B * (2 * Hq * d * 2 + Hq * 2),
         "total": kI + kv_rows + state + small,
         "kI": kI, "kv_rows": kv_rows, "state": state, "small": small,
@@ -91,7 +92,7 @@ STAGE_KERNELS = {
     "linear_prefix_scan": (r"prefix_scan_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
     "linear_chunk_output": (r"chunk_output_kernel<", ["linear.hip", "common.hpp", "kernels.hpp"]),
     "decode_score_state": (r"decode_score_state_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
-    "decode_select": (r"decode_topm_kernel<|decode_select_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
+    "decode_select": (r"decode_topm_kernel<|decode_merge_kernel<", ["decode.hip", "common.hpp", "kernels.hpp"]),
     "bwd_sparse": (r"sparse_bwd_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
     "bwd_sparse_query": (r"sparse_bwd_q_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),
     "bwd_sparse_keys": (r"sparse_bwd_walk_kernel<", ["backward.hip", "common.hpp", "kernels.hpp"]),

@@ -540,12 +540,16 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
     // the window variant launches the state groups only (no indexer scan)
     da.tiles_per_seq = window ? 0 : (max_ctx + lisa::kDecodeTile - 1) / lisa::kDecodeTile;
     const int dI = window ? 64 : dims->idx_dim;  // any supported width: no score groups run
-    LISA_HIP(timed(ST_DEC_SCORE_STATE, s, [&] { return lisa::launch_decode_score_state(da, dims->dtype, D, dI, s); }),
+    // with the indexer, the state step runs in the select's launch, beside
+    // the selects (it does not need the scores)
+    LISA_HIP(timed(ST_DEC_SCORE_STATE, s,
+                   [&] { return lisa::launch_decode_score_state(da, dims->dtype, D, dI, window, s); }),
              "indexer-scan/state launch");
     if (!window)
         LISA_HIP(timed(ST_DEC_SELECT, s, [&] {
                      return lisa::launch_decode_select(scores, map, B, G, dims->top_m, max_ctx, idx,
-                                                       reinterpret_cast<int32_t *>(ws + w.cand), s);
+                                                       reinterpret_cast<int32_t *>(ws + w.cand), &da, dims->dtype, D,
+                                                       s);
                  }),
                  "top-M select launch");
 

@@ -143,77 +143,101 @@ __device__ void score_group(const DecodeScoreArgs &a, int sb, u32x4 *stage) {
 // Linear-attention step of one query head, one column slice of its state:
 // state group uu is (sequence b, head h, slice part), the slice being value
 // columns [part*D/CS, (part+1)*D/CS) of S (all D rows), so o_lin's columns
-// of the slice are complete within the group.  The state loads are issued
-// before anything else, as they wait for nothing.
-template <typename T, int D>
-__device__ void state_group(const DecodeScoreArgs &a, int uu, float *smem) {
+// of the slice are complete within the group.  It runs on 256 threads (tid
+// 0..255), which may be a quarter of a larger work-group: sync() is a
+// barrier every thread of the work-group reaches the same number of times,
+// so an inactive group (active false: past the last) still takes part.  The
+// state loads are issued before anything else, as they wait for nothing.
+template <typename T, int D, typename Sync>
+__device__ void state_group(const DecodeScoreArgs &a, int uu, float *smem, int tid, bool active, Sync &&sync) {
     constexpr int CS = D / 32;        // column slices per head
     constexpr int NQ = D / 4;         // float4 columns of a state row
     constexpr int NQP = NQ / CS;      // float4 columns of the slice
     constexpr int RG = 256 / NQP;     // row groups
     constexpr int RPT = D / RG;       // rows per thread
-    const int tid = threadIdx.x;
     const int part = uu % CS, u = uu / CS;
-    const int Hq = a.Hq, b = u / Hq, h = u % Hq;
+    const int Hq = a.Hq, b = active ? u / Hq : 0, h = u % Hq;
     const int g = (int)(((int64_t)h * a.G) / Hq);
     const int jq = part * NQP + tid % NQP, rg = tid / NQP;
     f32x4 *S = reinterpret_cast<f32x4 *>(a.state + ((size_t)b * Hq + h) * D * D);
     f32x4 sv[RPT];
+    if (active) {
 #pragma unroll
-    for (int s = 0; s < RPT; ++s) sv[s] = __builtin_nontemporal_load(&S[(rg + RG * s) * NQ + jq]);
+        for (int s = 0; s < RPT; ++s) sv[s] = __builtin_nontemporal_load(&S[(rg + RG * s) * NQ + jq]);
+    }
     const int64_t row0 = a.map.table ? 0 : a.cu[b];
     const int32_t *ptab = a.map.table ? a.map.table + (size_t)b * a.map.max_blocks : nullptr;
-    const int L = cache_len(a.map, b, a.max_ctx);
+    const int L = active ? cache_len(a.map, b, a.max_ctx) : 0;
     float *olin = a.olin + ((size_t)b * Hq + h) * D + part * NQP * 4;
-    if (L < 1) {
-        if (tid < NQP * 4) olin[tid] = 0.0f;
-        return;
-    }
-    const int64_t trow = cache_row(a.map, row0, ptab, L - 1);
+    const bool work = active && L >= 1;
+    if (active && !work && tid < NQP * 4) olin[tid] = 0.0f;
     float *kk = smem, *vv = smem + D, *qq = smem + 2 * D, *red = smem + 3 * D;
-    const T *kc = reinterpret_cast<const T *>(a.k_cache);
-    const T *vc = reinterpret_cast<const T *>(a.v_cache);
-    const T *qp = reinterpret_cast<const T *>(a.q);
-    if (tid < D) {
+    if (work && tid < D) {
+        const int64_t trow = cache_row(a.map, row0, ptab, L - 1);
+        const T *kc = reinterpret_cast<const T *>(a.k_cache);
+        const T *vc = reinterpret_cast<const T *>(a.v_cache);
+        const T *qp = reinterpret_cast<const T *>(a.q);
         kk[tid] = Elt<T>::to_f32(kc[((size_t)trow * a.G + g) * D + tid]);
         vv[tid] = Elt<T>::to_f32(vc[((size_t)trow * a.G + g) * D + tid]);
         qq[tid] = Elt<T>::to_f32(qp[((size_t)b * Hq + h) * D + tid]);
     }
-    __syncthreads();
-    const f32x4 v4 = *reinterpret_cast<const f32x4 *>(vv + 4 * jq);
-    f32x4 o = {0, 0, 0, 0};
+    sync();
+    if (work) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(vv + 4 * jq);
+        f32x4 o = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < RPT; ++s) {
-        const int i = rg + RG * s;
-        const float ki = kk[i], qi = qq[i];
-        f32x4 x = sv[s];
-        x[0] = fmaf(ki, v4[0], x[0]);
-        x[1] = fmaf(ki, v4[1], x[1]);
-        x[2] = fmaf(ki, v4[2], x[2]);
-        x[3] = fmaf(ki, v4[3], x[3]);
-        __builtin_nontemporal_store(x, &S[i * NQ + jq]);
-        o[0] = fmaf(qi, x[0], o[0]);
-        o[1] = fmaf(qi, x[1], o[1]);
-        o[2] = fmaf(qi, x[2], o[2]);
-        o[3] = fmaf(qi, x[3], o[3]);
+        for (int s = 0; s < RPT; ++s) {
+            const int i = rg + RG * s;
+            const float ki = kk[i], qi = qq[i];
+            f32x4 x = sv[s];
+            x[0] = fmaf(ki, v4[0], x[0]);
+            x[1] = fmaf(ki, v4[1], x[1]);
+            x[2] = fmaf(ki, v4[2], x[2]);
+            x[3] = fmaf(ki, v4[3], x[3]);
+            __builtin_nontemporal_store(x, &S[i * NQ + jq]);
+            o[0] = fmaf(qi, x[0], o[0]);
+            o[1] = fmaf(qi, x[1], o[1]);
+            o[2] = fmaf(qi, x[2], o[2]);
+            o[3] = fmaf(qi, x[3], o[3]);
+        }
+        *reinterpret_cast<f32x4 *>(red + rg * (NQP * 4) + 4 * (tid % NQP)) = o;
     }
-    *reinterpret_cast<f32x4 *>(red + rg * (NQP * 4) + 4 * (tid % NQP)) = o;
-    __syncthreads();
-    if (tid < NQP * 4) {
+    sync();
+    if (work && tid < NQP * 4) {
         float acc = 0.0f;
         for (int r = 0; r < RG; ++r) acc += red[r * (NQP * 4) + tid];
         olin[tid] = acc;
+    }
+}
+constexpr int kStateFloats = 3 * 128 + 1024;  // a state group's LDS (D <= 128)
+
+// the state groups of a launch of 1024-thread work-groups: four per group
+// state groups first + 4 wg + sub (sub = 0..3) of a launch of 1024-thread
+// work-groups, up to n_state
+template <typename T, int D>
+__device__ void state_quads(const DecodeScoreArgs &a, int first, int wg, int n_state, float *smem) {
+    const int sub = threadIdx.x >> 8, uu = first + 4 * wg + sub;
+    state_group<T, D>(a, uu, smem + sub * kStateFloats, threadIdx.x & 255, uu < n_state, [] { __syncthreads(); });
+}
+__device__ __forceinline__ void state_quads_any(const DecodeScoreArgs &a, int dtype, int d, int first, int wg,
+                                                int n_state, float *smem) {
+    if (dtype == 1) {
+        if (d == 128) state_quads<uint16_t, 128>(a, first, wg, n_state, smem);
+        else state_quads<uint16_t, 64>(a, first, wg, n_state, smem);
+    } else {
+        if (d == 128) state_quads<float, 128>(a, first, wg, n_state, smem);
+        else state_quads<float, 64>(a, first, wg, n_state, smem);
     }
 }
 
 template <typename T, int D, int DI, int HIPAD>
 __global__ __launch_bounds__(256) void decode_score_state_kernel(DecodeScoreArgs a, int n_state) {
     // state groups: 3 vectors + the reduction rows; score groups: 64 key rows per wave
-    constexpr int kStateBytes = (3 * 128 + 1024) * 4;
+    constexpr int kStateBytes = kStateFloats * 4;
     constexpr int kStageBytes = 4 * 64 * DI * (int)Elt<T>::kBytes;
     __shared__ u32x4 smem[(kStateBytes > kStageBytes ? kStateBytes : kStageBytes) / 16];
     if ((int)blockIdx.x < n_state)
-        state_group<T, D>(a, blockIdx.x, reinterpret_cast<float *>(smem));
+        state_group<T, D>(a, blockIdx.x, reinterpret_cast<float *>(smem), threadIdx.x, true, [] { __syncthreads(); });
     else
         score_group<T, DI, HIPAD>(a, blockIdx.x - n_state, smem);
 }
@@ -294,9 +318,23 @@ __device__ void wave_kth_u32(const uint32_t (&kr)[NE], int c, uint32_t m, uint32
 // part_len * (part + 1))),
 // writing the part's set (positions, ascending) to row 2 bg + part of idx;
 // decode_merge_kernel then merges the two.
+// Work-groups past the first nbg of the launch (in part 0) do state groups
+// state_first .. n_state - 1 of the linear-attention step instead, four each
+// (state_quads): that step does not need the scores, so it runs beside the
+// selects, off the scan's critical path (16K decode, 1.5B shapes: 36.9 ->
+// 34.2 us per step; ragged 7B batch: 103 -> 98 us, where the state stream
+// is longer than the selects).
 template <int NT, int EPT, int CAP>
 __global__ __launch_bounds__(NT) void decode_topm_kernel(const float *scores, CacheMap map,
-                                                         int G, int M, int max_ctx, int part_len, int32_t *idx) {
+                                                         int G, int M, int max_ctx, int part_len, int32_t *idx,
+                                                         int nbg, DecodeScoreArgs sa, int state_first,
+                                                         int n_state, int dtype, int d) {
+    static_assert(NT == 1024, "state groups run four to a work-group");
+    __shared__ __attribute__((aligned(16))) float st_smem[4 * kStateFloats];
+    if ((int)blockIdx.x >= nbg) {
+        if (blockIdx.y == 0) state_quads_any(sa, dtype, d, state_first, (int)blockIdx.x - nbg, n_state, st_smem);
+        return;
+    }
     constexpr int NW = NT / 64;
     constexpr int NWORD = (NT * EPT + 31) / 32;  // bitmap words
     constexpr int WPL = (NWORD + 63) / 64;       // bitmap words per lane of wave 0
@@ -704,8 +742,10 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(const float *scores, c
 }
 
 template <typename T, int D, int DI, int HIPAD>
-hipError_t launch_ss(const DecodeScoreArgs &a, hipStream_t s) {
-    const int n_state = a.B * a.Hq * (D / 32);  // column slices of every head's state
+hipError_t launch_ss(const DecodeScoreArgs &a, bool with_state, hipStream_t s) {
+    // state groups: column slices of every head's state (else the select
+    // launch runs them)
+    const int n_state = with_state ? a.B * a.Hq * (D / 32) : 0;
     const int n_score = a.B * a.tiles_per_seq;
     launch_kernel((decode_score_state_kernel<T, D, DI, HIPAD>), dim3(n_state + n_score),
                        dim3(256), 0, s, a, n_state);
@@ -713,10 +753,11 @@ hipError_t launch_ss(const DecodeScoreArgs &a, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t dispatch_ss(const DecodeScoreArgs &a, int d, int dI, hipStream_t s) {
+hipError_t dispatch_ss(const DecodeScoreArgs &a, int d, int dI, bool with_state, hipStream_t s) {
     const bool h8 = a.HI > 4;
-#define LISA_SS(D_, DI_)                                                                 \
-    if (d == D_ && dI == DI_) return h8 ? launch_ss<T, D_, DI_, 8>(a, s) : launch_ss<T, D_, DI_, 4>(a, s);
+#define LISA_SS(D_, DI_)                                                                                \
+    if (d == D_ && dI == DI_)                                                                            \
+        return h8 ? launch_ss<T, D_, DI_, 8>(a, with_state, s) : launch_ss<T, D_, DI_, 4>(a, with_state, s);
     LISA_SS(64, 32) LISA_SS(64, 64) LISA_SS(128, 32) LISA_SS(128, 64)
 #undef LISA_SS
     return hipErrorInvalidValue;
@@ -724,28 +765,34 @@ hipError_t dispatch_ss(const DecodeScoreArgs &a, int d, int dI, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI,
+hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI, bool with_state,
                                      hipStream_t s) {
-    return dtype == 1 ? dispatch_ss<uint16_t>(a, d, dI, s) : dispatch_ss<float>(a, d, dI, s);
+    return dtype == 1 ? dispatch_ss<uint16_t>(a, d, dI, with_state, s) : dispatch_ss<float>(a, d, dI, with_state, s);
 }
 
 hipError_t launch_decode_select(const float *scores, const CacheMap &cu, int B, int G, int M,
-                                int max_ctx, int32_t *idx, int32_t *cand, hipStream_t s) {
+                                int max_ctx, int32_t *idx, int32_t *cand, const DecodeScoreArgs *st, int dtype,
+                                int d, hipStream_t s) {
     const dim3 grid(B * G);
+    const int n_state = st ? B * st->Hq * (d / 32) : 0;
+    const int first = 0;                // the select launch runs every state group
+    const int nsw = (n_state + 3) / 4;  // state work-groups
+    const DecodeScoreArgs sa = st ? *st : DecodeScoreArgs{};
+    const dim3 sgrid((unsigned)(B * G + nsw));
     // above 33,792 positions: two parts of 32,768 (keys in registers), then a merge
     if (max_ctx > 33 * 1024) {
         if (!cand || max_ctx > 2 * 32768 || M > 2048) return hipErrorInvalidValue;
-        launch_kernel((decode_topm_kernel<1024, 32, 1024>), dim3(B * G, 2), dim3(1024), 0, s, scores, cu, G, M,
-                      max_ctx, 32768, cand);
+        launch_kernel((decode_topm_kernel<1024, 32, 1024>), dim3(B * G + nsw, 2), dim3(1024), 0, s, scores, cu, G,
+                      M, max_ctx, 32768, cand, B * G, sa, first, n_state, dtype, d);
         launch_kernel((decode_merge_kernel<1024, 4>), grid, dim3(1024), 0, s, scores, (const int32_t *)cand, M,
                       max_ctx, idx);
         return hipGetLastError();
     }
-#define LISA_TOPM(NT_, E, CAP_)                                                                   \
-    if (max_ctx <= (E) * (NT_)) {                                                                 \
-        launch_kernel((decode_topm_kernel<NT_, E, CAP_>), grid, dim3(NT_), 0, s, scores, cu, G, \
-                           M, max_ctx, max_ctx, idx);                                             \
-        return hipGetLastError();                                                                 \
+#define LISA_TOPM(NT_, E, CAP_)                                                                    \
+    if (max_ctx <= (E) * (NT_)) {                                                                  \
+        launch_kernel((decode_topm_kernel<NT_, E, CAP_>), sgrid, dim3(NT_), 0, s, scores, cu, G, \
+                      M, max_ctx, max_ctx, idx, B * G, sa, first, n_state, dtype, d);              \
+        return hipGetLastError();                                                                  \
     }
     // keys per thread stay in registers: 1024 threads (128 VGPRs) up to 33,792
     // positions (longer contexts take the two-part path above)

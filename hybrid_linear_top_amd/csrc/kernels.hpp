@@ -72,12 +72,16 @@ struct DecodeScoreArgs {
 };
 constexpr int kDecodeTile = 128;  // tokens per score work-group
 
-hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI,
+// with_state: the score launch runs the linear-attention state step (no
+// select launch follows); else the select launch runs it, beside the selects
+hipError_t launch_decode_score_state(const DecodeScoreArgs &a, int dtype, int d, int dI, bool with_state,
                                      hipStream_t s);
-// cand: workspace of B * G * 2 * M int32 (decode_cand_entries), used above
-// 33,792 positions (two parts, then a merge); may be null below
+// cand: workspace of B * G * 2 * M int32 (decode_cand_bytes), used above
+// 33,792 positions (two parts, then a merge); may be null below.  st: when
+// not null, the launch also runs the state step of st (dtype, head dim d).
 hipError_t launch_decode_select(const float *scores, const CacheMap &map, int B, int G, int M,
-                                int max_ctx, int32_t *idx, int32_t *cand, hipStream_t s);
+                                int max_ctx, int32_t *idx, int32_t *cand, const DecodeScoreArgs *st, int dtype,
+                                int d, hipStream_t s);
 inline size_t decode_cand_bytes(int B, int G, int M, int max_ctx) {
     return max_ctx > 33 * 1024 ? (size_t)B * G * 2 * M * 4 : 0;
 }
