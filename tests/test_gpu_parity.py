@@ -104,6 +104,20 @@ def test_prefill_max_length_sampled_rows():
     _say("  ", rep)
 
 
+def test_prefill_two_sequences_long_sampled_rows():
+    """Two sequences of 8400 positions at d = 128, three groups, M = 130
+    (index rows not 16-byte aligned), in the group-major unit order of
+    batches above one sequence; rows at both ends and across the middle."""
+    cfg = _pcfg(8400, 6, 3, 128, 4, 64, 130, B=2, seed=38)
+    _say("prefill", cfg.name, "(sampled rows)")
+    inp = gen.make_prefill_inputs(cfg)
+    rng = np.random.default_rng(38)
+    rows = sorted(set([0, 1, 15, 16, 17, 2000, 8191, 8192, 8399] + rng.integers(0, cfg.n, size=8).tolist()))
+    rep = {}
+    parity.prefill_parity(cfg, inp, rows=rows, report=rep)
+    _say("  ", rep)
+
+
 def test_prefill_config3_all_rows():
     """The 16K 7B-shaped workload in the benchmark's launch configuration,
     every row: index sets of all 16384 x 4 units, all outputs and the state."""
@@ -230,6 +244,9 @@ CONTINUE_CASES = [
     (_pcfg(1300, 8, 2, 128, 4, 64, 128, seed=33), 1299),    # one new token (a decode step by prefill)
     (_pcfg(2500, 12, 2, 128, 4, 64, 256, seed=34), 1100),   # sampled threshold active
     (_pcfg(520, 4, 2, 64, 4, 64, 100, dtype="f32", seed=35), 129),
+    # 300 new tokens after 8200: sets at the largest prefill M drawn from a
+    # long cached context
+    (_pcfg(8500, 8, 2, 128, 4, 64, 512, seed=37), 8200),
 ]
 
 
