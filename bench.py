@@ -710,6 +710,28 @@ def copy_calibration(nbytes=1 << 30):
     return nbytes
 
 
+def gather_sweep(mib=(1, 2, 4, 8, 16, 32), reps=5):
+    """Random 256-byte row gather rate (GB/s) against the table size, with the
+    gather probe of measure_peaks."""
+    import torch
+    from hybrid_linear_top_amd import lisa
+    src = torch.ones((max(mib) << 20) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(1 << 21, dtype=torch.float32, device="cuda")
+    out = {}
+    for m in mib:
+        times, work = [], 0.0
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            work = lisa.peak_probe(lisa.LISA_PROBE_GATHER, src, sink, m << 20, 8)
+            e1.record()
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        out[f"{m}_mib_gbs"] = round(work / (sorted(times)[len(times) // 2] * 1e-3) / 1e9, 1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -730,6 +752,8 @@ def main():
     ap.add_argument("--phase-markers", action="store_true",
                     help="launch a 4 KiB calibration copy before each phase (splits profiler databases)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak calibration")
+    ap.add_argument("--gather-sweep", action="store_true",
+                    help="print the row-gather probe's rate for tables of 1 to 32 MiB and exit")
     ap.add_argument("--counter-summary", nargs="+", metavar="DB",
                     help="kernel-trace database of a --phase-markers run, then one rocprofv3 --pmc database "
                          "per counter pass: write profiles/counters.json and the table, and exit")
@@ -764,6 +788,9 @@ def main():
     import torch
     torch.cuda.set_device(0)
     t_start = time.time()
+    if args.gather_sweep:
+        print(json.dumps({"gather_sweep": gather_sweep()}), flush=True)
+        return
     if args.copy_calibration:
         nb = copy_calibration()
         print(json.dumps({"copy_calibration_bytes": nb}), flush=True)
