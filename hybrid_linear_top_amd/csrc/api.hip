@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <atomic>
 #include <mutex>
@@ -42,6 +43,23 @@ constexpr int kMaxDecodeCtx = 65536;  // the select kernel keeps up to 64 keys p
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// LISA_LOG=1 in the environment: each call that passed its checks prints its
+// entry point and shapes to stderr before it enqueues (read once per process).
+bool log_on() {
+    static const bool on = [] {
+        const char *e = std::getenv("LISA_LOG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+void log_call(const char *what, const lisa_dims *d, int B, const char *k1, int64_t v1, const char *k2, int64_t v2) {
+    if (!log_on()) return;
+    std::fprintf(stderr,
+                 "lisa: %s B=%d %s=%lld %s=%lld heads=%d/%d d=%d indexer=%dx%d top_m=%d chunk=%d %s\n", what, B,
+                 k1, (long long)v1, k2, (long long)v2, d->num_q_heads, d->num_kv_heads, d->head_dim, d->idx_heads,
+                 d->idx_dim, d->top_m, d->chunk, d->dtype == LISA_BF16 ? "bf16" : "f32");
+}
 
 int elt_bytes(int dtype) { return dtype == LISA_BF16 ? 2 : 4; }
 
@@ -359,6 +377,7 @@ lisa_status prefill_impl(const lisa_dims *dims, int32_t B, int32_t past, int32_t
     const PrefillWs w = prefill_ws(dims, B, n, window ? n : past + n);
     if (workspace_bytes < w.total)
         return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+    log_call(window ? "prefill_window" : "prefill", dims, B, "past", past, "n", n);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const int G = dims->num_kv_heads, Hq = dims->num_q_heads, D = dims->head_dim;
@@ -512,6 +531,9 @@ lisa_status decode_impl(const lisa_dims *dims, int32_t B, const int64_t *cu_ctx,
         if (workspace_bytes < w.total)
             return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
     }
+    log_call(window ? "decode_step_window" : paged ? "decode_step_paged" : use_scratch ? "decode_step_noalloc"
+                                                                             : "decode_step",
+             dims, B, "max_ctx", max_ctx, "pool_rows", pool_rows);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const int G = dims->num_kv_heads, Hq = dims->num_q_heads, D = dims->head_dim;
@@ -782,6 +804,7 @@ lisa_status lisa_prefill_backward(const lisa_dims *dims, int32_t B, int32_t n, c
     const BwdWs w = bwd_ws(dims, B, n);
     if (workspace_bytes < w.total)
         return fail(LISA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+    log_call("prefill_backward", dims, B, "n", n, "state_grad", d_state_in != nullptr);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
 

@@ -46,6 +46,20 @@ class LisaError(RuntimeError):
         self.message = message
 
 
+# Tests set this to fill every buffer the binding allocates (outputs and
+# workspaces) with a poison pattern before the call, so that an element the
+# library fails to write shows up: 0xFF bytes (NaN) for floating-point and
+# workspace bytes, 0x7F bytes for int32 sets (-1 is their padding value).
+POISON_FRESH_BUFFERS = False
+
+
+def _fresh(t):
+    if POISON_FRESH_BUFFERS:
+        import torch
+        t.view(torch.uint8).fill_(0x7F if t.dtype == torch.int32 else 0xFF)
+    return t
+
+
 def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m hybrid_linear_top_amd.build`")
@@ -265,15 +279,15 @@ def prefill(dims: LisaDims, q, k, v, q_idx, k_idx, w_idx, gate, state_in=None, o
     B, n = int(q.shape[0]), int(q.shape[1])
     dev = q.device
     if out is None:
-        out = torch.empty_like(q)
+        out = _fresh(torch.empty_like(q))
     if state_out is None:
-        state_out = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
-                                dtype=torch.float32, device=dev)
+        state_out = _fresh(torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
+                                dtype=torch.float32, device=dev))
     if topm_out is None:
-        topm_out = torch.empty((B, n, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev)
+        topm_out = _fresh(torch.empty((B, n, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev))
     wsb = lisa_prefill_workspace_bytes(dims, B, n)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        workspace = _fresh(torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev))
     _check(lisa_prefill(dims, B, n, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
                         _ptr(w_idx), _ptr(gate), _ptr(state_in), _ptr(out), _ptr(state_out),
                         _ptr(topm_out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -290,15 +304,15 @@ def prefill_continue(dims: LisaDims, past: int, q, k_cache, v_cache, q_idx, k_id
     B, n = int(q.shape[0]), int(q.shape[1])
     dev = q.device
     if out is None:
-        out = torch.empty_like(q)
+        out = _fresh(torch.empty_like(q))
     if state_out is None:
-        state_out = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
-                                dtype=torch.float32, device=dev)
+        state_out = _fresh(torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
+                                dtype=torch.float32, device=dev))
     if topm_out is None:
-        topm_out = torch.empty((B, n, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev)
+        topm_out = _fresh(torch.empty((B, n, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev))
     wsb = lisa_prefill_continue_workspace_bytes(dims, B, past, n)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        workspace = _fresh(torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev))
     _check(lisa_prefill_continue(dims, B, past, n, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(q_idx), _ptr(k_idx_cache), _ptr(w_idx), _ptr(gate),
                                  _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(topm_out),
@@ -314,13 +328,13 @@ def prefill_window(dims: LisaDims, past: int, q, k_cache, v_cache, gate, state_i
     B, n = int(q.shape[0]), int(q.shape[1])
     dev = q.device
     if out is None:
-        out = torch.empty_like(q)
+        out = _fresh(torch.empty_like(q))
     if state_out is None:
-        state_out = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
-                                dtype=torch.float32, device=dev)
+        state_out = _fresh(torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim),
+                                dtype=torch.float32, device=dev))
     wsb = lisa_prefill_workspace_bytes(dims, B, n)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        workspace = _fresh(torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev))
     _check(lisa_prefill_window(dims, B, past, n, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(gate),
                                _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace),
                                workspace.numel(), _stream(stream)))
@@ -333,10 +347,10 @@ def decode_step_window(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache
     import torch
     B = int(q.shape[0])
     if out is None:
-        out = torch.empty_like(q)
+        out = _fresh(torch.empty_like(q))
     wsb = lisa_decode_workspace_bytes(dims, B, max_ctx)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+        workspace = _fresh(torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device))
     _check(lisa_decode_step_window(dims, B, _ptr(cu_ctx), max_ctx, _ptr(q), _ptr(k_cache),
                                    _ptr(v_cache), _ptr(gate), _ptr(state), _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -352,14 +366,14 @@ def prefill_backward(dims: LisaDims, q, k, v, gate, topm, d_out, state_in=None, 
     B, n = int(q.shape[0]), int(q.shape[1])
     dev = q.device
     f32 = dict(dtype=torch.float32, device=dev)
-    dq = torch.empty(tuple(q.shape), **f32)
-    dk = torch.empty(tuple(k.shape), **f32)
-    dv = torch.empty(tuple(v.shape), **f32)
-    dgate = torch.empty(tuple(gate.shape), **f32)
-    dsi = torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim), **f32) if want_state_grad else None
+    dq = _fresh(torch.empty(tuple(q.shape), **f32))
+    dk = _fresh(torch.empty(tuple(k.shape), **f32))
+    dv = _fresh(torch.empty(tuple(v.shape), **f32))
+    dgate = _fresh(torch.empty(tuple(gate.shape), **f32))
+    dsi = _fresh(torch.empty((B, dims.num_q_heads, dims.head_dim, dims.head_dim), **f32)) if want_state_grad else None
     wsb = lisa_prefill_backward_workspace_bytes(dims, B, n)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        workspace = _fresh(torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev))
     _check(lisa_prefill_backward(dims, B, n, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(state_in),
                                  _ptr(topm), _ptr(d_out), _ptr(d_state_out), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(dgate), _ptr(dsi), _ptr(workspace), workspace.numel(),
@@ -378,12 +392,12 @@ def decode_step_paged(dims: LisaDims, lengths, block_table, block_size: int, max
     max_blocks = int(block_table.shape[1])
     num_pages = int(k_pages.shape[0]) // block_size
     if out is None:
-        out = torch.empty_like(q)
+        out = _fresh(torch.empty_like(q))
     if topm_out is None:
-        topm_out = torch.empty((B, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=q.device)
+        topm_out = _fresh(torch.empty((B, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=q.device))
     wsb = lisa_decode_workspace_bytes(dims, B, max_ctx)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+        workspace = _fresh(torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device))
     _check(lisa_decode_step_paged(dims, B, _ptr(lengths), _ptr(block_table), block_size, max_blocks,
                                   num_pages, max_ctx, _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                   _ptr(q_idx), _ptr(k_idx_pages), _ptr(w_idx), _ptr(gate),
@@ -399,12 +413,12 @@ def decode_step(dims: LisaDims, cu_ctx, max_ctx: int, q, k_cache, v_cache, q_idx
     B = int(q.shape[0])
     dev = q.device
     if out is None:
-        out = torch.empty_like(q)
+        out = _fresh(torch.empty_like(q))
     if topm_out is None:
-        topm_out = torch.empty((B, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev)
+        topm_out = _fresh(torch.empty((B, dims.num_kv_heads, dims.top_m), dtype=torch.int32, device=dev))
     wsb = lisa_decode_workspace_bytes(dims, B, max_ctx)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        workspace = _fresh(torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev))
     _check(lisa_decode_step(dims, B, _ptr(cu_ctx), int(max_ctx), _ptr(q), _ptr(k_cache),
                             _ptr(v_cache), _ptr(q_idx), _ptr(k_idx_cache), _ptr(w_idx), _ptr(gate),
                             _ptr(state), _ptr(out), _ptr(topm_out), _ptr(workspace),

@@ -8,3 +8,22 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _poison_fresh_buffers(request):
+    """GPU tests: the binding fills every output and workspace it allocates
+    with a poison pattern first (NaN bytes; 0x7F in int32 sets), so an
+    element the library leaves unwritten fails the comparison."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    from hybrid_linear_top_amd import lisa
+    lisa.POISON_FRESH_BUFFERS = True
+    try:
+        yield
+    finally:
+        lisa.POISON_FRESH_BUFFERS = False
