@@ -45,6 +45,9 @@
  *   - Non-finite inputs are undefined behaviour (no fault, unspecified
  *     values).  The library allocates nothing; the workspace comes from the
  *     caller and must be at least the size the *_workspace_bytes query gives.
+ *   - With LISA_LOG=1 in the environment (read once per process), every call
+ *     that passed its checks prints one line to stderr naming the entry point
+ *     and its shapes, before it enqueues anything.
  *
  * Supported shapes: head_dim in {64, 128}; idx_dim in {32, 64};
  * 1 <= idx_heads <= 8; num_q_heads % num_kv_heads == 0 with r <= 16;
