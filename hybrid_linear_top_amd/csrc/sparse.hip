@@ -34,7 +34,9 @@ __device__ __forceinline__ f32x2 f32x2_hi(f32x4 v) { return f32x2{v[2], v[3]}; }
 
 template <typename T, int D, int NW>
 struct SparseSmem {
-    static constexpr int kVStride = D + 8 / Elt<T>::kBytes;  // row pad: 8 bytes
+    // row pad: bf16 32 bytes (the 4-row transposing reads of V^T are then
+    // conflict-free), fp32 8 bytes
+    static constexpr int kVStride = D + (Elt<T>::kBytes == 2 ? 16 : 2);
     static constexpr int kVBytes = NW * kChunk * kVStride * Elt<T>::kBytes;
     static constexpr int kMergeStride = 32 + 16 * (D + 1);  // max[16] sum[16] O[head][D+1]
     static constexpr int kMergeBytes = NW * kMergeStride * 4;
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
 
-        // --- stage the 32 V rows in LDS (row-major, rows padded by 8 bytes) --
+        // --- stage the 32 V rows in LDS (row-major, padded rows) ------------
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             unsigned char *row = reinterpret_cast<unsigned char *>(vs + (kb * 16 + col) * VS);
@@ -232,9 +234,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
             for (int kc = 0; kc < KC; ++kc) {
                 unsigned char *dst = row + (kc * 32 + grp * 8) * Elt<T>::kBytes;
                 if constexpr (Elt<T>::kBytes == 2) {
-                    const u32x4 raw = reinterpret_cast<const Frag<uint16_t> &>(vf8[kb][kc]).v;
-                    reinterpret_cast<u32x2 *>(dst)[0] = u32x2{raw[0], raw[1]};
-                    reinterpret_cast<u32x2 *>(dst)[1] = u32x2{raw[2], raw[3]};
+                    *reinterpret_cast<u32x4 *>(dst) = reinterpret_cast<const Frag<uint16_t> &>(vf8[kb][kc]).v;
                 } else {
                     const Frag<float> &ff = reinterpret_cast<const Frag<float> &>(vf8[kb][kc]);
                     reinterpret_cast<u32x2 *>(dst)[0] = __builtin_bit_cast(u32x2, f32x2_lo(ff.lo));
@@ -248,18 +248,37 @@ __global__ __launch_bounds__(NW * 64) void sparse_gate_kernel(SparseArgs a) {
         // --- O^T += V^T P^T --------------------------------------------------
         Frag<T> pf;
         pf.set(p);  // K-slot e <-> chunk slot (e<4 ? 4*grp+e : 16+4*grp+e-4)
+        if constexpr (Elt<T>::kBytes == 2 && NW <= 8) {
+            // V^T fragments by the transposing read (as in the prefill
+            // kernel): lane (col, grp) gets V[row][16 mb + col] for the rows
+            // of its K-slots, 4 grp .. +3 and 16 + 4 grp .. +3 (the 16-wave
+            // variant, at 128 VGPRs, keeps the element reads: this form
+            // spilled 35 registers there)
+            const unsigned char *vb = reinterpret_cast<const unsigned char *>(vs);
+            constexpr int VRB = VS * 2;  // row bytes
+            const int vr_base = (grp * 4 + (col >> 2)) * VRB + (col & 3) * 8;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int dim = mb * 16 + col;
-            T vv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = (e < 4) ? (grp * 4 + e) : (16 + grp * 4 + e - 4);
-                vv[e] = vs[row * VS + dim];
+            for (int mb = 0; mb < MB; ++mb) {
+                const u32x2 lo = lds_read_tr16(vb + vr_base + mb * 32);
+                const u32x2 hi = lds_read_tr16(vb + vr_base + 16 * VRB + mb * 32);
+                Frag<T> vf;
+                vf.v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                o[mb] = mma16(vf, pf, o[mb]);
             }
-            Frag<T> vf;
-            vf.set_bits(vv);
-            o[mb] = mma16(vf, pf, o[mb]);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int dim = mb * 16 + col;
+                T vv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int row = (e < 4) ? (grp * 4 + e) : (16 + grp * 4 + e - 4);
+                    vv[e] = vs[row * VS + dim];
+                }
+                Frag<T> vf;
+                vf.set_bits(vv);
+                o[mb] = mma16(vf, pf, o[mb]);
+            }
         }
         wave_lds_sync();
     }
