@@ -680,6 +680,22 @@ def test_prefill_negative_scores(cfg):
     _say("  ", rep)
 
 
+@pytest.mark.parametrize("case", _random_cases(83, 6), ids=lambda c: f"G{c[0]}r{c[1]}d{c[2]}s{c[6]}")
+def test_prefill_random_long_any_sign(case):
+    """Random shapes at lengths where late queries start from a sampled
+    threshold (and may trim or rescan), with head weights of either sign."""
+    G, r, d, dI, HI, dtype, seed = case
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1500, 3500))
+    M = int(rng.integers(1, 513))
+    w_dist = str(rng.choice(["u01", "signed", "neg"]))
+    cfg = _pcfg(n, G * r, G, d, HI, dI, M, dtype=dtype, seed=seed % 1000, w_dist=w_dist)
+    _say("prefill random long", cfg.name, "seed", cfg.seed)
+    rep = {}
+    parity.prefill_parity(cfg, gen.make_prefill_inputs(cfg), report=rep)
+    _say("  ", rep)
+
+
 @pytest.mark.parametrize("w_dist", ["signed", "neg"])
 @pytest.mark.parametrize("lengths", [[8000, 300], [17000], [33792, 18000], [40000, 5]],
                          ids=["ctx8000", "ctx17000", "ctx33792", "ctx40000"])
