@@ -50,6 +50,8 @@ PREFILL_SMALL = [
     _pcfg(1500, 12, 2, 128, 4, 64, 256, seed=7),  # several compactions per query
     _pcfg(300, 8, 2, 128, 4, 64, 130, seed=8),    # index rows not 16-byte aligned (M % 4 = 2)
     _pcfg(180, 6, 3, 64, 4, 32, 37, seed=9),      # d = 64 with odd M
+    _pcfg(1300, 4, 2, 128, 4, 64, 1, seed=10),    # M = 1: the argmax of every row (bf16)
+    _pcfg(900, 6, 2, 64, 2, 32, 2, seed=12),      # M = 2
 ]
 
 
@@ -151,6 +153,10 @@ DECODE_SMALL = [
     _dcfg(4, 1, 64, 4, 32, 512, [33792, 17409, 9000], seed=6),
     _dcfg(4, 2, 64, 2, 32, 64, [17409, 25000], seed=7),
     _dcfg(2, 1, 64, 1, 32, 256, [65536, 100], seed=9),         # the longest decode context
+    # degenerate set sizes: M = 1 (the argmax, lowest index on ties) and 2,
+    # at contexts that take the shortcut, the exact passes and the two parts
+    _dcfg(6, 2, 128, 4, 64, 1, [1, 5, 3000, 17000], seed=10),
+    _dcfg(4, 2, 64, 3, 32, 2, [2, 9000, 40000], seed=11),
 ]
 
 
